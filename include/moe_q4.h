@@ -1,0 +1,188 @@
+/*
+ * moe_q4.h -- C ABI of the MI355X (gfx950) sigmoid-routed Q4 MoE expert layer.
+ *
+ * The layer (sources are pages of pull-request text, cited by title):
+ *   - "feat(laguna): Laguna-S-2.1 decode on the CUDA engine"
+ *     (thewafflehaus/butter pull request 69): a hybrid MoE whose router is
+ *     a sigmoid top-10 with a score-correction bias, plus an always-on
+ *     shared expert; Q4-requantised expert weights; decode runs the experts
+ *     as gathered Q4 GEMVs, gate+up fused with SwiGLU, the shared expert in
+ *     the same gather.
+ *   - "feat(laguna): batched prefill with tensor-core projections, fused
+ *     MoE, CTA scheduling" (same pull request; thewafflehaus/FFAI pull
+ *     request 70): grouped-GEMM MoE with descriptors built on the device,
+ *     fused gate+up expert stacks, descending-size expert order and an
+ *     N-banded workgroup order for weight reuse in cache.
+ *   - thewafflehaus/FFAI pull request 72, the Nemotron MoE commits: CSR
+ *     offsets and router-sorted token indices, gather-on-read, a
+ *     deterministic non-atomic scatter-add, routed+shared summed before
+ *     anything else ("ffai_add3"), a K-loop that must not read past a
+ *     weight buffer (tile-select fix), and no device-to-host copy inside a
+ *     captured stream.
+ *
+ * What one layer call computes, for every token t (x_t in R^d):
+ *   l    = W_r x_t                       router logits, fp32 accumulate
+ *   s    = 1 / (1 + exp(-l))             sigmoid scores
+ *   sel  = the k experts with the largest s + b (ties: lower id first),
+ *          listed by descending s + b -- the bias b only selects
+ *   w_j  = s[sel_j] / sum_j s[sel_j]    unbiased, normalised to 1
+ *   h_e  = silu(W_g[e] x_t) * (W_u[e] x_t),  y_e = W_d[e] h_e
+ *   y_t  = (sum_{j=0..k-1} w_j * y_{sel_j}) + y_shared(x_t)
+ * Routed terms are summed in j order, then the shared expert is added.
+ * No float atomics anywhere: results are bitwise reproducible run to run.
+ *
+ * Conventions for every call
+ *   - Every array argument is a DEVICE pointer owned by the caller, who
+ *     keeps it alive until the work enqueued on `stream` has finished.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue kernels: they never allocate, free, synchronise or copy
+ *     device-to-host, so they can be captured into a HIP graph.
+ *   - All arguments are validated on the host before any HIP call; a
+ *     failed check returns a negative MOE_E* code and enqueues nothing.
+ *   - MOE_EHIP is returned when a kernel launch is rejected by the runtime
+ *     (the error reported by hipGetLastError right after the launch).
+ *   - Expert ids passed back in (topk_ids) must lie in [0, E); this is not
+ *     checked on the device.
+ *
+ * Storage formats
+ *   x         bf16 bit patterns, row-major [T][d]
+ *   w_router  float32 [E][d];   bias  float32 [E]
+ *   y         float32 [T][d]
+ *   Q4 matrix of shape [rows][K] (K % 32 == 0), two arrays:
+ *     qs      uint8 [rows][K/2]:  byte i of a row holds element 2i in its
+ *             low nibble and element 2i+1 in its high nibble
+ *     scales  uint16 [rows][K/32]: IEEE fp16 bits, one per 32-element block
+ *     value = (q - 8) * scale          (q the 4-bit code, 0..15)
+ *   w13  [E][2I][d]  gate rows 0..I-1, up rows I..2I-1 of every expert
+ *   w2   [E][d][I]
+ *   s13  [2*I_shared][d], s2 [d][I_shared]   (shared expert, same split)
+ *
+ * Two execution paths, chosen on the host from T alone (or forced by the
+ * flags below, identically in all three calls):
+ *   small-T path (T <= MOE_GEMV_MAX_T): the router runs as a GEMV, no
+ *     routing build is needed, and every (token, expert) pair streams its
+ *     expert rows through a fused dequant-GEMV with SwiGLU; the down
+ *     projection is fused with the combine.
+ *   grouped path (larger T): an MFMA router GEMM, an on-device routing
+ *     build (histogram, scan, stable scatter, group order, tile counts),
+ *     and grouped GEMMs that dequantise Q4 in registers into fp16 MFMA
+ *     operands, with the shared expert as one more always-present group,
+ *     then a fixed-order combine.
+ *   Activations feed the fp16 grouped GEMMs: |x| and the SwiGLU outputs
+ *   must stay within the fp16 range (65504) on that path.
+ */
+#ifndef MOE_Q4_H
+#define MOE_Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ---------------------------------------------------- */
+#define MOE_OK            0
+#define MOE_EINVAL       (-1)  /* null pointer, non-positive size, k > E          */
+#define MOE_EALIGN       (-2)  /* an array not 16-byte aligned                    */
+#define MOE_EUNSUPPORTED (-3)  /* d, I or I_shared not a multiple of 32, E > 1024,
+                                  k > 32, or a size beyond the chosen path's range */
+#define MOE_ENOSPACE     (-4)  /* routing workspace or scratch smaller than needed */
+#define MOE_EHIP         (-5)  /* the HIP runtime rejected a kernel launch          */
+
+/* ---- flags (pass the same value to all three calls) ------------------- */
+#define MOE_FLAG_DEFAULT      0u
+#define MOE_FLAG_FORCE_GROUPED 1u  /* grouped path even when T is small            */
+#define MOE_FLAG_FORCE_GEMV    2u  /* small-T path even when T is larger (T <= 64)  */
+#define MOE_FLAG_ID_ORDER      4u  /* schedule groups in id order, not by size     */
+#define MOE_FLAG_NO_BANDING    8u  /* M-tile-major workgroup order, not N-banded   */
+
+#define MOE_GEMV_MAX_T      8    /* default small-T threshold                       */
+#define MOE_GEMV_FORCE_MAX_T 64  /* largest T the small-T path accepts              */
+
+typedef struct moe_dims {
+  int32_t T;         /* tokens in this call                         */
+  int32_t d;         /* hidden size                                 */
+  int32_t E;         /* routed experts                              */
+  int32_t k;         /* experts chosen per token                    */
+  int32_t I;         /* routed expert intermediate size             */
+  int32_t I_shared;  /* shared expert intermediate size             */
+} moe_dims;
+
+typedef struct moe_q4 {
+  const uint8_t*  qs;      /* [rows][K/2] packed codes, 16-byte aligned      */
+  const uint16_t* scales;  /* [rows][K/32] fp16 bits, 16-byte aligned        */
+} moe_q4;
+
+typedef struct moe_q4_weights {
+  moe_q4 w13;  /* [E][2I][d]                */
+  moe_q4 w2;   /* [E][d][I]                 */
+  moe_q4 s13;  /* [2*I_shared][d]           */
+  moe_q4 s2;   /* [d][I_shared]             */
+} moe_q4_weights;
+
+/* Byte offsets of the regions inside the routing workspace, so that tests
+ * and tools can read what the routing build wrote.  Sizes are in elements.
+ * Pairs are p = t*k + j; groups are the E experts plus the shared expert
+ * as group E. */
+typedef struct moe_routing_layout {
+  size_t logits;       /* float [T][E]      router logits (scratch of moe_route) */
+  size_t counts;       /* int32 [E+1]       rows per group (group E = T)         */
+  size_t offsets;      /* int32 [E+1]       CSR exclusive prefix over experts     */
+  size_t sorted_pair;  /* int32 [P]         pair id at each sorted position       */
+  size_t pair_pos;     /* int32 [P]         sorted position of each pair          */
+  size_t row_expert;   /* int32 [P]         expert of each sorted position        */
+  size_t group_order;  /* int32 [E+1]       groups in schedule order              */
+  size_t mt_prefix;    /* int32 [E+2]       exclusive prefix of M-tiles per order */
+  size_t chunk_counts; /* int32 [chunks][E] per-chunk histogram (build scratch)   */
+  size_t total;        /* bytes required                                          */
+} moe_routing_layout;
+
+/* 0 when the shape is supported on the path `flags` selects, else a
+ * negative code.  Host only. */
+int moe_supports(const moe_dims* dims, uint32_t flags);
+
+/* Path `flags` selects for this shape: 0 = small-T GEMV path, 1 = grouped. */
+int moe_path(const moe_dims* dims, uint32_t flags);
+
+/* Routing workspace size in bytes (0 if the shape is unsupported). */
+size_t moe_routing_bytes(const moe_dims* dims, uint32_t flags);
+
+/* Fill `out` with the routing workspace layout.  Returns MOE_OK or a code. */
+int moe_routing_layout_of(const moe_dims* dims, uint32_t flags, moe_routing_layout* out);
+
+/* Scratch size in bytes needed by moe_q4_forward (0 if unsupported). */
+size_t moe_scratch_bytes(const moe_dims* dims, uint32_t flags);
+
+/* Router and expert selection.
+ * Writes topk_ids int32 [T][k] and topk_w float [T][k] (descending s + b;
+ * weights sum to 1).  Uses the logits region of `routing` as scratch. */
+int moe_route(const moe_dims* dims, const uint16_t* x_bf16, const float* w_router,
+              const float* bias, int32_t* topk_ids, float* topk_w,
+              void* routing, size_t routing_bytes, uint32_t flags, void* stream);
+
+/* Routing build for the grouped path: per-expert counts, CSR offsets, the
+ * stable (expert, token) order of the pairs and its inverse, the expert of
+ * every sorted row, the group schedule order (largest first, ties to the
+ * lower id; MOE_FLAG_ID_ORDER: id order) and the M-tile prefix.  On the
+ * small-T path it enqueues nothing and returns MOE_OK. */
+int moe_build_descriptors(const moe_dims* dims, const int32_t* topk_ids,
+                          void* routing, size_t routing_bytes, uint32_t flags,
+                          void* stream);
+
+/* Expert computation and combine: writes y float [T][d].
+ * `routing` must hold what moe_build_descriptors wrote for the same
+ * topk_ids (grouped path only); `scratch` holds intermediate activations
+ * and per-pair outputs and needs moe_scratch_bytes() bytes. */
+int moe_q4_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids,
+                   const float* topk_w, const void* routing, size_t routing_bytes,
+                   const moe_q4_weights* weights, float* y, void* scratch,
+                   size_t scratch_bytes, uint32_t flags, void* stream);
+
+/* Static string for a return code; never NULL. */
+const char* moe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_Q4_H */

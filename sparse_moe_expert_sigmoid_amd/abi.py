@@ -1,0 +1,188 @@
+"""ctypes binding of libmoe_q4.so: the C ABI of include/moe_q4.h, argument marshalling only.
+
+Array arguments may be torch tensors (their ``data_ptr()`` is passed) or raw
+integer device addresses.  ``stream=None`` means torch's current stream on
+the current device.  Every call raises MoeError on a non-zero return code
+unless ``check=False``, in which case the code is returned.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, c_char_p, c_int, c_int32, c_size_t, c_uint32, c_void_p
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(HERE, "libmoe_q4.so")
+
+MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EUNSUPPORTED, MOE_ENOSPACE, MOE_EHIP = 0, -1, -2, -3, -4, -5
+MOE_FLAG_DEFAULT = 0
+MOE_FLAG_FORCE_GROUPED = 1
+MOE_FLAG_FORCE_GEMV = 2
+MOE_FLAG_ID_ORDER = 4
+MOE_FLAG_NO_BANDING = 8
+MOE_GEMV_MAX_T = 8
+MOE_GEMV_FORCE_MAX_T = 64
+
+EXPORTED_SYMBOLS = (
+    "moe_supports", "moe_path", "moe_routing_bytes", "moe_routing_layout_of", "moe_scratch_bytes",
+    "moe_route", "moe_build_descriptors", "moe_q4_forward", "moe_strerror",
+)
+
+
+class Dims(Structure):
+    _fields_ = [("T", c_int32), ("d", c_int32), ("E", c_int32), ("k", c_int32), ("I", c_int32),
+                ("I_shared", c_int32)]
+
+    @classmethod
+    def of(cls, dims) -> "Dims":
+        if isinstance(dims, Dims):
+            return dims
+        return cls(dims.T, dims.d, dims.E, dims.k, dims.I, dims.I_shared)
+
+
+class _Q4(Structure):
+    _fields_ = [("qs", c_void_p), ("scales", c_void_p)]
+
+
+class _Weights(Structure):
+    _fields_ = [("w13", _Q4), ("w2", _Q4), ("s13", _Q4), ("s2", _Q4)]
+
+
+_LAYOUT_FIELDS = ("logits", "counts", "offsets", "sorted_pair", "pair_pos", "row_expert", "group_order",
+                  "mt_prefix", "chunk_counts", "total")
+
+
+class RoutingLayout(Structure):
+    _fields_ = [(n, c_size_t) for n in _LAYOUT_FIELDS]
+
+    def as_dict(self) -> dict:
+        return {n: int(getattr(self, n)) for n in _LAYOUT_FIELDS}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        super().__init__(f"{what}: {moe_strerror(code)} ({code})" if what else f"{moe_strerror(code)} ({code})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises ImportError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise ImportError(f"{lib_path} is missing: build it with `python -m sparse_moe_expert_sigmoid_amd.build`")
+    L = ctypes.CDLL(lib_path)
+    D = POINTER(Dims)
+    L.moe_supports.argtypes = [D, c_uint32]
+    L.moe_supports.restype = c_int
+    L.moe_path.argtypes = [D, c_uint32]
+    L.moe_path.restype = c_int
+    L.moe_routing_bytes.argtypes = [D, c_uint32]
+    L.moe_routing_bytes.restype = c_size_t
+    L.moe_routing_layout_of.argtypes = [D, c_uint32, POINTER(RoutingLayout)]
+    L.moe_routing_layout_of.restype = c_int
+    L.moe_scratch_bytes.argtypes = [D, c_uint32]
+    L.moe_scratch_bytes.restype = c_size_t
+    L.moe_route.argtypes = [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_uint32,
+                            c_void_p]
+    L.moe_route.restype = c_int
+    L.moe_build_descriptors.argtypes = [D, c_void_p, c_void_p, c_size_t, c_uint32, c_void_p]
+    L.moe_build_descriptors.restype = c_int
+    L.moe_q4_forward.argtypes = [D, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, POINTER(_Weights), c_void_p,
+                                 c_void_p, c_size_t, c_uint32, c_void_p]
+    L.moe_q4_forward.restype = c_int
+    L.moe_strerror.argtypes = [c_int]
+    L.moe_strerror.restype = c_char_p
+    _lib = L
+    return L
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _nbytes(a, given):
+    if given is not None:
+        return given
+    if a is None or isinstance(a, int):
+        return 0
+    return a.numel() * a.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _done(rc: int, check: bool, what: str) -> int:
+    if rc != MOE_OK and check:
+        raise MoeError(rc, what)
+    return rc
+
+
+def moe_strerror(code: int) -> str:
+    return lib().moe_strerror(code).decode()
+
+
+def moe_supports(dims, flags: int = 0) -> int:
+    return lib().moe_supports(ctypes.byref(Dims.of(dims)), flags)
+
+
+def moe_path(dims, flags: int = 0) -> int:
+    return lib().moe_path(ctypes.byref(Dims.of(dims)), flags)
+
+
+def moe_routing_bytes(dims, flags: int = 0) -> int:
+    return lib().moe_routing_bytes(ctypes.byref(Dims.of(dims)), flags)
+
+
+def moe_routing_layout_of(dims, flags: int = 0) -> dict:
+    out = RoutingLayout()
+    rc = lib().moe_routing_layout_of(ctypes.byref(Dims.of(dims)), flags, ctypes.byref(out))
+    _done(rc, True, "moe_routing_layout_of")
+    return out.as_dict()
+
+
+def moe_scratch_bytes(dims, flags: int = 0) -> int:
+    return lib().moe_scratch_bytes(ctypes.byref(Dims.of(dims)), flags)
+
+
+def moe_route(dims, x, w_router, bias, topk_ids, topk_w, routing, routing_bytes=None, flags: int = 0,
+              stream=None, check: bool = True) -> int:
+    rc = lib().moe_route(ctypes.byref(Dims.of(dims)), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(topk_ids),
+                         _ptr(topk_w), _ptr(routing), _nbytes(routing, routing_bytes), flags, _stream(stream))
+    return _done(rc, check, "moe_route")
+
+
+def moe_build_descriptors(dims, topk_ids, routing, routing_bytes=None, flags: int = 0, stream=None,
+                          check: bool = True) -> int:
+    rc = lib().moe_build_descriptors(ctypes.byref(Dims.of(dims)), _ptr(topk_ids), _ptr(routing),
+                                     _nbytes(routing, routing_bytes), flags, _stream(stream))
+    return _done(rc, check, "moe_build_descriptors")
+
+
+def _weights(w) -> _Weights:
+    """w: mapping with w13_qs, w13_sc, w2_qs, w2_sc, s13_qs, s13_sc, s2_qs, s2_sc."""
+    return _Weights(_Q4(_ptr(w["w13_qs"]), _ptr(w["w13_sc"])), _Q4(_ptr(w["w2_qs"]), _ptr(w["w2_sc"])),
+                    _Q4(_ptr(w["s13_qs"]), _ptr(w["s13_sc"])), _Q4(_ptr(w["s2_qs"]), _ptr(w["s2_sc"])))
+
+
+def moe_q4_forward(dims, x, topk_ids, topk_w, routing, weights, y, scratch, routing_bytes=None,
+                   scratch_bytes=None, flags: int = 0, stream=None, check: bool = True) -> int:
+    ws = weights if isinstance(weights, _Weights) else _weights(weights)
+    rc = lib().moe_q4_forward(ctypes.byref(Dims.of(dims)), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(routing),
+                              _nbytes(routing, routing_bytes), ctypes.byref(ws), _ptr(y), _ptr(scratch),
+                              _nbytes(scratch, scratch_bytes), flags, _stream(stream))
+    return _done(rc, check, "moe_q4_forward")

@@ -1,0 +1,66 @@
+// Host-visible launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Device pointers into the caller's routing workspace.
+struct Routing {
+  float* logits;       // [T][E]
+  int* counts;         // [E+1]
+  int* offsets;        // [E+1]
+  int* sorted_pair;    // [P]
+  int* pair_pos;       // [P]
+  int* row_expert;     // [P]
+  int* group_order;    // [E+1]
+  int* mt_prefix;      // [E+2]
+  int* chunk_counts;   // [chunks][E]
+};
+
+struct Shape {
+  int T, d, E, k, I, Is;
+};
+
+struct Q4 {
+  const uint8_t* qs;
+  const uint16_t* sc;
+};
+
+// router.hip
+hipError_t launch_router_gemv(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
+                              hipStream_t st);
+hipError_t launch_router_mfma(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
+                              hipStream_t st);
+hipError_t launch_topk(const Shape& s, const float* logits, const float* bias, int32_t* topk_ids, float* topk_w,
+                       hipStream_t st);
+
+// build.hip
+hipError_t launch_build(const Shape& s, const int32_t* topk_ids, const Routing& r, uint32_t flags,
+                        hipStream_t st);
+
+// gemv.hip  (small-T path)
+hipError_t launch_gemv_gateup(const Shape& s, const uint16_t* x, const int32_t* topk_ids, Q4 w13, Q4 s13,
+                              float* h_r, float* h_s, hipStream_t st);
+hipError_t launch_gemv_down_combine(const Shape& s, const int32_t* topk_ids, const float* topk_w, Q4 w2, Q4 s2,
+                                    const float* h_r, const float* h_s, float* y, hipStream_t st);
+
+// grouped.hip  (grouped path)
+struct GroupedOut {
+  _Float16* x16;   // [T][d]   fp16 copy of x
+  _Float16* h_r;   // [P][I]   sorted rows
+  _Float16* h_s;   // [T][Is]
+  float* y_pair;   // [P][d]   sorted rows
+  float* y_s;      // [T][d]
+};
+int grouped_max_mtiles(const Shape& s);
+hipError_t launch_grouped_gateup(const Shape& s, const uint16_t* x, const Routing& r, Q4 w13, Q4 s13,
+                                 const GroupedOut& o, uint32_t flags, hipStream_t st);
+hipError_t launch_grouped_down(const Shape& s, const Routing& r, Q4 w2, Q4 s2, const GroupedOut& o,
+                               uint32_t flags, hipStream_t st);
+hipError_t launch_combine(const Shape& s, const float* topk_w, const Routing& r, const GroupedOut& o, float* y,
+                          hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,66 @@
+"""Device buffers for one MoE layer and the three-call sequence route -> build -> forward.
+
+Marshalling only: every step of the layer runs in the HIP library.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import abi
+
+WEIGHT_KEYS = ("w13_qs", "w13_sc", "w2_qs", "w2_sc", "s13_qs", "s13_sc", "s2_qs", "s2_sc")
+
+
+def to_device(a: np.ndarray, device) -> torch.Tensor:
+    """numpy -> torch on `device`; uint16 bit patterns travel as int16 (same bytes)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+class DeviceWeights(dict):
+    """The router and expert arrays of one layer, resident on the GPU."""
+
+    @classmethod
+    def upload(cls, inp: dict, device="cuda") -> "DeviceWeights":
+        w = cls()
+        w.dims = inp["dims"]
+        w["w_router"] = to_device(inp["w_router"], device)
+        w["bias"] = to_device(inp["bias"], device)
+        for key in WEIGHT_KEYS:
+            w[key] = to_device(inp[key], device)
+        return w
+
+
+class Workspace:
+    """Outputs and caller-owned workspaces for a layer call of a given shape and flags."""
+
+    def __init__(self, dims, flags: int = 0, device="cuda"):
+        self.dims = dims
+        self.flags = flags
+        rc = abi.moe_supports(dims, flags)
+        if rc != abi.MOE_OK:
+            raise abi.MoeError(rc, "moe_supports")
+        T, k, d = dims.T, dims.k, dims.d
+        self.routing = torch.zeros(abi.moe_routing_bytes(dims, flags), dtype=torch.uint8, device=device)
+        self.scratch = torch.empty(max(abi.moe_scratch_bytes(dims, flags), 256), dtype=torch.uint8, device=device)
+        self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=device)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.y = torch.empty((T, d), dtype=torch.float32, device=device)
+        self.layout = abi.moe_routing_layout_of(dims, flags)
+
+    def routing_view(self, name: str, count: int, dtype=torch.int32) -> torch.Tensor:
+        off = self.layout[name]
+        nbytes = count * torch.tensor([], dtype=dtype).element_size()
+        return self.routing[off:off + nbytes].view(dtype)
+
+
+def layer_call(x: torch.Tensor, w: DeviceWeights, ws: Workspace, stream=None) -> torch.Tensor:
+    """Enqueue route, build and forward for tokens x (bf16 bits as int16 [T][d]); returns ws.y."""
+    dims, f = ws.dims, ws.flags
+    abi.moe_route(dims, x, w["w_router"], w["bias"], ws.topk_ids, ws.topk_w, ws.routing, flags=f, stream=stream)
+    abi.moe_build_descriptors(dims, ws.topk_ids, ws.routing, flags=f, stream=stream)
+    abi.moe_q4_forward(dims, x, ws.topk_ids, ws.topk_w, ws.routing, w, ws.y, ws.scratch, flags=f, stream=stream)
+    return ws.y

@@ -1,0 +1,170 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+entry point, sizes its workspaces as documented, and rejects bad arguments
+with the documented codes before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+import sparse_moe_expert_sigmoid_amd as moe
+from sparse_moe_expert_sigmoid_amd import abi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe_q4.h")
+BIG = synth.CONFIGS["prefill"].dims
+TINY = synth.CONFIGS["tiny"].dims
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced: every call below fails validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = abi.lib()
+    names = declared_functions()
+    assert set(names) == set(abi.EXPORTED_SYMBOLS), names
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_error_strings_are_total():
+    for code in (0, -1, -2, -3, -4, -5, -99, 7):
+        s = moe.moe_strerror(code)
+        assert isinstance(s, str) and s
+
+
+def d(**kw):
+    base = dict(T=TINY.T, d=TINY.d, E=TINY.E, k=TINY.k, I=TINY.I, I_shared=TINY.I_shared)
+    base.update(kw)
+    return abi.Dims(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), abi.MOE_EINVAL), (dict(d=0), abi.MOE_EINVAL), (dict(E=0), abi.MOE_EINVAL),
+    (dict(k=0), abi.MOE_EINVAL), (dict(k=17), abi.MOE_EINVAL), (dict(I=0), abi.MOE_EINVAL),
+    (dict(I_shared=-32), abi.MOE_EINVAL),
+    (dict(d=48), abi.MOE_EUNSUPPORTED), (dict(I=100), abi.MOE_EUNSUPPORTED), (dict(I_shared=40), abi.MOE_EUNSUPPORTED),
+    (dict(E=1025, k=4), abi.MOE_EUNSUPPORTED), (dict(E=64, k=33), abi.MOE_EUNSUPPORTED),
+])
+def test_supports_codes(kw, code):
+    assert moe.moe_supports(d(**kw)) == code
+    assert moe.moe_routing_bytes(d(**kw)) == 0
+    assert moe.moe_scratch_bytes(d(**kw)) == 0
+
+
+def test_flags_validation():
+    assert moe.moe_supports(TINY, abi.MOE_FLAG_FORCE_GEMV | abi.MOE_FLAG_FORCE_GROUPED) == abi.MOE_EINVAL
+    assert moe.moe_supports(TINY, 1 << 7) == abi.MOE_EINVAL
+    assert moe.moe_supports(BIG, abi.MOE_FLAG_FORCE_GEMV) == abi.MOE_EUNSUPPORTED  # T = 2048 > 64
+    assert moe.moe_supports(d(T=64, d=4096, E=256, k=10, I=1024, I_shared=1024), abi.MOE_FLAG_FORCE_GEMV) == 0
+    assert moe.moe_supports(d(d=16384), abi.MOE_FLAG_FORCE_GEMV) == abi.MOE_EUNSUPPORTED
+    assert moe.moe_supports(d(d=16384), abi.MOE_FLAG_FORCE_GROUPED) == 0
+
+
+def test_path_selection():
+    assert moe.moe_path(d(T=1)) == 0
+    assert moe.moe_path(d(T=abi.MOE_GEMV_MAX_T)) == 0
+    assert moe.moe_path(d(T=abi.MOE_GEMV_MAX_T + 1)) == 1
+    assert moe.moe_path(d(T=1), abi.MOE_FLAG_FORCE_GROUPED) == 1
+    assert moe.moe_path(d(T=40), abi.MOE_FLAG_FORCE_GEMV) == 0
+
+
+def align(v):
+    return (v + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("dims", [TINY, BIG, synth.CONFIGS["decode"].dims, synth.CONFIGS["long_prefill"].dims])
+def test_workspace_sizes_closed_form(dims):
+    T, E, k, dd, I, Is = dims.T, dims.E, dims.k, dims.d, dims.I, dims.I_shared
+    P = T * k
+    chunks = (T + 255) // 256
+    routing = (align(T * E * 4) + 2 * align((E + 1) * 4) + 3 * align(P * 4) + align((E + 1) * 4)
+               + align((E + 2) * 4) + align(chunks * E * 4))
+    assert moe.moe_routing_bytes(dims) == routing
+    lay = moe.moe_routing_layout_of(dims)
+    assert lay["total"] == routing and lay["logits"] == 0
+    offs = [lay[n] for n in ("logits", "counts", "offsets", "sorted_pair", "pair_pos", "row_expert",
+                             "group_order", "mt_prefix", "chunk_counts")]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    gemv = align(P * I * 4) + align(T * Is * 4)
+    grouped = align(T * dd * 2) + align(P * I * 2) + align(T * Is * 2) + align(P * dd * 4) + align(T * dd * 4)
+    want = gemv if moe.moe_path(dims) == 0 else grouped
+    assert moe.moe_scratch_bytes(dims) == want
+    assert moe.moe_scratch_bytes(dims, abi.MOE_FLAG_FORCE_GROUPED) == grouped
+
+
+WEIGHTS = {k: FAKE for k in ("w13_qs", "w13_sc", "w2_qs", "w2_sc", "s13_qs", "s13_sc", "s2_qs", "s2_sc")}
+R = 1 << 20
+
+
+def route(dims=TINY, **kw):
+    args = dict(x=FAKE, w_router=FAKE, bias=FAKE, topk_ids=FAKE, topk_w=FAKE, routing=FAKE, routing_bytes=R)
+    args.update(kw)
+    return moe.moe_route(dims, **args, stream=0, check=False)
+
+
+def test_route_validation():
+    assert route(dims=d(k=0)) == abi.MOE_EINVAL
+    for name in ("x", "w_router", "bias", "topk_ids", "topk_w", "routing"):
+        assert route(**{name: 0}) == abi.MOE_EINVAL, name
+    assert route(x=FAKE + 2) == abi.MOE_EALIGN
+    assert route(w_router=FAKE + 8) == abi.MOE_EALIGN
+    assert route(routing=FAKE + 4) == abi.MOE_EALIGN
+    assert route(bias=FAKE + 2) == abi.MOE_EALIGN
+    assert route(routing_bytes=moe.moe_routing_bytes(TINY) - 1) == abi.MOE_ENOSPACE
+
+
+def build(dims=TINY, flags=0, **kw):
+    args = dict(topk_ids=FAKE, routing=FAKE, routing_bytes=R)
+    args.update(kw)
+    return moe.moe_build_descriptors(dims, **args, flags=flags, stream=0, check=False)
+
+
+def test_build_validation():
+    assert build(topk_ids=0) == abi.MOE_EINVAL
+    assert build(routing=0) == abi.MOE_EINVAL
+    assert build(topk_ids=FAKE + 2) == abi.MOE_EALIGN
+    assert build(routing_bytes=16) == abi.MOE_ENOSPACE
+    assert build(flags=abi.MOE_FLAG_FORCE_GEMV | abi.MOE_FLAG_FORCE_GROUPED) == abi.MOE_EINVAL
+    # the small-T path needs no routing build: accepted, nothing enqueued
+    assert build(dims=d(T=1)) == abi.MOE_OK
+
+
+def forward(dims=TINY, flags=abi.MOE_FLAG_FORCE_GROUPED, weights=None, **kw):
+    args = dict(x=FAKE, topk_ids=FAKE, topk_w=FAKE, routing=FAKE, y=FAKE, scratch=FAKE, routing_bytes=R,
+                scratch_bytes=1 << 30)
+    args.update(kw)
+    return moe.moe_q4_forward(dims, weights=dict(WEIGHTS, **(weights or {})), **args, flags=flags, stream=0,
+                              check=False)
+
+
+def test_forward_validation():
+    for name in ("x", "topk_ids", "topk_w", "y", "scratch", "routing"):
+        assert forward(**{name: 0}) == abi.MOE_EINVAL, name
+    for name in WEIGHTS:
+        assert forward(weights={name: 0}) == abi.MOE_EINVAL, name
+        assert forward(weights={name: FAKE + 8}) == abi.MOE_EALIGN, name
+    assert forward(x=FAKE + 2) == abi.MOE_EALIGN
+    assert forward(y=FAKE + 4) == abi.MOE_EALIGN
+    assert forward(scratch=FAKE + 8) == abi.MOE_EALIGN
+    assert forward(scratch_bytes=moe.moe_scratch_bytes(TINY, abi.MOE_FLAG_FORCE_GROUPED) - 1) == abi.MOE_ENOSPACE
+    assert forward(routing_bytes=100) == abi.MOE_ENOSPACE
+    assert forward(dims=d(d=40)) == abi.MOE_EUNSUPPORTED
+    # the small-T path does not read the routing workspace
+    assert forward(flags=0, routing=0, scratch=0) == abi.MOE_EINVAL  # scratch is still required
+
+
+def test_header_documents_every_code():
+    text = open(HEADER).read()
+    for name, value in [("MOE_OK", 0), ("MOE_EINVAL", -1), ("MOE_EALIGN", -2), ("MOE_EUNSUPPORTED", -3),
+                        ("MOE_ENOSPACE", -4), ("MOE_EHIP", -5)]:
+        assert re.search(rf"#define {name}\s+\(?{value}\)?", text), name
+        assert getattr(abi, name) == value
+    for name in ("MOE_FLAG_FORCE_GROUPED", "MOE_FLAG_FORCE_GEMV", "MOE_FLAG_ID_ORDER", "MOE_FLAG_NO_BANDING",
+                 "MOE_GEMV_MAX_T"):
+        m = re.search(rf"#define {name}\s+(\d+)u?", text)
+        assert m and int(m.group(1)) == getattr(abi, name), name
+    assert ctypes.sizeof(abi.Dims) == 24

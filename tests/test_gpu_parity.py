@@ -1,0 +1,139 @@
+"""GPU parity of the HIP layer against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from sparse_moe_expert_sigmoid_amd import abi
+from sparse_moe_expert_sigmoid_amd.layer import DeviceWeights, Workspace, layer_call, to_device
+from gpu_util import check_parity, check_routing_build, run, say
+
+pytestmark = pytest.mark.gpu
+
+GROUPED = abi.MOE_FLAG_FORCE_GROUPED
+GEMV = abi.MOE_FLAG_FORCE_GEMV
+
+SMALL = {
+    # name: (dims, bias recipe)
+    "tiny": (synth.CONFIGS["tiny"].dims, "uniform"),
+    "ragged": (synth.Dims(T=37, d=96, E=20, k=3, I=160, I_shared=96), "uniform"),
+    "multi_tile": (synth.Dims(T=300, d=512, E=4, k=2, I=256, I_shared=384), "uniform"),
+    "single_expert": (synth.Dims(T=5, d=64, E=1, k=1, I=32, I_shared=64), "uniform"),
+    "full_mixture": (synth.Dims(T=9, d=128, E=6, k=6, I=64, I_shared=32), "uniform"),
+    "one_token": (synth.Dims(T=1, d=256, E=16, k=4, I=128, I_shared=128), "uniform"),
+    "skewed": (synth.Dims(T=200, d=256, E=32, k=4, I=96, I_shared=128), "zipf"),
+}
+
+
+@pytest.mark.parametrize("flags", [0, GROUPED, GEMV], ids=["default", "grouped", "gemv"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_shapes(name, flags):
+    dims, bias = SMALL[name]
+    if flags == GEMV and dims.T > abi.MOE_GEMV_FORCE_MAX_T:
+        pytest.skip("the small-T path is limited to T <= 64")
+    say(f"[case] small {name} flags={flags} dims={dims}")
+    inp = synth.make_inputs(dims, seed=100 + len(name), bias=bias)
+    ws, _ = run(inp, flags)
+    check_parity(inp, ws, label=f"{name}/{flags}")
+    if abi.moe_path(dims, flags) == 1:
+        check_routing_build(ws)
+
+
+def test_tiny_paths_agree_and_are_deterministic():
+    inp = synth.make_inputs(synth.CONFIGS["tiny"])
+    w = DeviceWeights.upload(inp)
+    x = to_device(inp["x"], "cuda")
+    a, _ = run(inp, 0, w, x)
+    b, _ = run(inp, 0, w, x)
+    assert torch.equal(a.y, b.y) and torch.equal(a.topk_ids, b.topk_ids)
+    g1, _ = run(inp, GROUPED, w, x)
+    g2, _ = run(inp, GROUPED, w, x)
+    assert torch.equal(g1.y, g2.y)
+    assert torch.equal(a.topk_ids, g1.topk_ids)
+    rel = (a.y - g1.y).norm() / g1.y.norm()
+    assert rel < 5e-3
+
+
+@pytest.mark.parametrize("flags", [GROUPED | abi.MOE_FLAG_ID_ORDER, GROUPED | abi.MOE_FLAG_NO_BANDING,
+                                   GROUPED | abi.MOE_FLAG_ID_ORDER | abi.MOE_FLAG_NO_BANDING])
+def test_schedule_order_does_not_change_bits(flags):
+    dims = synth.Dims(T=300, d=512, E=12, k=3, I=256, I_shared=384)
+    inp = synth.make_inputs(dims, seed=7, bias="zipf")
+    w = DeviceWeights.upload(inp)
+    x = to_device(inp["x"], "cuda")
+    base, _ = run(inp, GROUPED, w, x)
+    other, _ = run(inp, flags, w, x)
+    check_routing_build(other)
+    assert torch.equal(base.y, other.y)
+
+
+@pytest.mark.parametrize("flags", [0, GROUPED])
+def test_doubling_down_scales_doubles_output(flags):
+    dims = synth.Dims(T=24, d=256, E=8, k=2, I=128, I_shared=64)
+    inp = synth.make_inputs(dims, seed=9)
+    a, w = run(inp, flags)
+    inp2 = dict(inp)
+    for key in ("w2_sc", "s2_sc"):
+        inp2[key] = (inp[key].view(np.float16) * np.float16(2)).view(np.uint16)
+    b, _ = run(inp2, flags)
+    assert torch.equal(b.y, 2 * a.y)
+
+
+@pytest.mark.parametrize("flags", [0, GROUPED])
+def test_graph_capture_replays_match_eager(flags):
+    dims = synth.Dims(T=6 if flags == 0 else 150, d=256, E=16, k=4, I=128, I_shared=128)
+    inp = synth.make_inputs(dims, seed=11)
+    w = DeviceWeights.upload(inp)
+    x = to_device(inp["x"], "cuda")
+    eager, _ = run(inp, flags, w, x)
+    ref = eager.y.clone()
+    ws = Workspace(dims, flags)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer_call(x, w, ws, stream=s)  # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        layer_call(x, w, ws, stream=s)
+    for i in range(3):
+        ws.y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ws.y, ref), f"replay {i}"
+        _ = (ws.y * 2).sum().item()  # eager work between replays
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+def sample_tokens(T, n, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(T, size=min(n, T), replace=False).tolist()) | {0, T - 1} | set(int(e) for e in extra)
+    return np.array(sorted(pick))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["decode", "batched_decode", "prefill", "long_prefill"])
+def test_full_size_workloads(name):
+    cfg = synth.CONFIGS[name]
+    say(f"[case] full {name} dims={cfg.dims}")
+    inp = synth.make_inputs(cfg)
+    ws, w = run(inp, 0)
+    T = cfg.dims.T
+    extra = inp["outlier_rows"][:4] if len(inp["outlier_rows"]) else ()
+    tokens = np.arange(T) if T <= 1 else sample_tokens(T, 12, 5, extra)
+    check_parity(inp, ws, tokens=tokens, label=name)
+    if abi.moe_path(cfg.dims) == 1:
+        check_routing_build(ws)
+        counts = ws.routing_view("counts", cfg.dims.E).cpu().numpy()
+        say(f"[groups] {name}: distinct={int((counts > 0).sum())} max={counts.max()} median={int(np.median(counts))}")
+    # bitwise reproducible
+    x = to_device(inp["x"], "cuda")
+    again, _ = run(inp, 0, w, x)
+    assert torch.equal(again.y, ws.y)
+    if T == 64:
+        gemv, _ = run(inp, GEMV, w, x)
+        assert torch.equal(gemv.topk_ids, ws.topk_ids)
+        check_parity(inp, gemv, tokens=tokens, label=name + "/gemv")
