@@ -1,0 +1,395 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X Q4 MoE expert layer (route -> build -> forward) on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|batched_decode|prefill|long_prefill]
+
+One step is one call of the whole layer on one batch of synthetic tokens:
+moe_route + moe_build_descriptors + moe_q4_forward.  Steps are captured in
+a HIP graph that cycles through L independent layer copies (weights and
+tokens), so that successive steps do not find the previous step's weights
+in the 256 MB MALL, as in a model with many layers.  W warm-up steps run
+first, then exactly K steps are timed with HIP events on the launch stream,
+bracketed by device synchronisation.
+
+The primary workload (default: single-token decode, d=4096, E=256, top-10,
+I=1024, shared I=1024) gives `value`; the 2048-token prefill chunk is
+measured the same way and reported under `secondary`.  Per-kernel average
+durations come from graphs that replay only that kernel's nodes, extracted
+from the captured layer graph, timed with HIP events on the same stream.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at T=1 and T=2048; % HBM roofline / % bf16 MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+COPIES = {"decode": 8, "batched_decode": 8, "prefill": 2, "long_prefill": 2}
+
+
+# ----------------------------------------------------------------------------- HIP graph helpers (ctypes)
+
+class _KernelNodeParams(ctypes.Structure):
+    _fields_ = [("blockDim", ctypes.c_uint * 3), ("extra", ctypes.c_void_p), ("func", ctypes.c_void_p),
+                ("gridDim", ctypes.c_uint * 3), ("kernelParams", ctypes.c_void_p),
+                ("sharedMemBytes", ctypes.c_uint)]
+
+
+class Hip:
+    """The HIP runtime already loaded in this process (torch's), for graph capture and node surgery."""
+
+    def __init__(self):
+        path = None
+        for line in open("/proc/self/maps"):
+            if "libamdhip64.so" in line:
+                path = line.split()[-1]
+                break
+        self.L = ctypes.CDLL(path or "libamdhip64.so")
+        self.live = []
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with hipError {rc}")
+
+    def begin_capture(self, stream: int):
+        self._ok(self.L.hipStreamBeginCapture(ctypes.c_void_p(stream), 2), "hipStreamBeginCapture")  # relaxed
+
+    def end_capture(self, stream: int) -> ctypes.c_void_p:
+        g = ctypes.c_void_p()
+        self._ok(self.L.hipStreamEndCapture(ctypes.c_void_p(stream), ctypes.byref(g)), "hipStreamEndCapture")
+        self.live.append(g)
+        return g
+
+    def instantiate(self, graph) -> ctypes.c_void_p:
+        ex = ctypes.c_void_p()
+        self._ok(self.L.hipGraphInstantiate(ctypes.byref(ex), graph, None, None, ctypes.c_size_t(0)),
+                 "hipGraphInstantiate")
+        return ex
+
+    def launch(self, exec_, stream: int):
+        self._ok(self.L.hipGraphLaunch(exec_, ctypes.c_void_p(stream)), "hipGraphLaunch")
+
+    def kernel_nodes(self, graph, stream: int):
+        """[(kernel name, params)] of the graph's kernel nodes, in graph order."""
+        n = ctypes.c_size_t(0)
+        self._ok(self.L.hipGraphGetNodes(graph, None, ctypes.byref(n)), "hipGraphGetNodes")
+        nodes = (ctypes.c_void_p * n.value)()
+        self._ok(self.L.hipGraphGetNodes(graph, nodes, ctypes.byref(n)), "hipGraphGetNodes")
+        self.L.hipKernelNameRefByPtr.restype = ctypes.c_char_p
+        out = []
+        for node in nodes:
+            t = ctypes.c_int(-1)
+            self._ok(self.L.hipGraphNodeGetType(ctypes.c_void_p(node), ctypes.byref(t)), "hipGraphNodeGetType")
+            if t.value != 0:  # hipGraphNodeTypeKernel
+                continue
+            p = _KernelNodeParams()
+            self._ok(self.L.hipGraphKernelNodeGetParams(ctypes.c_void_p(node), ctypes.byref(p)),
+                     "hipGraphKernelNodeGetParams")
+            name = self.L.hipKernelNameRefByPtr(ctypes.c_void_p(p.func), ctypes.c_void_p(stream))
+            out.append(((name or b"?").decode(), p))
+        return out
+
+    def chain_graph(self, params_list):
+        """A new graph running the given kernel nodes one after another."""
+        g = ctypes.c_void_p()
+        self._ok(self.L.hipGraphCreate(ctypes.byref(g), ctypes.c_uint(0)), "hipGraphCreate")
+        prev = None
+        for p in params_list:
+            node = ctypes.c_void_p()
+            deps = (ctypes.c_void_p * 1)(prev) if prev is not None else None
+            self._ok(self.L.hipGraphAddKernelNode(ctypes.byref(node), g, deps, ctypes.c_size_t(1 if deps else 0),
+                                                  ctypes.byref(p)), "hipGraphAddKernelNode")
+            prev = node
+        self.live.append(g)
+        return g
+
+
+def short_name(mangled: str) -> str:
+    for key, nice in (("k_router_gemv", "router_gemv"), ("k_router_mfma", "router_mfma"), ("k_topk", "topk"),
+                      ("k_build_count", "build_count"), ("k_build_scatter", "build_scatter"),
+                      ("k_gemv_gateup", "gemv_gateup"), ("k_gemv_down_combine", "gemv_down_combine"),
+                      ("k_x_to_f16", "x_to_f16"), ("k_groupedILb1", "grouped_gateup"),
+                      ("k_groupedILb0", "grouped_down"), ("k_combine", "combine")):
+        if key in mangled:
+            return nice
+    return mangled
+
+
+# ----------------------------------------------------------------------------- workload
+
+def device_copy(cfg, seed, torch, device):
+    """A further independent layer copy drawn on the GPU with torch's seeded generator, with the
+    same distributions as the numpy generator (x ~ N(0,1) -> bf16, W_r ~ N(0, 0.02), Q4 codes uniform,
+    scales ~ U(0.005, 0.02) -> fp16, bias per the workload's recipe)."""
+    dims = cfg.dims
+    T, d, E, I, Is = dims.T, dims.d, dims.E, dims.I, dims.I_shared
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def qs(*shape):
+        return torch.randint(0, 256, shape, dtype=torch.uint8, device=device, generator=g)
+
+    def sc(*shape):
+        return (torch.rand(shape, device=device, generator=g) * 0.015 + 0.005).half().view(torch.int16)
+
+    x = torch.randn((T, d), device=device, generator=g)
+    if cfg.outlier_frac:
+        n_out = int(round(cfg.outlier_frac * T))
+        rows = torch.randperm(T, device=device, generator=g)[:n_out]
+        x[rows] *= 8.0
+    w = {
+        "w_router": torch.randn((E, d), device=device, generator=g) * 0.02,
+        "w13_qs": qs(E, 2 * I, d // 2), "w13_sc": sc(E, 2 * I, d // 32),
+        "w2_qs": qs(E, d, I // 2), "w2_sc": sc(E, d, I // 32),
+        "s13_qs": qs(2 * Is, d // 2), "s13_sc": sc(2 * Is, d // 32),
+        "s2_qs": qs(d, Is // 2), "s2_sc": sc(d, Is // 32),
+    }
+    if cfg.bias == "zipf":
+        pmf = np.arange(1, E + 1, dtype=np.float64) ** -1.2
+        pmf /= pmf.sum()
+        perm = torch.randperm(E, device=device, generator=g)
+        b = torch.empty(E, device=device)
+        b[perm] = torch.tensor(pmf, dtype=torch.float32, device=device)
+        w["bias"] = b
+    else:
+        w["bias"] = torch.rand(E, device=device, generator=g) * 0.2 - 0.1
+    return x.bfloat16().view(torch.int16), w
+
+
+def expert_bytes(dims):
+    gu = 2 * dims.I * dims.d // 2 + 2 * dims.I * dims.d // 32 * 2
+    dn = dims.d * dims.I // 2 + dims.d * dims.I // 32 * 2
+    sgu = 2 * dims.I_shared * dims.d // 2 + 2 * dims.I_shared * dims.d // 32 * 2
+    sdn = dims.d * dims.I_shared // 2 + dims.d * dims.I_shared // 32 * 2
+    return gu, dn, sgu, sdn
+
+
+def layer_flops(dims):
+    T, d, E, P, I, Is = dims.T, dims.d, dims.E, dims.T * dims.k, dims.I, dims.I_shared
+    router = 2 * T * d * E
+    routed = 2 * P * (2 * I * d + d * I)
+    shared = 2 * T * (2 * Is * d + d * Is)
+    return router, routed, shared
+
+
+def source_hash(*files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_sample=False):
+    cfg = synth.CONFIGS[name]
+    dims = cfg.dims
+    device = "cuda"
+    L = COPIES[name]
+    inp0 = synth.make_inputs(cfg)
+    weights = [layer.DeviceWeights.upload(inp0)]
+    xs = [layer.to_device(inp0["x"], device)]
+    for c in range(1, L):
+        x, w = device_copy(cfg, 7000 + 100 * c + cfg.index, torch, device)
+        dw = layer.DeviceWeights()
+        dw.update(w)
+        dw.dims = dims
+        weights.append(dw)
+        xs.append(x)
+    spaces = [layer.Workspace(dims, 0) for _ in range(L)]
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for c in range(L):  # eager pass: surfaces launch errors outside capture
+            layer.layer_call(xs[c], weights[c], spaces[c], stream=sh)
+    torch.cuda.synchronize()
+
+    def capture(copies):
+        hip.begin_capture(sh)
+        for c in copies:
+            layer.layer_call(xs[c], weights[c], spaces[c], stream=sh)
+        g = hip.end_capture(sh)
+        return g, hip.instantiate(g)
+
+    full_graph, full_exec = capture(range(L))
+    rem = steps % L
+    rem_exec = capture(range(rem))[1] if rem else None
+
+    def run_steps(n):
+        for _ in range(n // L):
+            hip.launch(full_exec, sh)
+        if n % L:
+            hip.launch(rem_exec if n % L == rem else capture(range(n % L))[1], sh)
+
+    with torch.cuda.stream(stream):
+        run_steps(warmup)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    run_steps(steps)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    ms_per_step = ms / steps
+
+    # per-kernel average durations from graphs of that kernel's nodes alone
+    nodes = hip.kernel_nodes(full_graph, sh)
+    by_kernel = {}
+    for kname, p in nodes:
+        by_kernel.setdefault(short_name(kname), []).append(p)
+    kernel_us = {}
+    reps = 50
+    for kname, plist in by_kernel.items():
+        ex = hip.instantiate(hip.chain_graph(plist))
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                hip.launch(ex, sh)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            hip.launch(ex, sh)
+        b.record(stream)
+        torch.cuda.synchronize()
+        kernel_us[kname] = a.elapsed_time(b) * 1000.0 / (reps * len(plist))
+
+    # routing statistics of copy 0 (distinct experts decide the bytes a call must read)
+    ids = spaces[0].topk_ids.cpu().numpy()
+    distinct = int(np.unique(ids).size)
+    gu, dn, sgu, sdn = expert_bytes(dims)
+    T, d, E, P = dims.T, dims.d, dims.E, dims.T * dims.k
+    layer_bytes = (E * d * 4 + E * 4 + T * d * 2 + distinct * (gu + dn) + (sgu + sdn) + T * d * 4
+                   + P * 8)
+    router, routed, shared = layer_flops(dims)
+    layer_flop = router + routed + shared
+    path = abi.moe_path(dims, 0)
+    tokens_per_s = T / (ms_per_step / 1000.0)
+    res = {
+        "workload": name, "dims": dict(T=T, d=d, E=E, k=dims.k, I=dims.I, I_shared=dims.I_shared),
+        "path": "gemv" if path == 0 else "grouped", "layer_copies": L, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_per_step, "tokens_per_s": tokens_per_s, "distinct_experts": distinct,
+        "kernel_avg_us": {k: round(v, 3) for k, v in kernel_us.items()},
+        "layer_algorithmic_bytes": layer_bytes, "layer_algorithmic_flop": layer_flop,
+        "layer_hbm_frac": layer_bytes / (ms_per_step / 1000.0) / (HBM_PEAK_GBS * 1e9),
+        "layer_mfma_frac": layer_flop / (ms_per_step / 1000.0) / (MFMA_F16_PEAK_TFLOPS * 1e12),
+    }
+    if path == 0:
+        kname = "gemv_gateup"
+        per_launch = T * dims.k * gu + T * sgu + T * d * 2 + (P * dims.I + T * dims.I_shared) * 4
+        achieved = per_launch / (kernel_us[kname] * 1e-6) / 1e9
+        res["roofline"] = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                           "algorithmic_bytes_per_launch": per_launch,
+                           "avg_launch_us": round(kernel_us[kname], 3)}
+    else:
+        kname = "grouped_gateup"
+        per_launch = 2 * (P * 2 * dims.I + T * 2 * dims.I_shared) * d
+        achieved = per_launch / (kernel_us[kname] * 1e-6) / 1e12
+        res["roofline"] = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),
+                           "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                           "algorithmic_flop_per_launch": per_launch, "avg_launch_us": round(kernel_us[kname], 3)}
+    res["_inp0"] = inp0
+    return res
+
+
+def cpu_baseline(inp, budget_s=15.0):
+    """The oracle as it stands, on the host, on a bounded sample of the primary workload's tokens."""
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    T = inp["dims"].T
+    done, t0 = 0, time.perf_counter()
+    calls = 0
+    while True:
+        tokens = np.arange(T) if T <= 16 else np.arange(16) + (16 * calls) % max(T - 16, 1)
+        oracle.forward(inp, tokens=tokens)
+        done += len(tokens)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 50:
+            break
+    return {"value": round(done / el, 4), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{calls} oracle layer calls of {len(tokens)} token(s) each on the workload's layer copy 0, "
+                      f"{el:.1f} s wall on the host"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=800)
+    ap.add_argument("--warmup", type=int, default=80)
+    ap.add_argument("--workload", default="decode", choices=["decode", "batched_decode", "prefill", "long_prefill"])
+    ap.add_argument("--secondary", default="prefill", help="second workload reported alongside ('none' to skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this layer is built and measured on a single MI355X; "
+              "multi-GPU (expert-parallel) runs are not part of it. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from sparse_moe_expert_sigmoid_amd import abi, layer
+    abi.lib()  # fails loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(3)
+    hip = Hip()
+    prim = run_workload(args.workload, args.steps, args.warmup, torch, hip, abi, layer, synth)
+    sec = None
+    if args.secondary and args.secondary != "none" and args.secondary != args.workload:
+        n = max(20, args.steps // 40)
+        sec = run_workload(args.secondary, n, max(4, n // 10), torch, hip, abi, layer, synth)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(prim["_inp0"])
+    dims = prim["dims"]
+    out = {
+        "metric": METRIC,
+        "value": round(prim["tokens_per_s"], 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(prim["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if prim["path"] == "gemv" else "f16",
+        "data": "synthetic (seeded; Q4 codes uniform, fp16 scales U(0.005,0.02), x N(0,1) bf16)",
+        "config": {"workload": f"{args.workload}: T={dims['T']} d={dims['d']} E={dims['E']} top-{dims['k']} "
+                               f"I={dims['I']} shared I={dims['I_shared']} Q4 block-32",
+                   "path": prim["path"], "layer_copies": prim["layer_copies"], "parallelism": "single GPU"},
+        "roofline": prim["roofline"],
+        "cpu_baseline": cpu,
+        "layer": {k: prim[k] for k in ("layer_hbm_frac", "layer_mfma_frac", "layer_algorithmic_bytes",
+                                       "layer_algorithmic_flop", "distinct_experts", "kernel_avg_us")},
+        "kernel_sources": source_hash("sparse_moe_expert_sigmoid_amd/csrc/gemv.hip",
+                                      "sparse_moe_expert_sigmoid_amd/csrc/grouped.hip"),
+    }
+    if sec is not None:
+        sec.pop("_inp0", None)
+        out["secondary"] = sec
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
