@@ -11,7 +11,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/moe_q4.h"
+#include "moe_q4.h"
 #include "moe_kernels.hpp"
 
 namespace {

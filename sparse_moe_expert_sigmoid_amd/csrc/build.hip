@@ -22,7 +22,7 @@
 // result does not depend on scheduling or atomic order.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
-#include "../../include/moe_q4.h"
+#include "moe_q4.h"
 
 namespace moe {
 

@@ -49,55 +49,57 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
   const int i0 = blockIdx.x * 16 + wave * 4;
   if (i0 >= Iw) return;  // Iw % 32 == 0: a wavefront's 4 rows are all valid or all past the end
   const int nb = d / 32;
-
-  // activation pairs and per-block sums for this lane's blocks
-  uint32_t xp[NCH][2][4][4];
-  float xs[NCH][2];
-  const uint16_t* xr = x + (size_t)t * d;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c)
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      const int b = 128 * c + 2 * lane + bb;
-      float sum = 0.f;
-#pragma unroll
-      for (int dw = 0; dw < 4; ++dw) {
-        u32x4 u = {0u, 0u, 0u, 0u};
-        if (b < nb) u = ld16(xr + 32 * b + 8 * dw);
-        x_bf16_pairs(u, xp[c][bb][dw]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          sum += bf16_bits_to_float(u[m] & 0xFFFFu) + bf16_bits_to_float(u[m] >> 16);
-      }
-      xs[c][bb] = sum;
-    }
+  const size_t qstride = d / 2, sstride = d / 32;
 
   float acc[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) acc[r] = 0.f;
-  const size_t qstride = d / 2, sstride = d / 32;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int b0 = 128 * c + 2 * lane;
-    const bool ok0 = b0 < nb, ok1 = b0 + 1 < nb;  // nb may be odd: each block is guarded
+    // Block indices past the row end are clamped to a valid block (so every load is issued
+    // unconditionally and stays in bounds) and their contribution is masked to zero.
+    int bi[2];
+    bool ok[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int b = 128 * c + 2 * lane + bb;
+      ok[bb] = b < nb;
+      bi[bb] = ok[bb] ? b : nb - 1;
+    }
+    // 1) activation slices of this lane's blocks (L2-resident), issued first
+    u32x4 u[2][4];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int dw = 0; dw < 4; ++dw) u[bb][dw] = ld16(x + (size_t)t * d + 32 * bi[bb] + 8 * dw);
+    // 2) weight codes and scales of 8 rows: all loads in flight before any arithmetic
     u32x4 q[8][2];
-    uint32_t sv[8];
+    uint32_t sv[8][2];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int row = (r < 4) ? (i0 + r) : (Iw + i0 + r - 4);
-      const uint8_t* p = qs + row * qstride + 16 * (size_t)b0;
-      const uint16_t* sp = sc + row * sstride + b0;  // d/32 may be odd: 16-bit scale loads
-      q[r][0] = q[r][1] = u32x4{0u, 0u, 0u, 0u};
-      sv[r] = 0u;
-      if (ok0) {
-        q[r][0] = ld16(p);
-        sv[r] = (uint32_t)sp[0];
-      }
-      if (ok1) {
-        q[r][1] = ld16(p + 16);
-        sv[r] |= (uint32_t)sp[1] << 16;
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        q[r][bb] = ld16(qs + row * qstride + 16 * (size_t)bi[bb]);
+        sv[r][bb] = sc[row * sstride + bi[bb]];
       }
     }
+    // 3) activation pairs and block sums
+    uint32_t xp[2][4][4];
+    float xs[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      float sum = 0.f;
+#pragma unroll
+      for (int dw = 0; dw < 4; ++dw) {
+        x_bf16_pairs(u[bb][dw], xp[bb][dw]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          sum += bf16_bits_to_float(u[bb][dw][m] & 0xFFFFu) + bf16_bits_to_float(u[bb][dw][m] >> 16);
+      }
+      xs[bb] = ok[bb] ? sum : 0.f;
+    }
+    // 4) dot products
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
 #pragma unroll
@@ -108,10 +110,10 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
           uint32_t cp[4];
           codes_bf16_pairs(q[r][bb][dw], cp);
 #pragma unroll
-          for (int m = 0; m < 4; ++m) dot = dot2_bf16(cp[m], xp[c][bb][dw][m], dot);
+          for (int m = 0; m < 4; ++m) dot = dot2_bf16(cp[m], xp[bb][dw][m], dot);
         }
-        const float dsc = fp16_bits_to_float(bb ? (sv[r] >> 16) : (sv[r] & 0xFFFFu));
-        acc[r] = fmaf(dsc, fmaf(16.f, dot, -24.f * xs[c][bb]), acc[r]);
+        const float dsc = ok[bb] ? fp16_bits_to_float(sv[r][bb]) : 0.f;
+        acc[r] = fmaf(dsc, fmaf(16.f, dot, -24.f * xs[bb]), acc[r]);
       }
     }
   }
@@ -167,16 +169,25 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
       h = h_s + (size_t)t * Is;
     }
     const int nbk = Kw / 32;
+    const size_t qstride = Kw / 2, sstride = Kw / 32;
+    // clamped block and row indices: every load is issued unconditionally and stays in bounds
+    int bi[NCH];
+    bool ok[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int b = bl + 32 * c;
+      ok[c] = b < nbk;
+      bi[c] = ok[c] ? b : nbk - 1;
+    }
+    // 1) the matching h values (L2-resident)
     float hv[NCH][32];
     float hsum[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int b = bl + 32 * c;
       float s = 0.f;
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
-        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (b < nbk) f = *reinterpret_cast<const float4*>(h + 32 * b + 4 * v);
+        const float4 f = *reinterpret_cast<const float4*>(h + 32 * bi[c] + 4 * v);
         hv[c][4 * v + 0] = f.x;
         hv[c][4 * v + 1] = f.y;
         hv[c][4 * v + 2] = f.z;
@@ -185,34 +196,43 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
       }
       hsum[c] = s;
     }
-    const size_t qstride = Kw / 2, sstride = Kw / 32;
-#pragma unroll 2
-    for (int rr = 0; rr < 8; ++rr) {
-      const int n = n0 + 2 * rr + half;
-      float acc = 0.f;
-      if (n < d) {
+    constexpr int RB = 8 / NCH;  // rows per load batch
+#pragma unroll
+    for (int r0 = 0; r0 < 8; r0 += RB) {
+      // 2) codes and scales of RB rows for this lane's blocks, all in flight together
+      u32x4 q[RB][NCH];
+      uint32_t sv[RB][NCH];
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        const int n = min(n0 + 2 * (r0 + rr) + half, d - 1);
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          const int b = bl + 32 * c;
-          if (b < nbk) {
-            const u32x4 q = ld16(qs + n * qstride + 16 * (size_t)b);
-            const float dsc = fp16_bits_to_float(sc[n * sstride + b]);
-            float dot = 0.f;
-#pragma unroll
-            for (int dw = 0; dw < 4; ++dw) {
-              const uint32_t lo = q[dw] & 0x0F0F0F0Fu, hi = (q[dw] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-              for (int bt = 0; bt < 4; ++bt) {
-                dot = fmaf(hv[c][8 * dw + 2 * bt], (float)((lo >> (8 * bt)) & 0xFFu), dot);
-                dot = fmaf(hv[c][8 * dw + 2 * bt + 1], (float)((hi >> (8 * bt)) & 0xFFu), dot);
-              }
-            }
-            acc = fmaf(dsc, fmaf(-8.f, hsum[c], dot), acc);
-          }
+          q[rr][c] = ld16(qs + n * qstride + 16 * (size_t)bi[c]);
+          sv[rr][c] = sc[n * sstride + bi[c]];
         }
       }
-      acc = half_wave_sum(acc);
-      if (bl == 0) part[slot][2 * rr + half] = acc;
+      // 3) dot products: codes converted exactly with v_cvt_f32_ubyte, offset folded per block
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          float dot = 0.f;
+#pragma unroll
+          for (int dw = 0; dw < 4; ++dw) {
+            const uint32_t lo = q[rr][c][dw] & 0x0F0F0F0Fu, hi = (q[rr][c][dw] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int bt = 0; bt < 4; ++bt) {
+              dot = fmaf(hv[c][8 * dw + 2 * bt], (float)((lo >> (8 * bt)) & 0xFFu), dot);
+              dot = fmaf(hv[c][8 * dw + 2 * bt + 1], (float)((hi >> (8 * bt)) & 0xFFu), dot);
+            }
+          }
+          const float dsc = ok[c] ? fp16_bits_to_float(sv[rr][c]) : 0.f;
+          acc = fmaf(dsc, fmaf(-8.f, hsum[c], dot), acc);
+        }
+        acc = half_wave_sum(acc);
+        if (bl == 0) part[slot][2 * (r0 + rr) + half] = acc;
+      }
     }
   }
   __syncthreads();

@@ -27,26 +27,60 @@
 // the activation tile.  K is permuted consistently: MFMA k-lane group G of
 // step s holds elements 32G + 8s .. 32G + 8s + 7 of the 128-wide chunk, which
 // are exactly dword s of Q4 block G.
+#include <type_traits>
+
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
-#include "../../include/moe_q4.h"
+#include "moe_q4.h"
 
 namespace moe {
 
 // LDS tile: 128 rows x 128 halves (256 B) per buffer, no padding.  The 16 B
 // chunk c of row r is stored in slot c ^ (r & 15), so the 16 lanes that read
 // one MFMA operand (16 rows, same chunk) hit 16 different slots, i.e. all 64
-// banks once.  Tiles arrive by global_load_lds_dwordx4: one instruction moves
-// 64 x 16 B into 1 KB of consecutive LDS (4 rows), lane l filling slot l%16
-// of row l/16, so the swizzle is applied on the global address side.
+// banks once.  Tiles arrive by buffer_load_dwordx4 ... lds: one instruction
+// moves 64 x 16 B into 1 KB of consecutive LDS (4 rows), lane l filling slot
+// l%16 of row l/16, so the swizzle is applied on the global offset side.
+//
+// All global loads are buffer loads whose per-lane offset is fixed for the
+// whole K loop; the K advance is a scalar offset, so the main loop spends
+// its vector instructions on dequantisation, not on address arithmetic.
 constexpr int kRowBytes = kGroupedBK * 2;
+constexpr int kTileBytes = kGroupedBM * kRowBytes;  // 32 KB
+constexpr int kStages = 3;        // pipeline depth (LDS ring of kStages activation tiles)
+constexpr int kLoadsPerStep = 16; // vector-memory ops per lane per K step: 8 tile loads, 4 code blocks, 4 scales
+
+// s_waitcnt vmcnt(N), leaving the LDS and export counters alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// s_waitcnt vmcnt(N) lgkmcnt(0): this wavefront's loads older than the N youngest have landed
+// (including tile loads into LDS) and its own LDS reads are complete.
+template <int N>
+__device__ __forceinline__ void vm_lgkm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+// Workgroup barrier without a memory fence.  The ordering it needs is provided by the explicit
+// waits above: every wavefront waits for its own tile loads and LDS reads before arriving, so after
+// the barrier the new tile is in LDS and nobody still reads the buffer that is refilled next.
+// (__syncthreads() would also wait for the younger tile loads still in flight.)
+__device__ __forceinline__ void tile_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 struct GArgs {
   const _Float16* a_r;      // A rows: gate+up -> x16 [T][d] (gathered); down -> h_r [P][I] (sorted rows)
   const _Float16* a_s;      // A rows of the shared group: gate+up -> x16; down -> h_s [T][Is]
+  uint32_t a_r_bytes, a_s_bytes;
   Q4 wr;                    // routed stack (w13 or w2)
   Q4 ws;                    // shared expert (s13 or s2)
-  _Float16* h_r;            // gate+up outputs
+  _Float16* h_r;            // gate+up outputs (element order permuted in groups of 8)
   _Float16* h_s;
   float* y_r;               // down outputs
   float* y_s;
@@ -62,83 +96,268 @@ struct GArgs {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+__device__ __forceinline__ int ufl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Per-tile state handed from the work-item decode to the main loop.
+struct TileCtx {
+  __amdgpu_buffer_rsrc_t rq, rs, ra;
+  uint32_t aoff[8];
+  uint32_t qoff[4], soff[4];
+  uint32_t rdo[4];
+  bool nok[4];
+  int c0, wave, nit, nkb, Kdim, Iw, mlen, rbase, G, n, lane;
+  bool ktail, shared;
+};
+
+// Main loop and epilogue of one tile with NMT active 16-row slices (known
+// at compile time, so the K loop has no per-MFMA conditions).  Slices of the
+// wavefront's four 16-column weight slices that lie past the N edge are
+// computed on a valid row and discarded in the epilogue.
+template <bool GATEUP, int NMT>
+__device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, char* As) {
+  constexpr int BK = kGroupedBK;
+  auto issue_a = [&](int it, int buf) {
+    const int kb = it * BK * 2;
+    if (c.ktail && it == c.nit - 1) {  // uniform
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // a chunk past the row end re-reads the tile's first chunk of the same row: finite data
+        // that meets zero weights (the weights' K tail is masked to zero below)
+        const int chunk = (c.lane & 15) ^ ((32 * c.wave + 4 * i + (c.lane >> 4)) & 15);
+        const uint32_t off = c.aoff[i] - (it * BK + 8 * chunk >= c.Kdim ? 16u * (uint32_t)chunk : 0u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            c.ra, (lds_void*)(As + buf * kTileBytes + (32 * c.wave + 4 * i) * kRowBytes), 16, (int)off, kb, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            c.ra, (lds_void*)(As + buf * kTileBytes + (32 * c.wave + 4 * i) * kRowBytes), 16, (int)c.aoff[i], kb, 0, 0);
+    }
+  };
+  auto load_w = [&](int it, u32x4* qd, uint32_t* sd) {
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+      qd[ns] = __builtin_amdgcn_raw_buffer_load_b128(c.rq, (int)c.qoff[ns], it * 64, 0);
+      sd[ns] = __builtin_amdgcn_raw_buffer_load_b16(c.rs, (int)c.soff[ns], it * 8, 0);
+    }
+  };
+
+  floatx4 acc[NMT][4];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) acc[mt][ns] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // One K iteration (4 MFMA K-steps of 32) on LDS buffer `buf`, software-pipelined: while the 4*NMT
+  // MFMAs of step s run, the activation fragments of step s+1 are read from LDS and its four weight
+  // fragments are dequantised; sched_group_barrier interleaves the three instruction streams so the
+  // matrix core is fed back to back.
+  // One K iteration (4 MFMA K-steps of 32) on LDS buffer `buf`, software-pipelined: while the 4*NMT
+  // MFMAs of step s run, the activation fragments of step s+1 are read from LDS and its four weight
+  // fragments are dequantised; sched_group_barrier interleaves the three instruction streams so the
+  // matrix core is fed back to back.  The loop body has no branches, so the accumulators keep their
+  // registers across iterations.
+  auto compute = [&](int buf, const u32x4* q, const uint32_t* sc_in, int it) __attribute__((always_inline)) {
+    const char* At = As + buf * kTileBytes;
+    half2v d2[4];
+    const bool tail = c.ktail && it == c.nit - 1;  // uniform
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+      // K tail: blocks past the row end weigh zero (the step's loads have landed: no register in flight)
+      const uint32_t bits = (tail && it * 4 + c.G >= c.nkb) ? 0u : sc_in[ns];
+      const _Float16 dv = __builtin_bit_cast(_Float16, (uint16_t)bits);
+      d2[ns] = half2v{dv, dv};
+    }
+    half8 a_cur[NMT], b_cur[4];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) a_cur[mt] = *reinterpret_cast<const half8*>(At + c.rdo[0] + mt * 16 * kRowBytes);
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) b_cur[ns] = dequant8_general(q[ns][0], d2[ns]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      half8 a_nxt[NMT], b_nxt[4];
+      if (s < 3) {
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+          a_nxt[mt] = *reinterpret_cast<const half8*>(At + c.rdo[s + 1] + mt * 16 * kRowBytes);
+      }
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns)
+          acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur[mt], b_cur[ns], acc[mt][ns], 0, 0, 0);
+      if (s < 3) {
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) b_nxt[ns] = dequant8_general(q[ns][s + 1], d2[ns]);
+        __builtin_amdgcn_sched_group_barrier(0x100, NMT, 0);  // DS reads of step s+1 first
+#pragma unroll
+        for (int i = 0; i < 4 * NMT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // then up to three VALU
+        }
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) a_cur[mt] = a_nxt[mt];
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) b_cur[ns] = b_nxt[ns];
+      }
+    }
+  };
+
+  // kStages-deep pipeline: while step `it` is computed, the activation tiles and weight blocks of
+  // steps it+1 .. it+kStages-1 are in flight (LDS ring of kStages tiles, weights in registers).
+  constexpr int NS = kStages;
+  u32x4 q[NS][4];
+  uint32_t sc[NS][4];
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st) {
+    if (st < c.nit) {
+      issue_a(st, st);
+      load_w(st, q[st], sc[st]);
+    }
+  }
+  // Wait until step `it` has landed (younger steps stay in flight), then barrier.
+  auto arrive = [&](int it) __attribute__((always_inline)) {
+    const int younger = min(NS - 2, c.nit - 1 - it);
+    static_assert(kStages <= 4, "the waits below cover up to two younger steps");
+    if (younger >= 2) vm_lgkm_wait<2 * kLoadsPerStep>();
+    else if (younger == 1) vm_lgkm_wait<kLoadsPerStep>();
+    else vm_lgkm_wait<0>();
+    tile_barrier();  // every wavefront's part of tile `it` is in LDS; tile it-1 is no longer read
+  };
+  // Main loop over whole groups of NS steps: the compute is unconditional (only the load issue and the
+  // wait depth depend on the trip count), so the accumulators stay in their registers.
+  int it0 = 0;
+  for (; it0 + NS <= c.nit; it0 += NS) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int it = it0 + st;
+      arrive(it);
+      if (it + NS - 1 < c.nit) {
+        const int nxt = (st + NS - 1) % NS;  // folded: st is an unrolled constant
+        issue_a(it + NS - 1, nxt);
+        load_w(it + NS - 1, q[nxt], sc[nxt]);
+      }
+      compute(st, q[st], sc[st], it);
+    }
+  }
+  // The remaining nit % NS steps (their loads were issued above or in the prologue).
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st) {
+    const int it = it0 + st;
+    if (it < c.nit) {
+      arrive(it);
+      compute(st, q[st], sc[st], it);
+    }
+  }
+
+  // ---- epilogue.  D layout: lane holds column n of rows 4G..4G+3 of each 16x16 tile.
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = mt * 16 + 4 * c.G + i;
+      if (row >= c.mlen) continue;
+      if (GATEUP) {
+        _Float16* out = c.shared ? a.h_s : a.h_r;
+#pragma unroll
+        for (int xh = 0; xh < 2; ++xh) {
+          if (!c.nok[xh]) continue;
+          const float gv = acc[mt][xh][i], uv = acc[mt][2 + xh][i];
+          const int col = c.c0 + 16 * xh + c.n;  // stored in the dequant pair order within groups of 8
+          out[(size_t)(c.rbase + row) * c.Iw + (col & ~7) + perm_slot(col & 7)] = (_Float16)(siluf_(gv) * uv);
+        }
+      } else {
+        float* out = c.shared ? a.y_s : a.y_r;
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) {
+          if (!c.nok[ns]) continue;
+          out[(size_t)(c.rbase + row) * a.d + c.c0 + 16 * ns + c.n] = acc[mt][ns][i];
+        }
+      }
+    }
+  }
+}
+
 template <bool GATEUP>
-__global__ __launch_bounds__(256, 2) void k_grouped(GArgs a) {
+__global__ __launch_bounds__(256, 1) void k_grouped(GArgs a) {
   constexpr int BM = kGroupedBM, BK = kGroupedBK;
   constexpr int BANDW = GATEUP ? kGateUpBandCols : kDownBandCols;
-  __shared__ __attribute__((aligned(1024))) char As[2][BM * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) char As[kStages * kTileBytes];
   __shared__ int s_prefix[kMaxExperts + 2];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = ufl(tid >> 6);
   const int ngroups = a.E + 1;
   for (int i = tid; i <= ngroups; i += 256) s_prefix[i] = a.mt_prefix[i];
   __syncthreads();
   const int nb = a.nbands;
-  const int n_items = s_prefix[ngroups] * nb;
-  if ((int)blockIdx.x >= n_items) return;
-  const int item = xcd_remap(blockIdx.x, n_items);
-  int lo = 0, hi = ngroups;  // s_prefix[lo]*nb <= item < s_prefix[hi]*nb
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_prefix[mid] * nb <= item) lo = mid; else hi = mid;
+  const int n_mt = ufl(s_prefix[ngroups]);
+  // Work item -> (group rank, band, M-tile).  Workgroups are dispatched round-robin over the 8 XCDs
+  // (own L2 each).  With a multiple of 8 bands, XCD x takes the bands = x (mod 8) of every group, in
+  // schedule order: each XCD gets the same mix of group sizes (balanced), and all M-tiles that read
+  // one weight band run on one XCD, adjacent in time.  Otherwise items go round-robin in schedule order.
+  int rank, band, mtile;
+  {
+    const int bid = blockIdx.x;
+    const bool per_xcd = (nb % 8) == 0 && !(a.flags & MOE_FLAG_NO_BANDING);
+    const int nbx = per_xcd ? nb / 8 : nb;  // bands per group seen by this walk
+    const int item = per_xcd ? bid >> 3 : bid;
+    if (item >= n_mt * nbx) return;
+    int lo = 0, hi = ngroups;  // s_prefix[lo]*nbx <= item < s_prefix[hi]*nbx
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ufl(s_prefix[mid]) * nbx <= item) lo = mid; else hi = mid;
+    }
+    rank = lo;
+    const int p0 = ufl(s_prefix[rank]);
+    const int nmt = ufl(s_prefix[rank + 1]) - p0;
+    const int local = item - p0 * nbx;
+    if (a.flags & MOE_FLAG_NO_BANDING) {
+      mtile = local / nbx;
+      band = local % nbx;
+    } else {
+      band = local / nmt;
+      mtile = local % nmt;
+    }
+    if (per_xcd) band = 8 * band + (bid & 7);
   }
-  const int rank = lo;
-  const int g = a.group_order[rank];
-  const int nmt = s_prefix[rank + 1] - s_prefix[rank];
-  const int local = item - s_prefix[rank] * nb;
-  int band, mtile;
-  if (a.flags & MOE_FLAG_NO_BANDING) {
-    mtile = local / nb;
-    band = local % nb;
-  } else {
-    band = local / nmt;
-    mtile = local % nmt;
-  }
+  const int g = ufl(a.group_order[rank]);
   const bool shared = (g == a.E);
-  const int cnt = shared ? a.T : a.counts[g];
+  const int cnt = shared ? a.T : ufl(a.counts[g]);
   const int Iw = shared ? a.Is : a.I;
   const int Kdim = GATEUP ? a.d : Iw;
   const int Ndim = GATEUP ? Iw : a.d;
   if (band * BANDW >= Ndim) return;  // uniform across the workgroup
   const int m0 = mtile * BM;
   const int mlen = min(BM, cnt - m0);
-  const int rbase = shared ? m0 : a.offsets[g] + m0;  // first output row (token or sorted position)
-  const size_t wrows = GATEUP ? 2 * (size_t)Iw : (size_t)a.d;
-  const uint8_t* Wq = shared ? a.ws.qs : a.wr.qs + (size_t)g * wrows * (Kdim / 2);
-  const uint16_t* Ws = shared ? a.ws.sc : a.wr.sc + (size_t)g * wrows * (Kdim / 32);
+  const int gbase = shared ? 0 : ufl(a.offsets[g]);
+  const int rbase = gbase + m0;  // first output row (token for the shared group, else sorted position)
+  const uint32_t wrows = GATEUP ? 2u * (uint32_t)Iw : (uint32_t)a.d;
+  const uint32_t qstride = (uint32_t)Kdim / 2, sstride = (uint32_t)Kdim / 32;
+  const uint8_t* Wq = shared ? a.ws.qs : a.wr.qs + (size_t)g * wrows * qstride;
+  const uint16_t* Ws = shared ? a.ws.sc : a.wr.sc + (size_t)g * wrows * sstride;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Wq, wrows * qstride);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(Ws, wrows * sstride * 2);
+  const __amdgpu_buffer_rsrc_t ra = shared ? make_rsrc(a.a_s, a.a_s_bytes) : make_rsrc(a.a_r, a.a_r_bytes);
 
-  // ---- A rows staged by this wavefront: rows 32*wave + 4*i + lane/16, slot lane%16
-  const char* abase = reinterpret_cast<const char*>(shared ? a.a_s : a.a_r);
-  uint32_t aoff[8];  // byte offset of the row start, plus the swizzled chunk
+  // ---- activation rows staged by this wavefront: rows 32*wave + 4*i + lane/16, slot lane%16
+  uint32_t aoff[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = 32 * wave + 4 * i + (lane >> 4);
-    const int rr = row < mlen ? row : 0;  // rows past the group read row 0: finite, and discarded
-    size_t arow;
+    const int rr = row < mlen ? row : 0;  // rows past the group re-read row 0: finite, and never stored
+    uint32_t arow;
     if (GATEUP)
-      arow = shared ? (size_t)(m0 + rr) : (size_t)(a.sorted_pair[a.offsets[g] + m0 + rr] / a.k);
+      arow = shared ? (uint32_t)(m0 + rr) : (uint32_t)(a.sorted_pair[rbase + rr] / a.k);
     else
-      arow = shared ? (size_t)(m0 + rr) : (size_t)(a.offsets[g] + m0 + rr);
-    const int chunk = (lane & 15) ^ (row & 15);
-    aoff[i] = (uint32_t)(arow * (size_t)Kdim * 2 + 16 * chunk);
+      arow = (uint32_t)(rbase + rr);
+    aoff[i] = arow * (uint32_t)Kdim * 2u + 16u * (uint32_t)((lane & 15) ^ (row & 15));
   }
+  const int nit = (Kdim + BK - 1) / BK;
   const bool ktail = (Kdim % BK) != 0;
-  auto issue_a = [&](int it, int buf) {
-    const uint32_t kb = (uint32_t)it * BK * 2;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t off = aoff[i] + kb;
-      // a chunk past the end of the row reads the tile's first chunk instead: finite data that
-      // meets zero weights (the weight K tail is zero-filled)
-      if (ktail && (int)(it * BK + 8 * ((lane & 15) ^ ((32 * wave + 4 * i + (lane >> 4)) & 15))) >= Kdim)
-        off = aoff[i] - 16 * (uint32_t)((lane & 15) ^ ((32 * wave + 4 * i + (lane >> 4)) & 15)) + kb;
-      __builtin_amdgcn_global_load_lds(abase + off, (lds_void*)&As[buf][(32 * wave + 4 * i) * kRowBytes], 16, 0, 0);
-    }
-  };
-
   // ---- this wavefront's weight rows: four 16-row slices
   const int n = lane & 15, G = lane >> 4;
-  int wrow[4];
+  uint32_t qoff[4], soff[4];
   bool nok[4];
   int c0;
   if (GATEUP) {
@@ -147,7 +366,9 @@ __global__ __launch_bounds__(256, 2) void k_grouped(GArgs a) {
     for (int ns = 0; ns < 4; ++ns) {
       const int col = c0 + 16 * (ns & 1);
       nok[ns] = col < Iw;
-      wrow[ns] = (ns < 2 ? 0 : Iw) + (nok[ns] ? col : 0) + n;
+      const uint32_t wrow = (ns < 2 ? 0u : (uint32_t)Iw) + (uint32_t)(nok[ns] ? col : 0) + (uint32_t)n;
+      qoff[ns] = wrow * qstride + 16u * (uint32_t)G;
+      soff[ns] = (wrow * sstride + (uint32_t)G) * 2u;
     }
   } else {
     c0 = band * BANDW + wave * 64;  // output columns c0 .. c0+63
@@ -155,113 +376,43 @@ __global__ __launch_bounds__(256, 2) void k_grouped(GArgs a) {
     for (int ns = 0; ns < 4; ++ns) {
       const int col = c0 + 16 * ns;
       nok[ns] = col < a.d;
-      wrow[ns] = (nok[ns] ? col : 0) + n;
+      const uint32_t wrow = (uint32_t)(nok[ns] ? col : 0) + (uint32_t)n;
+      qoff[ns] = wrow * qstride + 16u * (uint32_t)G;
+      soff[ns] = (wrow * sstride + (uint32_t)G) * 2u;
     }
   }
-  const size_t qstride = Kdim / 2, sstride = Kdim / 32;
   const int nkb = Kdim / 32;
-  const int nit = (Kdim + BK - 1) / BK;
+  // LDS read offsets for the four K-steps: row n of every 16-row slice, swizzled chunk 4G+s
+  uint32_t rdo[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) rdo[s] = (uint32_t)(n * kRowBytes + 16 * ((4 * G + s) ^ n));
 
-  u32x4 q[4];
-  uint32_t sc[4];
-  auto load_w = [&](int it, u32x4* qd, uint32_t* sd) {
-    const int blk = it * 4 + G;
+  TileCtx c;
+  c.rq = rq; c.rs = rs; c.ra = ra;
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
-      if (nok[ns] && blk < nkb) {  // never read past the row: the K tail is zero-filled
-        qd[ns] = ld16(Wq + wrow[ns] * qstride + 16 * (size_t)blk);
-        sd[ns] = Ws[wrow[ns] * sstride + blk];
-      } else {
-        qd[ns] = u32x4{0u, 0u, 0u, 0u};
-        sd[ns] = 0u;
-      }
-    }
-  };
-
-  floatx4 acc[8][4];
+  for (int i = 0; i < 8; ++i) c.aoff[i] = aoff[i];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+  for (int ns = 0; ns < 4; ++ns) { c.qoff[ns] = qoff[ns]; c.soff[ns] = soff[ns]; c.nok[ns] = nok[ns]; }
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) acc[mt][ns] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  load_w(0, q, sc);
-  issue_a(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);  // all counters: the first tile has landed in LDS
-  __syncthreads();
-  for (int it = 0; it < nit; ++it) {
-    const int cur = it & 1;
-    const bool more = it + 1 < nit;
-    u32x4 qn[4];
-    uint32_t sn[4];
-    if (more) {
-      issue_a(it + 1, cur ^ 1);
-      load_w(it + 1, qn, sn);
-    }
-    half2v d2[4];
-#pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
-      const _Float16 dv = __builtin_bit_cast(_Float16, (uint16_t)sc[ns]);
-      d2[ns] = half2v{dv, dv};
-    }
-    const char* Acur = As[cur];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      half8 b[4];
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) b[ns] = dequant8_f16(q[ns][s], d2[ns]);
-      const int slot = (4 * G + s) ^ n;  // row mt*16 + n has (row & 15) == n
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        if (mt * 16 < mlen) {
-          const half8 am = *reinterpret_cast<const half8*>(Acur + (mt * 16 + n) * kRowBytes + 16 * slot);
-#pragma unroll
-          for (int ns = 0; ns < 4; ++ns)
-            if (nok[ns]) acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, b[ns], acc[mt][ns], 0, 0, 0);
-        }
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) {
-        q[ns] = qn[ns];
-        sc[ns] = sn[ns];
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // next tile in LDS, next weights in registers
-    __syncthreads();
-  }
-
-  // ---- epilogue.  D layout: lane holds column n of rows 4G..4G+3 of each 16x16 tile.
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    if (mt * 16 >= mlen) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = mt * 16 + 4 * G + i;
-      if (row >= mlen) continue;
-      if (GATEUP) {
-        _Float16* out = shared ? a.h_s : a.h_r;
-#pragma unroll
-        for (int xh = 0; xh < 2; ++xh) {
-          if (!nok[xh]) continue;
-          const float gv = acc[mt][xh][i], uv = acc[mt][2 + xh][i];
-          out[(size_t)(rbase + row) * Iw + c0 + 16 * xh + n] = (_Float16)(siluf_(gv) * uv);
-        }
-      } else {
-        float* out = shared ? a.y_s : a.y_r;
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
-          if (!nok[ns]) continue;
-          out[(size_t)(rbase + row) * a.d + c0 + 16 * ns + n] = acc[mt][ns][i];
-        }
-      }
-    }
+  for (int s4 = 0; s4 < 4; ++s4) c.rdo[s4] = rdo[s4];
+  c.c0 = c0; c.wave = wave; c.nit = nit; c.nkb = nkb; c.Kdim = Kdim; c.Iw = Iw; c.mlen = mlen; c.rbase = rbase;
+  c.G = G; c.n = n; c.lane = lane; c.ktail = ktail; c.shared = shared;
+  switch ((mlen + 15) >> 4) {
+    case 1: grouped_tile<GATEUP, 1>(a, c, As); break;
+    case 2: grouped_tile<GATEUP, 2>(a, c, As); break;
+    case 3: grouped_tile<GATEUP, 3>(a, c, As); break;
+    case 4: grouped_tile<GATEUP, 4>(a, c, As); break;
+    case 5: grouped_tile<GATEUP, 5>(a, c, As); break;
+    case 6: grouped_tile<GATEUP, 6>(a, c, As); break;
+    case 7: grouped_tile<GATEUP, 7>(a, c, As); break;
+    default: grouped_tile<GATEUP, 8>(a, c, As); break;
   }
 }
 
-// bf16 -> fp16 copy of the activations for the gate+up A operand.  The
-// conversion is exact inside the fp16 range; round-toward-zero saturates
-// values beyond it to +-65504.
+// bf16 -> fp16 copy of the activations for the gate+up A operand, stored in
+// the dequant pair order inside every group of 8 (x0 x4 x1 x5 x2 x6 x3 x7).
+// The conversion is exact inside the fp16 range; round-toward-zero
+// saturates values beyond it to +-65504.
 __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, _Float16* __restrict__ x16,
                                                   size_t n8) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -273,7 +424,9 @@ __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x
     const float hi = __builtin_bit_cast(float, v[m] & 0xFFFF0000u);
     v[m] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
   }
-  *reinterpret_cast<u32x4*>(x16 + 8 * i) = v;
+  uint32_t o[4];
+  x_bf16_pairs(v, o);  // same 16-bit lane shuffle as for bf16 pairs
+  *reinterpret_cast<u32x4*>(x16 + 8 * i) = u32x4{o[0], o[1], o[2], o[3]};
 }
 
 // Combine: y[t] = (sum_j w[t,j] * y_pair[pair_pos[t*k+j]]) + y_shared[t], j ascending, no atomics.
@@ -328,6 +481,7 @@ hipError_t launch_grouped_gateup(const Shape& s, const uint16_t* x, const Routin
   GArgs a = make_args(s, r, flags);
   a.a_r = o.x16;
   a.a_s = o.x16;
+  a.a_r_bytes = a.a_s_bytes = (uint32_t)((size_t)s.T * s.d * 2);
   a.wr = w13;
   a.ws = s13;
   a.h_r = o.h_r;
@@ -344,6 +498,8 @@ hipError_t launch_grouped_down(const Shape& s, const Routing& r, Q4 w2, Q4 s2, c
   GArgs a = make_args(s, r, flags);
   a.a_r = o.h_r;
   a.a_s = o.h_s;
+  a.a_r_bytes = (uint32_t)((size_t)s.T * s.k * s.I * 2);
+  a.a_s_bytes = (uint32_t)((size_t)s.T * s.Is * 2);
   a.wr = w2;
   a.ws = s2;
   a.y_r = o.y_pair;

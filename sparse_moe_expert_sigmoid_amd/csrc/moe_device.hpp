@@ -45,26 +45,64 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
 }
 
 // ---------------------------------------------------------------- dequant to fp16 (MFMA operand)
-// Eight codes of one dword -> eight fp16 weights (q - 8) * d in natural
-// element order.  Each nibble is placed in the low mantissa bits of an fp16
-// whose exponent makes it 1024 + q exactly; subtracting 1032 gives q - 8
-// exactly, and one packed multiply by the scale rounds once to fp16.
-__device__ __forceinline__ half8 dequant8_f16(uint32_t w, half2v d2) {
-  const uint32_t t = w >> 4;  // byte j of t has element 2j+1 in its low nibble
+// Eight codes of one dword (element m in bits 4m..4m+3) -> eight fp16
+// weights (q - 8) * d, in the pair order (e0,e4) (e1,e5) (e2,e6) (e3,e7):
+// each pair needs one shift and one mask.  The activation operands are stored
+// in the same order within every group of 8 (kPermInGroup).
+//
+// Fast form (|d| < 0.5): a nibble placed in bits 7..10 of an fp16 is the
+// number q * 2^-17 (subnormal or the first binade, where the encoding is
+// linear), so one packed FMA q*2^-17 * (d*2^17) - 8d gives (q - 8) * d with a
+// single rounding; d*2^17 stays finite for |d| < 0.5.
+// General form: nibble in the low mantissa of 1024.0 (exactly 1024 + q),
+// minus 1032 (exact), times d (one rounding).
+struct Q4Scale {
+  half2v mul;   // fast: (d*2^17, d*2^17); general: (d, d)
+  half2v add;   // fast: (-8d, -8d)
+};
+
+__device__ __forceinline__ Q4Scale q4_scale_fast(uint32_t d_bits) {
+  const _Float16 dv = __builtin_bit_cast(_Float16, (uint16_t)d_bits);
+  const half2v d2 = {dv, dv};
+  Q4Scale s;
+  s.mul = d2 * half2v{(_Float16)512.0f, (_Float16)512.0f} * half2v{(_Float16)256.0f, (_Float16)256.0f};
+  s.add = d2 * half2v{(_Float16)-8.0f, (_Float16)-8.0f};
+  return s;
+}
+__device__ __forceinline__ bool q4_scale_fast_ok(uint32_t d_bits) { return (d_bits & 0x7FFFu) < 0x3800u; }
+
+__device__ __forceinline__ half8 dequant8_fast(uint32_t w, const Q4Scale& s) {
+  const uint32_t M = 0x07800780u;
+  const uint32_t p0 = (w << 7) & M, p1 = (w << 3) & M, p2 = (w >> 1) & M, p3 = (w >> 5) & M;
+  // fused multiply-add: one rounding
+  const half2v r0 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p0), s.mul, s.add);
+  const half2v r1 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p1), s.mul, s.add);
+  const half2v r2 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p2), s.mul, s.add);
+  const half2v r3 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p3), s.mul, s.add);
+  return half8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+__device__ __forceinline__ half8 dequant8_general(uint32_t w, half2v d2) {
   const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
-  half8 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // bytes: [w.b_j, -, t.b_j, -]  (perm pool: t = bytes 4..7, w = bytes 0..3)
-    const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
-    const uint32_t p = __builtin_amdgcn_perm(t, w, sel);
-    const uint32_t m = (p & 0x000F000Fu) | 0x64006400u;
-    half2v v = __builtin_bit_cast(half2v, m);
-    v = (v - off) * d2;
-    r[2 * j] = v[0];
-    r[2 * j + 1] = v[1];
-  }
-  return r;
+  const uint32_t M = 0x000F000Fu, C = 0x64006400u;
+  const uint32_t t = w >> 4;
+  const uint32_t p0 = (w & M) | C, p1 = (t & M) | C, p2 = ((w >> 8) & M) | C, p3 = ((t >> 8) & M) | C;
+  const half2v r0 = (__builtin_bit_cast(half2v, p0) - off) * d2;
+  const half2v r1 = (__builtin_bit_cast(half2v, p1) - off) * d2;
+  const half2v r2 = (__builtin_bit_cast(half2v, p2) - off) * d2;
+  const half2v r3 = (__builtin_bit_cast(half2v, p3) - off) * d2;
+  return half8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+// Position, inside a group of 8 stored activations, of logical element c % 8
+// (the inverse of the pair order above: stored slot i holds element
+// 0,4,1,5,2,6,3,7 [i]).
+__device__ __forceinline__ int perm_slot(int c8) { return (c8 < 4) ? 2 * c8 : 2 * (c8 - 4) + 1; }
+
+// Buffer resource for raw (unstructured) loads; accesses at or past
+// num_bytes return zero.  Word 3 is the gfx9-family raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
 }
 
 // ---------------------------------------------------------------- GEMV helpers (bf16 dot2)
@@ -93,14 +131,40 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // ---------------------------------------------------------------- reductions
+// DPP lane exchanges (no LDS traffic): quad xor 1, quad xor 2, mirror inside
+// 8 lanes, mirror inside 16 lanes.  After the four steps every lane of a
+// 16-lane row holds the row's reduction; rows are then combined with two
+// cross-lane permutes.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return v;
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  v = row16_sum(v);
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
   return v;
 }
 __device__ __forceinline__ float half_wave_sum(float v) {  // within each 32-lane half
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  v = row16_sum(v);
+  v += __shfl_xor(v, 16, kWave);
   return v;
 }
 

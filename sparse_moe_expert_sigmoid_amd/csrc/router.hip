@@ -12,40 +12,57 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Small T: one wavefront per expert streams its router row once per group of
-// 8 tokens (the row stays in L2 for the next group) and reduces each dot
-// product across the wave.  Lane l reads 16 contiguous bytes of the row at
-// 4l + 256m, so each load instruction covers 1 KB of the row.
+// Small T: one workgroup of 256 threads per expert.  Thread i holds 4
+// consecutive router weights at 4i + 1024m (m < NM), loaded once for all
+// tokens; tokens are processed 8 at a time and each dot product is reduced
+// across the wavefront (DPP) and then across the 4 wavefronts in LDS.
+template <int NM>
 __global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict__ x, const float* __restrict__ W,
                                                      float* __restrict__ logits, int T, int d, int E) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
+  __shared__ float red[4][8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = blockIdx.x;
   const float* wr = W + (size_t)e * d;
+  float4 wv[NM];
+  bool ok[NM];
+  int col[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const int c = 4 * tid + 1024 * m;
+    ok[m] = c < d;
+    col[m] = ok[m] ? c : d - 4;  // clamped: every load in bounds, masked below
+    wv[m] = *reinterpret_cast<const float4*>(wr + col[m]);
+  }
   for (int t0 = 0; t0 < T; t0 += 8) {
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int c = 4 * lane; c < d; c += 256) {
-      const float4 wv = *reinterpret_cast<const float4*>(wr + c);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (t0 + i < T) {
-          const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + i) * d + c);
-          float a = acc[i];
-          a = fmaf(wv.x, bf16_bits_to_float(xv.x & 0xFFFFu), a);
-          a = fmaf(wv.y, bf16_bits_to_float(xv.x >> 16), a);
-          a = fmaf(wv.z, bf16_bits_to_float(xv.y & 0xFFFFu), a);
-          a = fmaf(wv.w, bf16_bits_to_float(xv.y >> 16), a);
-          acc[i] = a;
-        }
-      }
-    }
+    uint2 xv[8][NM];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float s = wave_sum(acc[i]);
-      if (lane == 0 && t0 + i < T) logits[(size_t)(t0 + i) * E + e] = s;
+      const int t = min(t0 + i, T - 1);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) xv[i][m] = *reinterpret_cast<const uint2*>(x + (size_t)t * d + col[m]);
     }
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float a = 0.f;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        float p = wv[m].x * bf16_bits_to_float(xv[i][m].x & 0xFFFFu);
+        p = fmaf(wv[m].y, bf16_bits_to_float(xv[i][m].x >> 16), p);
+        p = fmaf(wv[m].z, bf16_bits_to_float(xv[i][m].y & 0xFFFFu), p);
+        p = fmaf(wv[m].w, bf16_bits_to_float(xv[i][m].y >> 16), p);
+        a += ok[m] ? p : 0.f;
+      }
+      acc[i] = wave_sum(a);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[wave][i] = acc[i];
+    }
+    __syncthreads();
+    if (tid < 8 && t0 + tid < T)
+      logits[(size_t)(t0 + tid) * E + e] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+    __syncthreads();
   }
 }
 
@@ -118,73 +135,90 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: one wavefront per token.  Lane l holds experts l, l+64, ...; each
-// of the k rounds takes the lane-local best untaken (key, id) and reduces it
-// across the wave with the total order (larger key first, then lower id).
+// Top-k: one wavefront per token.  Lane l holds experts l, l+64, ... as
+// 64-bit sort keys (order-preserving bits of s + b, then the complement of
+// the expert id), so "larger key, then lower id" is a plain unsigned max.
+// Each of the k rounds takes the lane's best untaken key and reduces it over
+// the wavefront: four DPP steps inside each 16-lane row, then two
+// cross-row exchanges.  Every lane ends with the winner.
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  if (f != f) return 1u;  // NaN ranks below every number but above empty slots
+  if (f == 0.f) f = 0.f;  // -0 and +0 are the same key (then the lower id wins)
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_step_dpp(uint32_t& hi, uint32_t& lo) {
+  const uint32_t oh = (uint32_t)dpp_i<CTRL>((int)hi), ol = (uint32_t)dpp_i<CTRL>((int)lo);
+  const bool take = (oh > hi) || (oh == hi && ol > lo);
+  hi = take ? oh : hi;
+  lo = take ? ol : lo;
+}
+__device__ __forceinline__ void argmax_step_xor(uint32_t& hi, uint32_t& lo, int mask) {
+  const uint32_t oh = (uint32_t)__shfl_xor((int)hi, mask, 64), ol = (uint32_t)__shfl_xor((int)lo, mask, 64);
+  const bool take = (oh > hi) || (oh == hi && ol > lo);
+  hi = take ? oh : hi;
+  lo = take ? ol : lo;
+}
+
+template <int NPER>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
                                               int32_t* __restrict__ ids, float* __restrict__ w, int T, int E,
                                               int k) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  constexpr int kPer = kMaxExperts / 64;
-  float key[kPer], sc[kPer];
-  uint32_t taken = 0;
+  uint32_t key[NPER];
+  float sc[NPER];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
       const float s = sigmoidf_(logits[(size_t)t * E + e]);
-      float kv = s + bias[e];
-      if (kv != kv) kv = -INFINITY;  // a NaN score ranks last but stays selectable
-      key[i] = kv;
+      key[i] = ordered_bits(s + bias[e]);
       sc[i] = s;
     } else {
-      key[i] = -INFINITY;
+      key[i] = 0u;  // empty slot: never wins (every real key is >= 1)
       sc[i] = 0.f;
-      taken |= 1u << i;
     }
   }
   float my_s = 0.f;
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    float best = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    uint32_t hi = 0u, lo = 0u;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = lane + 64 * i;
-      if (!((taken >> i) & 1u) && (key[i] > best || (key[i] == best && e < bi))) {
-        best = key[i];
-        bi = e;
+    for (int i = 0; i < NPER; ++i) {
+      const uint32_t l2 = ~(uint32_t)(lane + 64 * i);
+      if (key[i] > hi || (key[i] == hi && l2 > lo)) {
+        hi = key[i];
+        lo = l2;
       }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ob = __shfl_xor(best, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ob > best || (ob == best && oi < bi)) {
-        best = ob;
-        bi = oi;
-      }
-    }
+    argmax_step_dpp<kDppXor1>(hi, lo);
+    argmax_step_dpp<kDppXor2>(hi, lo);
+    argmax_step_dpp<kDppHalfMirror>(hi, lo);
+    argmax_step_dpp<kDppMirror>(hi, lo);
+    argmax_step_xor(hi, lo, 16);
+    argmax_step_xor(hi, lo, 32);
+    const int win = (int)~lo;
     float s_sel = 0.f;
-    if ((bi & 63) == lane) {
-      const int i = bi >> 6;
+    if ((win & 63) == lane) {
 #pragma unroll
-      for (int q = 0; q < kPer; ++q)
-        if (q == i) {
-          taken |= 1u << q;
-          s_sel = sc[q];
+      for (int i = 0; i < NPER; ++i)
+        if (i == (win >> 6)) {
+          key[i] = 0u;  // taken
+          s_sel = sc[i];
         }
     }
-    s_sel = __shfl(s_sel, bi & 63, 64);
+    s_sel = __shfl(s_sel, win & 63, 64);
     if (lane == j) {
       my_s = s_sel;
-      my_id = bi;
+      my_id = win;
     }
   }
   float tot = 0.f;
-  for (int j = 0; j < k; ++j) tot += __shfl(my_s, j, 64);
+  for (int j = 0; j < k; ++j) tot += __shfl(my_s, j, 64);  // slot order, same in every lane
   if (lane < k) {
     ids[(size_t)t * k + lane] = my_id;
     w[(size_t)t * k + lane] = my_s / tot;
@@ -193,7 +227,12 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 
 hipError_t launch_router_gemv(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
                               hipStream_t st) {
-  hipLaunchKernelGGL(k_router_gemv, dim3((s.E + 3) / 4), dim3(256), 0, st, x, w_router, logits, s.T, s.d, s.E);
+  const int nm = (s.d + 1023) / 1024;
+  const dim3 grid(s.E), block(256);
+  if (nm <= 1) hipLaunchKernelGGL(k_router_gemv<1>, grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
+  else if (nm <= 2) hipLaunchKernelGGL(k_router_gemv<2>, grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
+  else if (nm <= 4) hipLaunchKernelGGL(k_router_gemv<4>, grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
+  else hipLaunchKernelGGL(k_router_gemv<8>, grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
   return hipGetLastError();
 }
 
@@ -206,7 +245,13 @@ hipError_t launch_router_mfma(const Shape& s, const uint16_t* x, const float* w_
 
 hipError_t launch_topk(const Shape& s, const float* logits, const float* bias, int32_t* topk_ids, float* topk_w,
                        hipStream_t st) {
-  hipLaunchKernelGGL(k_topk, dim3((s.T + 3) / 4), dim3(256), 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  const dim3 grid((s.T + 3) / 4), block(256);
+  const int nper = (s.E + 63) / 64;
+  if (nper <= 1) hipLaunchKernelGGL(k_topk<1>, grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  else if (nper <= 2) hipLaunchKernelGGL(k_topk<2>, grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  else if (nper <= 4) hipLaunchKernelGGL(k_topk<4>, grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  else if (nper <= 8) hipLaunchKernelGGL(k_topk<8>, grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  else hipLaunchKernelGGL(k_topk<16>, grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
   return hipGetLastError();
 }
 
