@@ -24,7 +24,7 @@ namespace moe {
 template <int NCH>
 __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
                                                      Q4 w13, Q4 s13, float* __restrict__ h_r, float* __restrict__ h_s,
-                                                     int T, int d, int k, int I, int Is) {
+                                                     int T, int d, int k, int I, int Is, uint32_t mask, uint32_t magic) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int job = blockIdx.y;
   const int P = T * k;
@@ -108,12 +108,12 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
 #pragma unroll
         for (int dw = 0; dw < 4; ++dw) {
           uint32_t cp[4];
-          codes_bf16_pairs(q[r][bb][dw], cp);
+          codes_bf16_pairs(q[r][bb][dw], mask, magic, cp);
 #pragma unroll
           for (int m = 0; m < 4; ++m) dot = dot2_bf16(cp[m], xp[bb][dw][m], dot);
         }
         const float dsc = ok[bb] ? fp16_bits_to_float(sv[r][bb]) : 0.f;
-        acc[r] = fmaf(dsc, fmaf(16.f, dot, -24.f * xs[bb]), acc[r]);
+        acc[r] = fmaf(dsc, fmaf(-136.f, xs[bb], dot), acc[r]);
       }
     }
   }
@@ -252,10 +252,10 @@ hipError_t launch_gemv_gateup(const Shape& s, const uint16_t* x, const int32_t* 
   dim3 grid((Imax + 15) / 16, s.T * s.k + s.T);
   if (s.d <= 4096)
     hipLaunchKernelGGL(k_gemv_gateup<1>, grid, dim3(256), 0, st, x, topk_ids, w13, s13, h_r, h_s, s.T, s.d, s.k, s.I,
-                       s.Is);
+                       s.Is, 0x000F000Fu, 0x43004300u);
   else
     hipLaunchKernelGGL(k_gemv_gateup<2>, grid, dim3(256), 0, st, x, topk_ids, w13, s13, h_r, h_s, s.T, s.d, s.k, s.I,
-                       s.Is);
+                       s.Is, 0x000F000Fu, 0x43004300u);
   return hipGetLastError();
 }
 

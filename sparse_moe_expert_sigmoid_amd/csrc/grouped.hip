@@ -92,6 +92,7 @@ struct GArgs {
   int T, d, E, k, I, Is;
   int nbands;
   uint32_t flags;
+  uint32_t dq_mask, dq_magic;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -106,6 +107,7 @@ struct TileCtx {
   uint32_t rdo[4];
   bool nok[4];
   int c0, wave, nit, nkb, Kdim, Iw, mlen, rbase, G, n, lane;
+  uint32_t dq_mask, dq_magic;  // 0x000F000F (uniform) and 0x64006400 (kept in a VGPR)
   bool ktail, shared;
 };
 
@@ -173,7 +175,7 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) a_cur[mt] = *reinterpret_cast<const half8*>(At + c.rdo[0] + mt * 16 * kRowBytes);
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) b_cur[ns] = dequant8_general(q[ns][0], d2[ns]);
+    for (int ns = 0; ns < 4; ++ns) b_cur[ns] = dequant8_general(q[ns][0], d2[ns], c.dq_mask, c.dq_magic);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       half8 a_nxt[NMT], b_nxt[4];
@@ -189,7 +191,7 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
           acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur[mt], b_cur[ns], acc[mt][ns], 0, 0, 0);
       if (s < 3) {
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) b_nxt[ns] = dequant8_general(q[ns][s + 1], d2[ns]);
+        for (int ns = 0; ns < 4; ++ns) b_nxt[ns] = dequant8_general(q[ns][s + 1], d2[ns], c.dq_mask, c.dq_magic);
         __builtin_amdgcn_sched_group_barrier(0x100, NMT, 0);  // DS reads of step s+1 first
 #pragma unroll
         for (int i = 0; i < 4 * NMT; ++i) {
@@ -397,6 +399,8 @@ __global__ __launch_bounds__(256, 1) void k_grouped(GArgs a) {
   for (int s4 = 0; s4 < 4; ++s4) c.rdo[s4] = rdo[s4];
   c.c0 = c0; c.wave = wave; c.nit = nit; c.nkb = nkb; c.Kdim = Kdim; c.Iw = Iw; c.mlen = mlen; c.rbase = rbase;
   c.G = G; c.n = n; c.lane = lane; c.ktail = ktail; c.shared = shared;
+  c.dq_mask = a.dq_mask;
+  c.dq_magic = a.dq_magic;
   switch ((mlen + 15) >> 4) {
     case 1: grouped_tile<GATEUP, 1>(a, c, As); break;
     case 2: grouped_tile<GATEUP, 2>(a, c, As); break;
@@ -469,6 +473,8 @@ static GArgs make_args(const Shape& s, const Routing& r, uint32_t flags) {
   a.mt_prefix = r.mt_prefix;
   a.T = s.T; a.d = s.d; a.E = s.E; a.k = s.k; a.I = s.I; a.Is = s.Is;
   a.flags = flags;
+  a.dq_mask = 0x000F000Fu;
+  a.dq_magic = 0x64006400u;
   return a;
 }
 

@@ -44,6 +44,14 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }
 
+// (a & mask) | bits in one v_and_or_b32.  gfx9 VOP3 encodings take at most one scalar or literal
+// operand, so the mask travels in an SGPR and `bits` in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask_s, uint32_t bits_v) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask_s), "v"(bits_v));
+  return r;
+}
+
 // ---------------------------------------------------------------- dequant to fp16 (MFMA operand)
 // Eight codes of one dword (element m in bits 4m..4m+3) -> eight fp16
 // weights (q - 8) * d, in the pair order (e0,e4) (e1,e5) (e2,e6) (e3,e7):
@@ -82,11 +90,11 @@ __device__ __forceinline__ half8 dequant8_fast(uint32_t w, const Q4Scale& s) {
   return half8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 
-__device__ __forceinline__ half8 dequant8_general(uint32_t w, half2v d2) {
+__device__ __forceinline__ half8 dequant8_general(uint32_t w, half2v d2, uint32_t M, uint32_t C) {
+  // M = 0x000F000F (SGPR), C = 0x64006400 (VGPR): p_j = (1024 + e_j, 1024 + e_{j+4}) as fp16 bits
   const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const uint32_t M = 0x000F000Fu, C = 0x64006400u;
   const uint32_t t = w >> 4;
-  const uint32_t p0 = (w & M) | C, p1 = (t & M) | C, p2 = ((w >> 8) & M) | C, p3 = ((t >> 8) & M) | C;
+  const uint32_t p0 = and_or(w, M, C), p1 = and_or(t, M, C), p2 = and_or(w >> 8, M, C), p3 = and_or(t >> 8, M, C);
   const half2v r0 = (__builtin_bit_cast(half2v, p0) - off) * d2;
   const half2v r1 = (__builtin_bit_cast(half2v, p1) - off) * d2;
   const half2v r2 = (__builtin_bit_cast(half2v, p2) - off) * d2;
@@ -106,17 +114,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // ---------------------------------------------------------------- GEMV helpers (bf16 dot2)
-// For v_dot2_f32_bf16 the codes are mapped to bf16 values 1 + q/16 (exact:
-// bits 0x3F80 | q << 3) and paired as (e0,e4), (e1,e5), (e2,e6), (e3,e7) of
-// a dword, so that every pair comes from one shift and one and-or.  With
-// x in matching pairs, sum x*(1 + q/16) = X + Q/16 where X = sum x and
-// Q = sum x*q; the block's contribution is then d * (16*dot - 24*X) =
-// d * (Q - 8X) = d * sum x*(q - 8).
-__device__ __forceinline__ void codes_bf16_pairs(uint32_t w, uint32_t out[4]) {
-  out[0] = ((w << 3) & 0x00780078u) | 0x3F803F80u;
-  out[1] = ((w >> 1) & 0x00780078u) | 0x3F803F80u;
-  out[2] = ((w >> 5) & 0x00780078u) | 0x3F803F80u;
-  out[3] = ((w >> 9) & 0x00780078u) | 0x3F803F80u;
+// For v_dot2_f32_bf16 each code becomes the bf16 value 128 + q (the nibble in
+// the low mantissa bits of 128.0, exact), paired as (e0,e4), (e1,e5), (e2,e6),
+// (e3,e7) of a dword so that every pair is one and-or (after at most one
+// shift).  With x in matching pairs, a block's dot is sum x*(128 + q) =
+// 128*X + Q (X = sum x, Q = sum x*q), and its contribution d * (dot - 136*X)
+// = d * (Q - 8X) = d * sum x*(q - 8).  `mask` (0x000F000F) and `magic`
+// (0x43004300) are passed in registers so that each pair is a single
+// v_and_or_b32.
+__device__ __forceinline__ void codes_bf16_pairs(uint32_t w, uint32_t mask, uint32_t magic, uint32_t out[4]) {
+  const uint32_t t = w >> 4;
+  out[0] = and_or(w, mask, magic);
+  out[1] = and_or(t, mask, magic);
+  out[2] = and_or(w >> 8, mask, magic);
+  out[3] = and_or(t >> 8, mask, magic);
 }
 // 8 consecutive bf16 values (u0..u3, each a pair (x_2m, x_2m+1)) -> pairs
 // (x0,x4), (x1,x5), (x2,x6), (x3,x7).

@@ -14,12 +14,12 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // Small T: one workgroup of 256 threads per expert.  Thread i holds 4
 // consecutive router weights at 4i + 1024m (m < NM), loaded once for all
-// tokens; tokens are processed 8 at a time and each dot product is reduced
+// tokens; tokens are processed TB at a time and each dot product is reduced
 // across the wavefront (DPP) and then across the 4 wavefronts in LDS.
-template <int NM>
+template <int NM, int TB>
 __global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict__ x, const float* __restrict__ W,
                                                      float* __restrict__ logits, int T, int d, int E) {
-  __shared__ float red[4][8];
+  __shared__ float red[4][TB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e = blockIdx.x;
   const float* wr = W + (size_t)e * d;
@@ -33,17 +33,17 @@ __global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict_
     col[m] = ok[m] ? c : d - 4;  // clamped: every load in bounds, masked below
     wv[m] = *reinterpret_cast<const float4*>(wr + col[m]);
   }
-  for (int t0 = 0; t0 < T; t0 += 8) {
-    uint2 xv[8][NM];
+  for (int t0 = 0; t0 < T; t0 += TB) {
+    uint2 xv[TB][NM];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < TB; ++i) {
       const int t = min(t0 + i, T - 1);
 #pragma unroll
       for (int m = 0; m < NM; ++m) xv[i][m] = *reinterpret_cast<const uint2*>(x + (size_t)t * d + col[m]);
     }
-    float acc[8];
+    float acc[TB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < TB; ++i) {
       float a = 0.f;
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
@@ -57,10 +57,10 @@ __global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict_
     }
     if (lane == 0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) red[wave][i] = acc[i];
+      for (int i = 0; i < TB; ++i) red[wave][i] = acc[i];
     }
     __syncthreads();
-    if (tid < 8 && t0 + tid < T)
+    if (tid < TB && t0 + tid < T)
       logits[(size_t)(t0 + tid) * E + e] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
     __syncthreads();
   }
@@ -139,8 +139,8 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
 // 64-bit sort keys (order-preserving bits of s + b, then the complement of
 // the expert id), so "larger key, then lower id" is a plain unsigned max.
 // Each of the k rounds takes the lane's best untaken key and reduces it over
-// the wavefront: four DPP steps inside each 16-lane row, then two
-// cross-row exchanges.  Every lane ends with the winner.
+// the wavefront: four DPP steps inside each 16-lane row, then the four row
+// winners are compared in scalar registers.  Every lane ends with the winner.
 __device__ __forceinline__ uint32_t ordered_bits(float f) {
   if (f != f) return 1u;  // NaN ranks below every number but above empty slots
   if (f == 0.f) f = 0.f;  // -0 and +0 are the same key (then the lower id wins)
@@ -151,12 +151,6 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
 template <int CTRL>
 __device__ __forceinline__ void argmax_step_dpp(uint32_t& hi, uint32_t& lo) {
   const uint32_t oh = (uint32_t)dpp_i<CTRL>((int)hi), ol = (uint32_t)dpp_i<CTRL>((int)lo);
-  const bool take = (oh > hi) || (oh == hi && ol > lo);
-  hi = take ? oh : hi;
-  lo = take ? ol : lo;
-}
-__device__ __forceinline__ void argmax_step_xor(uint32_t& hi, uint32_t& lo, int mask) {
-  const uint32_t oh = (uint32_t)__shfl_xor((int)hi, mask, 64), ol = (uint32_t)__shfl_xor((int)lo, mask, 64);
   const bool take = (oh > hi) || (oh == hi && ol > lo);
   hi = take ? oh : hi;
   lo = take ? ol : lo;
@@ -199,8 +193,21 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
     argmax_step_dpp<kDppXor2>(hi, lo);
     argmax_step_dpp<kDppHalfMirror>(hi, lo);
     argmax_step_dpp<kDppMirror>(hi, lo);
-    argmax_step_xor(hi, lo, 16);
-    argmax_step_xor(hi, lo, 32);
+    // every lane of a 16-lane row holds the row's best; combine the four rows in scalar registers
+    {
+      uint32_t bh = (uint32_t)__builtin_amdgcn_readlane((int)hi, 0), bl = (uint32_t)__builtin_amdgcn_readlane((int)lo, 0);
+#pragma unroll
+      for (int r = 1; r < 4; ++r) {
+        const uint32_t oh = (uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r);
+        const uint32_t ol = (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+        if (oh > bh || (oh == bh && ol > bl)) {
+          bh = oh;
+          bl = ol;
+        }
+      }
+      hi = bh;
+      lo = bl;
+    }
     const int win = (int)~lo;
     float s_sel = 0.f;
     if ((win & 63) == lane) {
@@ -211,28 +218,36 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
           s_sel = sc[i];
         }
     }
-    s_sel = __shfl(s_sel, win & 63, 64);
+    s_sel = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_sel), win & 63));
     if (lane == j) {
       my_s = s_sel;
       my_id = win;
     }
   }
   float tot = 0.f;
-  for (int j = 0; j < k; ++j) tot += __shfl(my_s, j, 64);  // slot order, same in every lane
+  for (int j = 0; j < k; ++j)  // slot order, same value in every lane
+    tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_s), j));
   if (lane < k) {
     ids[(size_t)t * k + lane] = my_id;
     w[(size_t)t * k + lane] = my_s / tot;
   }
 }
 
+template <int NM>
+static void router_gemv_tb(const Shape& s, const uint16_t* x, const float* w_router, float* logits, hipStream_t st) {
+  const dim3 grid(s.E), block(256);
+  if (s.T == 1) hipLaunchKernelGGL((k_router_gemv<NM, 1>), grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
+  else if (s.T <= 4) hipLaunchKernelGGL((k_router_gemv<NM, 4>), grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
+  else hipLaunchKernelGGL((k_router_gemv<NM, 8>), grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
+}
+
 hipError_t launch_router_gemv(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
                               hipStream_t st) {
   const int nm = (s.d + 1023) / 1024;
-  const dim3 grid(s.E), block(256);
-  if (nm <= 1) hipLaunchKernelGGL(k_router_gemv<1>, grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
-  else if (nm <= 2) hipLaunchKernelGGL(k_router_gemv<2>, grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
-  else if (nm <= 4) hipLaunchKernelGGL(k_router_gemv<4>, grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
-  else hipLaunchKernelGGL(k_router_gemv<8>, grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
+  if (nm <= 1) router_gemv_tb<1>(s, x, w_router, logits, st);
+  else if (nm <= 2) router_gemv_tb<2>(s, x, w_router, logits, st);
+  else if (nm <= 4) router_gemv_tb<4>(s, x, w_router, logits, st);
+  else router_gemv_tb<8>(s, x, w_router, logits, st);
   return hipGetLastError();
 }
 
