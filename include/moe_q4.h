@@ -68,8 +68,9 @@
  *     and grouped GEMMs that dequantise Q4 in registers into fp16 MFMA
  *     operands, with the shared expert as one more always-present group,
  *     then a fixed-order combine.
- *   Activations feed the fp16 grouped GEMMs: |x| and the SwiGLU outputs
- *   must stay within the fp16 range (65504) on that path.
+ *   The SwiGLU outputs are kept in fp16 between the two projections on
+ *   both paths, and x is converted to fp16 for the grouped GEMMs: those
+ *   values must stay within the fp16 range (65504).
  */
 #ifndef MOE_Q4_H
 #define MOE_Q4_H

@@ -82,8 +82,8 @@ ScratchLayout scratch_layout(const moe_dims* d, int path) {
   ScratchLayout S{};
   size_t off = 0;
   if (path == 0) {
-    S.h_r = off; off += align256(P * d->I * 4);
-    S.h_s = off; off += align256(T * d->I_shared * 4);
+    S.h_r = off; off += align256(P * d->I * 2);
+    S.h_s = off; off += align256(T * d->I_shared * 2);
   } else {
     S.x16 = off;    off += align256(T * d->d * 2);
     S.h_r = off;    off += align256(P * d->I * 2);
@@ -216,8 +216,8 @@ int moe_q4_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* 
   const moe::Q4 s13{w->s13.qs, w->s13.scales}, s2{w->s2.qs, w->s2.scales};
   (void)hipGetLastError();
   if (path == 0) {
-    float* h_r = reinterpret_cast<float*>(sb + S.h_r);
-    float* h_s = reinterpret_cast<float*>(sb + S.h_s);
+    _Float16* h_r = reinterpret_cast<_Float16*>(sb + S.h_r);
+    _Float16* h_s = reinterpret_cast<_Float16*>(sb + S.h_s);
     if (moe::launch_gemv_gateup(s, x_bf16, topk_ids, w13, s13, h_r, h_s, st) != hipSuccess) return MOE_EHIP;
     return hip_rc(moe::launch_gemv_down_combine(s, topk_ids, topk_w, w2, s2, h_r, h_s, y, st));
   }

@@ -18,20 +18,23 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // Gate+up with SwiGLU.  grid = (ceil(max(I, Is)/16), P + T); a workgroup of 4
 // wavefronts covers 16 h-rows of one job, a wavefront 4 h-rows (4 gate rows
-// and the 4 matching up rows).  Lane l owns Q4 blocks 2l and 2l+1 of every
-// 128-block chunk of the row (32 contiguous code bytes, 4 scale bytes).
-// h is written in fp32: h_r[p][I] for pair p, h_s[t][Is] for the shared expert.
+// and the 4 matching up rows).  Lane l owns Q4 blocks l and l + 64 of every
+// 128-block chunk of the row, so that each load instruction of a wavefront
+// covers 1 KiB of contiguous codes (or 128 contiguous scale bytes).
+// h is written in fp16 (h_r[p][I] for pair p, h_s[t][Is] for the shared
+// expert), each group of 8 stored in the pair order of the down kernel: slot
+// i of a group holds element 0,4,1,5,2,6,3,7 [i].
 template <int NCH>
 __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
-                                                     Q4 w13, Q4 s13, float* __restrict__ h_r, float* __restrict__ h_s,
+                                                     Q4 w13, Q4 s13, _Float16* __restrict__ h_r, _Float16* __restrict__ h_s,
                                                      int T, int d, int k, int I, int Is, uint32_t mask, uint32_t magic) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int job = blockIdx.y;
   const int P = T * k;
   int t, Iw;
   const uint8_t* qs;
   const uint16_t* sc;
-  float* out;
+  _Float16* out;
   if (job < P) {
     t = job / k;
     const int e = ids[job];
@@ -60,10 +63,12 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
     // unconditionally and stays in bounds) and their contribution is masked to zero.
     int bi[2];
     bool ok[2];
+    float okf[2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
-      const int b = 128 * c + 2 * lane + bb;
+      const int b = 128 * c + 64 * bb + lane;
       ok[bb] = b < nb;
+      okf[bb] = ok[bb] ? 1.f : 0.f;
       bi[bb] = ok[bb] ? b : nb - 1;
     }
     // 1) activation slices of this lane's blocks (L2-resident), issued first
@@ -112,22 +117,24 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
 #pragma unroll
           for (int m = 0; m < 4; ++m) dot = dot2_bf16(cp[m], xp[bb][dw][m], dot);
         }
-        const float dsc = ok[bb] ? fp16_bits_to_float(sv[r][bb]) : 0.f;
+        // masked by a multiply (not a select), so that the scale load is never made conditional
+        const float dsc = fp16_bits_to_float(sv[r][bb]) * okf[bb];
         acc[r] = fmaf(dsc, fmaf(-136.f, xs[bb], dot), acc[r]);
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < 8; ++r) acc[r] = wave_sum(acc[r]);
-  if (lane < 4) {
+  for (int r = 0; r < 8; ++r) acc[r] = wave_sum_hi(acc[r]);
+  if (lane >= 60) {  // lanes 60..63 hold the sums; lane 60 + r writes h-row i0 + r
     float g = acc[0], u = acc[4];
 #pragma unroll
     for (int r = 1; r < 4; ++r)
-      if (lane == r) {
+      if (lane == 60 + r) {
         g = acc[r];
         u = acc[4 + r];
       }
-    out[i0 + lane] = siluf_(g) * u;
+    const int i = i0 + lane - 60;
+    out[(i & ~7) + perm_slot(i & 7)] = (_Float16)(siluf_(g) * u);
   }
 }
 
@@ -139,14 +146,25 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
 // lane l%32 owns block l%32 (+32c) of the row and keeps the matching 32 h
 // values in registers.  Partial dot products meet in LDS and one thread per
 // row sums them in slot order: y = sum_j w_j * dot_j, then + shared.
+//
+// Dot products use v_dot2_f32_f16 on fp16 codes built with one and-or each:
+// for a dword w of codes (element m in bits 4m..4m+3), w & 0x000F000F placed
+// in the mantissa of 1024.0 gives the pair (1024 + e0, 1024 + e4), and
+// w & 0x00F000F0 gives (1024 + 16 e1, 1024 + 16 e5), both exact; w >> 8 gives
+// elements 2, 6 and 3, 7 the same way.  h arrives in the matching pair order
+// (h0,h4) (h1,h5) (h2,h6) (h3,h7); the pairs that meet a 16x code are taken
+// as h/16 (exact).  With A = sum of h over the 1024+q pairs and B over the
+// 1024+16q pairs, a block's dot is 1024 A + 64 B + sum h*q, so starting each
+// block's accumulation at -(1032 A + 72 B) leaves sum h*(q - 8).
 template <int NCH>
 __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __restrict__ ids,
                                                             const float* __restrict__ topk_w, Q4 w2, Q4 s2,
-                                                            const float* __restrict__ h_r,
-                                                            const float* __restrict__ h_s, float* __restrict__ y,
-                                                            int T, int d, int k, int I, int Is) {
+                                                            const _Float16* __restrict__ h_r,
+                                                            const _Float16* __restrict__ h_s, float* __restrict__ y,
+                                                            int T, int d, int k, int I, int Is, uint32_t mask_lo,
+                                                            uint32_t mask_hi, uint32_t magic) {
   __shared__ float part[kMaxTopK + 1][16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
   const int t = blockIdx.y;
   const int n0 = blockIdx.x * 16;
@@ -154,7 +172,7 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
   for (int slot = wave; slot <= k; slot += nw) {
     const uint8_t* qs;
     const uint16_t* sc;
-    const float* h;
+    const _Float16* h;
     int Kw;
     if (slot < k) {
       const int e = ids[(size_t)t * k + slot];
@@ -172,34 +190,41 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
     const size_t qstride = Kw / 2, sstride = Kw / 32;
     // clamped block and row indices: every load is issued unconditionally and stays in bounds
     int bi[NCH];
-    bool ok[NCH];
+    float okf[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int b = bl + 32 * c;
-      ok[c] = b < nbk;
-      bi[c] = ok[c] ? b : nbk - 1;
+      okf[c] = b < nbk ? 1.f : 0.f;
+      bi[c] = b < nbk ? b : nbk - 1;
     }
-    // 1) the matching h values (L2-resident)
-    float hv[NCH][32];
-    float hsum[NCH];
+    // 1) the matching h values (L2-resident): pairs, the 1024+16q pairs pre-divided by 16
+    u32x4 hp[NCH][4];
+    float c0[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      float s = 0.f;
+      float sa = 0.f, sb = 0.f;
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const float4 f = *reinterpret_cast<const float4*>(h + 32 * bi[c] + 4 * v);
-        hv[c][4 * v + 0] = f.x;
-        hv[c][4 * v + 1] = f.y;
-        hv[c][4 * v + 2] = f.z;
-        hv[c][4 * v + 3] = f.w;
-        s += (f.x + f.y) + (f.z + f.w);
+      for (int g = 0; g < 4; ++g) {
+        u32x4 v = ld16(h + 32 * bi[c] + 8 * g);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const half2v hv = as_half2(v[m]);
+          const float s2v = (float)hv[0] + (float)hv[1];
+          if (m & 1) {
+            sb += s2v;
+            v[m] = __builtin_bit_cast(uint32_t, hv * half2v{(_Float16)0.0625f, (_Float16)0.0625f});
+          } else {
+            sa += s2v;
+          }
+        }
+        hp[c][g] = v;
       }
-      hsum[c] = s;
+      c0[c] = -(1032.f * sa + 72.f * sb);
     }
-    constexpr int RB = 8 / NCH;  // rows per load batch
+    // 2) codes and scales of RB row pairs for this lane's blocks, all in flight together; 3) dots
+    constexpr int RB = 8 / NCH;
 #pragma unroll
     for (int r0 = 0; r0 < 8; r0 += RB) {
-      // 2) codes and scales of RB rows for this lane's blocks, all in flight together
       u32x4 q[RB][NCH];
       uint32_t sv[RB][NCH];
 #pragma unroll
@@ -211,27 +236,30 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
           sv[rr][c] = sc[n * sstride + bi[c]];
         }
       }
-      // 3) dot products: codes converted exactly with v_cvt_f32_ubyte, offset folded per block
+      float acc[RB];
 #pragma unroll
       for (int rr = 0; rr < RB; ++rr) {
-        float acc = 0.f;
+        acc[rr] = 0.f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          float dot = 0.f;
+          float dot = c0[c];
 #pragma unroll
-          for (int dw = 0; dw < 4; ++dw) {
-            const uint32_t lo = q[rr][c][dw] & 0x0F0F0F0Fu, hi = (q[rr][c][dw] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-            for (int bt = 0; bt < 4; ++bt) {
-              dot = fmaf(hv[c][8 * dw + 2 * bt], (float)((lo >> (8 * bt)) & 0xFFu), dot);
-              dot = fmaf(hv[c][8 * dw + 2 * bt + 1], (float)((hi >> (8 * bt)) & 0xFFu), dot);
-            }
+          for (int g = 0; g < 4; ++g) {
+            const uint32_t w = q[rr][c][g], w8 = w >> 8;
+            dot = dot2_f16(and_or(w, mask_lo, magic), hp[c][g][0], dot);
+            dot = dot2_f16(and_or(w, mask_hi, magic), hp[c][g][1], dot);
+            dot = dot2_f16(and_or(w8, mask_lo, magic), hp[c][g][2], dot);
+            dot = dot2_f16(and_or(w8, mask_hi, magic), hp[c][g][3], dot);
           }
-          const float dsc = ok[c] ? fp16_bits_to_float(sv[rr][c]) : 0.f;
-          acc = fmaf(dsc, fmaf(-8.f, hsum[c], dot), acc);
+          // masked by a multiply (not a select), so that the scale load is never made conditional
+          acc[rr] = fmaf(fp16_bits_to_float(sv[rr][c]) * okf[c], dot, acc[rr]);
         }
-        acc = half_wave_sum(acc);
-        if (bl == 0) part[slot][2 * (r0 + rr) + half] = acc;
+      }
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) acc[rr] = half_wave_sum_hi(acc[rr]);
+      if (bl == 16) {
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) part[slot][2 * (r0 + rr) + half] = acc[rr];
       }
     }
   }
@@ -247,7 +275,7 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
 }
 
 hipError_t launch_gemv_gateup(const Shape& s, const uint16_t* x, const int32_t* topk_ids, Q4 w13, Q4 s13,
-                              float* h_r, float* h_s, hipStream_t st) {
+                              _Float16* h_r, _Float16* h_s, hipStream_t st) {
   const int Imax = s.I > s.Is ? s.I : s.Is;
   dim3 grid((Imax + 15) / 16, s.T * s.k + s.T);
   if (s.d <= 4096)
@@ -260,16 +288,16 @@ hipError_t launch_gemv_gateup(const Shape& s, const uint16_t* x, const int32_t* 
 }
 
 hipError_t launch_gemv_down_combine(const Shape& s, const int32_t* topk_ids, const float* topk_w, Q4 w2, Q4 s2,
-                                    const float* h_r, const float* h_s, float* y, hipStream_t st) {
+                                    const _Float16* h_r, const _Float16* h_s, float* y, hipStream_t st) {
   const int nw = (s.k + 1) < 16 ? (s.k + 1) : 16;
   const int Imax = s.I > s.Is ? s.I : s.Is;
   dim3 grid((s.d + 15) / 16, s.T);
   if (Imax <= 1024)
     hipLaunchKernelGGL(k_gemv_down_combine<1>, grid, dim3(64 * nw), 0, st, topk_ids, topk_w, w2, s2, h_r, h_s, y, s.T,
-                       s.d, s.k, s.I, s.Is);
+                       s.d, s.k, s.I, s.Is, 0x000F000Fu, 0x00F000F0u, 0x64006400u);
   else
     hipLaunchKernelGGL(k_gemv_down_combine<2>, grid, dim3(64 * nw), 0, st, topk_ids, topk_w, w2, s2, h_r, h_s, y, s.T,
-                       s.d, s.k, s.I, s.Is);
+                       s.d, s.k, s.I, s.Is, 0x000F000Fu, 0x00F000F0u, 0x64006400u);
   return hipGetLastError();
 }
 

@@ -37,6 +37,10 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 __device__ __forceinline__ uint32_t ld4(const void* p) {
   return *reinterpret_cast<const uint32_t*>(p);
 }
+// Reinterpret by value.  (clang's __builtin_bit_cast applied directly to an
+// element of an ext_vector_type lvalue, as in bit_cast(v[m]), reads element 0
+// whatever m is; routing the element through a by-value parameter avoids it.)
+__device__ __forceinline__ half2v as_half2(uint32_t bits) { return __builtin_bit_cast(half2v, bits); }
 __device__ __forceinline__ float fp16_bits_to_float(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
@@ -137,6 +141,9 @@ __device__ __forceinline__ void x_bf16_pairs(const u32x4 u, uint32_t out[4]) {
   out[2] = __builtin_amdgcn_perm(u[3], u[1], 0x05040100u);
   out[3] = __builtin_amdgcn_perm(u[3], u[1], 0x07060302u);
 }
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c, false);
+}
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
@@ -144,16 +151,24 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // ---------------------------------------------------------------- reductions
 // DPP lane exchanges (no LDS traffic): quad xor 1, quad xor 2, mirror inside
 // 8 lanes, mirror inside 16 lanes.  After the four steps every lane of a
-// 16-lane row holds the row's reduction; rows are then combined with two
-// cross-lane permutes.
+// 16-lane row holds the row's reduction.  The gfx9 row broadcasts then carry
+// lane 15 of each row into the next row (row_bcast:15) and lane 31 into rows
+// 2 and 3 (row_bcast:31).
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // row_half_mirror
 constexpr int kDppMirror = 0x140;     // row_mirror
+constexpr int kDppBcast15 = 0x142;    // row_bcast:15
+constexpr int kDppBcast31 = 0x143;    // row_bcast:31
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f_rows(float v) {  // rows outside ROW_MASK receive 0
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
 }
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
@@ -167,15 +182,22 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f<kDppMirror>(v);
   return v;
 }
+// Sum over each 32-lane half; the result is valid in lanes 16..31 (first
+// half) and 48..63 (second half).
+__device__ __forceinline__ float half_wave_sum_hi(float v) {
+  v = row16_sum(v);
+  return v + dpp_f_rows<kDppBcast15, 0xA>(v);
+}
+// Sum over the wavefront; the result is valid in lanes 48..63.
+__device__ __forceinline__ float wave_sum_hi(float v) {
+  v = half_wave_sum_hi(v);
+  return v + dpp_f_rows<kDppBcast31, 0xC>(v);
+}
+// Sum over the wavefront, in every lane.
 __device__ __forceinline__ float wave_sum(float v) {
   v = row16_sum(v);
   v += __shfl_xor(v, 16, kWave);
   v += __shfl_xor(v, 32, kWave);
-  return v;
-}
-__device__ __forceinline__ float half_wave_sum(float v) {  // within each 32-lane half
-  v = row16_sum(v);
-  v += __shfl_xor(v, 16, kWave);
   return v;
 }
 

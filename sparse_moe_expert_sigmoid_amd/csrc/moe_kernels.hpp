@@ -43,9 +43,9 @@ hipError_t launch_build(const Shape& s, const int32_t* topk_ids, const Routing& 
 
 // gemv.hip  (small-T path)
 hipError_t launch_gemv_gateup(const Shape& s, const uint16_t* x, const int32_t* topk_ids, Q4 w13, Q4 s13,
-                              float* h_r, float* h_s, hipStream_t st);
+                              _Float16* h_r, _Float16* h_s, hipStream_t st);
 hipError_t launch_gemv_down_combine(const Shape& s, const int32_t* topk_ids, const float* topk_w, Q4 w2, Q4 s2,
-                                    const float* h_r, const float* h_s, float* y, hipStream_t st);
+                                    const _Float16* h_r, const _Float16* h_s, float* y, hipStream_t st);
 
 // grouped.hip  (grouped path)
 struct GroupedOut {

@@ -20,17 +20,17 @@ template <int NM, int TB>
 __global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict__ x, const float* __restrict__ W,
                                                      float* __restrict__ logits, int T, int d, int E) {
   __shared__ float red[4][TB];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int e = blockIdx.x;
   const float* wr = W + (size_t)e * d;
   float4 wv[NM];
-  bool ok[NM];
+  float okf[NM];
   int col[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     const int c = 4 * tid + 1024 * m;
-    ok[m] = c < d;
-    col[m] = ok[m] ? c : d - 4;  // clamped: every load in bounds, masked below
+    okf[m] = c < d ? 1.f : 0.f;
+    col[m] = c < d ? c : d - 4;  // clamped: every load in bounds, masked below
     wv[m] = *reinterpret_cast<const float4*>(wr + col[m]);
   }
   for (int t0 = 0; t0 < T; t0 += TB) {
@@ -51,11 +51,11 @@ __global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict_
         p = fmaf(wv[m].y, bf16_bits_to_float(xv[i][m].x >> 16), p);
         p = fmaf(wv[m].z, bf16_bits_to_float(xv[i][m].y & 0xFFFFu), p);
         p = fmaf(wv[m].w, bf16_bits_to_float(xv[i][m].y >> 16), p);
-        a += ok[m] ? p : 0.f;
+        a = fmaf(okf[m], p, a);
       }
-      acc[i] = wave_sum(a);
+      acc[i] = wave_sum_hi(a);
     }
-    if (lane == 0) {
+    if (lane == 63) {
 #pragma unroll
       for (int i = 0; i < TB; ++i) red[wave][i] = acc[i];
     }
@@ -64,6 +64,24 @@ __global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict_
       logits[(size_t)(t0 + tid) * E + e] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
     __syncthreads();
   }
+}
+
+template <int NM>
+static void router_gemv_tb(const Shape& s, const uint16_t* x, const float* w_router, float* logits, hipStream_t st) {
+  const dim3 grid(s.E), block(256);
+  if (s.T == 1) hipLaunchKernelGGL((k_router_gemv<NM, 1>), grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
+  else if (s.T <= 4) hipLaunchKernelGGL((k_router_gemv<NM, 4>), grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
+  else hipLaunchKernelGGL((k_router_gemv<NM, 8>), grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
+}
+
+hipError_t launch_router_gemv(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
+                              hipStream_t st) {
+  const int nm = (s.d + 1023) / 1024;
+  if (nm <= 1) router_gemv_tb<1>(s, x, w_router, logits, st);
+  else if (nm <= 2) router_gemv_tb<2>(s, x, w_router, logits, st);
+  else if (nm <= 4) router_gemv_tb<4>(s, x, w_router, logits, st);
+  else router_gemv_tb<8>(s, x, w_router, logits, st);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -136,11 +154,11 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // Top-k: one wavefront per token.  Lane l holds experts l, l+64, ... as
-// 64-bit sort keys (order-preserving bits of s + b, then the complement of
-// the expert id), so "larger key, then lower id" is a plain unsigned max.
-// Each of the k rounds takes the lane's best untaken key and reduces it over
-// the wavefront: four DPP steps inside each 16-lane row, then the four row
-// winners are compared in scalar registers.  Every lane ends with the winner.
+// order-preserving unsigned keys of s + b (empty and taken slots hold 0,
+// below every real key).  Each of the k rounds finds the largest key (per
+// lane, then four DPP max steps inside each 16-lane row, then the four row
+// maxima in scalar registers) and then the lowest expert id that holds it,
+// from one ballot per key register: ties go to the lower id.
 __device__ __forceinline__ uint32_t ordered_bits(float f) {
   if (f != f) return 1u;  // NaN ranks below every number but above empty slots
   if (f == 0.f) f = 0.f;  // -0 and +0 are the same key (then the lower id wins)
@@ -149,74 +167,61 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
 }
 
 template <int CTRL>
-__device__ __forceinline__ void argmax_step_dpp(uint32_t& hi, uint32_t& lo) {
-  const uint32_t oh = (uint32_t)dpp_i<CTRL>((int)hi), ol = (uint32_t)dpp_i<CTRL>((int)lo);
-  const bool take = (oh > hi) || (oh == hi && ol > lo);
-  hi = take ? oh : hi;
-  lo = take ? ol : lo;
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  const uint32_t o = (uint32_t)dpp_i<CTRL>((int)v);
+  return o > v ? o : v;
 }
 
+// Selection for one token by one wavefront: writes ids[0..k) and w[0..k).
 template <int NPER>
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
-                                              int32_t* __restrict__ ids, float* __restrict__ w, int T, int E,
-                                              int k) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+__device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, const float* __restrict__ bias,
+                                          int32_t* __restrict__ ids, float* __restrict__ w, int E, int k, int lane) {
   uint32_t key[NPER];
   float sc[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
-      const float s = sigmoidf_(logits[(size_t)t * E + e]);
+      const float s = sigmoidf_(lrow[e]);
       key[i] = ordered_bits(s + bias[e]);
       sc[i] = s;
     } else {
-      key[i] = 0u;  // empty slot: never wins (every real key is >= 1)
+      key[i] = 0u;
       sc[i] = 0.f;
     }
   }
   float my_s = 0.f;
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    uint32_t hi = 0u, lo = 0u;
+    uint32_t m = key[0];
+#pragma unroll
+    for (int i = 1; i < NPER; ++i) m = key[i] > m ? key[i] : m;
+    m = dpp_max_u32<kDppXor1>(m);
+    m = dpp_max_u32<kDppXor2>(m);
+    m = dpp_max_u32<kDppHalfMirror>(m);
+    m = dpp_max_u32<kDppMirror>(m);
+    uint32_t M = (uint32_t)__builtin_amdgcn_readlane((int)m, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+      const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)m, 16 * r);
+      M = o > M ? o : M;
+    }
+    // lowest expert id holding M: the first key register with a hit, then its lowest lane
+    int win = 0;
+    bool found = false;
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
-      const uint32_t l2 = ~(uint32_t)(lane + 64 * i);
-      if (key[i] > hi || (key[i] == hi && l2 > lo)) {
-        hi = key[i];
-        lo = l2;
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(key[i] == M);
+      if (!found && hit != 0) {
+        win = 64 * i + (int)__builtin_ctzll(hit);
+        found = true;
       }
     }
-    argmax_step_dpp<kDppXor1>(hi, lo);
-    argmax_step_dpp<kDppXor2>(hi, lo);
-    argmax_step_dpp<kDppHalfMirror>(hi, lo);
-    argmax_step_dpp<kDppMirror>(hi, lo);
-    // every lane of a 16-lane row holds the row's best; combine the four rows in scalar registers
-    {
-      uint32_t bh = (uint32_t)__builtin_amdgcn_readlane((int)hi, 0), bl = (uint32_t)__builtin_amdgcn_readlane((int)lo, 0);
+    float s_sel = sc[0];
 #pragma unroll
-      for (int r = 1; r < 4; ++r) {
-        const uint32_t oh = (uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r);
-        const uint32_t ol = (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
-        if (oh > bh || (oh == bh && ol > bl)) {
-          bh = oh;
-          bl = ol;
-        }
-      }
-      hi = bh;
-      lo = bl;
-    }
-    const int win = (int)~lo;
-    float s_sel = 0.f;
-    if ((win & 63) == lane) {
-#pragma unroll
-      for (int i = 0; i < NPER; ++i)
-        if (i == (win >> 6)) {
-          key[i] = 0u;  // taken
-          s_sel = sc[i];
-        }
+    for (int i = 0; i < NPER; ++i) {
+      if ((win >> 6) == i) s_sel = sc[i];
+      if (lane + 64 * i == win) key[i] = 0u;  // taken
     }
     s_sel = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_sel), win & 63));
     if (lane == j) {
@@ -228,27 +233,19 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   for (int j = 0; j < k; ++j)  // slot order, same value in every lane
     tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_s), j));
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    w[(size_t)t * k + lane] = my_s / tot;
+    ids[lane] = my_id;
+    w[lane] = my_s / tot;
   }
 }
 
-template <int NM>
-static void router_gemv_tb(const Shape& s, const uint16_t* x, const float* w_router, float* logits, hipStream_t st) {
-  const dim3 grid(s.E), block(256);
-  if (s.T == 1) hipLaunchKernelGGL((k_router_gemv<NM, 1>), grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
-  else if (s.T <= 4) hipLaunchKernelGGL((k_router_gemv<NM, 4>), grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
-  else hipLaunchKernelGGL((k_router_gemv<NM, 8>), grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
-}
-
-hipError_t launch_router_gemv(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
-                              hipStream_t st) {
-  const int nm = (s.d + 1023) / 1024;
-  if (nm <= 1) router_gemv_tb<1>(s, x, w_router, logits, st);
-  else if (nm <= 2) router_gemv_tb<2>(s, x, w_router, logits, st);
-  else if (nm <= 4) router_gemv_tb<4>(s, x, w_router, logits, st);
-  else router_gemv_tb<8>(s, x, w_router, logits, st);
-  return hipGetLastError();
+template <int NPER>
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
+                                              int32_t* __restrict__ ids, float* __restrict__ w, int T, int E,
+                                              int k) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_wave<NPER>(logits + (size_t)t * E, bias, ids + (size_t)t * k, w + (size_t)t * k, E, k, lane);
 }
 
 hipError_t launch_router_mfma(const Shape& s, const uint16_t* x, const float* w_router, float* logits,

@@ -89,7 +89,7 @@ def test_workspace_sizes_closed_form(dims):
     offs = [lay[n] for n in ("logits", "counts", "offsets", "sorted_pair", "pair_pos", "row_expert",
                              "group_order", "mt_prefix", "chunk_counts")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    gemv = align(P * I * 4) + align(T * Is * 4)
+    gemv = align(P * I * 2) + align(T * Is * 2)
     grouped = align(T * dd * 2) + align(P * I * 2) + align(T * Is * 2) + align(P * dd * 4) + align(T * dd * 4)
     want = gemv if moe.moe_path(dims) == 0 else grouped
     assert moe.moe_scratch_bytes(dims) == want
