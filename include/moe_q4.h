@@ -69,8 +69,9 @@
  *     operands, with the shared expert as one more always-present group,
  *     then a fixed-order combine.
  *   The SwiGLU outputs are kept in fp16 between the two projections on
- *   both paths, and x is converted to fp16 for the grouped GEMMs: those
- *   values must stay within the fp16 range (65504).
+ *   both paths; on the grouped path x is converted to fp16 for the GEMMs
+ *   and every expert's down-projection output is stored in fp16 before the
+ *   combine: those values must stay within the fp16 range (65504).
  */
 #ifndef MOE_Q4_H
 #define MOE_Q4_H

@@ -88,8 +88,8 @@ ScratchLayout scratch_layout(const moe_dims* d, int path) {
     S.x16 = off;    off += align256(T * d->d * 2);
     S.h_r = off;    off += align256(P * d->I * 2);
     S.h_s = off;    off += align256(T * d->I_shared * 2);
-    S.y_pair = off; off += align256(P * d->d * 4);
-    S.y_s = off;    off += align256(T * d->d * 4);
+    S.y_pair = off; off += align256(P * d->d * 2);
+    S.y_s = off;    off += align256(T * d->d * 2);
   }
   S.total = off;
   return S;
@@ -226,8 +226,8 @@ int moe_q4_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* 
   o.x16 = reinterpret_cast<_Float16*>(sb + S.x16);
   o.h_r = reinterpret_cast<_Float16*>(sb + S.h_r);
   o.h_s = reinterpret_cast<_Float16*>(sb + S.h_s);
-  o.y_pair = reinterpret_cast<float*>(sb + S.y_pair);
-  o.y_s = reinterpret_cast<float*>(sb + S.y_s);
+  o.y_pair = reinterpret_cast<_Float16*>(sb + S.y_pair);
+  o.y_s = reinterpret_cast<_Float16*>(sb + S.y_s);
   if (moe::launch_grouped_gateup(s, x_bf16, r, w13, s13, o, flags, st) != hipSuccess) return MOE_EHIP;
   if (moe::launch_grouped_down(s, r, w2, s2, o, flags, st) != hipSuccess) return MOE_EHIP;
   return hip_rc(moe::launch_combine(s, topk_w, r, o, y, st));

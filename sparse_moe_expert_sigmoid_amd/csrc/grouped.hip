@@ -49,6 +49,10 @@ constexpr int kRowBytes = kGroupedBK * 2;
 constexpr int kTileBytes = kGroupedBM * kRowBytes;  // 32 KB
 constexpr int kStages = 3;        // pipeline depth (LDS ring of kStages activation tiles)
 constexpr int kLoadsPerStep = 16; // vector-memory ops per lane per K step: 8 tile loads, 4 code blocks, 4 scales
+// A buffer offset past every buffer this path addresses (all are below 2^32 - 64 bytes): buffer
+// loads at it return zeros without a memory access.  The range check uses the per-lane offset
+// only, so it holds whatever scalar offset the K loop adds.
+constexpr uint32_t kOffsetOOB = 0xFFFFFFF0u;
 
 // s_waitcnt vmcnt(N), leaving the LDS and export counters alone (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -82,8 +86,8 @@ struct GArgs {
   Q4 ws;                    // shared expert (s13 or s2)
   _Float16* h_r;            // gate+up outputs (element order permuted in groups of 8)
   _Float16* h_s;
-  float* y_r;               // down outputs
-  float* y_s;
+  _Float16* y_r;            // down outputs (fp16)
+  _Float16* y_s;
   const int* counts;
   const int* offsets;
   const int* sorted_pair;
@@ -270,11 +274,11 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
           out[(size_t)(c.rbase + row) * c.Iw + (col & ~7) + perm_slot(col & 7)] = (_Float16)(siluf_(gv) * uv);
         }
       } else {
-        float* out = c.shared ? a.y_s : a.y_r;
+        _Float16* out = c.shared ? a.y_s : a.y_r;
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns) {
           if (!c.nok[ns]) continue;
-          out[(size_t)(c.rbase + row) * a.d + c.c0 + 16 * ns + c.n] = acc[mt][ns][i];
+          out[(size_t)(c.rbase + row) * a.d + c.c0 + 16 * ns + c.n] = (_Float16)acc[mt][ns][i];
         }
       }
     }
@@ -347,13 +351,15 @@ __global__ __launch_bounds__(256, 1) void k_grouped(GArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = 32 * wave + 4 * i + (lane >> 4);
-    const int rr = row < mlen ? row : 0;  // rows past the group re-read row 0: finite, and never stored
+    const int rr = row < mlen ? row : 0;
     uint32_t arow;
     if (GATEUP)
       arow = shared ? (uint32_t)(m0 + rr) : (uint32_t)(a.sorted_pair[rbase + rr] / a.k);
     else
       arow = (uint32_t)(rbase + rr);
-    aoff[i] = arow * (uint32_t)Kdim * 2u + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+    // Rows past the group get an offset beyond the buffer: the load still counts in vmcnt but
+    // fetches nothing and fills its LDS slot with zeros (those rows are never stored).
+    aoff[i] = row < mlen ? arow * (uint32_t)Kdim * 2u + 16u * (uint32_t)((lane & 15) ^ (row & 15)) : kOffsetOOB;
   }
   const int nit = (Kdim + BK - 1) / BK;
   const bool ktail = (Kdim % BK) != 0;
@@ -434,27 +440,39 @@ __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x
 }
 
 // Combine: y[t] = (sum_j w[t,j] * y_pair[pair_pos[t*k+j]]) + y_shared[t], j ascending, no atomics.
+// Per-pair and shared outputs arrive in fp16; every thread sums 8 columns in fp32.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ topk_w, const int* __restrict__ pair_pos,
-                                                 const float* __restrict__ y_r, const float* __restrict__ y_s,
+                                                 const _Float16* __restrict__ y_r, const _Float16* __restrict__ y_s,
                                                  float* __restrict__ y, int d, int k) {
-  const int per_row = (d + 1023) / 1024;
+  const int per_row = (d + 2047) / 2048;
   const int t = blockIdx.x / per_row;
-  const int col = ((blockIdx.x % per_row) * 256 + threadIdx.x) * 4;
+  const int col = ((blockIdx.x % per_row) * 256 + threadIdx.x) * 8;
   if (col >= d) return;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   for (int j = 0; j < k; ++j) {
     const int pp = pair_pos[(size_t)t * k + j];
     if (pp < 0) continue;
     const float w = topk_w[(size_t)t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(y_r + (size_t)pp * d + col);
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
+    const u32x4 v = ld16(y_r + (size_t)pp * d + col);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const half2v h = as_half2(v[m]);
+      acc[2 * m] = fmaf(w, (float)h[0], acc[2 * m]);
+      acc[2 * m + 1] = fmaf(w, (float)h[1], acc[2 * m + 1]);
+    }
   }
-  const float4 s = *reinterpret_cast<const float4*>(y_s + (size_t)t * d + col);
-  *reinterpret_cast<float4*>(y + (size_t)t * d + col) =
-      make_float4(acc.x + s.x, acc.y + s.y, acc.z + s.z, acc.w + s.w);
+  const u32x4 sv = ld16(y_s + (size_t)t * d + col);
+  float4 o0, o1;
+  {
+    const half2v h0 = as_half2(sv[0]), h1 = as_half2(sv[1]), h2 = as_half2(sv[2]), h3 = as_half2(sv[3]);
+    o0 = make_float4(acc[0] + (float)h0[0], acc[1] + (float)h0[1], acc[2] + (float)h1[0], acc[3] + (float)h1[1]);
+    o1 = make_float4(acc[4] + (float)h2[0], acc[5] + (float)h2[1], acc[6] + (float)h3[0], acc[7] + (float)h3[1]);
+  }
+  float4* yo = reinterpret_cast<float4*>(y + (size_t)t * d + col);
+  yo[0] = o0;
+  yo[1] = o1;
 }
 
 int grouped_max_mtiles(const Shape& s) {
@@ -518,7 +536,7 @@ hipError_t launch_grouped_down(const Shape& s, const Routing& r, Q4 w2, Q4 s2, c
 
 hipError_t launch_combine(const Shape& s, const float* topk_w, const Routing& r, const GroupedOut& o, float* y,
                           hipStream_t st) {
-  dim3 grid(((s.d + 1023) / 1024) * s.T);
+  dim3 grid(((s.d + 2047) / 2048) * s.T);
   hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, st, topk_w, r.pair_pos, o.y_pair, o.y_s, y, s.d, s.k);
   return hipGetLastError();
 }

@@ -52,8 +52,8 @@ struct GroupedOut {
   _Float16* x16;   // [T][d]   fp16 copy of x
   _Float16* h_r;   // [P][I]   sorted rows
   _Float16* h_s;   // [T][Is]
-  float* y_pair;   // [P][d]   sorted rows
-  float* y_s;      // [T][d]
+  _Float16* y_pair;  // [P][d]   sorted rows
+  _Float16* y_s;     // [T][d]
 };
 int grouped_max_mtiles(const Shape& s);
 hipError_t launch_grouped_gateup(const Shape& s, const uint16_t* x, const Routing& r, Q4 w13, Q4 s13,

@@ -87,43 +87,41 @@ hipError_t launch_router_gemv(const Shape& s, const uint16_t* x, const float* w_
 // ---------------------------------------------------------------------------
 // Larger T: bf16 MFMA.  x is bf16 already; each fp32 router weight is split
 // into hi = bf16(w) and lo = bf16(w - hi) so that two bf16 MFMAs reproduce
-// the fp32 product to about 2^-17 relative.  A workgroup computes 64 tokens x
-// 64 experts; wave w owns experts [16w, 16w+16) of the block and all 64
-// tokens (four 16x16x32 MFMA tiles per K-step, hi and lo).
+// the fp32 product to about 2^-17 relative.  A workgroup computes one 16 x 16
+// tile (16 tokens x 16 experts); its four wavefronts take interleaved quarters
+// of K (steps of 32) and their partial tiles are summed in LDS in a fixed
+// order.  With 16 x 16 tiles the grid has T/16 * E/16 workgroups, enough
+// wavefronts per SIMD to hide the load latency without software pipelining.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kRouterUnroll = 8;  // K steps whose loads are issued together
 
 __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict__ x, const float* __restrict__ W,
                                                      float* __restrict__ logits, int T, int d, int E) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ floatx4 part[4][64];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, G = lane >> 4;
-  const int t0 = blockIdx.x * 64;
-  const int e0 = blockIdx.y * 64 + wave * 16;
-  if (e0 >= E) return;  // whole wave idle: no barriers in this kernel
-  const bool e_ok = (e0 + n) < E;
-  const float* wrow = W + (size_t)(e_ok ? e0 + n : 0) * d + 8 * G;
-  const uint16_t* xrow[4];
-  bool t_ok[4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int t = t0 + 16 * mt + n;
-    t_ok[mt] = t < T;
-    xrow[mt] = x + (size_t)(t_ok[mt] ? t : 0) * d + 8 * G;
+  // Workgroups go round-robin over the 8 XCDs (own L2 each).  When the expert blocks divide evenly,
+  // XCD x takes a fixed eighth of them for every token block, so each L2 holds only its eighth of
+  // the router weights while the token blocks stream past.
+  const int neb = (E + 15) / 16;
+  int eb, tb;
+  if (neb % 8 == 0) {
+    const int per = neb / 8, item = blockIdx.x >> 3;
+    eb = (blockIdx.x & 7) * per + item % per;
+    tb = item / per;
+  } else {
+    eb = blockIdx.x % neb;
+    tb = blockIdx.x / neb;
   }
-  floatx4 acc[4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < d; k0 += 32) {
-    float wv[8];
-    if (e_ok) {
-      const float4 w0 = *reinterpret_cast<const float4*>(wrow + k0);
-      const float4 w1 = *reinterpret_cast<const float4*>(wrow + k0 + 4);
-      wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
-      wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) wv[i] = 0.f;
-    }
+  const int t0 = tb * 16, e0 = eb * 16;
+  const int t = min(t0 + n, T - 1), e = min(e0 + n, E - 1);  // clamped rows: computed, never stored
+  const uint16_t* xrow = x + (size_t)t * d + 8 * G;
+  const float* wrow = W + (size_t)e * d + 8 * G;
+  const int nsteps = d / 32;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto step = [&](const u32x4& a, const float4& w0, const float4& w1) __attribute__((always_inline)) {
+    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     bf16x8 bhi, blo;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -131,24 +129,38 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
       bhi[i] = h;
       blo[i] = (__bf16)(wv[i] - (float)h);
     }
+    const bf16x8 a8 = __builtin_bit_cast(bf16x8, a);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, bhi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, blo, acc, 0, 0, 0);
+  };
+  // wave w takes steps w, w+4, w+8, ...: whole batches of kRouterUnroll steps with all loads issued
+  // first, then the remaining steps one at a time
+  int s0 = wave;
+  for (; s0 + 4 * (kRouterUnroll - 1) < nsteps; s0 += 4 * kRouterUnroll) {
+    u32x4 av[kRouterUnroll];
+    float4 w0[kRouterUnroll], w1[kRouterUnroll];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      u32x4 av = {0u, 0u, 0u, 0u};
-      if (t_ok[mt]) av = ld16(xrow[mt] + k0);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, av);
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bhi, acc[mt], 0, 0, 0);
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, blo, acc[mt], 0, 0, 0);
+    for (int u = 0; u < kRouterUnroll; ++u) {
+      av[u] = ld16(xrow + 32 * (s0 + 4 * u));
+      w0[u] = *reinterpret_cast<const float4*>(wrow + 32 * (s0 + 4 * u));
+      w1[u] = *reinterpret_cast<const float4*>(wrow + 32 * (s0 + 4 * u) + 4);
     }
+#pragma unroll
+    for (int u = 0; u < kRouterUnroll; ++u) step(av[u], w0[u], w1[u]);
   }
-  // D layout: lane holds column n (expert) of rows 4G..4G+3 (tokens).
-  if (!e_ok) return;
+  for (; s0 < nsteps; s0 += 4)
+    step(ld16(xrow + 32 * s0), *reinterpret_cast<const float4*>(wrow + 32 * s0),
+         *reinterpret_cast<const float4*>(wrow + 32 * s0 + 4));
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  const floatx4 r = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+  // D layout: lane holds column n (expert e0+n) of rows 4G..4G+3 (tokens)
+  if (e0 + n >= E) return;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 16 * mt + 4 * G + i;
-      if (t < T) logits[(size_t)t * E + e0 + n] = acc[mt][i];
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int tt = t0 + 4 * G + i;
+    if (tt < T) logits[(size_t)tt * E + e0 + n] = r[i];
   }
 }
 
@@ -250,11 +262,10 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 
 hipError_t launch_router_mfma(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
                               hipStream_t st) {
-  hipLaunchKernelGGL(k_router_mfma, dim3((s.T + 63) / 64, (s.E + 63) / 64), dim3(256), 0, st, x, w_router, logits,
-                     s.T, s.d, s.E);
+  const dim3 grid(((s.T + 15) / 16) * ((s.E + 15) / 16)), block(256);
+  hipLaunchKernelGGL(k_router_mfma, grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
   return hipGetLastError();
 }
-
 hipError_t launch_topk(const Shape& s, const float* logits, const float* bias, int32_t* topk_ids, float* topk_w,
                        hipStream_t st) {
   const dim3 grid((s.T + 3) / 4), block(256);

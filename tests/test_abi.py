@@ -90,7 +90,7 @@ def test_workspace_sizes_closed_form(dims):
                              "group_order", "mt_prefix", "chunk_counts")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     gemv = align(P * I * 2) + align(T * Is * 2)
-    grouped = align(T * dd * 2) + align(P * I * 2) + align(T * Is * 2) + align(P * dd * 4) + align(T * dd * 4)
+    grouped = align(T * dd * 2) + align(P * I * 2) + align(T * Is * 2) + align(P * dd * 2) + align(T * dd * 2)
     want = gemv if moe.moe_path(dims) == 0 else grouped
     assert moe.moe_scratch_bytes(dims) == want
     assert moe.moe_scratch_bytes(dims, abi.MOE_FLAG_FORCE_GROUPED) == grouped

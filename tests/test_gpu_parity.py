@@ -76,7 +76,12 @@ def test_doubling_down_scales_doubles_output(flags):
     for key in ("w2_sc", "s2_sc"):
         inp2[key] = (inp[key].view(np.float16) * np.float16(2)).view(np.uint16)
     b, _ = run(inp2, flags)
-    assert torch.equal(b.y, 2 * a.y)
+    # Exact doubling, except where an fp16 intermediate (grouped path: per-pair down outputs) falls in
+    # the fp16 subnormal range, whose absolute spacing 2^-24 does not scale: at most k such roundings
+    # per output element.
+    diff = (b.y - 2 * a.y).abs()
+    assert float(diff.max()) <= dims.k * 2.0 ** -24 * 2, float(diff.max())
+    assert float((diff == 0).float().mean()) > 0.99
 
 
 @pytest.mark.parametrize("flags", [0, GROUPED])
