@@ -12,14 +12,14 @@
 // buffer when K is not a multiple of the tile ("tile-select fix").
 //
 // Work items: for each group (expert, or the shared expert as group E) in
-// schedule order, its M-tiles of up to 128 rows times the N-bands of the
+// schedule order, its M-tiles of up to 96 rows times the N-bands of the
 // output.  Default order is band-major inside a group (all M-tiles of one
 // weight band adjacent), and the launch index is remapped so that each XCD
 // (own L2) receives a contiguous run of items.  The grid is sized for the
 // largest possible tile count; surplus workgroups exit at once, so the launch
 // shape does not depend on device data and the call can be graph-captured.
 //
-// Inner loop (per 128-wide K step): the workgroup stages its 128 activation
+// Inner loop (per 128-wide K step): the workgroup stages its 96 activation
 // rows x 128 columns as fp16 in LDS (double-buffered); each wavefront owns
 // four 16-column weight slices, loads one 16-byte Q4 block per slice and
 // lane, dequantises it in registers straight into the B-operand layout of
@@ -35,7 +35,7 @@
 
 namespace moe {
 
-// LDS tile: 128 rows x 128 halves (256 B) per buffer, no padding.  The 16 B
+// LDS tile: 96 rows x 128 halves (256 B) per buffer, no padding.  The 16 B
 // chunk c of row r is stored in slot c ^ (r & 15), so the 16 lanes that read
 // one MFMA operand (16 rows, same chunk) hit 16 different slots, i.e. all 64
 // banks once.  Tiles arrive by buffer_load_dwordx4 ... lds: one instruction
@@ -46,9 +46,11 @@ namespace moe {
 // whole K loop; the K advance is a scalar offset, so the main loop spends
 // its vector instructions on dequantisation, not on address arithmetic.
 constexpr int kRowBytes = kGroupedBK * 2;
-constexpr int kTileBytes = kGroupedBM * kRowBytes;  // 32 KB
-constexpr int kStages = 3;        // pipeline depth (LDS ring of kStages activation tiles)
-constexpr int kLoadsPerStep = 16; // vector-memory ops per lane per K step: 8 tile loads, 4 code blocks, 4 scales
+constexpr int kTileBytes = kGroupedBM * kRowBytes;  // 24 KB
+constexpr int kStages = 2;        // pipeline depth (LDS ring of kStages activation tiles)
+constexpr int kTileLoads = kTileBytes / (256 * 16);  // buffer_load ... lds per lane per tile (6)
+constexpr int kLoadsPerStep = kTileLoads + 8;        // vector-memory ops per lane per K step (+4 code blocks, 4 scales)
+constexpr int kRowsPerWave = kGroupedBM / 4;         // activation rows staged by each wavefront (24)
 // A buffer offset past every buffer this path addresses (all are below 2^32 - 64 bytes): buffer
 // loads at it return zeros without a memory access.  The range check uses the per-lane offset
 // only, so it holds whatever scalar offset the K loop adds.
@@ -106,9 +108,11 @@ __device__ __forceinline__ int ufl(int v) { return __builtin_amdgcn_readfirstlan
 // Per-tile state handed from the work-item decode to the main loop.
 struct TileCtx {
   __amdgpu_buffer_rsrc_t rq, rs, ra;
-  uint32_t aoff[8];
-  uint32_t qoff[4], soff[4];
-  uint32_t rdo[4];
+  uint32_t aoff[kTileLoads];
+  uint32_t qoff, soff;         // per-lane part of the weight offsets (row n, block G)
+  int qns[4], sns[4];          // per-slice part (uniform): first weight row of slice ns
+  uint32_t rdo;                // LDS read offset of row n (chunk swizzle applied per K-step)
+  int gx;                      // 4G ^ n: swizzled chunk of K-step s is gx ^ s
   bool nok[4];
   int c0, wave, nit, nkb, Kdim, Iw, mlen, rbase, G, n, lane;
   uint32_t dq_mask, dq_magic;  // 0x000F000F (uniform) and 0x64006400 (kept in a VGPR)
@@ -126,26 +130,28 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
     const int kb = it * BK * 2;
     if (c.ktail && it == c.nit - 1) {  // uniform
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < kTileLoads; ++i) {
         // a chunk past the row end re-reads the tile's first chunk of the same row: finite data
         // that meets zero weights (the weights' K tail is masked to zero below)
-        const int chunk = (c.lane & 15) ^ ((32 * c.wave + 4 * i + (c.lane >> 4)) & 15);
+        const int chunk = (c.lane & 15) ^ ((kRowsPerWave * c.wave + 4 * i + (c.lane >> 4)) & 15);
         const uint32_t off = c.aoff[i] - (it * BK + 8 * chunk >= c.Kdim ? 16u * (uint32_t)chunk : 0u);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            c.ra, (lds_void*)(As + buf * kTileBytes + (32 * c.wave + 4 * i) * kRowBytes), 16, (int)off, kb, 0, 0);
+            c.ra, (lds_void*)(As + buf * kTileBytes + (kRowsPerWave * c.wave + 4 * i) * kRowBytes), 16, (int)off, kb,
+            0, 0);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < kTileLoads; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            c.ra, (lds_void*)(As + buf * kTileBytes + (32 * c.wave + 4 * i) * kRowBytes), 16, (int)c.aoff[i], kb, 0, 0);
+            c.ra, (lds_void*)(As + buf * kTileBytes + (kRowsPerWave * c.wave + 4 * i) * kRowBytes), 16,
+            (int)c.aoff[i], kb, 0, 0);
     }
   };
   auto load_w = [&](int it, u32x4* qd, uint32_t* sd) {
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
-      qd[ns] = __builtin_amdgcn_raw_buffer_load_b128(c.rq, (int)c.qoff[ns], it * 64, 0);
-      sd[ns] = __builtin_amdgcn_raw_buffer_load_b16(c.rs, (int)c.soff[ns], it * 8, 0);
+      qd[ns] = __builtin_amdgcn_raw_buffer_load_b128(c.rq, (int)c.qoff, c.qns[ns] + it * 64, 0);
+      sd[ns] = __builtin_amdgcn_raw_buffer_load_b16(c.rs, (int)c.soff, c.sns[ns] + it * 8, 0);
     }
   };
 
@@ -155,15 +161,10 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) acc[mt][ns] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // One K iteration (4 MFMA K-steps of 32) on LDS buffer `buf`, software-pipelined: while the 4*NMT
-  // MFMAs of step s run, the activation fragments of step s+1 are read from LDS and its four weight
-  // fragments are dequantised; sched_group_barrier interleaves the three instruction streams so the
-  // matrix core is fed back to back.
-  // One K iteration (4 MFMA K-steps of 32) on LDS buffer `buf`, software-pipelined: while the 4*NMT
-  // MFMAs of step s run, the activation fragments of step s+1 are read from LDS and its four weight
-  // fragments are dequantised; sched_group_barrier interleaves the three instruction streams so the
-  // matrix core is fed back to back.  The loop body has no branches, so the accumulators keep their
-  // registers across iterations.
+  // One K iteration (4 MFMA K-steps of 32) on LDS buffer `buf`.  Within a K-step the activation
+  // fragment of each 16-row slice is read from LDS just before its four MFMAs (one slice ahead), and
+  // the four weight fragments of the next K-step are dequantised between the MFMAs.  The loop body has
+  // no branches, so the accumulators keep their registers across iterations.
   auto compute = [&](int buf, const u32x4* q, const uint32_t* sc_in, int it) __attribute__((always_inline)) {
     const char* At = As + buf * kTileBytes;
     half2v d2[4];
@@ -175,35 +176,27 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
       const _Float16 dv = __builtin_bit_cast(_Float16, (uint16_t)bits);
       d2[ns] = half2v{dv, dv};
     }
-    half8 a_cur[NMT], b_cur[4];
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) a_cur[mt] = *reinterpret_cast<const half8*>(At + c.rdo[0] + mt * 16 * kRowBytes);
+    half8 b_cur[4];
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) b_cur[ns] = dequant8_general(q[ns][0], d2[ns], c.dq_mask, c.dq_magic);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      half8 a_nxt[NMT], b_nxt[4];
-      if (s < 3) {
+      const char* Ar = At + c.rdo + 16 * (c.gx ^ s);
+      half8 b_nxt[4];
+      half8 a_cur = *reinterpret_cast<const half8*>(Ar);
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt)
-          a_nxt[mt] = *reinterpret_cast<const half8*>(At + c.rdo[s + 1] + mt * 16 * kRowBytes);
-      }
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
+      for (int mt = 0; mt < NMT; ++mt) {
+        half8 a_nxt;
+        if (mt + 1 < NMT) a_nxt = *reinterpret_cast<const half8*>(Ar + (mt + 1) * 16 * kRowBytes);
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns)
-          acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur[mt], b_cur[ns], acc[mt][ns], 0, 0, 0);
+          acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur, b_cur[ns], acc[mt][ns], 0, 0, 0);
+        if (s < 3 && mt < 4) b_nxt[mt] = dequant8_general(q[mt][s + 1], d2[mt], c.dq_mask, c.dq_magic);
+        if (mt + 1 < NMT) a_cur = a_nxt;
+      }
       if (s < 3) {
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) b_nxt[ns] = dequant8_general(q[ns][s + 1], d2[ns], c.dq_mask, c.dq_magic);
-        __builtin_amdgcn_sched_group_barrier(0x100, NMT, 0);  // DS reads of step s+1 first
-#pragma unroll
-        for (int i = 0; i < 4 * NMT; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // then up to three VALU
-        }
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) a_cur[mt] = a_nxt[mt];
+        for (int ns = NMT; ns < 4; ++ns) b_nxt[ns] = dequant8_general(q[ns][s + 1], d2[ns], c.dq_mask, c.dq_magic);
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns) b_cur[ns] = b_nxt[ns];
       }
@@ -225,7 +218,7 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
   // Wait until step `it` has landed (younger steps stay in flight), then barrier.
   auto arrive = [&](int it) __attribute__((always_inline)) {
     const int younger = min(NS - 2, c.nit - 1 - it);
-    static_assert(kStages <= 4, "the waits below cover up to two younger steps");
+    static_assert(kStages <= 3, "the waits below cover up to two younger steps");
     if (younger >= 2) vm_lgkm_wait<2 * kLoadsPerStep>();
     else if (younger == 1) vm_lgkm_wait<kLoadsPerStep>();
     else vm_lgkm_wait<0>();
@@ -286,7 +279,7 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
 }
 
 template <bool GATEUP>
-__global__ __launch_bounds__(256, 1) void k_grouped(GArgs a) {
+__global__ __launch_bounds__(256, 2) void k_grouped(GArgs a) {
   constexpr int BM = kGroupedBM, BK = kGroupedBK;
   constexpr int BANDW = GATEUP ? kGateUpBandCols : kDownBandCols;
   __shared__ __attribute__((aligned(1024))) char As[kStages * kTileBytes];
@@ -346,11 +339,11 @@ __global__ __launch_bounds__(256, 1) void k_grouped(GArgs a) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(Ws, wrows * sstride * 2);
   const __amdgpu_buffer_rsrc_t ra = shared ? make_rsrc(a.a_s, a.a_s_bytes) : make_rsrc(a.a_r, a.a_r_bytes);
 
-  // ---- activation rows staged by this wavefront: rows 32*wave + 4*i + lane/16, slot lane%16
-  uint32_t aoff[8];
+  // ---- activation rows staged by this wavefront: rows kRowsPerWave*wave + 4*i + lane/16, slot lane%16
+  uint32_t aoff[kTileLoads];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 32 * wave + 4 * i + (lane >> 4);
+  for (int i = 0; i < kTileLoads; ++i) {
+    const int row = kRowsPerWave * wave + 4 * i + (lane >> 4);
     const int rr = row < mlen ? row : 0;
     uint32_t arow;
     if (GATEUP)
@@ -363,9 +356,10 @@ __global__ __launch_bounds__(256, 1) void k_grouped(GArgs a) {
   }
   const int nit = (Kdim + BK - 1) / BK;
   const bool ktail = (Kdim % BK) != 0;
-  // ---- this wavefront's weight rows: four 16-row slices
+  // ---- this wavefront's weight rows: four 16-row slices; slice ns starts at weight row rowbase[ns]
+  // (uniform), lane (n, G) reads row rowbase[ns] + n, block G of every 4-block K chunk
   const int n = lane & 15, G = lane >> 4;
-  uint32_t qoff[4], soff[4];
+  int rowbase[4];
   bool nok[4];
   int c0;
   if (GATEUP) {
@@ -374,9 +368,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped(GArgs a) {
     for (int ns = 0; ns < 4; ++ns) {
       const int col = c0 + 16 * (ns & 1);
       nok[ns] = col < Iw;
-      const uint32_t wrow = (ns < 2 ? 0u : (uint32_t)Iw) + (uint32_t)(nok[ns] ? col : 0) + (uint32_t)n;
-      qoff[ns] = wrow * qstride + 16u * (uint32_t)G;
-      soff[ns] = (wrow * sstride + (uint32_t)G) * 2u;
+      rowbase[ns] = (ns < 2 ? 0 : Iw) + (nok[ns] ? col : 0);
     }
   } else {
     c0 = band * BANDW + wave * 64;  // output columns c0 .. c0+63
@@ -384,25 +376,25 @@ __global__ __launch_bounds__(256, 1) void k_grouped(GArgs a) {
     for (int ns = 0; ns < 4; ++ns) {
       const int col = c0 + 16 * ns;
       nok[ns] = col < a.d;
-      const uint32_t wrow = (uint32_t)(nok[ns] ? col : 0) + (uint32_t)n;
-      qoff[ns] = wrow * qstride + 16u * (uint32_t)G;
-      soff[ns] = (wrow * sstride + (uint32_t)G) * 2u;
+      rowbase[ns] = nok[ns] ? col : 0;
     }
   }
   const int nkb = Kdim / 32;
-  // LDS read offsets for the four K-steps: row n of every 16-row slice, swizzled chunk 4G+s
-  uint32_t rdo[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) rdo[s] = (uint32_t)(n * kRowBytes + 16 * ((4 * G + s) ^ n));
 
   TileCtx c;
   c.rq = rq; c.rs = rs; c.ra = ra;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c.aoff[i] = aoff[i];
+  for (int i = 0; i < kTileLoads; ++i) c.aoff[i] = aoff[i];
+  c.qoff = (uint32_t)n * qstride + 16u * (uint32_t)G;
+  c.soff = ((uint32_t)n * sstride + (uint32_t)G) * 2u;
 #pragma unroll
-  for (int ns = 0; ns < 4; ++ns) { c.qoff[ns] = qoff[ns]; c.soff[ns] = soff[ns]; c.nok[ns] = nok[ns]; }
-#pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) c.rdo[s4] = rdo[s4];
+  for (int ns = 0; ns < 4; ++ns) {
+    c.qns[ns] = ufl((int)((uint32_t)rowbase[ns] * qstride));
+    c.sns[ns] = ufl((int)((uint32_t)rowbase[ns] * sstride * 2u));
+    c.nok[ns] = nok[ns];
+  }
+  c.rdo = (uint32_t)(n * kRowBytes);
+  c.gx = (4 * G) ^ n;
   c.c0 = c0; c.wave = wave; c.nit = nit; c.nkb = nkb; c.Kdim = Kdim; c.Iw = Iw; c.mlen = mlen; c.rbase = rbase;
   c.G = G; c.n = n; c.lane = lane; c.ktail = ktail; c.shared = shared;
   c.dq_mask = a.dq_mask;
@@ -413,9 +405,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped(GArgs a) {
     case 3: grouped_tile<GATEUP, 3>(a, c, As); break;
     case 4: grouped_tile<GATEUP, 4>(a, c, As); break;
     case 5: grouped_tile<GATEUP, 5>(a, c, As); break;
-    case 6: grouped_tile<GATEUP, 6>(a, c, As); break;
-    case 7: grouped_tile<GATEUP, 7>(a, c, As); break;
-    default: grouped_tile<GATEUP, 8>(a, c, As); break;
+    default: grouped_tile<GATEUP, 6>(a, c, As); break;
   }
 }
 

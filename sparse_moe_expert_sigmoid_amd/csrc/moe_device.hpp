@@ -22,7 +22,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kBlockK = 32;           // Q4 block length
 constexpr int kGemvMaxChunks = 2;     // small-T path: d <= 2 * 4096, I <= 2 * 1024
-constexpr int kGroupedBM = 128;       // grouped GEMM: rows per M-tile
+constexpr int kGroupedBM = 96;        // grouped GEMM: rows per M-tile
 constexpr int kGroupedBK = 128;       // grouped GEMM: K per main-loop iteration (4 blocks)
 constexpr int kGateUpBandCols = 128;  // grouped gate+up: h columns per workgroup
 constexpr int kDownBandCols = 256;    // grouped down: output columns per workgroup
