@@ -133,7 +133,8 @@ def short_name(mangled: str) -> str:
 def device_copy(cfg, seed, torch, device):
     """A further independent layer copy drawn on the GPU with torch's seeded generator, with the
     same distributions as the numpy generator (x ~ N(0,1) -> bf16, W_r ~ N(0, 0.02), Q4 codes uniform,
-    scales ~ U(0.005, 0.02) -> fp16, bias per the workload's recipe)."""
+    scales ~ U(0.005, 0.02) -> fp16, bias per the workload's recipe).  Scales are drawn i.i.d., so
+    drawing them directly in the library's 16-row-group layout gives the same distribution."""
     dims = cfg.dims
     T, d, E, I, Is = dims.T, dims.d, dims.E, dims.I, dims.I_shared
     g = torch.Generator(device=device)

@@ -48,10 +48,13 @@
  *   x         bf16 bit patterns, row-major [T][d]
  *   w_router  float32 [E][d];   bias  float32 [E]
  *   y         float32 [T][d]
- *   Q4 matrix of shape [rows][K] (K % 32 == 0), two arrays:
+ *   Q4 matrix of shape [rows][K] (K % 32 == 0, rows % 16 == 0), two arrays:
  *     qs      uint8 [rows][K/2]:  byte i of a row holds element 2i in its
  *             low nibble and element 2i+1 in its high nibble
- *     scales  uint16 [rows][K/32]: IEEE fp16 bits, one per 32-element block
+ *     scales  uint16 [rows/16][K/32][16]: IEEE fp16 bits, one per 32-element
+ *             block, in groups of 16 rows: the scale of row r, block b is
+ *             element ((r/16)*(K/32) + b)*16 + r%16 (so the 16 scales an
+ *             MFMA slice of 16 rows needs for one block are contiguous)
  *     value = (q - 8) * scale          (q the 4-bit code, 0..15)
  *   w13  [E][2I][d]  gate rows 0..I-1, up rows I..2I-1 of every expert
  *   w2   [E][d][I]

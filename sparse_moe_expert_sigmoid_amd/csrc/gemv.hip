@@ -77,18 +77,33 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
       for (int dw = 0; dw < 4; ++dw) u[bb][dw] = ld16(x + (size_t)t * d + 32 * bi[bb] + 8 * dw);
-    // 2) weight codes and scales of 8 rows: all loads in flight before any arithmetic
+    // 2) weight codes of 8 rows and their scales: all loads in flight before any arithmetic.  Scales
+    // are stored in 16-row groups ([rows/16][K/32][16]); the 4 gate (and the 4 up) rows of this
+    // wavefront lie in one group, so one 8-byte load per block brings all four.
     u32x4 q[8][2];
-    uint32_t sv[8][2];
+    uint2 sg[2][2];  // [gate/up][bb]: fp16 scales of rows +0..+3
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int row = (r < 4) ? (i0 + r) : (Iw + i0 + r - 4);
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb) {
-        q[r][bb] = ld16(qs + row * qstride + 16 * (size_t)bi[bb]);
-        sv[r][bb] = sc[row * sstride + bi[bb]];
-      }
+      for (int bb = 0; bb < 2; ++bb) q[r][bb] = ld16(qs + row * qstride + 16 * (size_t)bi[bb]);
     }
+#pragma unroll
+    for (int gu = 0; gu < 2; ++gu) {
+      const int r0 = gu ? Iw + i0 : i0;  // i0 % 4 == 0: rows r0 .. r0+3 share a 16-row group
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+        sg[gu][bb] = *reinterpret_cast<const uint2*>(sc + ((size_t)(r0 >> 4) * sstride + bi[bb]) * 16 + (r0 & 15));
+    }
+    uint32_t sv[8][2];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const uint2 v = sg[r >> 2][bb];
+        const uint32_t d = ((r & 3) < 2) ? v.x : v.y;
+        sv[r][bb] = (r & 1) ? (d >> 16) : (d & 0xFFFFu);
+      }
     // 3) activation pairs and block sums
     uint32_t xp[2][4][4];
     float xs[2];
@@ -142,8 +157,8 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
 // Down projection fused with the combine.  grid = (ceil(d/16), T); the
 // workgroup has min(k+1, 16) wavefronts that take the slots j = wave,
 // wave + nw, ... (slot k is the shared expert).  A wavefront computes the
-// 16 output rows of its slot, two rows at a time (one per 32-lane half);
-// lane l%32 owns block l%32 (+32c) of the row and keeps the matching 32 h
+// 16 output rows of its slot, two rows at a time (32-lane half h takes rows
+// 8h .. 8h+7); lane l%32 owns block l%32 (+32c) of the row and keeps the matching 32 h
 // values in registers.  Partial dot products meet in LDS and one thread per
 // row sums them in slot order: y = sum_j w_j * dot_j, then + shared.
 //
@@ -222,19 +237,21 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
       c0[c] = -(1032.f * sa + 72.f * sb);
     }
     // 2) codes and scales of RB row pairs for this lane's blocks, all in flight together; 3) dots
+    // Half h of the wavefront takes rows n0 + 8h .. n0 + 8h + 7 (n0 % 16 == 0, d % 32 == 0: all valid),
+    // so the 8 scales a lane needs for its block are 16 contiguous bytes of the [rows/16][K/32][16]
+    // scale layout: one load per chunk.
+    u32x4 sc8[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) sc8[c] = ld16(sc + ((size_t)(n0 >> 4) * sstride + bi[c]) * 16 + 8 * half);
     constexpr int RB = 8 / NCH;
 #pragma unroll
     for (int r0 = 0; r0 < 8; r0 += RB) {
       u32x4 q[RB][NCH];
-      uint32_t sv[RB][NCH];
 #pragma unroll
       for (int rr = 0; rr < RB; ++rr) {
-        const int n = min(n0 + 2 * (r0 + rr) + half, d - 1);
+        const int n = n0 + 8 * half + r0 + rr;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          q[rr][c] = ld16(qs + n * qstride + 16 * (size_t)bi[c]);
-          sv[rr][c] = sc[n * sstride + bi[c]];
-        }
+        for (int c = 0; c < NCH; ++c) q[rr][c] = ld16(qs + n * qstride + 16 * (size_t)bi[c]);
       }
       float acc[RB];
 #pragma unroll
@@ -251,15 +268,17 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
             dot = dot2_f16(and_or(w8, mask_lo, magic), hp[c][g][2], dot);
             dot = dot2_f16(and_or(w8, mask_hi, magic), hp[c][g][3], dot);
           }
-          // masked by a multiply (not a select), so that the scale load is never made conditional
-          acc[rr] = fmaf(fp16_bits_to_float(sv[rr][c]) * okf[c], dot, acc[rr]);
+          const int k8 = r0 + rr;  // compile-time: halfword k8 of the lane's 8 scales
+          const uint32_t sbits = (sc8[c][k8 >> 1] >> (16 * (k8 & 1))) & 0xFFFFu;
+          // masked by a multiply (not a select), so that no load is made conditional
+          acc[rr] = fmaf(fp16_bits_to_float(sbits) * okf[c], dot, acc[rr]);
         }
       }
 #pragma unroll
       for (int rr = 0; rr < RB; ++rr) acc[rr] = half_wave_sum_hi(acc[rr]);
       if (bl == 16) {
 #pragma unroll
-        for (int rr = 0; rr < RB; ++rr) part[slot][2 * (r0 + rr) + half] = acc[rr];
+        for (int rr = 0; rr < RB; ++rr) part[slot][8 * half + r0 + rr] = acc[rr];
       }
     }
   }

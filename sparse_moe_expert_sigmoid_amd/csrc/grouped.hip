@@ -48,9 +48,10 @@ namespace moe {
 constexpr int kRowBytes = kGroupedBK * 2;
 constexpr int kTileBytes = kGroupedBM * kRowBytes;  // 24 KB
 constexpr int kStages = 2;        // pipeline depth (LDS ring of kStages activation tiles)
-constexpr int kTileLoads = kTileBytes / (256 * 16);  // buffer_load ... lds per lane per tile (6)
+constexpr int kGroupedThreads = 64 * kGroupedWaves;
+constexpr int kTileLoads = kTileBytes / (kGroupedThreads * 16);  // buffer_load ... lds per lane per tile
 constexpr int kLoadsPerStep = kTileLoads + 8;        // vector-memory ops per lane per K step (+4 code blocks, 4 scales)
-constexpr int kRowsPerWave = kGroupedBM / 4;         // activation rows staged by each wavefront (24)
+constexpr int kRowsPerWave = kGroupedBM / kGroupedWaves;  // activation rows staged by each wavefront
 // A buffer offset past every buffer this path addresses (all are below 2^32 - 64 bytes): buffer
 // loads at it return zeros without a memory access.  The range check uses the per-lane offset
 // only, so it holds whatever scalar offset the K loop adds.
@@ -110,7 +111,8 @@ struct TileCtx {
   __amdgpu_buffer_rsrc_t rq, rs, ra;
   uint32_t aoff[kTileLoads];
   uint32_t qoff, soff;         // per-lane part of the weight offsets (row n, block G)
-  int qns[4], sns[4];          // per-slice part (uniform): first weight row of slice ns
+  uint32_t qoff_tail, soff_tail;  // the same, block clamped to the row's last, for the K tail iteration
+  int qns[4], sns[4];          // per-slice part (uniform): slice ns's first code row, first scale group
   uint32_t rdo;                // LDS read offset of row n (chunk swizzle applied per K-step)
   int gx;                      // 4G ^ n: swizzled chunk of K-step s is gx ^ s
   bool nok[4];
@@ -148,10 +150,14 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
     }
   };
   auto load_w = [&](int it, u32x4* qd, uint32_t* sd) {
+    // in the K tail iteration, lanes whose block lies past the row end re-read the row's last block
+    // (their scale is masked to zero): every access stays inside the weight matrix
+    const bool tail = c.ktail && it == c.nit - 1;  // uniform
+    const uint32_t qo = tail ? c.qoff_tail : c.qoff, so = tail ? c.soff_tail : c.soff;
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
-      qd[ns] = __builtin_amdgcn_raw_buffer_load_b128(c.rq, (int)c.qoff, c.qns[ns] + it * 64, 0);
-      sd[ns] = __builtin_amdgcn_raw_buffer_load_b16(c.rs, (int)c.soff, c.sns[ns] + it * 8, 0);
+      qd[ns] = __builtin_amdgcn_raw_buffer_load_b128(c.rq, (int)qo, c.qns[ns] + it * 64, 0);
+      sd[ns] = __builtin_amdgcn_raw_buffer_load_b16(c.rs, (int)so, c.sns[ns] + it * 128, 0);
     }
   };
 
@@ -164,21 +170,22 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
   // One K iteration (4 MFMA K-steps of 32) on LDS buffer `buf`.  Within a K-step the activation
   // fragment of each 16-row slice is read from LDS just before its four MFMAs (one slice ahead), and
   // the four weight fragments of the next K-step are dequantised between the MFMAs.  The loop body has
-  // no branches, so the accumulators keep their registers across iterations.
-  auto compute = [&](int buf, const u32x4* q, const uint32_t* sc_in, int it) __attribute__((always_inline)) {
+  // no branches around the MFMAs, so the accumulators keep their registers across iterations.
+  auto compute = [&](int buf, const u32x4* q, const half2v* d2, bool large) __attribute__((always_inline)) {
     const char* At = As + buf * kTileBytes;
-    half2v d2[4];
-    const bool tail = c.ktail && it == c.nit - 1;  // uniform
+    SmallScale ss[4];
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
-      // K tail: blocks past the row end weigh zero (the step's loads have landed: no register in flight)
-      const uint32_t bits = (tail && it * 4 + c.G >= c.nkb) ? 0u : sc_in[ns];
-      const _Float16 dv = __builtin_bit_cast(_Float16, (uint16_t)bits);
-      d2[ns] = half2v{dv, dv};
-    }
+    for (int ns = 0; ns < 4; ++ns) ss[ns] = small_scale(d2[ns]);
+    // small-scale form; redone in the general form when a scale of this iteration is too large for it
+    // (`large` is uniform, so this is a scalar branch that is normally not taken)
+    auto deq = [&](uint32_t w, int ns) __attribute__((always_inline)) {
+      half8 r = dequant8_small(w, ss[ns]);
+      if (__builtin_expect(large, 0)) r = dequant8_general(w, d2[ns], c.dq_mask, c.dq_magic);
+      return r;
+    };
     half8 b_cur[4];
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) b_cur[ns] = dequant8_general(q[ns][0], d2[ns], c.dq_mask, c.dq_magic);
+    for (int ns = 0; ns < 4; ++ns) b_cur[ns] = deq(q[ns][0], ns);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const char* Ar = At + c.rdo + 16 * (c.gx ^ s);
@@ -191,16 +198,32 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns)
           acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur, b_cur[ns], acc[mt][ns], 0, 0, 0);
-        if (s < 3 && mt < 4) b_nxt[mt] = dequant8_general(q[mt][s + 1], d2[mt], c.dq_mask, c.dq_magic);
+        if (s < 3 && mt < 4) b_nxt[mt] = deq(q[mt][s + 1], mt);
         if (mt + 1 < NMT) a_cur = a_nxt;
       }
       if (s < 3) {
 #pragma unroll
-        for (int ns = NMT; ns < 4; ++ns) b_nxt[ns] = dequant8_general(q[ns][s + 1], d2[ns], c.dq_mask, c.dq_magic);
+        for (int ns = NMT; ns < 4; ++ns) b_nxt[ns] = deq(q[ns][s + 1], ns);
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns) b_cur[ns] = b_nxt[ns];
       }
     }
+  };
+  // Scales of iteration `it` (the K tail's blocks weigh zero), and whether any scale the wavefront uses
+  // in this iteration is too large for the small-scale form.
+  auto run_step = [&](int buf, const u32x4* q, const uint32_t* sc_in, int it) __attribute__((always_inline)) {
+    half2v d2[4];
+    const bool tail = c.ktail && it == c.nit - 1;  // uniform
+    bool small = true;
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+      // the step's loads have landed: no register in flight is overwritten here
+      const uint32_t bits = (tail && it * 4 + c.G >= c.nkb) ? 0u : sc_in[ns];
+      small = small && small_scale_ok(bits);
+      const _Float16 dv = __builtin_bit_cast(_Float16, (uint16_t)bits);
+      d2[ns] = half2v{dv, dv};
+    }
+    compute(buf, q, d2, __builtin_amdgcn_ballot_w64(!small) != 0);
   };
 
   // kStages-deep pipeline: while step `it` is computed, the activation tiles and weight blocks of
@@ -237,7 +260,7 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
         issue_a(it + NS - 1, nxt);
         load_w(it + NS - 1, q[nxt], sc[nxt]);
       }
-      compute(st, q[st], sc[st], it);
+      run_step(st, q[st], sc[st], it);
     }
   }
   // The remaining nit % NS steps (their loads were issued above or in the prologue).
@@ -246,7 +269,7 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
     const int it = it0 + st;
     if (it < c.nit) {
       arrive(it);
-      compute(st, q[st], sc[st], it);
+      run_step(st, q[st], sc[st], it);
     }
   }
 
@@ -279,7 +302,7 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
 }
 
 template <bool GATEUP>
-__global__ __launch_bounds__(256, 2) void k_grouped(GArgs a) {
+__global__ __launch_bounds__(kGroupedThreads, 8 / kGroupedWaves) void k_grouped(GArgs a) {
   constexpr int BM = kGroupedBM, BK = kGroupedBK;
   constexpr int BANDW = GATEUP ? kGateUpBandCols : kDownBandCols;
   __shared__ __attribute__((aligned(1024))) char As[kStages * kTileBytes];
@@ -287,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void k_grouped(GArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = ufl(tid >> 6);
   const int ngroups = a.E + 1;
-  for (int i = tid; i <= ngroups; i += 256) s_prefix[i] = a.mt_prefix[i];
+  for (int i = tid; i <= ngroups; i += kGroupedThreads) s_prefix[i] = a.mt_prefix[i];
   __syncthreads();
   const int nb = a.nbands;
   const int n_mt = ufl(s_prefix[ngroups]);
@@ -385,12 +408,19 @@ __global__ __launch_bounds__(256, 2) void k_grouped(GArgs a) {
   c.rq = rq; c.rs = rs; c.ra = ra;
 #pragma unroll
   for (int i = 0; i < kTileLoads; ++i) c.aoff[i] = aoff[i];
+  // Scales are stored in 16-row groups, [rows/16][K/32][16]: slice ns (16 rows from rowbase[ns], a
+  // multiple of 16) has the 16 scales of block b at byte ((rowbase/16)*(K/32) + b)*32, so lane (n, G)
+  // reads byte 2*lane of a 128-byte run per 4-block iteration.
+  const int Glast = (nkb - 1) - 4 * (nit - 1);  // last valid block of the final iteration, relative
+  const int Gt = G < Glast ? G : Glast;
   c.qoff = (uint32_t)n * qstride + 16u * (uint32_t)G;
-  c.soff = ((uint32_t)n * sstride + (uint32_t)G) * 2u;
+  c.soff = 2u * (uint32_t)lane;
+  c.qoff_tail = (uint32_t)n * qstride + 16u * (uint32_t)Gt;
+  c.soff_tail = 2u * (uint32_t)(n + 16 * Gt);
 #pragma unroll
   for (int ns = 0; ns < 4; ++ns) {
     c.qns[ns] = ufl((int)((uint32_t)rowbase[ns] * qstride));
-    c.sns[ns] = ufl((int)((uint32_t)rowbase[ns] * sstride * 2u));
+    c.sns[ns] = ufl((int)((uint32_t)(rowbase[ns] / 16) * sstride * 32u));
     c.nok[ns] = nok[ns];
   }
   c.rdo = (uint32_t)(n * kRowBytes);
@@ -503,7 +533,7 @@ hipError_t launch_grouped_gateup(const Shape& s, const uint16_t* x, const Routin
   const int Imax = s.I > s.Is ? s.I : s.Is;
   a.nbands = (Imax + kGateUpBandCols - 1) / kGateUpBandCols;
   const long grid = (long)grouped_max_mtiles(s) * a.nbands;
-  hipLaunchKernelGGL(k_grouped<true>, dim3((unsigned)grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_grouped<true>, dim3((unsigned)grid), dim3(kGroupedThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -520,7 +550,7 @@ hipError_t launch_grouped_down(const Shape& s, const Routing& r, Q4 w2, Q4 s2, c
   a.y_s = o.y_s;
   a.nbands = (s.d + kDownBandCols - 1) / kDownBandCols;
   const long grid = (long)grouped_max_mtiles(s) * a.nbands;
-  hipLaunchKernelGGL(k_grouped<false>, dim3((unsigned)grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_grouped<false>, dim3((unsigned)grid), dim3(kGroupedThreads), 0, st, a);
   return hipGetLastError();
 }
 

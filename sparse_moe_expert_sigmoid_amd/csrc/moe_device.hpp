@@ -24,8 +24,12 @@ constexpr int kBlockK = 32;           // Q4 block length
 constexpr int kGemvMaxChunks = 2;     // small-T path: d <= 2 * 4096, I <= 2 * 1024
 constexpr int kGroupedBM = 96;        // grouped GEMM: rows per M-tile
 constexpr int kGroupedBK = 128;       // grouped GEMM: K per main-loop iteration (4 blocks)
-constexpr int kGateUpBandCols = 128;  // grouped gate+up: h columns per workgroup
-constexpr int kDownBandCols = 256;    // grouped down: output columns per workgroup
+#ifndef MOE_GROUPED_WAVES
+#define MOE_GROUPED_WAVES 4
+#endif
+constexpr int kGroupedWaves = MOE_GROUPED_WAVES;  // grouped GEMM: wavefronts per workgroup
+constexpr int kGateUpBandCols = 32 * kGroupedWaves;  // grouped gate+up: h columns per workgroup
+constexpr int kDownBandCols = 64 * kGroupedWaves;    // grouped down: output columns per workgroup
 constexpr int kBuildChunk = 256;      // routing build: tokens per workgroup
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
@@ -59,41 +63,14 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask_s, uint32_t
 // ---------------------------------------------------------------- dequant to fp16 (MFMA operand)
 // Eight codes of one dword (element m in bits 4m..4m+3) -> eight fp16
 // weights (q - 8) * d, in the pair order (e0,e4) (e1,e5) (e2,e6) (e3,e7):
-// each pair needs one shift and one mask.  The activation operands are stored
-// in the same order within every group of 8 (kPermInGroup).
+// each pair needs one mask (after at most one shift).  The activation
+// operands are stored in the same order within every group of 8 (see
+// perm_slot).  Both forms below round (q - 8) * d once, so they give the
+// same bits.
 //
-// Fast form (|d| < 0.5): a nibble placed in bits 7..10 of an fp16 is the
-// number q * 2^-17 (subnormal or the first binade, where the encoding is
-// linear), so one packed FMA q*2^-17 * (d*2^17) - 8d gives (q - 8) * d with a
-// single rounding; d*2^17 stays finite for |d| < 0.5.
-// General form: nibble in the low mantissa of 1024.0 (exactly 1024 + q),
-// minus 1032 (exact), times d (one rounding).
-struct Q4Scale {
-  half2v mul;   // fast: (d*2^17, d*2^17); general: (d, d)
-  half2v add;   // fast: (-8d, -8d)
-};
-
-__device__ __forceinline__ Q4Scale q4_scale_fast(uint32_t d_bits) {
-  const _Float16 dv = __builtin_bit_cast(_Float16, (uint16_t)d_bits);
-  const half2v d2 = {dv, dv};
-  Q4Scale s;
-  s.mul = d2 * half2v{(_Float16)512.0f, (_Float16)512.0f} * half2v{(_Float16)256.0f, (_Float16)256.0f};
-  s.add = d2 * half2v{(_Float16)-8.0f, (_Float16)-8.0f};
-  return s;
-}
-__device__ __forceinline__ bool q4_scale_fast_ok(uint32_t d_bits) { return (d_bits & 0x7FFFu) < 0x3800u; }
-
-__device__ __forceinline__ half8 dequant8_fast(uint32_t w, const Q4Scale& s) {
-  const uint32_t M = 0x07800780u;
-  const uint32_t p0 = (w << 7) & M, p1 = (w << 3) & M, p2 = (w >> 1) & M, p3 = (w >> 5) & M;
-  // fused multiply-add: one rounding
-  const half2v r0 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p0), s.mul, s.add);
-  const half2v r1 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p1), s.mul, s.add);
-  const half2v r2 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p2), s.mul, s.add);
-  const half2v r3 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p3), s.mul, s.add);
-  return half8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-}
-
+// General form: the pair's nibbles placed in the low mantissa of 1024.0
+// (v_and_or_b32 with 0x64006400) are exactly 1024 + q; minus 1032 (exact),
+// times d (one rounding).
 __device__ __forceinline__ half8 dequant8_general(uint32_t w, half2v d2, uint32_t M, uint32_t C) {
   // M = 0x000F000F (SGPR), C = 0x64006400 (VGPR): p_j = (1024 + e_j, 1024 + e_{j+4}) as fp16 bits
   const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
@@ -103,6 +80,30 @@ __device__ __forceinline__ half8 dequant8_general(uint32_t w, half2v d2, uint32_
   const half2v r1 = (__builtin_bit_cast(half2v, p1) - off) * d2;
   const half2v r2 = (__builtin_bit_cast(half2v, p2) - off) * d2;
   const half2v r3 = (__builtin_bit_cast(half2v, p3) - off) * d2;
+  return half8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+// Small-scale form, for |d| < 2^-4: a nibble masked into bits 4..7 of an
+// fp16 with zero exponent is the subnormal q * 2^-20 (exact), and one packed
+// FMA with (d * 2^20, -8d) -- both exact, d * 2^20 <= 65504 -- gives
+// (q - 8) * d with a single rounding.  Three shifts, four ands, four FMAs.
+struct SmallScale {
+  half2v mul, add;  // (d * 2^20, d * 2^20), (-8d, -8d)
+};
+__device__ __forceinline__ SmallScale small_scale(half2v d2) {
+  const half2v k = {(_Float16)1024.0f, (_Float16)1024.0f};
+  return SmallScale{d2 * k * k, d2 * half2v{(_Float16)-8.0f, (_Float16)-8.0f}};
+}
+// |d| < 2^-4 (also false for inf and NaN)
+__device__ __forceinline__ bool small_scale_ok(uint32_t d_bits) { return (d_bits & 0x7FFFu) < 0x2C00u; }
+
+__device__ __forceinline__ half8 dequant8_small(uint32_t w, const SmallScale& s) {
+  const uint32_t M = 0x00F000F0u;
+  const uint32_t p0 = (w << 4) & M, p1 = w & M, p2 = (w >> 4) & M, p3 = (w >> 8) & M;
+  const half2v r0 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p0), s.mul, s.add);
+  const half2v r1 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p1), s.mul, s.add);
+  const half2v r2 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p2), s.mul, s.add);
+  const half2v r3 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p3), s.mul, s.add);
   return half8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 

@@ -12,6 +12,14 @@ from . import abi
 WEIGHT_KEYS = ("w13_qs", "w13_sc", "w2_qs", "w2_sc", "s13_qs", "s13_sc", "s2_qs", "s2_sc")
 
 
+def pack_scales(sc: np.ndarray) -> np.ndarray:
+    """Q4 scales [..., rows, K/32] -> the library's layout [..., rows/16, K/32, 16] (an index
+    permutation: the scale of row r, block b moves to ((r/16)*(K/32) + b)*16 + r%16)."""
+    *lead, rows, nkb = sc.shape
+    assert rows % 16 == 0, rows
+    return np.ascontiguousarray(sc.reshape(*lead, rows // 16, 16, nkb).swapaxes(-1, -2))
+
+
 def to_device(a: np.ndarray, device) -> torch.Tensor:
     """numpy -> torch on `device`; uint16 bit patterns travel as int16 (same bytes)."""
     a = np.ascontiguousarray(a)
@@ -30,7 +38,7 @@ class DeviceWeights(dict):
         w["w_router"] = to_device(inp["w_router"], device)
         w["bias"] = to_device(inp["bias"], device)
         for key in WEIGHT_KEYS:
-            w[key] = to_device(inp[key], device)
+            w[key] = to_device(pack_scales(inp[key]) if key.endswith("_sc") else inp[key], device)
         return w
 
 
