@@ -100,7 +100,9 @@ extern "C" {
 #define MOE_FLAG_FORCE_GROUPED 1u  /* grouped path even when T is small            */
 #define MOE_FLAG_FORCE_GEMV    2u  /* small-T path even when T is larger (T <= 64)  */
 #define MOE_FLAG_ID_ORDER      4u  /* schedule groups in id order, not by size     */
-#define MOE_FLAG_NO_BANDING    8u  /* M-tile-major workgroup order, not N-banded   */
+#define MOE_FLAG_NO_BANDING    8u  /* grouped GEMMs: workgroups in plain item order  */
+#define MOE_FLAG_BAND_MAJOR   16u  /* grouped GEMMs: N-banded order, all M-tiles of a
+                                      weight band on one XCD (weight reuse in L2)  */
 
 #define MOE_GEMV_MAX_T      8    /* default small-T threshold                       */
 #define MOE_GEMV_FORCE_MAX_T 64  /* largest T the small-T path accepts              */

@@ -20,6 +20,7 @@ MOE_FLAG_FORCE_GROUPED = 1
 MOE_FLAG_FORCE_GEMV = 2
 MOE_FLAG_ID_ORDER = 4
 MOE_FLAG_NO_BANDING = 8
+MOE_FLAG_BAND_MAJOR = 16
 MOE_GEMV_MAX_T = 8
 MOE_GEMV_FORCE_MAX_T = 64
 

@@ -36,7 +36,9 @@ int check_dims(const moe_dims* d, uint32_t flags) {
   if (d->T < 1 || d->d < 1 || d->E < 1 || d->k < 1 || d->I < 1 || d->I_shared < 1) return MOE_EINVAL;
   if (d->k > d->E) return MOE_EINVAL;
   if ((flags & MOE_FLAG_FORCE_GROUPED) && (flags & MOE_FLAG_FORCE_GEMV)) return MOE_EINVAL;
-  if (flags & ~(uint32_t)(MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_GEMV | MOE_FLAG_ID_ORDER | MOE_FLAG_NO_BANDING))
+  if ((flags & MOE_FLAG_NO_BANDING) && (flags & MOE_FLAG_BAND_MAJOR)) return MOE_EINVAL;
+  if (flags & ~(uint32_t)(MOE_FLAG_FORCE_GROUPED | MOE_FLAG_FORCE_GEMV | MOE_FLAG_ID_ORDER | MOE_FLAG_NO_BANDING |
+                          MOE_FLAG_BAND_MAJOR))
     return MOE_EINVAL;
   if (d->d % 32 || d->I % 32 || d->I_shared % 32) return MOE_EUNSUPPORTED;
   if (d->E > kMaxExperts || d->k > kMaxTopK) return MOE_EUNSUPPORTED;

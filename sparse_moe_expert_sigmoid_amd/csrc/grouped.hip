@@ -13,9 +13,10 @@
 //
 // Work items: for each group (expert, or the shared expert as group E) in
 // schedule order, its M-tiles of up to 96 rows times the N-bands of the
-// output.  Default order is band-major inside a group (all M-tiles of one
-// weight band adjacent), and the launch index is remapped so that each XCD
-// (own L2) receives a contiguous run of items.  The grid is sized for the
+// output, M-tile-major by default (the bands of one M-tile adjacent; runs of
+// 8 items per XCD so that the workgroups sharing an activation tile share an
+// L2), or band-major (all M-tiles of one weight band on one XCD) on request.
+// The grid is sized for the
 // largest possible tile count; surplus workgroups exit at once, so the launch
 // shape does not depend on device data and the call can be graph-captured.
 //
@@ -98,6 +99,7 @@ struct GArgs {
   const int* mt_prefix;
   int T, d, E, k, I, Is;
   int nbands;
+  int order;                // work-item order (see k_grouped)
   uint32_t flags;
   uint32_t dq_mask, dq_magic;
 };
@@ -320,10 +322,23 @@ __global__ __launch_bounds__(kGroupedThreads, 8 / kGroupedWaves) void k_grouped(
   // one weight band run on one XCD, adjacent in time.  Otherwise items go round-robin in schedule order.
   int rank, band, mtile;
   {
+    // Work items in schedule order of the groups.  Workgroups are dispatched round-robin over the 8
+    // XCDs (own L2 each), so the launch index is remapped (uniform choice, a.order):
+    //  0: items are M-tile-major (the bands of one M-tile adjacent) and every run of 8 consecutive
+    //     items goes to one XCD: the workgroups that share an activation tile share an L2;
+    //  1: band-major inside a group, XCD x taking the bands = x (mod 8) of every group: all M-tiles
+    //     that read one weight band run on one XCD, adjacent in time (needs nbands % 8 == 0);
+    //  2: items M-tile-major in launch order.
     const int bid = blockIdx.x;
-    const bool per_xcd = (nb % 8) == 0 && !(a.flags & MOE_FLAG_NO_BANDING);
-    const int nbx = per_xcd ? nb / 8 : nb;  // bands per group seen by this walk
-    const int item = per_xcd ? bid >> 3 : bid;
+    const int order = (a.order == 1 && nb % 8 != 0) ? 2 : a.order;
+    const int nbx = order == 1 ? nb / 8 : nb;  // bands per group seen by this walk
+    int item;
+    if (order == 0) {
+      const int sl = bid >> 3;
+      item = (((sl >> 3) << 3) + (bid & 7)) * 8 + (sl & 7);
+    } else {
+      item = order == 1 ? bid >> 3 : bid;
+    }
     if (item >= n_mt * nbx) return;
     int lo = 0, hi = ngroups;  // s_prefix[lo]*nbx <= item < s_prefix[hi]*nbx
     while (hi - lo > 1) {
@@ -334,14 +349,13 @@ __global__ __launch_bounds__(kGroupedThreads, 8 / kGroupedWaves) void k_grouped(
     const int p0 = ufl(s_prefix[rank]);
     const int nmt = ufl(s_prefix[rank + 1]) - p0;
     const int local = item - p0 * nbx;
-    if (a.flags & MOE_FLAG_NO_BANDING) {
+    if (order == 1) {
+      band = 8 * (local / nmt) + (bid & 7);
+      mtile = local % nmt;
+    } else {
       mtile = local / nbx;
       band = local % nbx;
-    } else {
-      band = local / nmt;
-      mtile = local % nmt;
     }
-    if (per_xcd) band = 8 * band + (bid & 7);
   }
   const int g = ufl(a.group_order[rank]);
   const bool shared = (g == a.E);
@@ -511,6 +525,7 @@ static GArgs make_args(const Shape& s, const Routing& r, uint32_t flags) {
   a.mt_prefix = r.mt_prefix;
   a.T = s.T; a.d = s.d; a.E = s.E; a.k = s.k; a.I = s.I; a.Is = s.Is;
   a.flags = flags;
+  a.order = (flags & MOE_FLAG_NO_BANDING) ? 2 : (flags & MOE_FLAG_BAND_MAJOR) ? 1 : 0;
   a.dq_mask = 0x000F000Fu;
   a.dq_magic = 0x64006400u;
   return a;
@@ -532,7 +547,7 @@ hipError_t launch_grouped_gateup(const Shape& s, const uint16_t* x, const Routin
   a.h_s = o.h_s;
   const int Imax = s.I > s.Is ? s.I : s.Is;
   a.nbands = (Imax + kGateUpBandCols - 1) / kGateUpBandCols;
-  const long grid = (long)grouped_max_mtiles(s) * a.nbands;
+  const long grid = ((long)grouped_max_mtiles(s) * a.nbands + 63) / 64 * 64;  // whole runs of 8 x 8 items
   hipLaunchKernelGGL(k_grouped<true>, dim3((unsigned)grid), dim3(kGroupedThreads), 0, st, a);
   return hipGetLastError();
 }
@@ -549,7 +564,7 @@ hipError_t launch_grouped_down(const Shape& s, const Routing& r, Q4 w2, Q4 s2, c
   a.y_r = o.y_pair;
   a.y_s = o.y_s;
   a.nbands = (s.d + kDownBandCols - 1) / kDownBandCols;
-  const long grid = (long)grouped_max_mtiles(s) * a.nbands;
+  const long grid = ((long)grouped_max_mtiles(s) * a.nbands + 63) / 64 * 64;  // whole runs of 8 x 8 items
   hipLaunchKernelGGL(k_grouped<false>, dim3((unsigned)grid), dim3(kGroupedThreads), 0, st, a);
   return hipGetLastError();
 }

@@ -57,6 +57,8 @@ def test_supports_codes(kw, code):
 
 def test_flags_validation():
     assert moe.moe_supports(TINY, abi.MOE_FLAG_FORCE_GEMV | abi.MOE_FLAG_FORCE_GROUPED) == abi.MOE_EINVAL
+    assert moe.moe_supports(TINY, abi.MOE_FLAG_NO_BANDING | abi.MOE_FLAG_BAND_MAJOR) == abi.MOE_EINVAL
+    assert moe.moe_supports(TINY, abi.MOE_FLAG_BAND_MAJOR) == abi.MOE_OK
     assert moe.moe_supports(TINY, 1 << 7) == abi.MOE_EINVAL
     assert moe.moe_supports(BIG, abi.MOE_FLAG_FORCE_GEMV) == abi.MOE_EUNSUPPORTED  # T = 2048 > 64
     assert moe.moe_supports(d(T=64, d=4096, E=256, k=10, I=1024, I_shared=1024), abi.MOE_FLAG_FORCE_GEMV) == 0
@@ -164,7 +166,7 @@ def test_header_documents_every_code():
         assert re.search(rf"#define {name}\s+\(?{value}\)?", text), name
         assert getattr(abi, name) == value
     for name in ("MOE_FLAG_FORCE_GROUPED", "MOE_FLAG_FORCE_GEMV", "MOE_FLAG_ID_ORDER", "MOE_FLAG_NO_BANDING",
-                 "MOE_GEMV_MAX_T"):
+                 "MOE_FLAG_BAND_MAJOR", "MOE_GEMV_MAX_T"):
         m = re.search(rf"#define {name}\s+(\d+)u?", text)
         assert m and int(m.group(1)) == getattr(abi, name), name
     assert ctypes.sizeof(abi.Dims) == 24

@@ -55,7 +55,8 @@ def test_tiny_paths_agree_and_are_deterministic():
 
 
 @pytest.mark.parametrize("flags", [GROUPED | abi.MOE_FLAG_ID_ORDER, GROUPED | abi.MOE_FLAG_NO_BANDING,
-                                   GROUPED | abi.MOE_FLAG_ID_ORDER | abi.MOE_FLAG_NO_BANDING])
+                                   GROUPED | abi.MOE_FLAG_ID_ORDER | abi.MOE_FLAG_NO_BANDING,
+                                   GROUPED | abi.MOE_FLAG_BAND_MAJOR])
 def test_schedule_order_does_not_change_bits(flags):
     dims = synth.Dims(T=300, d=512, E=12, k=3, I=256, I_shared=384)
     inp = synth.make_inputs(dims, seed=7, bias="zipf")
@@ -65,6 +66,19 @@ def test_schedule_order_does_not_change_bits(flags):
     other, _ = run(inp, flags, w, x)
     check_routing_build(other)
     assert torch.equal(base.y, other.y)
+
+
+def test_band_major_order_does_not_change_bits():
+    # 8 weight bands in both GEMMs (I = 1024 at 128 columns, d = 2048 at 256), so the band-major walk is
+    # the one that runs (it needs a multiple of 8 bands)
+    dims = synth.Dims(T=300, d=2048, E=12, k=3, I=1024, I_shared=1024)
+    inp = synth.make_inputs(dims, seed=17, bias="zipf")
+    w = DeviceWeights.upload(inp)
+    x = to_device(inp["x"], "cuda")
+    base, _ = run(inp, GROUPED, w, x)
+    other, _ = run(inp, GROUPED | abi.MOE_FLAG_BAND_MAJOR, w, x)
+    assert torch.equal(base.y, other.y)
+    check_parity(inp, other, tokens=np.arange(0, 300, 37), label="band_major")
 
 
 @pytest.mark.parametrize("flags", [0, GROUPED])
