@@ -199,7 +199,8 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
         if (mt + 1 < NMT) a_nxt = *reinterpret_cast<const half8*>(Ar + (mt + 1) * 16 * kRowBytes);
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns)
-          acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur, b_cur[ns], acc[mt][ns], 0, 0, 0);
+          // weights as the A operand: the tile comes out transposed (see the epilogue)
+          acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b_cur[ns], a_cur, acc[mt][ns], 0, 0, 0);
         if (s < 3 && mt < 4) b_nxt[mt] = deq(q[mt][s + 1], mt);
         if (mt + 1 < NMT) a_cur = a_nxt;
       }
@@ -275,29 +276,51 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
     }
   }
 
-  // ---- epilogue.  D layout: lane holds column n of rows 4G..4G+3 of each 16x16 tile.
+  // ---- epilogue.  With the weights as the A operand, lane (n, G) holds, for activation row
+  // mt*16 + n, the four consecutive output columns 4G .. 4G+3 of each 16-column slice.
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
+    const int row = mt * 16 + c.n;
+    const bool live = row < c.mlen;
+    if (GATEUP) {
+      _Float16* out = c.shared ? a.h_s : a.h_r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = mt * 16 + 4 * c.G + i;
-      if (row >= c.mlen) continue;
-      if (GATEUP) {
-        _Float16* out = c.shared ? a.h_s : a.h_r;
+      for (int xh = 0; xh < 2; ++xh) {
+        // h columns c0 + 16xh + 4G + i; SiLU(gate) * up with a fast exponential and reciprocal
+        half2v h[2];
 #pragma unroll
-        for (int xh = 0; xh < 2; ++xh) {
-          if (!c.nok[xh]) continue;
-          const float gv = acc[mt][xh][i], uv = acc[mt][2 + xh][i];
-          const int col = c.c0 + 16 * xh + c.n;  // stored in the dequant pair order within groups of 8
-          out[(size_t)(c.rbase + row) * c.Iw + (col & ~7) + perm_slot(col & 7)] = (_Float16)(siluf_(gv) * uv);
+        for (int j = 0; j < 2; ++j) {
+          float hv[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float gv = acc[mt][xh][2 * j + e], uv = acc[mt][2 + xh][2 * j + e];
+            hv[e] = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;
+          }
+          h[j] = half2v{(_Float16)hv[0], (_Float16)hv[1]};
         }
-      } else {
-        _Float16* out = c.shared ? a.y_s : a.y_r;
+        // h is stored in the dequant pair order inside each group of 8 columns (slot 2m holds column
+        // m, slot 2m+1 column m+4): lanes G and G^1 (16 lanes apart) hold the two halves of a group.
+        // The even lane writes slots 0..3 (its columns 0, 1 with the partner's 4, 5), the odd lane
+        // slots 4..7 (the partner's 2, 3 with its own 6, 7).
+        const bool odd = c.G & 1;
+        const uint32_t give = __builtin_bit_cast(uint32_t, odd ? h[0] : h[1]);
+        const half2v got = as_half2((uint32_t)__shfl_xor((int)give, 16, 64));
+        const half2v mine = odd ? h[1] : h[0];
+        const half2v lo = odd ? got : mine, hi = odd ? mine : got;  // lo: columns of the even lane
+        const uint2 v = {__builtin_bit_cast(uint32_t, half2v{lo[0], hi[0]}),
+                         __builtin_bit_cast(uint32_t, half2v{lo[1], hi[1]})};
+        const int col = c.c0 + 16 * xh + 8 * (c.G >> 1) + 4 * (c.G & 1);
+        if (live && c.nok[xh]) *reinterpret_cast<uint2*>(out + (size_t)(c.rbase + row) * c.Iw + col) = v;
+      }
+    } else {
+      _Float16* out = c.shared ? a.y_s : a.y_r;
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
-          if (!c.nok[ns]) continue;
-          out[(size_t)(c.rbase + row) * a.d + c.c0 + 16 * ns + c.n] = (_Float16)acc[mt][ns][i];
-        }
+      for (int ns = 0; ns < 4; ++ns) {
+        const half2v p0 = {(_Float16)acc[mt][ns][0], (_Float16)acc[mt][ns][1]};
+        const half2v p1 = {(_Float16)acc[mt][ns][2], (_Float16)acc[mt][ns][3]};
+        const uint2 v = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+        if (live && c.nok[ns])
+          *reinterpret_cast<uint2*>(out + (size_t)(c.rbase + row) * a.d + c.c0 + 16 * ns + 4 * c.G) = v;
       }
     }
   }
