@@ -62,7 +62,7 @@ Layout routing_layout(const moe_dims* d) {
   const size_t nchunks = (T + kBuildChunk - 1) / kBuildChunk;
   Layout L{};
   size_t off = 0;
-  L.logits = off;       off += align256(T * E * 4);
+  L.logits = off;       off += align256((size_t)moe::kRouterParts * T * E * 4);
   L.counts = off;       off += align256((E + 1) * 4);
   L.offsets = off;      off += align256((E + 1) * 4);
   L.sorted_pair = off;  off += align256(P * 4);
@@ -172,10 +172,12 @@ int moe_route(const moe_dims* dims, const uint16_t* x_bf16, const float* w_route
   hipStream_t st = static_cast<hipStream_t>(stream);
   const moe::Routing r = routing_ptrs(routing, L);
   (void)hipGetLastError();
-  hipError_t e = choose_path(dims, flags) == 0 ? moe::launch_router_gemv(s, x_bf16, w_router, r.logits, st)
-                                                : moe::launch_router_mfma(s, x_bf16, w_router, r.logits, st);
+  const bool gemv = choose_path(dims, flags) == 0;
+  hipError_t e = gemv ? moe::launch_router_gemv(s, x_bf16, w_router, r.logits, st)
+                      : moe::launch_router_mfma(s, x_bf16, w_router, r.logits, st);
   if (e != hipSuccess) return MOE_EHIP;
-  return hip_rc(moe::launch_topk(s, r.logits, bias, topk_ids, topk_w, st));
+  const int nparts = gemv ? 1 : moe::kRouterParts;
+  return hip_rc(moe::launch_topk(s, r.logits, nparts, bias, topk_ids, topk_w, st));
 }
 
 int moe_build_descriptors(const moe_dims* dims, const int32_t* topk_ids, void* routing, size_t routing_bytes,

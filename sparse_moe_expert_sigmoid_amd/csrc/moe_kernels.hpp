@@ -32,10 +32,13 @@ struct Q4 {
 // router.hip
 hipError_t launch_router_gemv(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
                               hipStream_t st);
+// writes kRouterParts partial logit arrays [part][T][E] (K split in that many parts)
+constexpr int kRouterParts = 4;
 hipError_t launch_router_mfma(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
                               hipStream_t st);
-hipError_t launch_topk(const Shape& s, const float* logits, const float* bias, int32_t* topk_ids, float* topk_w,
-                       hipStream_t st);
+// logits: nparts partial arrays [nparts][T][E], summed in order
+hipError_t launch_topk(const Shape& s, const float* logits, int nparts, const float* bias, int32_t* topk_ids,
+                       float* topk_w, hipStream_t st);
 
 // build.hip
 hipError_t launch_build(const Shape& s, const int32_t* topk_ids, const Routing& r, uint32_t flags,

@@ -87,26 +87,36 @@ hipError_t launch_router_gemv(const Shape& s, const uint16_t* x, const float* w_
 // ---------------------------------------------------------------------------
 // Larger T: bf16 MFMA.  x is bf16 already; each fp32 router weight is split
 // into hi = bf16(w) and lo = bf16(w - hi) so that two bf16 MFMAs reproduce
-// the fp32 product to about 2^-17 relative.  A workgroup computes one 16 x 16
-// tile (16 tokens x 16 experts); its four wavefronts take interleaved quarters
-// of K (steps of 32) and their partial tiles are summed in LDS in a fixed
-// order.  With 16 x 16 tiles the grid has T/16 * E/16 workgroups, enough
-// wavefronts per SIMD to hide the load latency without software pipelining.
+// the fp32 product to about 2^-17 relative.  A workgroup computes a tile of
+// 32 tokens x 64 experts: K advances 64 at a time through a double-buffered
+// LDS stage (32 x 64 bf16 activations, 64 x 64 fp32 weights, rows padded so
+// that the 16 rows one MFMA operand reads fall in distinct banks).  Wavefront
+// w takes tokens 16(w&1) .. +15 and experts 32(w>>1) .. +31 (two 16 x 16
+// tiles, each with a hi and a lo MFMA per K step of 32).  K is split in
+// kRtSplit contiguous parts (blockIdx.y), each writing its own partial logits
+// [part][T][E]; the top-k sums the parts in order, so the result is fixed.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kRouterUnroll = 8;  // K steps whose loads are issued together
+constexpr int kRtT = 32, kRtE = 64, kRtK = 64;
+constexpr int kRtSplit = kRouterParts;  // K parts, each its own workgroup; partial logits summed by the top-k
+constexpr int kRtXStride = kRtK * 2 + 16;  // bytes per activation row in LDS (144)
+constexpr int kRtWStride = kRtK * 4 + 16;  // bytes per weight row in LDS (272)
 
 __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict__ x, const float* __restrict__ W,
                                                      float* __restrict__ logits, int T, int d, int E) {
-  __shared__ floatx4 part[4][64];
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __shared__ __attribute__((aligned(16))) char xs[2][kRtT * kRtXStride];
+  __shared__ __attribute__((aligned(16))) char ws[2][kRtE * kRtWStride];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, G = lane >> 4;
-  // Workgroups go round-robin over the 8 XCDs (own L2 each).  When the expert blocks divide evenly,
-  // XCD x takes a fixed eighth of them for every token block, so each L2 holds only its eighth of
-  // the router weights while the token blocks stream past.
-  const int neb = (E + 15) / 16;
+  // Workgroups go round-robin over the 8 XCDs (own L2 each).  When the expert blocks and the XCDs
+  // divide evenly, each XCD keeps a fixed share of the expert blocks for every token block, so its L2
+  // holds only its share of the router weights while the token blocks stream past.
+  const int neb = (E + kRtE - 1) / kRtE;
   int eb, tb;
-  if (neb % 8 == 0) {
+  if (neb <= 8 && 8 % neb == 0) {
+    eb = blockIdx.x % neb;  // blockIdx % 8 is the XCD, so XCD x always gets expert block x % neb
+    tb = blockIdx.x / neb;
+  } else if (neb % 8 == 0) {
     const int per = neb / 8, item = blockIdx.x >> 3;
     eb = (blockIdx.x & 7) * per + item % per;
     tb = item / per;
@@ -114,53 +124,91 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
     eb = blockIdx.x % neb;
     tb = blockIdx.x / neb;
   }
-  const int t0 = tb * 16, e0 = eb * 16;
-  const int t = min(t0 + n, T - 1), e = min(e0 + n, E - 1);  // clamped rows: computed, never stored
-  const uint16_t* xrow = x + (size_t)t * d + 8 * G;
-  const float* wrow = W + (size_t)e * d + 8 * G;
-  const int nsteps = d / 32;
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto step = [&](const u32x4& a, const float4& w0, const float4& w1) __attribute__((always_inline)) {
-    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    bf16x8 bhi, blo;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const __bf16 h = (__bf16)wv[i];
-      bhi[i] = h;
-      blo[i] = (__bf16)(wv[i] - (float)h);
-    }
-    const bf16x8 a8 = __builtin_bit_cast(bf16x8, a);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, bhi, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, blo, acc, 0, 0, 0);
-  };
-  // wave w takes steps w, w+4, w+8, ...: whole batches of kRouterUnroll steps with all loads issued
-  // first, then the remaining steps one at a time
-  int s0 = wave;
-  for (; s0 + 4 * (kRouterUnroll - 1) < nsteps; s0 += 4 * kRouterUnroll) {
-    u32x4 av[kRouterUnroll];
-    float4 w0[kRouterUnroll], w1[kRouterUnroll];
-#pragma unroll
-    for (int u = 0; u < kRouterUnroll; ++u) {
-      av[u] = ld16(xrow + 32 * (s0 + 4 * u));
-      w0[u] = *reinterpret_cast<const float4*>(wrow + 32 * (s0 + 4 * u));
-      w1[u] = *reinterpret_cast<const float4*>(wrow + 32 * (s0 + 4 * u) + 4);
-    }
-#pragma unroll
-    for (int u = 0; u < kRouterUnroll; ++u) step(av[u], w0[u], w1[u]);
+  const int t0 = tb * kRtT, e0 = eb * kRtE;
+  // staging: thread -> one 16-byte piece of the activation tile and four of the weight tile
+  const int xr = tid >> 3, xc = tid & 7;                     // 32 rows x 8 pieces
+  const uint16_t* xsrc = x + (size_t)min(t0 + xr, T - 1) * d + 8 * xc;
+  const int wr0 = tid >> 4, wc = tid & 15;  // 64 rows x 16 pieces: rows wr0 + 16j
+  const float* wsrc = W + (size_t)min(e0 + wr0, E - 1) * d + 4 * wc;
+  const size_t wstep = (size_t)16 * d;  // 16 rows further down (clamped rows only at the end of E)
+  const int wlast = E - 1 - e0 - wr0;   // rows beyond E re-read row E-1: j > wlast/16 is clamped
+  // this workgroup's part of K: stages [st0, st1) of 64 columns
+  const int nst_all = (d + kRtK - 1) / kRtK;
+  const int st0 = (nst_all * (int)blockIdx.y) / kRtSplit, st1 = (nst_all * ((int)blockIdx.y + 1)) / kRtSplit;
+  const bool half_tail = (d % kRtK) != 0 && st1 == nst_all;  // the last stage holds only one K step of 32
+  logits += (size_t)blockIdx.y * T * E;
+  const int wt = wave & 1, we = wave >> 1;
+  floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  u32x4 xv;
+  float4 wv0, wv1, wv2, wv3;
+#define MOE_RT_LOAD(st)                                                                             \
+  {                                                                                                  \
+    /* K columns past the end (half stage) re-read the stage's first half: loaded, never used */    \
+    const int k0_ = (st) * kRtK;                                                                     \
+    xv = ld16(xsrc + ((k0_ + 8 * xc < d) ? k0_ : k0_ - 32));                                         \
+    const int kw_ = (k0_ + 4 * wc < d) ? k0_ : k0_ - 32;                                            \
+    wv0 = *reinterpret_cast<const float4*>(wsrc + kw_);                                              \
+    wv1 = *reinterpret_cast<const float4*>(wsrc + (16 <= wlast ? wstep : 0) + kw_);                   \
+    wv2 = *reinterpret_cast<const float4*>(wsrc + (32 <= wlast ? 2 * wstep : 0) + kw_);               \
+    wv3 = *reinterpret_cast<const float4*>(wsrc + (48 <= wlast ? 3 * wstep : 0) + kw_);               \
   }
-  for (; s0 < nsteps; s0 += 4)
-    step(ld16(xrow + 32 * s0), *reinterpret_cast<const float4*>(wrow + 32 * s0),
-         *reinterpret_cast<const float4*>(wrow + 32 * s0 + 4));
-  part[wave][lane] = acc;
+#define MOE_RT_STORE(buf)                                                                           \
+  {                                                                                                  \
+    *reinterpret_cast<u32x4*>(xs[buf] + xr * kRtXStride + 16 * xc) = xv;                             \
+    char* w_ = ws[buf] + wr0 * kRtWStride + 16 * wc;                                                 \
+    *reinterpret_cast<float4*>(w_) = wv0;                                                            \
+    *reinterpret_cast<float4*>(w_ + 16 * kRtWStride) = wv1;                                          \
+    *reinterpret_cast<float4*>(w_ + 32 * kRtWStride) = wv2;                                          \
+    *reinterpret_cast<float4*>(w_ + 48 * kRtWStride) = wv3;                                          \
+  }
+  if (st0 < st1) {
+    MOE_RT_LOAD(st0);
+    MOE_RT_STORE(0);
+  }
   __syncthreads();
-  if (wave != 0) return;
-  const floatx4 r = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
-  // D layout: lane holds column n (expert e0+n) of rows 4G..4G+3 (tokens)
-  if (e0 + n >= E) return;
+  for (int st = st0; st < st1; ++st) {
+    const int buf = (st - st0) & 1;
+    if (st + 1 < st1) MOE_RT_LOAD(st + 1);  // in flight while this stage is computed
+    const int nk = (half_tail && st == st1 - 1) ? 1 : 2;  // uniform
+    for (int kk = 0; kk < nk; ++kk) {
+      const bf16x8 a8 = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(xs[buf] + (16 * wt + n) * kRtXStride + 64 * kk + 16 * G));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tt = t0 + 4 * G + i;
-    if (tt < T) logits[(size_t)tt * E + e0 + n] = r[i];
+      for (int j = 0; j < 2; ++j) {
+        const char* wrow = ws[buf] + (32 * we + 16 * j + n) * kRtWStride + 128 * kk + 32 * G;
+        const float4 w0 = *reinterpret_cast<const float4*>(wrow);
+        const float4 w1 = *reinterpret_cast<const float4*>(wrow + 16);
+        bf16x8 bhi, blo;
+        bhi[0] = (__bf16)w0.x; bhi[1] = (__bf16)w0.y; bhi[2] = (__bf16)w0.z; bhi[3] = (__bf16)w0.w;
+        bhi[4] = (__bf16)w1.x; bhi[5] = (__bf16)w1.y; bhi[6] = (__bf16)w1.z; bhi[7] = (__bf16)w1.w;
+        blo[0] = (__bf16)(w0.x - (float)bhi[0]); blo[1] = (__bf16)(w0.y - (float)bhi[1]);
+        blo[2] = (__bf16)(w0.z - (float)bhi[2]); blo[3] = (__bf16)(w0.w - (float)bhi[3]);
+        blo[4] = (__bf16)(w1.x - (float)bhi[4]); blo[5] = (__bf16)(w1.y - (float)bhi[5]);
+        blo[6] = (__bf16)(w1.z - (float)bhi[6]); blo[7] = (__bf16)(w1.w - (float)bhi[7]);
+        floatx4& acc = j ? acc1 : acc0;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, bhi, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, blo, acc, 0, 0, 0);
+      }
+    }
+    if (st + 1 < st1) {
+      __syncthreads();  // every wavefront is done with buffer buf ^ 1 (read two stages ago)
+      MOE_RT_STORE(buf ^ 1);
+      __syncthreads();
+    }
+  }
+#undef MOE_RT_LOAD
+#undef MOE_RT_STORE
+  const floatx4 accs[2] = {acc0, acc1};
+  // D layout: lane holds column n (expert) of rows 4G..4G+3 (tokens) of each 16 x 16 tile
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = e0 + 32 * we + 16 * j + n;
+    if (e >= E) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * wt + 4 * G + i;
+      if (t < T) logits[(size_t)t * E + e] = accs[j][i];
+    }
   }
 }
 
@@ -186,15 +234,18 @@ __device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
 
 // Selection for one token by one wavefront: writes ids[0..k) and w[0..k).
 template <int NPER>
-__device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, const float* __restrict__ bias,
-                                          int32_t* __restrict__ ids, float* __restrict__ w, int E, int k, int lane) {
+__device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t part_stride, int nparts,
+                                          const float* __restrict__ bias, int32_t* __restrict__ ids,
+                                          float* __restrict__ w, int E, int k, int lane) {
   uint32_t key[NPER];
   float sc[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
-      const float s = sigmoidf_(lrow[e]);
+      float l = lrow[e];
+      for (int p = 1; p < nparts; ++p) l += lrow[p * part_stride + e];  // partial logits, in order
+      const float s = sigmoidf_(l);
       key[i] = ordered_bits(s + bias[e]);
       sc[i] = s;
     } else {
@@ -251,30 +302,31 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, const 
 }
 
 template <int NPER>
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
-                                              int32_t* __restrict__ ids, float* __restrict__ w, int T, int E,
-                                              int k) {
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int nparts,
+                                              const float* __restrict__ bias, int32_t* __restrict__ ids,
+                                              float* __restrict__ w, int T, int E, int k) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= T) return;
-  topk_wave<NPER>(logits + (size_t)t * E, bias, ids + (size_t)t * k, w + (size_t)t * k, E, k, lane);
+  topk_wave<NPER>(logits + (size_t)t * E, (size_t)T * E, nparts, bias, ids + (size_t)t * k, w + (size_t)t * k, E,
+                  k, lane);
 }
 
 hipError_t launch_router_mfma(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
                               hipStream_t st) {
-  const dim3 grid(((s.T + 15) / 16) * ((s.E + 15) / 16)), block(256);
+  const dim3 grid(((s.T + kRtT - 1) / kRtT) * ((s.E + kRtE - 1) / kRtE), kRtSplit), block(256);
   hipLaunchKernelGGL(k_router_mfma, grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
   return hipGetLastError();
 }
-hipError_t launch_topk(const Shape& s, const float* logits, const float* bias, int32_t* topk_ids, float* topk_w,
-                       hipStream_t st) {
+hipError_t launch_topk(const Shape& s, const float* logits, int nparts, const float* bias, int32_t* topk_ids,
+                       float* topk_w, hipStream_t st) {
   const dim3 grid((s.T + 3) / 4), block(256);
   const int nper = (s.E + 63) / 64;
-  if (nper <= 1) hipLaunchKernelGGL(k_topk<1>, grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
-  else if (nper <= 2) hipLaunchKernelGGL(k_topk<2>, grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
-  else if (nper <= 4) hipLaunchKernelGGL(k_topk<4>, grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
-  else if (nper <= 8) hipLaunchKernelGGL(k_topk<8>, grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
-  else hipLaunchKernelGGL(k_topk<16>, grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  if (nper <= 1) hipLaunchKernelGGL(k_topk<1>, grid, block, 0, st, logits, nparts, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  else if (nper <= 2) hipLaunchKernelGGL(k_topk<2>, grid, block, 0, st, logits, nparts, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  else if (nper <= 4) hipLaunchKernelGGL(k_topk<4>, grid, block, 0, st, logits, nparts, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  else if (nper <= 8) hipLaunchKernelGGL(k_topk<8>, grid, block, 0, st, logits, nparts, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  else hipLaunchKernelGGL(k_topk<16>, grid, block, 0, st, logits, nparts, bias, topk_ids, topk_w, s.T, s.E, s.k);
   return hipGetLastError();
 }
 
