@@ -193,6 +193,24 @@ def source_hash(*files):
     return h.hexdigest()[:16]
 
 
+GEMV_SOURCES = ("sparse_moe_expert_sigmoid_amd/csrc/gemv.hip", "sparse_moe_expert_sigmoid_amd/csrc/moe_device.hpp")
+GROUPED_SOURCES = ("sparse_moe_expert_sigmoid_amd/csrc/grouped.hip", "sparse_moe_expert_sigmoid_amd/csrc/moe_device.hpp")
+
+
+def recorded_traffic(profile: str, sources) -> int | None:
+    """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE/WRITE_SIZE record (copy-calibrated), or
+    None when the kernel's sources changed since the counters were taken."""
+    try:
+        text = open(os.path.join(ROOT, "profiles", profile)).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines()
+                  if line.startswith(("traffic_bytes_per_launch: ", "source_sha256_16: ")))
+    if fields.get("source_sha256_16") != source_hash(*sources):
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_sample=False):
     cfg = synth.CONFIGS[name]
     dims = cfg.dims
@@ -291,10 +309,12 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
     }
     if path == 0:
         kname = "gemv_gateup"
-        per_launch = T * dims.k * gu + T * sgu + T * d * 2 + (P * dims.I + T * dims.I_shared) * 4
+        per_launch = T * dims.k * gu + T * sgu + T * d * 2 + (P * dims.I + T * dims.I_shared) * 2
         achieved = per_launch / (kernel_us[kname] * 1e-6) / 1e9
         res["roofline"] = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": recorded_traffic("gemv_gateup_decode_T1_traffic.md", GEMV_SOURCES)
+                           if name == "decode" else None,
                            "algorithmic_bytes_per_launch": per_launch,
                            "avg_launch_us": round(kernel_us[kname], 3)}
     else:
@@ -303,7 +323,9 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
         achieved = per_launch / (kernel_us[kname] * 1e-6) / 1e12
         res["roofline"] = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),
                            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                           "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                           "traffic": recorded_traffic("grouped_gateup_prefill_T2048_traffic.md", GROUPED_SOURCES)
+                           if name == "prefill" else None,
                            "algorithmic_flop_per_launch": per_launch, "avg_launch_us": round(kernel_us[kname], 3)}
     res["_inp0"] = inp0
     return res
@@ -334,6 +356,25 @@ def cpu_baseline(inp, budget_s=15.0):
                       f"{el:.1f} s wall on the host"}
 
 
+def traffic_run(name, torch, layer, synth):
+    """Three layer calls and two 256 MiB copies, nothing else: the run that rocprofv3 --pmc FETCH_SIZE /
+    WRITE_SIZE records for the traffic summaries under profiles/ (the copy calibrates the counters)."""
+    inp = synth.make_inputs(synth.CONFIGS[name])
+    w = layer.DeviceWeights.upload(inp)
+    x = layer.to_device(inp["x"], "cuda")
+    ws = layer.Workspace(inp["dims"], 0)
+    for _ in range(3):
+        layer.layer_call(x, w, ws)
+    a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_run": name, "layer_calls": 3, "copy_bytes": 256 << 20, "copies": 2}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -342,6 +383,9 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "batched_decode", "prefill", "long_prefill"])
     ap.add_argument("--secondary", default="prefill", help="second workload reported alongside ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-run", metavar="WORKLOAD", default=None,
+                    help="for hardware-counter collection only: run WORKLOAD's layer 3 times, then copy a 256 MiB "
+                         "device buffer twice (the calibration of FETCH_SIZE / WRITE_SIZE), print one line, exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this layer is built and measured on a single MI355X; "
@@ -355,6 +399,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(3)
+    if args.traffic_run:
+        traffic_run(args.traffic_run, torch, layer, synth)
+        return
     hip = Hip()
     prim = run_workload(args.workload, args.steps, args.warmup, torch, hip, abi, layer, synth)
     sec = None
