@@ -15,7 +15,8 @@
 //   group_order[E+1]               schedule order of the groups
 //   mt_prefix[E+2]                 exclusive prefix of M-tiles along group_order
 //
-// Two launches over chunks of 256 tokens.  Every token picks k distinct
+// Two launches over chunks of 256 tokens (the second with one more workgroup
+// that builds the group schedule while the others scatter).  Every token picks k distinct
 // experts, so inside an expert the stable order is token order: the rank of
 // token i of a chunk within expert e is the number of set bits below i in
 // the chunk's bitmask of e, plus the counts of the earlier chunks.  The
@@ -69,20 +70,33 @@ __device__ void block_exclusive_scan(int* v, int n, int* tmp /* [256] */) {
   __syncthreads();
 }
 
+// Scatter (workgroups 0 .. nchunks-1, one per chunk of tokens) and the group
+// schedule (workgroup nchunks, in parallel with them).
 __global__ __launch_bounds__(256) void k_build_scatter(const int32_t* __restrict__ ids, int T, int k, int E,
                                                        int nchunks, uint32_t flags, Routing r) {
-  __shared__ int cnt[kMaxExperts + 2];
+  __shared__ __attribute__((aligned(16))) int cnt[kMaxExperts + 4];
   __shared__ int off[kMaxExperts + 2];
   __shared__ int base[kMaxExperts + 2];
   __shared__ uint32_t masks[kMaxExperts * (kBuildChunk / 32)];
   __shared__ int tmp[256];
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x;
+  const bool schedule = chunk == nchunks;  // uniform
   constexpr int W = kBuildChunk / 32;
-
   for (int e = tid; e < E; e += 256) {
     int c = 0, b = 0;
-    for (int ch = 0; ch < nchunks; ++ch) {
+    int ch = 0;
+    for (; ch + 8 <= nchunks; ch += 8) {  // eight loads in flight per step
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = r.chunk_counts[(size_t)(ch + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        c += v[u];
+        if (ch + u < chunk) b += v[u];
+      }
+    }
+    for (; ch < nchunks; ++ch) {
       const int v = r.chunk_counts[(size_t)ch * E + e];
       c += v;
       if (ch < chunk) b += v;
@@ -92,39 +106,40 @@ __global__ __launch_bounds__(256) void k_build_scatter(const int32_t* __restrict
     base[e] = b;
   }
   if (tid == 0) off[E] = 0;
-  for (int i = tid; i < E * W; i += 256) masks[i] = 0u;
+  if (!schedule)
+    for (int i = tid; i < E * W; i += 256) masks[i] = 0u;
   __syncthreads();
   block_exclusive_scan(off, E + 1, tmp);  // off[E] = number of valid pairs
-
-  const int i = tid;
-  const int t = chunk * kBuildChunk + i;
-  if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      const int e = ids[(size_t)t * k + j];
-      if ((unsigned)e < (unsigned)E) atomicOr(&masks[e * W + (i >> 5)], 1u << (i & 31));
-    }
-  }
-  __syncthreads();
-  if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      const int p = t * k + j;
-      const int e = ids[(size_t)p];
-      if ((unsigned)e >= (unsigned)E) {
-        r.pair_pos[p] = -1;  // out-of-range id: the pair contributes nothing
-        continue;
+  if (!schedule) {
+    const int i = tid;
+    const int t = chunk * kBuildChunk + i;
+    if (t < T) {
+      for (int j = 0; j < k; ++j) {
+        const int e = ids[(size_t)t * k + j];
+        if ((unsigned)e < (unsigned)E) atomicOr(&masks[e * W + (i >> 5)], 1u << (i & 31));
       }
-      const int w = i >> 5;
-      int rank = __popc(masks[e * W + w] & ((1u << (i & 31)) - 1u));
-      for (int q = 0; q < w; ++q) rank += __popc(masks[e * W + q]);
-      const int pos = off[e] + base[e] + rank;
-      r.sorted_pair[pos] = p;
-      r.pair_pos[p] = pos;
-      r.row_expert[pos] = e;
     }
+    __syncthreads();
+    if (t < T) {
+      for (int j = 0; j < k; ++j) {
+        const int p = t * k + j;
+        const int e = ids[(size_t)p];
+        if ((unsigned)e >= (unsigned)E) {
+          r.pair_pos[p] = -1;  // out-of-range id: the pair contributes nothing
+          continue;
+        }
+        const int w = i >> 5;
+        int rank = __popc(masks[e * W + w] & ((1u << (i & 31)) - 1u));
+        for (int q = 0; q < w; ++q) rank += __popc(masks[e * W + q]);
+        const int pos = off[e] + base[e] + rank;
+        r.sorted_pair[pos] = p;
+        r.pair_pos[p] = pos;
+        r.row_expert[pos] = e;
+      }
+    }
+    return;
   }
-  if (chunk != 0) return;
-
-  // ---- group schedule (one workgroup) -------------------------------------
+  // ---- group schedule -------------------------------------------------------
   const int ng = E + 1;
   for (int e = tid; e < E; e += 256) {
     r.counts[e] = cnt[e];
@@ -134,9 +149,11 @@ __global__ __launch_bounds__(256) void k_build_scatter(const int32_t* __restrict
     r.counts[E] = T;
     r.offsets[E] = off[E];
   }
-  cnt[E] = T;
+  if (tid == 0) cnt[E] = T;
+  if (tid < 3) cnt[ng + tid] = -1;  // padding to a multiple of 4: never ranks above a real count
   __syncthreads();
   // rank of group g: larger count first, ties to the lower id (or id order)
+  const int n4 = (ng + 3) / 4;
   for (int g = tid; g < ng; g += 256) {
     const int cg = cnt[g];
     int rank;
@@ -144,9 +161,13 @@ __global__ __launch_bounds__(256) void k_build_scatter(const int32_t* __restrict
       rank = g;
     } else {
       rank = 0;
-      for (int h = 0; h < ng; ++h) {
-        const int ch = cnt[h];
-        rank += (ch > cg) || (ch == cg && h < g);
+      for (int h4 = 0; h4 < n4; ++h4) {
+        const int4 c4 = reinterpret_cast<const int4*>(cnt)[h4];
+        const int h = 4 * h4;
+        rank += (c4.x > cg) || (c4.x == cg && h < g);
+        rank += (c4.y > cg) || (c4.y == cg && h + 1 < g);
+        rank += (c4.z > cg) || (c4.z == cg && h + 2 < g);
+        rank += (c4.w > cg) || (c4.w == cg && h + 3 < g);
       }
     }
     r.group_order[rank] = g;
@@ -165,7 +186,8 @@ hipError_t launch_build(const Shape& s, const int32_t* topk_ids, const Routing& 
   hipLaunchKernelGGL(k_build_count, dim3(nchunks), dim3(256), 0, st, topk_ids, s.T, s.k, s.E, r.chunk_counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_build_scatter, dim3(nchunks), dim3(256), 0, st, topk_ids, s.T, s.k, s.E, nchunks, flags, r);
+  hipLaunchKernelGGL(k_build_scatter, dim3(nchunks + 1), dim3(256), 0, st, topk_ids, s.T, s.k, s.E, nchunks, flags,
+                     r);
   return hipGetLastError();
 }
 
