@@ -21,13 +21,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------- constants
 constexpr int kWave = 64;
 constexpr int kBlockK = 32;           // Q4 block length
-constexpr int kGemvMaxChunks = 2;     // small-T path: d <= 2 * 4096, I <= 2 * 1024
 constexpr int kGroupedBM = 96;        // grouped GEMM: rows per M-tile
 constexpr int kGroupedBK = 128;       // grouped GEMM: K per main-loop iteration (4 blocks)
-#ifndef MOE_GROUPED_WAVES
-#define MOE_GROUPED_WAVES 4
-#endif
-constexpr int kGroupedWaves = MOE_GROUPED_WAVES;  // grouped GEMM: wavefronts per workgroup
+constexpr int kGroupedWaves = 4;                  // grouped GEMM: wavefronts per workgroup (two per CU)
 constexpr int kGateUpBandCols = 32 * kGroupedWaves;  // grouped gate+up: h columns per workgroup
 constexpr int kDownBandCols = 64 * kGroupedWaves;    // grouped down: output columns per workgroup
 constexpr int kBuildChunk = 256;      // routing build: tokens per workgroup
@@ -37,9 +33,6 @@ constexpr int kMaxTopK = 32;
 // ---------------------------------------------------------------- loads
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
-}
-__device__ __forceinline__ uint32_t ld4(const void* p) {
-  return *reinterpret_cast<const uint32_t*>(p);
 }
 // Reinterpret by value.  (clang's __builtin_bit_cast applied directly to an
 // element of an ext_vector_type lvalue, as in bit_cast(v[m]), reads element 0
@@ -194,24 +187,8 @@ __device__ __forceinline__ float wave_sum_hi(float v) {
   v = half_wave_sum_hi(v);
   return v + dpp_f_rows<kDppBcast31, 0xC>(v);
 }
-// Sum over the wavefront, in every lane.
-__device__ __forceinline__ float wave_sum(float v) {
-  v = row16_sum(v);
-  v += __shfl_xor(v, 16, kWave);
-  v += __shfl_xor(v, 32, kWave);
-  return v;
-}
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 __device__ __forceinline__ float siluf_(float z) { return z / (1.0f + expf(-z)); }
-
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-// L2).  Map launch index -> work item so that each XCD receives a contiguous
-// run of the schedule: items that share a weight band then share an L2.
-__device__ __forceinline__ int xcd_remap(int bid, int n_items) {
-  const int x = bid & 7, within = bid >> 3;
-  const int q = n_items >> 3, rem = n_items & 7;
-  return x * q + (x < rem ? x : rem) + within;
-}
 
 }  // namespace moe
