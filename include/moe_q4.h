@@ -48,14 +48,19 @@
  *   x         bf16 bit patterns, row-major [T][d]
  *   w_router  float32 [E][d];   bias  float32 [E]
  *   y         float32 [T][d]
- *   Q4 matrix of shape [rows][K] (K % 32 == 0, rows % 16 == 0), two arrays:
- *     qs      uint8 [rows][K/2]:  byte i of a row holds element 2i in its
- *             low nibble and element 2i+1 in its high nibble
- *     scales  uint16 [rows/16][K/32][16]: IEEE fp16 bits, one per 32-element
- *             block, in groups of 16 rows: the scale of row r, block b is
- *             element ((r/16)*(K/32) + b)*16 + r%16 (so the 16 scales an
- *             MFMA slice of 16 rows needs for one block are contiguous)
+ *   Q4 matrix of shape [rows][K] (K % 32 == 0, rows % 16 == 0): 32-element
+ *   blocks of 16 code bytes and one fp16 scale, stored in groups of 16 rows
+ *   so that the 16 rows x 4 blocks one load instruction needs are one
+ *   contiguous KiB (codes) and 128 bytes (scales):
+ *     qs      uint8 [rows/16][K/32][16][16]: the 16-byte block b of row r
+ *             starts at byte ((r/16)*(K/32) + b)*256 + (r%16)*16; inside a
+ *             block, byte i holds element 2i in its low nibble and element
+ *             2i+1 in its high nibble
+ *     scales  uint16 [rows/16][K/32][16]: IEEE fp16 bits; the scale of row
+ *             r, block b is element ((r/16)*(K/32) + b)*16 + r%16
  *     value = (q - 8) * scale          (q the 4-bit code, 0..15)
+ *   Both are index permutations of the row-major arrays [rows][K/2] and
+ *   [rows][K/32] (the Python binding's pack_codes / pack_scales).
  *   w13  [E][2I][d]  gate rows 0..I-1, up rows I..2I-1 of every expert
  *   w2   [E][d][I]
  *   s13  [2*I_shared][d], s2 [d][I_shared]   (shared expert, same split)
@@ -117,8 +122,8 @@ typedef struct moe_dims {
 } moe_dims;
 
 typedef struct moe_q4 {
-  const uint8_t*  qs;      /* [rows][K/2] packed codes, 16-byte aligned      */
-  const uint16_t* scales;  /* [rows][K/32] fp16 bits, 16-byte aligned        */
+  const uint8_t*  qs;      /* [rows/16][K/32][16][16] codes, 16-byte aligned */
+  const uint16_t* scales;  /* [rows/16][K/32][16] fp16 bits, 16-byte aligned */
 } moe_q4;
 
 typedef struct moe_q4_weights {

@@ -158,7 +158,7 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
     const uint32_t qo = tail ? c.qoff_tail : c.qoff, so = tail ? c.soff_tail : c.soff;
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
-      qd[ns] = __builtin_amdgcn_raw_buffer_load_b128(c.rq, (int)qo, c.qns[ns] + it * 64, 0);
+      qd[ns] = __builtin_amdgcn_raw_buffer_load_b128(c.rq, (int)qo, c.qns[ns] + it * 1024, 0);
       sd[ns] = __builtin_amdgcn_raw_buffer_load_b16(c.rs, (int)so, c.sns[ns] + it * 128, 0);
     }
   };
@@ -445,18 +445,20 @@ __global__ __launch_bounds__(kGroupedThreads, 8 / kGroupedWaves) void k_grouped(
   c.rq = rq; c.rs = rs; c.ra = ra;
 #pragma unroll
   for (int i = 0; i < kTileLoads; ++i) c.aoff[i] = aoff[i];
-  // Scales are stored in 16-row groups, [rows/16][K/32][16]: slice ns (16 rows from rowbase[ns], a
-  // multiple of 16) has the 16 scales of block b at byte ((rowbase/16)*(K/32) + b)*32, so lane (n, G)
-  // reads byte 2*lane of a 128-byte run per 4-block iteration.
+  // Codes and scales are stored in 16-row groups: codes [rows/16][K/32][16][16 B], scales
+  // [rows/16][K/32][16].  Slice ns (16 rows from rowbase[ns], a multiple of 16) has the 16 code blocks
+  // of block column b at byte ((rowbase/16)*(K/32) + b)*256 and their scales at ((rowbase/16)*(K/32) +
+  // b)*32, so per 4-block iteration lane (n, G) reads bytes 16*lane of one contiguous KiB of codes and
+  // bytes 2*lane of one 128-byte run of scales.
   const int Glast = (nkb - 1) - 4 * (nit - 1);  // last valid block of the final iteration, relative
   const int Gt = G < Glast ? G : Glast;
-  c.qoff = (uint32_t)n * qstride + 16u * (uint32_t)G;
+  c.qoff = 16u * (uint32_t)lane;
   c.soff = 2u * (uint32_t)lane;
-  c.qoff_tail = (uint32_t)n * qstride + 16u * (uint32_t)Gt;
+  c.qoff_tail = 16u * (uint32_t)(n + 16 * Gt);
   c.soff_tail = 2u * (uint32_t)(n + 16 * Gt);
 #pragma unroll
   for (int ns = 0; ns < 4; ++ns) {
-    c.qns[ns] = ufl((int)((uint32_t)rowbase[ns] * qstride));
+    c.qns[ns] = ufl((int)((uint32_t)(rowbase[ns] / 16) * qstride * 16u));
     c.sns[ns] = ufl((int)((uint32_t)(rowbase[ns] / 16) * sstride * 32u));
     c.nok[ns] = nok[ns];
   }

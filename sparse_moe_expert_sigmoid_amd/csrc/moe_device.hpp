@@ -27,6 +27,7 @@ constexpr int kGroupedWaves = 4;                  // grouped GEMM: wavefronts pe
 constexpr int kGateUpBandCols = 32 * kGroupedWaves;  // grouped gate+up: h columns per workgroup
 constexpr int kDownBandCols = 64 * kGroupedWaves;    // grouped down: output columns per workgroup
 constexpr int kBuildChunk = 256;      // routing build: tokens per workgroup
+constexpr int kMaxGemvBlocksPerWave = 64;  // small-T path: Q4 blocks of K a wavefront stages (K <= 2048 per wave)
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 

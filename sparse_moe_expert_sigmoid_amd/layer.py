@@ -20,6 +20,16 @@ def pack_scales(sc: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(sc.reshape(*lead, rows // 16, 16, nkb).swapaxes(-1, -2))
 
 
+def pack_codes(qs: np.ndarray) -> np.ndarray:
+    """Q4 codes [..., rows, K/2] (row-major, byte i = elements 2i, 2i+1) -> the library's layout
+    [..., rows/16, K/32, 16, 16]: the 16-byte block b of row r moves to byte ((r/16)*(K/32) + b)*256 +
+    (r%16)*16 (an index permutation of whole blocks)."""
+    *lead, rows, half_k = qs.shape
+    assert rows % 16 == 0 and half_k % 16 == 0, qs.shape
+    nkb = half_k // 16
+    return np.ascontiguousarray(qs.reshape(*lead, rows // 16, 16, nkb, 16).swapaxes(-3, -2))
+
+
 def to_device(a: np.ndarray, device) -> torch.Tensor:
     """numpy -> torch on `device`; uint16 bit patterns travel as int16 (same bytes)."""
     a = np.ascontiguousarray(a)
@@ -38,7 +48,8 @@ class DeviceWeights(dict):
         w["w_router"] = to_device(inp["w_router"], device)
         w["bias"] = to_device(inp["bias"], device)
         for key in WEIGHT_KEYS:
-            w[key] = to_device(pack_scales(inp[key]) if key.endswith("_sc") else inp[key], device)
+            pack = pack_scales if key.endswith("_sc") else pack_codes
+            w[key] = to_device(pack(inp[key]), device)
         return w
 
 
