@@ -76,9 +76,9 @@
  *     and grouped GEMMs that dequantise Q4 in registers into fp16 MFMA
  *     operands, with the shared expert as one more always-present group,
  *     then a fixed-order combine.
- *   The SwiGLU outputs are kept in fp16 between the two projections on
- *   both paths; on the grouped path x is converted to fp16 for the GEMMs
- *   and every expert's down-projection output is stored in fp16 before the
+ *   Both paths round x to fp16 for the expert projections and keep the
+ *   SwiGLU outputs in fp16 between the two projections; the grouped path
+ *   also stores every expert's down-projection output in fp16 before the
  *   combine: those values must stay within the fp16 range (65504).
  */
 #ifndef MOE_Q4_H

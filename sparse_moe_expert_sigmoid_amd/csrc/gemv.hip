@@ -28,17 +28,22 @@ static_assert(kMaxGemvBlocksPerWave == kWave, "activation staging gives every la
 // wavefronts covers 16 h-rows (one 16-row group of gate rows and the matching
 // group of up rows) of one job; wavefront w takes the w-th quarter of K.  For
 // each 4-block tile a lane holds one gate and one up code block (row n, block
-// G); codes become the bf16 values 128 + q with one and-or per pair (after at
-// most one shift), v_dot2_f32_bf16 multiplies them with the activation pairs,
-// and per block d * (dot - 136 * sum x) restores d * sum x (q - 8).  Partial
-// sums meet across G (lane exchanges) and across the 4 quarters (LDS).
+// G).  The arithmetic is the down kernel's (below): codes become the fp16
+// pairs (1024 + e0, 1024 + e4) and (1024 + 16 e1, 1024 + 16 e5) with one
+// and-or each (elements 2, 6 and 3, 7 from the dword shifted by 8), x is
+// staged as the matching fp16 pairs with the 16x pairs pre-divided by 16, and
+// each block's v_dot2_f32_f16 chain starts at -(1032 A + 1152 B) (A the sum of
+// the plain pairs, B of the divided ones), leaving sum x (q - 8).  x is
+// rounded to fp16 (exact for bf16 values inside the fp16 normal range).
+// Partial sums meet across G (lane exchanges) and across the 4 quarters (LDS).
 // h is written in fp16 (h_r[p][I] for pair p, h_s[t][Is] for the shared
 // expert), each group of 8 stored in the pair order of the down kernel: slot
 // i of a group holds element 0,4,1,5,2,6,3,7 [i].
 __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
                                                      Q4 w13, Q4 s13, _Float16* __restrict__ h_r, _Float16* __restrict__ h_s,
-                                                     int T, int d, int k, int I, int Is, uint32_t mask, uint32_t magic) {
-  // x of this wavefront's quarter of K, per block: 16 dwords of bf16 pairs and the block sum
+                                                     int T, int d, int k, int I, int Is, uint32_t mask_lo, uint32_t mask_hi,
+                                                     uint32_t magic) {
+  // x of this wavefront's quarter of K, per block: 16 dwords of fp16 pairs and the block's starting value
   __shared__ __attribute__((aligned(16))) uint32_t xs[4][kMaxGemvBlocksPerWave][16];
   __shared__ float xsum[4][kMaxGemvBlocksPerWave];
   __shared__ float red[4][2][16];
@@ -81,19 +86,27 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
   {
     const int bl = min(b0 + lane, nkb - 1);
     const uint16_t* xb = x + (size_t)t * d + 32 * bl;
-    float sum = 0.f;
+    float sa = 0.f, sb = 0.f;
 #pragma unroll
     for (int dw = 0; dw < 4; ++dw) {
       const u32x4 u = ld16(xb + 8 * dw);
-      uint32_t pr[4];
-      x_bf16_pairs(u, pr);
+      float xf[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        sum += bf16_bits_to_float(u[m] & 0xFFFFu) + bf16_bits_to_float(u[m] >> 16);
-        xs[wave][lane][4 * dw + m] = pr[m];
+        xf[2 * m] = bf16_bits_to_float(u[m] & 0xFFFFu);
+        xf[2 * m + 1] = bf16_bits_to_float(u[m] >> 16);
       }
+      const half2v p0 = {(_Float16)xf[0], (_Float16)xf[4]};
+      const half2v p1 = {(_Float16)(0.0625f * xf[1]), (_Float16)(0.0625f * xf[5])};
+      const half2v p2 = {(_Float16)xf[2], (_Float16)xf[6]};
+      const half2v p3 = {(_Float16)(0.0625f * xf[3]), (_Float16)(0.0625f * xf[7])};
+      sa += ((float)p0[0] + (float)p0[1]) + ((float)p2[0] + (float)p2[1]);
+      sb += ((float)p1[0] + (float)p1[1]) + ((float)p3[0] + (float)p3[1]);
+      *reinterpret_cast<u32x4*>(xs[wave][lane] + 4 * dw) =
+          u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
     }
-    xsum[wave][lane] = sum;
+    xsum[wave][lane] = -(1032.f * sa + 1152.f * sb);
   }
   // codes and scales of up to kGemvTiles tiles per batch, all in flight before any arithmetic; blocks
   // past the row end (last tile) re-read the row's last block and weigh zero.
@@ -119,23 +132,23 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
       const float use = (tb + j < tw1 && b < nkb) ? 1.f : 0.f;
       const int lb = blk[j] - b0;      // its slot in the staged x
       const u32x4* xp = reinterpret_cast<const u32x4*>(xs[wave][lb]);
-      float dotg = 0.f, dotu = 0.f;
+      float dotg = xsum[wave][lb], dotu = dotg;
 #pragma unroll
       for (int dw = 0; dw < 4; ++dw) {
         const u32x4 xv = xp[dw];
-        uint32_t pg[4], pu[4];
-        codes_bf16_pairs(cg[j][dw], mask, magic, pg);
-        codes_bf16_pairs(cu[j][dw], mask, magic, pu);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          dotg = dot2_bf16(pg[m], xv[m], dotg);
-          dotu = dot2_bf16(pu[m], xv[m], dotu);
-        }
+        const uint32_t wg = cg[j][dw], wg8 = wg >> 8, wu = cu[j][dw], wu8 = wu >> 8;
+        dotg = dot2_f16(and_or(wg, mask_lo, magic), xv[0], dotg);
+        dotu = dot2_f16(and_or(wu, mask_lo, magic), xv[0], dotu);
+        dotg = dot2_f16(and_or(wg, mask_hi, magic), xv[1], dotg);
+        dotu = dot2_f16(and_or(wu, mask_hi, magic), xv[1], dotu);
+        dotg = dot2_f16(and_or(wg8, mask_lo, magic), xv[2], dotg);
+        dotu = dot2_f16(and_or(wu8, mask_lo, magic), xv[2], dotu);
+        dotg = dot2_f16(and_or(wg8, mask_hi, magic), xv[3], dotg);
+        dotu = dot2_f16(and_or(wu8, mask_hi, magic), xv[3], dotu);
       }
-      const float xsm = xsum[wave][lb];
       // masked by a multiply (not a select), so that no load is made conditional
-      accg = fmaf(fp16_bits_to_float(dg[j]) * use, fmaf(-136.f, xsm, dotg), accg);
-      accu = fmaf(fp16_bits_to_float(du[j]) * use, fmaf(-136.f, xsm, dotu), accu);
+      accg = fmaf(fp16_bits_to_float(dg[j]) * use, dotg, accg);
+      accu = fmaf(fp16_bits_to_float(du[j]) * use, dotu, accu);
     }
   }
 #undef MOE_GU_LOAD
@@ -287,7 +300,7 @@ hipError_t launch_gemv_gateup(const Shape& s, const uint16_t* x, const int32_t* 
   const int Imax = s.I > s.Is ? s.I : s.Is;
   dim3 grid((Imax + 15) / 16, s.T * s.k + s.T);
   hipLaunchKernelGGL(k_gemv_gateup, grid, dim3(256), 0, st, x, topk_ids, w13, s13, h_r, h_s, s.T, s.d, s.k, s.I, s.Is,
-                     0x000F000Fu, 0x43004300u);
+                     0x000F000Fu, 0x00F000F0u, 0x64006400u);
   return hipGetLastError();
 }
 
