@@ -214,11 +214,15 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // Top-k: one wavefront per token.  Lane l holds experts l, l+64, ... as
-// order-preserving unsigned keys of s + b (empty and taken slots hold 0,
-// below every real key).  Each of the k rounds finds the largest key (per
-// lane, then four DPP max steps inside each 16-lane row, then the four row
-// maxima in scalar registers) and then the lowest expert id that holds it,
-// from one ballot per key register: ties go to the lower id.
+// order-preserving unsigned keys of s + b (lanes past E hold 0, below every
+// real key).  The k-th largest key tau is found bit by bit from the top: a
+// candidate bit stays set when at least k keys are >= the candidate (one
+// ballot and popcount per key register), so the search costs 32 short steps
+// whatever k is.  The chosen experts are the keys above tau and, of the keys
+// equal to tau, the lowest ids (ties go to the lower id).  They are compacted
+// into LDS; each finds its slot by counting the chosen keys that rank before
+// it (a larger key, or an equal key and a lower id), and the weights are
+// normalised by the sum of the chosen scores taken in slot order.
 __device__ __forceinline__ uint32_t ordered_bits(float f) {
   if (f != f) return 1u;  // NaN ranks below every number but above empty slots
   if (f == 0.f) f = 0.f;  // -0 and +0 are the same key (then the lower id wins)
@@ -226,72 +230,102 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
-  const uint32_t o = (uint32_t)dpp_i<CTRL>((int)v);
-  return o > v ? o : v;
-}
+struct TopkLds {  // one wavefront's staging: the chosen entries in id order, then in slot order
+  uint32_t key[kMaxTopK];
+  int32_t id[kMaxTopK];
+  float s[kMaxTopK];
+  int32_t slot_id[kMaxTopK];
+  float slot_s[kMaxTopK];
+};
 
-// Selection for one token by one wavefront: writes ids[0..k) and w[0..k).
-template <int NPER>
-__device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t part_stride, int nparts,
+__device__ __forceinline__ int popc(uint64_t m) { return __builtin_popcountll(m); }
+
+// Selection for one token by one wavefront: writes ids[0..k) and w[0..k).  The wavefront reads
+// back only what its own lanes wrote to LDS: LDS operations of one wavefront are ordered.
+template <int NPER, int NPARTS>
+__device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t part_stride,
                                           const float* __restrict__ bias, int32_t* __restrict__ ids,
-                                          float* __restrict__ w, int E, int k, int lane) {
+                                          float* __restrict__ w, int E, int k, int lane, TopkLds& sm) {
+  // every load first, from clamped indices: one memory round trip
+  float lg[NPARTS][NPER], bs[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = min(lane + 64 * i, E - 1);
+    bs[i] = bias[e];
+#pragma unroll
+    for (int p = 0; p < NPARTS; ++p) lg[p][i] = lrow[p * part_stride + e];
+  }
   uint32_t key[NPER];
   float sc[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
-    const int e = lane + 64 * i;
-    if (e < E) {
-      float l = lrow[e];
-      for (int p = 1; p < nparts; ++p) l += lrow[p * part_stride + e];  // partial logits, in order
-      const float s = sigmoidf_(l);
-      key[i] = ordered_bits(s + bias[e]);
-      sc[i] = s;
-    } else {
-      key[i] = 0u;
-      sc[i] = 0.f;
+    float l = lg[0][i];
+#pragma unroll
+    for (int p = 1; p < NPARTS; ++p) l += lg[p][i];  // partial logits, in order
+    sc[i] = sigmoidf_(l);
+    const uint32_t valid = lane + 64 * i < E ? 0xFFFFFFFFu : 0u;
+    key[i] = ordered_bits(sc[i] + bs[i]) & valid;
+  }
+  // tau: the largest value with at least k keys >= it, i.e. the k-th largest key
+  uint32_t tau = 0u;
+#pragma unroll 4
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) cnt += popc(__builtin_amdgcn_ballot_w64(key[i] >= cand));
+    tau = cnt >= k ? cand : tau;
+  }
+  // chosen: every key above tau (fewer than k), then the lowest ids among the keys equal to tau
+  uint64_t chosen[NPER];
+  int need = k;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    chosen[i] = __builtin_amdgcn_ballot_w64(key[i] > tau);
+    need -= popc(chosen[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    uint64_t eq = __builtin_amdgcn_ballot_w64(key[i] == tau);
+    while (need > 0 && eq != 0) {
+      const uint64_t low = eq & (~eq + 1u);
+      chosen[i] |= low;
+      eq ^= low;
+      --need;
     }
   }
-  float my_s = 0.f;
-  int my_id = 0;
+  // compact the k chosen entries into LDS in id order
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const uint64_t m = chosen[i];
+    if ((m >> lane) & 1u) {
+      const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      sm.key[pos] = key[i];
+      sm.id[pos] = lane + 64 * i;
+      sm.s[pos] = sc[i];
+    }
+    base += popc(m);
+  }
+  // lane r < k takes entry r and counts the entries that rank before it: its slot
+  const int r = min(lane, k - 1);
+  const uint32_t K = sm.key[r];
+  const int I = sm.id[r];
+  const float S = sm.s[r];
+  int slot = 0;
   for (int j = 0; j < k; ++j) {
-    uint32_t m = key[0];
-#pragma unroll
-    for (int i = 1; i < NPER; ++i) m = key[i] > m ? key[i] : m;
-    m = dpp_max_u32<kDppXor1>(m);
-    m = dpp_max_u32<kDppXor2>(m);
-    m = dpp_max_u32<kDppHalfMirror>(m);
-    m = dpp_max_u32<kDppMirror>(m);
-    uint32_t M = (uint32_t)__builtin_amdgcn_readlane((int)m, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r) {
-      const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)m, 16 * r);
-      M = o > M ? o : M;
-    }
-    // lowest expert id holding M: the first key register with a hit, then its lowest lane
-    int win = 0;
-    bool found = false;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(key[i] == M);
-      if (!found && hit != 0) {
-        win = 64 * i + (int)__builtin_ctzll(hit);
-        found = true;
-      }
-    }
-    float s_sel = sc[0];
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      if ((win >> 6) == i) s_sel = sc[i];
-      if (lane + 64 * i == win) key[i] = 0u;  // taken
-    }
-    s_sel = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_sel), win & 63));
-    if (lane == j) {
-      my_s = s_sel;
-      my_id = win;
-    }
+    const uint32_t Kj = (uint32_t)__builtin_amdgcn_readlane((int)K, j);
+    const int Ij = __builtin_amdgcn_readlane(I, j);
+    slot += (Kj > K || (Kj == K && Ij < I)) ? 1 : 0;
   }
+  if (lane < k) {
+    sm.slot_id[slot] = I;
+    sm.slot_s[slot] = S;
+  }
+  const int q = min(lane, k - 1);
+  const int my_id = sm.slot_id[q];
+  const float my_s = sm.slot_s[q];
   float tot = 0.f;
   for (int j = 0; j < k; ++j)  // slot order, same value in every lane
     tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_s), j));
@@ -301,15 +335,16 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t
   }
 }
 
-template <int NPER>
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int nparts,
-                                              const float* __restrict__ bias, int32_t* __restrict__ ids,
-                                              float* __restrict__ w, int T, int E, int k) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+template <int NPER, int NPARTS>
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
+                                              int32_t* __restrict__ ids, float* __restrict__ w, int T, int E,
+                                              int k) {
+  __shared__ TopkLds sm[4];
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = blockIdx.x * 4 + wv;
   if (t >= T) return;
-  topk_wave<NPER>(logits + (size_t)t * E, (size_t)T * E, nparts, bias, ids + (size_t)t * k, w + (size_t)t * k, E,
-                  k, lane);
+  topk_wave<NPER, NPARTS>(logits + (size_t)t * E, (size_t)T * E, bias, ids + (size_t)t * k, w + (size_t)t * k, E,
+                          k, lane, sm[wv]);
 }
 
 hipError_t launch_router_mfma(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
@@ -318,16 +353,29 @@ hipError_t launch_router_mfma(const Shape& s, const uint16_t* x, const float* w_
   hipLaunchKernelGGL(k_router_mfma, grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
   return hipGetLastError();
 }
-hipError_t launch_topk(const Shape& s, const float* logits, int nparts, const float* bias, int32_t* topk_ids,
-                       float* topk_w, hipStream_t st) {
+template <int NPARTS>
+static hipError_t launch_topk_parts(const Shape& s, const float* logits, const float* bias, int32_t* topk_ids,
+                                    float* topk_w, hipStream_t st) {
   const dim3 grid((s.T + 3) / 4), block(256);
   const int nper = (s.E + 63) / 64;
-  if (nper <= 1) hipLaunchKernelGGL(k_topk<1>, grid, block, 0, st, logits, nparts, bias, topk_ids, topk_w, s.T, s.E, s.k);
-  else if (nper <= 2) hipLaunchKernelGGL(k_topk<2>, grid, block, 0, st, logits, nparts, bias, topk_ids, topk_w, s.T, s.E, s.k);
-  else if (nper <= 4) hipLaunchKernelGGL(k_topk<4>, grid, block, 0, st, logits, nparts, bias, topk_ids, topk_w, s.T, s.E, s.k);
-  else if (nper <= 8) hipLaunchKernelGGL(k_topk<8>, grid, block, 0, st, logits, nparts, bias, topk_ids, topk_w, s.T, s.E, s.k);
-  else hipLaunchKernelGGL(k_topk<16>, grid, block, 0, st, logits, nparts, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  if (nper <= 1)
+    hipLaunchKernelGGL((k_topk<1, NPARTS>), grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  else if (nper <= 2)
+    hipLaunchKernelGGL((k_topk<2, NPARTS>), grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  else if (nper <= 4)
+    hipLaunchKernelGGL((k_topk<4, NPARTS>), grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  else if (nper <= 8)
+    hipLaunchKernelGGL((k_topk<8, NPARTS>), grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
+  else
+    hipLaunchKernelGGL((k_topk<16, NPARTS>), grid, block, 0, st, logits, bias, topk_ids, topk_w, s.T, s.E, s.k);
   return hipGetLastError();
+}
+
+hipError_t launch_topk(const Shape& s, const float* logits, int nparts, const float* bias, int32_t* topk_ids,
+                       float* topk_w, hipStream_t st) {
+  if (nparts == 1) return launch_topk_parts<1>(s, logits, bias, topk_ids, topk_w, st);
+  if (nparts == kRouterParts) return launch_topk_parts<kRouterParts>(s, logits, bias, topk_ids, topk_w, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

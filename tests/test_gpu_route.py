@@ -1,0 +1,74 @@
+"""GPU expert selection through moe_route alone: slot order, ties and weights against the oracle.
+
+The selection rule (sigmoid scores, bias added for selection only, the k largest keys listed by
+descending key, equal keys to the lower expert id, weights = unbiased scores normalised to 1) is
+the oracle's select_experts / routing_weights.  Both router forms are covered: the GEMV router
+(one logit array) and the MFMA router (four partial logit arrays), and every key-register count
+of the top-k (E up to 1024, k up to 32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from sparse_moe_expert_sigmoid_amd import abi
+from sparse_moe_expert_sigmoid_amd.layer import Workspace, to_device
+from gpu_util import MARGIN, W_ABS, say
+
+pytestmark = pytest.mark.gpu
+
+PATHS = {"gemv_router": abi.MOE_FLAG_FORCE_GEMV, "mfma_router": abi.MOE_FLAG_FORCE_GROUPED}
+SHAPES = [(20, 4), (64, 10), (100, 1), (256, 10), (256, 32), (1000, 16), (1024, 32)]
+
+
+def route(inp: dict, flags: int):
+    dims = inp["dims"]
+    ws = Workspace(dims, flags)
+    abi.moe_route(dims, to_device(inp["x"], "cuda"), to_device(inp["w_router"], "cuda"),
+                  to_device(inp["bias"], "cuda"), ws.topk_ids, ws.topk_w, ws.routing, flags=flags)
+    torch.cuda.synchronize()
+    return ws.topk_ids.cpu().numpy(), ws.topk_w.cpu().numpy()
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("E,k", SHAPES, ids=[f"E{e}k{k}" for e, k in SHAPES])
+def test_exact_ties_go_to_the_lower_id(E, k, path):
+    # W_r = 0: every logit is exactly 0 and every score exactly 1/2 on both sides; the biases are
+    # multiples of 1/64 from a set of 8 values, so s + b is exact in fp32 and fp64 and most keys tie.
+    dims = synth.Dims(T=6, d=64, E=E, k=k, I=32, I_shared=32)
+    inp = synth.make_inputs(dims, seed=7 + E + k, weights=False)
+    rng = np.random.default_rng(E * 100 + k)
+    inp["w_router"] = np.zeros((E, dims.d), dtype=np.float32)
+    inp["bias"] = (rng.integers(0, 8, size=E) / 64.0).astype(np.float32)
+    say(f"[case] ties E={E} k={k} {path}")
+    ids, w = route(inp, PATHS[path])
+    s = np.full((dims.T, E), 0.5)
+    ref_ids, _ = oracle.select_experts(s, inp["bias"], k)
+    np.testing.assert_array_equal(ids, ref_ids)
+    np.testing.assert_allclose(w, oracle.routing_weights(s, ref_ids), rtol=0, atol=W_ABS)
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("E,k", SHAPES, ids=[f"E{e}k{k}" for e, k in SHAPES])
+def test_slot_order_matches_oracle(E, k, path):
+    dims = synth.Dims(T=40, d=256, E=E, k=k, I=32, I_shared=32)
+    inp = synth.make_inputs(dims, seed=11 + E + k, weights=False)
+    say(f"[case] order E={E} k={k} {path}")
+    ids, w = route(inp, PATHS[path])
+    s = oracle.sigmoid(oracle.router_logits(inp["x"], inp["w_router"]))
+    ref_ids, margin = oracle.select_experts(s, inp["bias"], k)
+    key = s + inp["bias"].astype(np.float64)[None, :]
+    ordered = 0
+    for t in range(dims.T):
+        if not margin[t] > MARGIN:
+            continue  # the k-th and (k+1)-th keys are too close for an fp32 router to be held to
+        assert sorted(ids[t]) == sorted(ref_ids[t]), (t, ids[t], ref_ids[t])
+        gaps = -np.diff(key[t, ref_ids[t]])
+        if gaps.size == 0 or gaps.min() > MARGIN:  # neighbours far enough apart: the order is fixed
+            np.testing.assert_array_equal(ids[t], ref_ids[t])
+            ordered += 1
+        ref_w = oracle.routing_weights(s[t:t + 1], ids[t:t + 1])[0]
+        np.testing.assert_allclose(w[t], ref_w, rtol=0, atol=W_ABS)
+    say(f"[route] E={E} k={k} {path}: order checked on {ordered}/{dims.T} tokens")
+    assert ordered > 0 or k == 1
