@@ -138,8 +138,8 @@ typedef struct moe_q4_weights {
  * Pairs are p = t*k + j; groups are the E experts plus the shared expert
  * as group E. */
 typedef struct moe_routing_layout {
-  size_t logits;       /* float [4][T][E]   router logits (scratch of moe_route; the
-                          grouped path's router writes 4 partial sums over K) */
+  size_t logits;       /* float [8][T][E]   router logits (scratch of moe_route; the
+                          grouped path's router writes 8 partial sums over K) */
   size_t counts;       /* int32 [E+1]       rows per group (group E = T)         */
   size_t offsets;      /* int32 [E+1]       CSR exclusive prefix over experts     */
   size_t sorted_pair;  /* int32 [P]         pair id at each sorted position       */

@@ -58,30 +58,6 @@ constexpr int kRowsPerWave = kGroupedBM / kGroupedWaves;  // activation rows sta
 // only, so it holds whatever scalar offset the K loop adds.
 constexpr uint32_t kOffsetOOB = 0xFFFFFFF0u;
 
-// s_waitcnt vmcnt(N), leaving the LDS and export counters alone (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-// s_waitcnt vmcnt(N) lgkmcnt(0): this wavefront's loads older than the N youngest have landed
-// (including tile loads into LDS) and its own LDS reads are complete.
-template <int N>
-__device__ __forceinline__ void vm_lgkm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
-}
-// Workgroup barrier without a memory fence.  The ordering it needs is provided by the explicit
-// waits above: every wavefront waits for its own tile loads and LDS reads before arriving, so after
-// the barrier the new tile is in LDS and nobody still reads the buffer that is refilled next.
-// (__syncthreads() would also wait for the younger tile loads still in flight.)
-__device__ __forceinline__ void tile_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 struct GArgs {
   const _Float16* a_r;      // A rows: gate+up -> x16 [T][d] (gathered); down -> h_r [P][I] (sorted rows)
   const _Float16* a_s;      // A rows of the shared group: gate+up -> x16; down -> h_s [T][Is]
@@ -104,7 +80,6 @@ struct GArgs {
   uint32_t dq_mask, dq_magic;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int ufl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

@@ -108,6 +108,31 @@ __device__ __forceinline__ int perm_slot(int c8) { return (c8 < 4) ? 2 * c8 : 2 
 
 // Buffer resource for raw (unstructured) loads; accesses at or past
 // num_bytes return zero.  Word 3 is the gfx9-family raw-buffer format.
+// s_waitcnt vmcnt(N), leaving the LDS and export counters alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// s_waitcnt vmcnt(N) lgkmcnt(0): this wavefront's loads older than the N youngest have landed
+// (including tile loads into LDS) and its own LDS reads are complete.
+template <int N>
+__device__ __forceinline__ void vm_lgkm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+// Workgroup barrier without a memory fence.  The ordering it needs comes from explicit waits: every
+// wavefront waits for its own loads into LDS (and its LDS reads) before arriving, so after the barrier
+// the new tile is in LDS and nobody still reads the buffer that is refilled next.
+// (__syncthreads() would also wait for younger loads still in flight.)
+__device__ __forceinline__ void tile_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;  // LDS destination of buffer loads into LDS
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
 }

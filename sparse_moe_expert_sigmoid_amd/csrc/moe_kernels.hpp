@@ -33,7 +33,7 @@ struct Q4 {
 hipError_t launch_router_gemv(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
                               hipStream_t st);
 // writes kRouterParts partial logit arrays [part][T][E] (K split in that many parts)
-constexpr int kRouterParts = 4;
+constexpr int kRouterParts = 8;
 hipError_t launch_router_mfma(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
                               hipStream_t st);
 // logits: nparts partial arrays [nparts][T][E], summed in order

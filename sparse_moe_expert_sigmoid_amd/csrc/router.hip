@@ -9,6 +9,10 @@
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 
+#ifndef MOE_RT_TA
+#define MOE_RT_TA 4
+#endif
+
 namespace moe {
 
 // ---------------------------------------------------------------------------
@@ -87,127 +91,171 @@ hipError_t launch_router_gemv(const Shape& s, const uint16_t* x, const float* w_
 // ---------------------------------------------------------------------------
 // Larger T: bf16 MFMA.  x is bf16 already; each fp32 router weight is split
 // into hi = bf16(w) and lo = bf16(w - hi) so that two bf16 MFMAs reproduce
-// the fp32 product to about 2^-17 relative.  A workgroup computes a tile of
-// 32 tokens x 64 experts: K advances 64 at a time through a double-buffered
-// LDS stage (32 x 64 bf16 activations, 64 x 64 fp32 weights, rows padded so
-// that the 16 rows one MFMA operand reads fall in distinct banks).  Wavefront
-// w takes tokens 16(w&1) .. +15 and experts 32(w>>1) .. +31 (two 16 x 16
-// tiles, each with a hi and a lo MFMA per K step of 32).  K is split in
-// kRtSplit contiguous parts (blockIdx.y), each writing its own partial logits
-// [part][T][E]; the top-k sums the parts in order, so the result is fixed.
+// the fp32 product to about 2^-17 relative.  A workgroup computes 16*TA
+// tokens x 256 experts over one of kRouterParts contiguous parts of K with 8
+// wavefronts: wavefront w takes the 64-expert block w % 4 and half w / 4 of
+// every chunk's K steps, and the two halves are added in LDS at the end
+// (lower half first).  The token tile is brought into LDS first, 1 KiB of
+// every token row per chunk of 16 K steps, with buffer loads straight into
+// LDS (rows past T read as zeros), so the activation operand never waits on
+// HBM inside the K loop; each wavefront streams its weights from memory into
+// MFMA registers -- lane (n, G) takes 8 consecutive K values of weight row
+// n -- with the next two K steps of 32 in flight, and splits them there.
+// Workgroups go round-robin over the 8 XCDs and workgroup b takes K part
+// b % kRouterParts, so each XCD keeps the same part of the router weights in
+// its L2 while the token tiles stream past.  The weights are the MFMA A
+// operand: a lane ends with 4 consecutive experts of one token, stored as
+// one 16-byte piece.  Every part writes its own partial logits [part][T][E];
+// the top-k sums the parts in order, so the result is fixed.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kRtT = 32, kRtE = 64, kRtK = 64;
-constexpr int kRtSplit = kRouterParts;  // K parts, each its own workgroup; partial logits summed by the top-k
-constexpr int kRtXStride = kRtK * 2 + 16;  // bytes per activation row in LDS (144)
-constexpr int kRtWStride = kRtK * 4 + 16;  // bytes per weight row in LDS (272)
+constexpr int kRtExp = 64, kRtK = 32;  // experts per wavefront, K per step
+constexpr int kRtBlocks = 4;           // 64-expert blocks per workgroup
+constexpr int kRtWaves = 2 * kRtBlocks;  // two K halves per block
+constexpr int kRtChunk = 16;           // K steps per LDS chunk: 1 KiB of each token row
+constexpr int kRtXRow = kRtChunk * kRtK * 2 + 16;  // LDS bytes per token row (padded against bank conflicts)
+static_assert(kRouterParts == 8, "one K part of the router weights per XCD");
 
-__global__ __launch_bounds__(256) void k_router_mfma(const uint16_t* __restrict__ x, const float* __restrict__ W,
-                                                     float* __restrict__ logits, int T, int d, int E) {
-  __shared__ __attribute__((aligned(16))) char xs[2][kRtT * kRtXStride];
-  __shared__ __attribute__((aligned(16))) char ws[2][kRtE * kRtWStride];
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+typedef float float2v __attribute__((ext_vector_type(2)));
+// hi = bf16(w) (round to nearest even), lo = bf16(w - hi); w - hi is exact in fp32, and the bf16 pair
+// hi is turned back into fp32 by placing each half in the top 16 bits
+__device__ __forceinline__ void split_pair(float w0, float w1, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{w0, w1}, bf16x2));
+  const float r0 = w0 - __builtin_bit_cast(float, hi << 16);
+  const float r1 = w1 - __builtin_bit_cast(float, hi & 0xFFFF0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{r0, r1}, bf16x2));
+}
+__device__ __forceinline__ void split_hi_lo(const float4 a, const float4 b, bf16x8& hi, bf16x8& lo) {
+  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+  split_pair(a.x, a.y, h0, l0);
+  split_pair(a.z, a.w, h1, l1);
+  split_pair(b.x, b.y, h2, l2);
+  split_pair(b.z, b.w, h3, l3);
+  hi = __builtin_bit_cast(bf16x8, u32x4{h0, h1, h2, h3});
+  lo = __builtin_bit_cast(bf16x8, u32x4{l0, l1, l2, l3});
+}
+
+template <int TA>
+__global__ __launch_bounds__(64 * kRtWaves) void k_router_mfma(const uint16_t* __restrict__ x,
+                                                               const float* __restrict__ W,
+                                                               float* __restrict__ logits, int T, int d, int E) {
+  static_assert(16 * TA % kRtWaves == 0, "token rows split evenly over the wavefronts");
+  static_assert(16 * TA * kRtXRow >= kRtBlocks * 4 * TA * 64 * 16, "the K-half sums fit in the token tile");
+  __shared__ __attribute__((aligned(16))) char xs[16 * TA * kRtXRow];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, G = lane >> 4;
-  // Workgroups go round-robin over the 8 XCDs (own L2 each).  When the expert blocks and the XCDs
-  // divide evenly, each XCD keeps a fixed share of the expert blocks for every token block, so its L2
-  // holds only its share of the router weights while the token blocks stream past.
-  const int neb = (E + kRtE - 1) / kRtE;
-  int eb, tb;
-  if (neb <= 8 && 8 % neb == 0) {
-    eb = blockIdx.x % neb;  // blockIdx % 8 is the XCD, so XCD x always gets expert block x % neb
-    tb = blockIdx.x / neb;
-  } else if (neb % 8 == 0) {
-    const int per = neb / 8, item = blockIdx.x >> 3;
-    eb = (blockIdx.x & 7) * per + item % per;
-    tb = item / per;
-  } else {
-    eb = blockIdx.x % neb;
-    tb = blockIdx.x / neb;
-  }
-  const int t0 = tb * kRtT, e0 = eb * kRtE;
-  // staging: thread -> one 16-byte piece of the activation tile and four of the weight tile
-  const int xr = tid >> 3, xc = tid & 7;                     // 32 rows x 8 pieces
-  const uint16_t* xsrc = x + (size_t)min(t0 + xr, T - 1) * d + 8 * xc;
-  const int wr0 = tid >> 4, wc = tid & 15;  // 64 rows x 16 pieces: rows wr0 + 16j
-  const float* wsrc = W + (size_t)min(e0 + wr0, E - 1) * d + 4 * wc;
-  const size_t wstep = (size_t)16 * d;  // 16 rows further down (clamped rows only at the end of E)
-  const int wlast = E - 1 - e0 - wr0;   // rows beyond E re-read row E-1: j > wlast/16 is clamped
-  // this workgroup's part of K: stages [st0, st1) of 64 columns
-  const int nst_all = (d + kRtK - 1) / kRtK;
-  const int st0 = (nst_all * (int)blockIdx.y) / kRtSplit, st1 = (nst_all * ((int)blockIdx.y + 1)) / kRtSplit;
-  const bool half_tail = (d % kRtK) != 0 && st1 == nst_all;  // the last stage holds only one K step of 32
-  logits += (size_t)blockIdx.y * T * E;
-  const int wt = wave & 1, we = wave >> 1;
-  floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  u32x4 xv;
-  float4 wv0, wv1, wv2, wv3;
-#define MOE_RT_LOAD(st)                                                                             \
-  {                                                                                                  \
-    /* K columns past the end (half stage) re-read the stage's first half: loaded, never used */    \
-    const int k0_ = (st) * kRtK;                                                                     \
-    xv = ld16(xsrc + ((k0_ + 8 * xc < d) ? k0_ : k0_ - 32));                                         \
-    const int kw_ = (k0_ + 4 * wc < d) ? k0_ : k0_ - 32;                                            \
-    wv0 = *reinterpret_cast<const float4*>(wsrc + kw_);                                              \
-    wv1 = *reinterpret_cast<const float4*>(wsrc + (16 <= wlast ? wstep : 0) + kw_);                   \
-    wv2 = *reinterpret_cast<const float4*>(wsrc + (32 <= wlast ? 2 * wstep : 0) + kw_);               \
-    wv3 = *reinterpret_cast<const float4*>(wsrc + (48 <= wlast ? 3 * wstep : 0) + kw_);               \
-  }
-#define MOE_RT_STORE(buf)                                                                           \
-  {                                                                                                  \
-    *reinterpret_cast<u32x4*>(xs[buf] + xr * kRtXStride + 16 * xc) = xv;                             \
-    char* w_ = ws[buf] + wr0 * kRtWStride + 16 * wc;                                                 \
-    *reinterpret_cast<float4*>(w_) = wv0;                                                            \
-    *reinterpret_cast<float4*>(w_ + 16 * kRtWStride) = wv1;                                          \
-    *reinterpret_cast<float4*>(w_ + 32 * kRtWStride) = wv2;                                          \
-    *reinterpret_cast<float4*>(w_ + 48 * kRtWStride) = wv3;                                          \
-  }
-  if (st0 < st1) {
-    MOE_RT_LOAD(st0);
-    MOE_RT_STORE(0);
-  }
-  __syncthreads();
-  for (int st = st0; st < st1; ++st) {
-    const int buf = (st - st0) & 1;
-    if (st + 1 < st1) MOE_RT_LOAD(st + 1);  // in flight while this stage is computed
-    const int nk = (half_tail && st == st1 - 1) ? 1 : 2;  // uniform
-    for (int kk = 0; kk < nk; ++kk) {
-      const bf16x8 a8 = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(xs[buf] + (16 * wt + n) * kRtXStride + 64 * kk + 16 * G));
+  const int blk = wave % kRtBlocks, kh = wave / kRtBlocks;
+  const int part = blockIdx.x % kRouterParts, item = blockIdx.x / kRouterParts;
+  const int neb = (E + kRtBlocks * kRtExp - 1) / (kRtBlocks * kRtExp);
+  const int t0 = (item / neb) * 16 * TA, e0 = ((item % neb) * kRtBlocks + blk) * kRtExp;
+  const bool active = e0 < E;  // uniform over the wavefront; idle ones still stage tokens and meet the barriers
+  logits += (size_t)part * T * E;
+  const int nst = d / kRtK;
+  const int st0 = (nst * part) / kRouterParts, ns = (nst * (part + 1)) / kRouterParts - st0;
+  const int rows = min(16 * TA, T - t0);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (size_t)t0 * d, (uint32_t)((size_t)rows * d * 2));
+  // weight rows past E re-read row E-1 and are never stored
+  const float* wr[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const char* wrow = ws[buf] + (32 * we + 16 * j + n) * kRtWStride + 128 * kk + 32 * G;
-        const float4 w0 = *reinterpret_cast<const float4*>(wrow);
-        const float4 w1 = *reinterpret_cast<const float4*>(wrow + 16);
-        bf16x8 bhi, blo;
-        bhi[0] = (__bf16)w0.x; bhi[1] = (__bf16)w0.y; bhi[2] = (__bf16)w0.z; bhi[3] = (__bf16)w0.w;
-        bhi[4] = (__bf16)w1.x; bhi[5] = (__bf16)w1.y; bhi[6] = (__bf16)w1.z; bhi[7] = (__bf16)w1.w;
-        blo[0] = (__bf16)(w0.x - (float)bhi[0]); blo[1] = (__bf16)(w0.y - (float)bhi[1]);
-        blo[2] = (__bf16)(w0.z - (float)bhi[2]); blo[3] = (__bf16)(w0.w - (float)bhi[3]);
-        blo[4] = (__bf16)(w1.x - (float)bhi[4]); blo[5] = (__bf16)(w1.y - (float)bhi[5]);
-        blo[6] = (__bf16)(w1.z - (float)bhi[6]); blo[7] = (__bf16)(w1.w - (float)bhi[7]);
-        floatx4& acc = j ? acc1 : acc0;
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, bhi, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, blo, acc, 0, 0, 0);
-      }
+  for (int b = 0; b < 4; ++b) wr[b] = W + (size_t)min(e0 + 16 * b + n, E - 1) * d + (size_t)st0 * kRtK + 8 * G;
+  floatx4 acc[4][TA];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int a = 0; a < TA; ++a) acc[b][a] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float4 wl[2][4][2];
+#define MOE_RT_LOAD(S, s)                                                    \
+  _Pragma("unroll") for (int b = 0; b < 4; ++b) {                            \
+    wl[S][b][0] = *reinterpret_cast<const float4*>(wr[b] + (s) * kRtK);      \
+    wl[S][b][1] = *reinterpret_cast<const float4*>(wr[b] + (s) * kRtK + 4);  \
+  }
+// all 16 hi products before the 16 lo ones: consecutive MFMAs on one accumulator stay 16 apart
+#define MOE_RT_MMA(S, s)                                                     \
+  {                                                                          \
+    bf16x8 xb[TA], hi[4], lo[4];                                             \
+    _Pragma("unroll") for (int a = 0; a < TA; ++a) xb[a] = __builtin_bit_cast( \
+        bf16x8, *reinterpret_cast<const u32x4*>(xs + (16 * a + n) * kRtXRow + ((s) - c0) * kRtK * 2 + 16 * G)); \
+    _Pragma("unroll") for (int b = 0; b < 4; ++b) split_hi_lo(wl[S][b][0], wl[S][b][1], hi[b], lo[b]); \
+    _Pragma("unroll") for (int b = 0; b < 4; ++b)                            \
+      _Pragma("unroll") for (int a = 0; a < TA; ++a)                         \
+        acc[b][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[b], xb[a], acc[b][a], 0, 0, 0); \
+    _Pragma("unroll") for (int b = 0; b < 4; ++b)                            \
+      _Pragma("unroll") for (int a = 0; a < TA; ++a)                         \
+        acc[b][a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[b], xb[a], acc[b][a], 0, 0, 0); \
+  }
+  for (int c0 = 0; c0 < ns; c0 += kRtChunk) {
+    const int cn = min(kRtChunk, ns - c0);
+    const int half = (cn + 1) / 2;
+    const int k0 = c0 + kh * half, kn = kh ? cn - half : half;  // this wavefront's K steps of the chunk
+    if (c0 > 0) {  // every wavefront is done reading the previous chunk
+      vm_lgkm_wait<0>();
+      tile_barrier();
     }
-    if (st + 1 < st1) {
-      __syncthreads();  // every wavefront is done with buffer buf ^ 1 (read two stages ago)
-      MOE_RT_STORE(buf ^ 1);
-      __syncthreads();
+    // the chunk: wavefront w loads rows w, w + 8, ... with one 1 KiB instruction per row; lanes past
+    // the chunk read on along the row (zeros past the tile) into padding that is never read
+#pragma unroll
+    for (int i = 0; i < 16 * TA / kRtWaves; ++i) {
+      const int r = wave + kRtWaves * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(xs + r * kRtXRow), 16,
+                                               r * d * 2 + (st0 + c0) * kRtK * 2 + 16 * lane, 0, 0, 0);
+    }
+    // the first two weight steps are issued behind the chunk, so waiting for all but them waits for
+    // exactly the chunk
+    if (active && kn > 1) {
+      MOE_RT_LOAD(0, k0);
+      MOE_RT_LOAD(1, k0 + 1);
+      vm_wait<16>();
+    } else if (active && kn == 1) {
+      MOE_RT_LOAD(0, k0);
+      vm_wait<8>();
+    } else {
+      vm_wait<0>();
+    }
+    tile_barrier();  // every row of the chunk is in LDS
+    if (active) {
+      for (int s = k0; s < k0 + kn; s += 2) {
+        MOE_RT_MMA(0, s);
+        if (s + 2 < k0 + kn) MOE_RT_LOAD(0, s + 2);
+        if (s + 1 < k0 + kn) {
+          MOE_RT_MMA(1, s + 1);
+          if (s + 3 < k0 + kn) MOE_RT_LOAD(1, s + 3);
+        }
+      }
     }
   }
 #undef MOE_RT_LOAD
-#undef MOE_RT_STORE
-  const floatx4 accs[2] = {acc0, acc1};
-  // D layout: lane holds column n (expert) of rows 4G..4G+3 (tokens) of each 16 x 16 tile
+#undef MOE_RT_MMA
+  // the upper K half hands its sums to the lower one through LDS (the token tile is no longer read)
+  vm_lgkm_wait<0>();
+  tile_barrier();
+  floatx4* red = reinterpret_cast<floatx4*>(xs) + (size_t)blk * 4 * TA * 64 + lane;
+  if (kh == 1 && active) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int e = e0 + 32 * we + 16 * j + n;
-    if (e >= E) continue;
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 16 * wt + 4 * G + i;
-      if (t < T) logits[(size_t)t * E + e] = accs[j][i];
+      for (int a = 0; a < TA; ++a) red[(b * TA + a) * 64] = acc[b][a];
+  }
+  vm_lgkm_wait<0>();
+  tile_barrier();
+  if (kh == 1 || !active) return;
+  // D layout (weights as A): lane holds token n of each 16-token block, experts 4G .. 4G+3
+  const bool vec = (E & 3) == 0;  // rows of the logits 16-byte aligned
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int e = e0 + 16 * b + 4 * G;
+#pragma unroll
+    for (int a = 0; a < TA; ++a) {
+      const floatx4 v = acc[b][a] + red[(b * TA + a) * 64];
+      const int t = t0 + 16 * a + n;
+      if (t >= T || e >= E) continue;
+      float* dst = logits + (size_t)t * E + e;
+      if (vec && e + 3 < E) {
+        *reinterpret_cast<floatx4*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (e + i < E) dst[i] = v[i];
+      }
     }
   }
 }
@@ -349,10 +397,13 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 
 hipError_t launch_router_mfma(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
                               hipStream_t st) {
-  const dim3 grid(((s.T + kRtT - 1) / kRtT) * ((s.E + kRtE - 1) / kRtE), kRtSplit), block(256);
-  hipLaunchKernelGGL(k_router_mfma, grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
+  constexpr int TA = MOE_RT_TA;
+  const int ntt = (s.T + 16 * TA - 1) / (16 * TA), neb = (s.E + kRtBlocks * kRtExp - 1) / (kRtBlocks * kRtExp);
+  const dim3 grid(ntt * neb * kRouterParts), block(64 * kRtWaves);
+  hipLaunchKernelGGL(k_router_mfma<TA>, grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
   return hipGetLastError();
 }
+
 template <int NPARTS>
 static hipError_t launch_topk_parts(const Shape& s, const float* logits, const float* bias, int32_t* topk_ids,
                                     float* topk_w, hipStream_t st) {

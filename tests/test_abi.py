@@ -83,7 +83,7 @@ def test_workspace_sizes_closed_form(dims):
     T, E, k, dd, I, Is = dims.T, dims.E, dims.k, dims.d, dims.I, dims.I_shared
     P = T * k
     chunks = (T + 255) // 256
-    routing = (align(4 * T * E * 4) + 2 * align((E + 1) * 4) + 3 * align(P * 4) + align((E + 1) * 4)
+    routing = (align(8 * T * E * 4) + 2 * align((E + 1) * 4) + 3 * align(P * 4) + align((E + 1) * 4)
                + align((E + 2) * 4) + align(chunks * E * 4))
     assert moe.moe_routing_bytes(dims) == routing
     lay = moe.moe_routing_layout_of(dims)
