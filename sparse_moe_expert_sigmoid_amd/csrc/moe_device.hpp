@@ -137,35 +137,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
 }
 
-// ---------------------------------------------------------------- GEMV helpers (bf16 dot2)
-// For v_dot2_f32_bf16 each code becomes the bf16 value 128 + q (the nibble in
-// the low mantissa bits of 128.0, exact), paired as (e0,e4), (e1,e5), (e2,e6),
-// (e3,e7) of a dword so that every pair is one and-or (after at most one
-// shift).  With x in matching pairs, a block's dot is sum x*(128 + q) =
-// 128*X + Q (X = sum x, Q = sum x*q), and its contribution d * (dot - 136*X)
-// = d * (Q - 8X) = d * sum x*(q - 8).  `mask` (0x000F000F) and `magic`
-// (0x43004300) are passed in registers so that each pair is a single
-// v_and_or_b32.
-__device__ __forceinline__ void codes_bf16_pairs(uint32_t w, uint32_t mask, uint32_t magic, uint32_t out[4]) {
-  const uint32_t t = w >> 4;
-  out[0] = and_or(w, mask, magic);
-  out[1] = and_or(t, mask, magic);
-  out[2] = and_or(w >> 8, mask, magic);
-  out[3] = and_or(t >> 8, mask, magic);
-}
-// 8 consecutive bf16 values (u0..u3, each a pair (x_2m, x_2m+1)) -> pairs
-// (x0,x4), (x1,x5), (x2,x6), (x3,x7).
+// ---------------------------------------------------------------- pair order
+// 8 consecutive 16-bit values (u0..u3, each a pair (x_2m, x_2m+1)) -> the
+// pairs (x0,x4), (x1,x5), (x2,x6), (x3,x7): the order in which one dword of
+// codes (element m in bits 4m..4m+3) is dequantised.
 __device__ __forceinline__ void x_bf16_pairs(const u32x4 u, uint32_t out[4]) {
   out[0] = __builtin_amdgcn_perm(u[2], u[0], 0x05040100u);
   out[1] = __builtin_amdgcn_perm(u[2], u[0], 0x07060302u);
   out[2] = __builtin_amdgcn_perm(u[3], u[1], 0x05040100u);
   out[3] = __builtin_amdgcn_perm(u[3], u[1], 0x07060302u);
 }
+
+// ---------------------------------------------------------------- GEMV helper
+// v_dot2_f32_f16: two fp16 products added to an fp32 accumulator.
 __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c, false);
-}
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
 // ---------------------------------------------------------------- reductions
@@ -189,10 +175,6 @@ template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_f_rows(float v) {  // rows outside ROW_MASK receive 0
   return __builtin_bit_cast(float,
                             __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 
 __device__ __forceinline__ float row16_sum(float v) {
