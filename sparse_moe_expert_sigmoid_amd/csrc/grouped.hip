@@ -287,16 +287,38 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
         const int col = c.c0 + 16 * xh + 8 * (c.G >> 1) + 4 * (c.G & 1);
         if (live && c.nok[xh]) *reinterpret_cast<uint2*>(out + (size_t)(c.rbase + row) * c.Iw + col) = v;
       }
-    } else {
-      _Float16* out = c.shared ? a.y_s : a.y_r;
+    }
+  }
+  if (!GATEUP) {
+    // The down tile goes out through LDS so that every store writes whole rows: 96 x 256 fp16 = the
+    // activation ring, 512 B per row, 16-byte chunk j of row r in slot j ^ (r & 31) (the 16 lanes that
+    // write one column chunk for 16 rows hit 16 different bank groups).
+    static_assert(kStages * kTileBytes >= kGroupedBM * kDownBandCols * 2, "the output tile fits in the ring");
+    vm_lgkm_wait<0>();
+    tile_barrier();  // every wavefront is done reading the activation ring
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int row = mt * 16 + c.n;
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns) {
         const half2v p0 = {(_Float16)acc[mt][ns][0], (_Float16)acc[mt][ns][1]};
         const half2v p1 = {(_Float16)acc[mt][ns][2], (_Float16)acc[mt][ns][3]};
-        const uint2 v = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
-        if (live && c.nok[ns])
-          *reinterpret_cast<uint2*>(out + (size_t)(c.rbase + row) * a.d + c.c0 + 16 * ns + 4 * c.G) = v;
+        const int chunk = 8 * c.wave + 2 * ns + (c.G >> 1);
+        *reinterpret_cast<uint2*>(As + row * (kDownBandCols * 2) + ((chunk ^ (row & 31)) * 16) + 8 * (c.G & 1)) =
+            uint2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
       }
+    }
+    vm_lgkm_wait<0>();
+    tile_barrier();
+    // thread t stores chunk t % 32 of rows t / 32, t / 32 + 8, ...: one wavefront store covers two rows
+    _Float16* out = c.shared ? a.y_s : a.y_r;
+    const int tid = (int)threadIdx.x, chunk = tid & 31;
+    const int col = c.c0 - 64 * c.wave + 8 * chunk;  // d % 32 == 0: a chunk is all inside d or all past it
+#pragma unroll
+    for (int i = 0; i < 2 * NMT; ++i) {
+      const int row = 8 * i + (tid >> 5);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(As + row * (kDownBandCols * 2) + ((chunk ^ (row & 31)) * 16));
+      if (row < c.mlen && col < a.d) *reinterpret_cast<u32x4*>(out + (size_t)(c.rbase + row) * a.d + col) = v;
     }
   }
 }
