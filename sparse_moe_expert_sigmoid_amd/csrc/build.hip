@@ -44,23 +44,26 @@ __global__ __launch_bounds__(256) void k_build_count(const int32_t* __restrict__
   for (int e = tid; e < E; e += 256) chunk_counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
 
-// Exclusive scan of v[0..n) in place (n <= 1024+2), 256 threads.
+// Exclusive scan of v[0..n) in place (n <= 1024+2), 256 threads: each thread sums a run of
+// consecutive elements, the run sums are scanned inside each wavefront with lane shifts and across
+// the 4 wavefronts through LDS, then every run is rewritten from its offset (two barriers).
 __device__ void block_exclusive_scan(int* v, int n, int* tmp /* [256] */) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (n + 255) / 256;
   const int lo = tid * per;
   int local = 0;
   for (int i = 0; i < per; ++i)
     if (lo + i < n) local += v[lo + i];
-  tmp[tid] = local;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const int add = tid >= o ? tmp[tid - o] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+  int incl = local;  // inclusive scan of the run sums inside the wavefront
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int up = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += up;
   }
-  int run = tmp[tid] - local;
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int w = 0; w < wave; ++w) run += tmp[w];
   for (int i = 0; i < per; ++i)
     if (lo + i < n) {
       const int c = v[lo + i];
@@ -74,10 +77,10 @@ __device__ void block_exclusive_scan(int* v, int n, int* tmp /* [256] */) {
 // schedule (workgroup nchunks, in parallel with them).
 __global__ __launch_bounds__(256) void k_build_scatter(const int32_t* __restrict__ ids, int T, int k, int E,
                                                        int nchunks, uint32_t flags, Routing r) {
-  __shared__ __attribute__((aligned(16))) int cnt[kMaxExperts + 4];
+  __shared__ int cnt[kMaxExperts + 1];
   __shared__ int off[kMaxExperts + 2];
   __shared__ int base[kMaxExperts + 2];
-  __shared__ uint32_t masks[kMaxExperts * (kBuildChunk / 32)];
+  __shared__ __attribute__((aligned(16))) uint32_t masks[kMaxExperts * (kBuildChunk / 32)];
   __shared__ int tmp[256];
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x;
@@ -150,24 +153,27 @@ __global__ __launch_bounds__(256) void k_build_scatter(const int32_t* __restrict
     r.offsets[E] = off[E];
   }
   if (tid == 0) cnt[E] = T;
-  if (tid < 3) cnt[ng + tid] = -1;  // padding to a multiple of 4: never ranks above a real count
+  // rank of group g: larger count first, ties to the lower id (or id order).  With the 64-bit key
+  // count * 2^32 + (2^32 - 1 - g) (the chunk masks' LDS is free here) the rank is the number of larger
+  // keys: one compare per group, two keys per LDS read.
+  uint64_t* key = reinterpret_cast<uint64_t*>(masks);
+  const int ng2 = (ng + 1) & ~1;  // padded with a zero key, below every real one
   __syncthreads();
-  // rank of group g: larger count first, ties to the lower id (or id order)
-  const int n4 = (ng + 3) / 4;
+  for (int g = tid; g < ng2; g += 256)
+    key[g] = g < ng ? ((uint64_t)(uint32_t)cnt[g] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)g) : 0ull;
+  __syncthreads();
   for (int g = tid; g < ng; g += 256) {
     const int cg = cnt[g];
+    const uint64_t kg = key[g];
     int rank;
     if (flags & MOE_FLAG_ID_ORDER) {
       rank = g;
     } else {
       rank = 0;
-      for (int h4 = 0; h4 < n4; ++h4) {
-        const int4 c4 = reinterpret_cast<const int4*>(cnt)[h4];
-        const int h = 4 * h4;
-        rank += (c4.x > cg) || (c4.x == cg && h < g);
-        rank += (c4.y > cg) || (c4.y == cg && h + 1 < g);
-        rank += (c4.z > cg) || (c4.z == cg && h + 2 < g);
-        rank += (c4.w > cg) || (c4.w == cg && h + 3 < g);
+#pragma unroll 8
+      for (int h2 = 0; h2 < ng2 / 2; ++h2) {
+        const ulonglong2 k2 = reinterpret_cast<const ulonglong2*>(key)[h2];
+        rank += (int)(k2.x > kg) + (int)(k2.y > kg);
       }
     }
     r.group_order[rank] = g;
