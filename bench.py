@@ -2,6 +2,7 @@
 """Throughput of the MI355X Q4 MoE expert layer (route -> build -> forward) on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|batched_decode|prefill|long_prefill]
+    python bench.py --all          (every workload, one JSON line with a list of them)
 
 One step is one call of the whole layer on one batch of synthetic tokens:
 moe_route + moe_build_descriptors + moe_q4_forward.  Steps are captured in
@@ -16,6 +17,9 @@ I=1024, shared I=1024) gives `value`; the 2048-token prefill chunk is
 measured the same way and reported under `secondary`.  Per-kernel average
 durations come from graphs that replay only that kernel's nodes, extracted
 from the captured layer graph, timed with HIP events on the same stream.
+For an HBM-bound dominant kernel the roofline object also carries the rate
+of torch's device copy kernel moving the same number of bytes
+(`copy_ceiling`): the practical streaming ceiling beside the nominal peak.
 
 Prints one JSON line.
 """
@@ -290,6 +294,9 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
     # routing statistics of copy 0 (distinct experts decide the bytes a call must read)
     ids = spaces[0].topk_ids.cpu().numpy()
     distinct = int(np.unique(ids).size)
+    sizes = np.bincount(ids.ravel(), minlength=dims.E)
+    group_stats = {"max": int(sizes.max()), "median": float(np.median(sizes)), "min": int(sizes.min()),
+                   "empty": int((sizes == 0).sum())}
     gu, dn, sgu, sdn = expert_bytes(dims)
     T, d, E, P = dims.T, dims.d, dims.E, dims.T * dims.k
     layer_bytes = (E * d * 4 + E * 4 + T * d * 2 + distinct * (gu + dn) + (sgu + sdn) + T * d * 4
@@ -302,6 +309,7 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
         "workload": name, "dims": dict(T=T, d=d, E=E, k=dims.k, I=dims.I, I_shared=dims.I_shared),
         "path": "gemv" if path == 0 else "grouped", "layer_copies": L, "steps": steps, "warmup": warmup,
         "ms_per_step": ms_per_step, "tokens_per_s": tokens_per_s, "distinct_experts": distinct,
+        "group_rows": group_stats,
         "kernel_avg_us": {k: round(v, 3) for k, v in kernel_us.items()},
         "layer_algorithmic_bytes": layer_bytes, "layer_algorithmic_flop": layer_flop,
         "layer_hbm_frac": layer_bytes / (ms_per_step / 1000.0) / (HBM_PEAK_GBS * 1e9),
@@ -331,6 +339,54 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
     return res
 
 
+def copy_ceiling(torch, nbytes_list):
+    """GB/s (bytes read + bytes written, per second) of torch's device-to-device copy kernel at the given
+    total byte counts: the practical streaming ceiling beside the nominal HBM peak.  Buffers rotate through
+    1 GiB windows so that repeated copies do not hit the 256 MB MALL."""
+    out = {}
+    pool = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    pool.fill_(1)
+    for nbytes in nbytes_list:
+        half = (nbytes // 2) & ~4095
+        nwin = (1 << 30) // half
+        reps = 40
+        srcs = [pool[i * half:(i + 1) * half] for i in range(nwin)]
+        dsts = [pool[(1 << 30) + i * half:(1 << 30) + (i + 1) * half] for i in range(nwin)]
+        for i in range(3):
+            dsts[i % nwin].copy_(srcs[i % nwin])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(reps):
+            dsts[(i + 3) % nwin].copy_(srcs[(i + 3) % nwin])
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1000.0 / reps
+        out[str(2 * half)] = {"us": round(us, 2), "gbs": round(2 * half / (us * 1e-6) / 1e9, 1)}
+    del pool
+    return out
+
+
+def host_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        import threadpoolctl
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpoolctl.threadpool_info()
+                if i.get("user_api") == "blas"]
+        blas = ", ".join(libs) or blas
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "blas": blas}
+
+
 def cpu_baseline(inp, budget_s=15.0):
     """The oracle as it stands, on the host, on a bounded sample of the primary workload's tokens."""
     import oracle
@@ -353,7 +409,7 @@ def cpu_baseline(inp, budget_s=15.0):
             break
     return {"value": round(done / el, 4), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{calls} oracle layer calls of {len(tokens)} token(s) each on the workload's layer copy 0, "
-                      f"{el:.1f} s wall on the host"}
+                      f"{el:.1f} s wall on the host", **host_info()}
 
 
 def traffic_run(name, torch, layer, synth):
@@ -383,6 +439,8 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "batched_decode", "prefill", "long_prefill"])
     ap.add_argument("--secondary", default="prefill", help="second workload reported alongside ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true",
+                    help="measure every workload (tiny excluded) and print one JSON line with a list of them")
     ap.add_argument("--traffic-run", metavar="WORKLOAD", default=None,
                     help="for hardware-counter collection only: run WORKLOAD's layer 3 times, then copy a 256 MiB "
                          "device buffer twice (the calibration of FETCH_SIZE / WRITE_SIZE), print one line, exit")
@@ -403,12 +461,28 @@ def main():
         traffic_run(args.traffic_run, torch, layer, synth)
         return
     hip = Hip()
+    if args.all:
+        rows = []
+        for wl, n in (("decode", args.steps), ("batched_decode", max(40, args.steps // 8)),
+                      ("prefill", max(20, args.steps // 40)), ("long_prefill", max(10, args.steps // 80))):
+            r = run_workload(wl, n, max(4, n // 10), torch, hip, abi, layer, synth)
+            r.pop("_inp0", None)
+            rows.append(r)
+            print(f"[bench] {wl}: {r['ms_per_step'] * 1000:.1f} us/step, {r['tokens_per_s']:.0f} tokens/s",
+                  file=sys.stderr, flush=True)
+        print(json.dumps({"metric": METRIC, "n_gpus": 1, "workloads": rows,
+                          "copy_ceiling": copy_ceiling(torch, [52 << 20, 1 << 30])}), flush=True)
+        return
     prim = run_workload(args.workload, args.steps, args.warmup, torch, hip, abi, layer, synth)
     sec = None
     if args.secondary and args.secondary != "none" and args.secondary != args.workload:
         n = max(20, args.steps // 40)
         sec = run_workload(args.secondary, n, max(4, n // 10), torch, hip, abi, layer, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(prim["_inp0"])
+    rl = prim["roofline"]
+    if rl["unit"] == "GB/s":
+        ceil = copy_ceiling(torch, [rl["algorithmic_bytes_per_launch"]])
+        rl["copy_ceiling"] = next(iter(ceil.values())) | {"bytes": int(next(iter(ceil)))}
     dims = prim["dims"]
     out = {
         "metric": METRIC,
@@ -421,7 +495,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if prim["path"] == "gemv" else "f16",
+        "dtype": "f16",
         "data": "synthetic (seeded; Q4 codes uniform, fp16 scales U(0.005,0.02), x N(0,1) bf16)",
         "config": {"workload": f"{args.workload}: T={dims['T']} d={dims['d']} E={dims['E']} top-{dims['k']} "
                                f"I={dims['I']} shared I={dims['I_shared']} Q4 block-32",
