@@ -9,9 +9,6 @@
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 
-#ifndef MOE_RT_TA
-#define MOE_RT_TA 4
-#endif
 
 namespace moe {
 
@@ -95,7 +92,9 @@ hipError_t launch_router_gemv(const Shape& s, const uint16_t* x, const float* w_
 // tokens x 256 experts over one of kRouterParts contiguous parts of K with 8
 // wavefronts: wavefront w takes the 64-expert block w % 4 and half w / 4 of
 // every chunk's K steps, and the two halves are added in LDS at the end
-// (lower half first).  The token tile is brought into LDS first, 1 KiB of
+// (lower half first).  When that gives few workgroups (small T) a workgroup
+// takes one 64-expert block and splits every chunk's K steps over 8
+// wavefronts instead, whose sums are added in LDS in wavefront order.  The token tile is brought into LDS first, 1 KiB of
 // every token row per chunk of 16 K steps, with buffer loads straight into
 // LDS (rows past T read as zeros), so the activation operand never waits on
 // HBM inside the K loop; each wavefront streams its weights from memory into
@@ -110,8 +109,6 @@ hipError_t launch_router_gemv(const Shape& s, const uint16_t* x, const float* w_
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRtExp = 64, kRtK = 32;  // experts per wavefront, K per step
-constexpr int kRtBlocks = 4;           // 64-expert blocks per workgroup
-constexpr int kRtWaves = 2 * kRtBlocks;  // two K halves per block
 constexpr int kRtChunk = 16;           // K steps per LDS chunk: 1 KiB of each token row
 constexpr int kRtXRow = kRtChunk * kRtK * 2 + 16;  // LDS bytes per token row (padded against bank conflicts)
 static_assert(kRouterParts == 8, "one K part of the router weights per XCD");
@@ -135,12 +132,14 @@ __device__ __forceinline__ void split_hi_lo(const float4 a, const float4 b, bf16
   lo = __builtin_bit_cast(bf16x8, u32x4{l0, l1, l2, l3});
 }
 
-template <int TA>
-__global__ __launch_bounds__(64 * kRtWaves) void k_router_mfma(const uint16_t* __restrict__ x,
-                                                               const float* __restrict__ W,
-                                                               float* __restrict__ logits, int T, int d, int E) {
+// TA 16-token blocks, EB 64-expert blocks per workgroup, every chunk's K steps split over KS wavefronts
+template <int TA, int EB, int KS>
+__global__ __launch_bounds__(64 * EB * KS) void k_router_mfma(const uint16_t* __restrict__ x,
+                                                              const float* __restrict__ W,
+                                                              float* __restrict__ logits, int T, int d, int E) {
+  constexpr int kRtBlocks = EB, kRtWaves = EB * KS;
   static_assert(16 * TA % kRtWaves == 0, "token rows split evenly over the wavefronts");
-  static_assert(16 * TA * kRtXRow >= kRtBlocks * 4 * TA * 64 * 16, "the K-half sums fit in the token tile");
+  static_assert(16 * TA * kRtXRow >= kRtBlocks * 4 * TA * 64 * 16, "the K-part sums fit in the token tile");
   __shared__ __attribute__((aligned(16))) char xs[16 * TA * kRtXRow];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, G = lane >> 4;
@@ -185,8 +184,7 @@ __global__ __launch_bounds__(64 * kRtWaves) void k_router_mfma(const uint16_t* _
   }
   for (int c0 = 0; c0 < ns; c0 += kRtChunk) {
     const int cn = min(kRtChunk, ns - c0);
-    const int half = (cn + 1) / 2;
-    const int k0 = c0 + kh * half, kn = kh ? cn - half : half;  // this wavefront's K steps of the chunk
+    const int k0 = c0 + (cn * kh) / KS, kn = c0 + (cn * (kh + 1)) / KS - k0;  // this wavefront's K steps
     if (c0 > 0) {  // every wavefront is done reading the previous chunk
       vm_lgkm_wait<0>();
       tile_barrier();
@@ -225,19 +223,28 @@ __global__ __launch_bounds__(64 * kRtWaves) void k_router_mfma(const uint16_t* _
   }
 #undef MOE_RT_LOAD
 #undef MOE_RT_MMA
-  // the upper K half hands its sums to the lower one through LDS (the token tile is no longer read)
-  vm_lgkm_wait<0>();
-  tile_barrier();
+  // the other K parts hand their sums to part 0 through LDS (the token tile is no longer read), one
+  // after another in part order
   floatx4* red = reinterpret_cast<floatx4*>(xs) + (size_t)blk * 4 * TA * 64 + lane;
-  if (kh == 1 && active) {
+  for (int r = 1; r < KS; ++r) {
+    vm_lgkm_wait<0>();
+    tile_barrier();
+    if (kh == r && active) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int a = 0; a < TA; ++a) red[(b * TA + a) * 64] = acc[b][a];
+        for (int a = 0; a < TA; ++a) red[(b * TA + a) * 64] = acc[b][a];
+    }
+    vm_lgkm_wait<0>();
+    tile_barrier();
+    if (kh == 0 && active && r + 1 < KS) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int a = 0; a < TA; ++a) acc[b][a] += red[(b * TA + a) * 64];
+    }
   }
-  vm_lgkm_wait<0>();
-  tile_barrier();
-  if (kh == 1 || !active) return;
+  if (kh != 0 || !active) return;
   // D layout (weights as A): lane holds token n of each 16-token block, experts 4G .. 4G+3
   const bool vec = (E & 3) == 0;  // rows of the logits 16-byte aligned
 #pragma unroll
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(64 * kRtWaves) void k_router_mfma(const uint16_t* _
     const int e = e0 + 16 * b + 4 * G;
 #pragma unroll
     for (int a = 0; a < TA; ++a) {
-      const floatx4 v = acc[b][a] + red[(b * TA + a) * 64];
+      const floatx4 v = KS > 1 ? acc[b][a] + red[(b * TA + a) * 64] : acc[b][a];
       const int t = t0 + 16 * a + n;
       if (t >= T || e >= E) continue;
       float* dst = logits + (size_t)t * E + e;
@@ -395,12 +402,21 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
                           k, lane, sm[wv]);
 }
 
+template <int TA, int EB, int KS>
+static void router_mfma_cfg(const Shape& s, const uint16_t* x, const float* w_router, float* logits, hipStream_t st) {
+  const int ntt = (s.T + 16 * TA - 1) / (16 * TA), neb = (s.E + EB * kRtExp - 1) / (EB * kRtExp);
+  const dim3 grid(ntt * neb * kRouterParts), block(64 * EB * KS);
+  hipLaunchKernelGGL((k_router_mfma<TA, EB, KS>), grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
+}
+
 hipError_t launch_router_mfma(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
                               hipStream_t st) {
-  constexpr int TA = MOE_RT_TA;
-  const int ntt = (s.T + 16 * TA - 1) / (16 * TA), neb = (s.E + kRtBlocks * kRtExp - 1) / (kRtBlocks * kRtExp);
-  const dim3 grid(ntt * neb * kRouterParts), block(64 * kRtWaves);
-  hipLaunchKernelGGL(k_router_mfma<TA>, grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
+  constexpr int TA = 4;
+  const int ntt = (s.T + 16 * TA - 1) / (16 * TA), neb4 = (s.E + 4 * kRtExp - 1) / (4 * kRtExp);
+  if (ntt * neb4 * kRouterParts >= 128)
+    router_mfma_cfg<TA, 4, 2>(s, x, w_router, logits, st);  // 256 experts x 2 K halves per workgroup
+  else
+    router_mfma_cfg<TA, 1, 8>(s, x, w_router, logits, st);  // small T: 64 experts x 8 K parts
   return hipGetLastError();
 }
 
