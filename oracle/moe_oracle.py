@@ -139,13 +139,15 @@ def swiglu_mlp(X: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
     return h @ w2.T
 
 
-def forward(inp: dict, tokens=None, ids_override: dict | None = None) -> dict:
+def forward(inp: dict, tokens=None, ids_override: dict | None = None, residual=None) -> dict:
     """The whole layer for the chosen tokens (all tokens by default).
 
     inp: a dict as produced by the input generator (x bf16 bits, w_router,
     bias, w13_qs/w13_sc, w2_qs/w2_sc, s13_qs/s13_sc, s2_qs/s2_sc, dims).
     ids_override: {token: [k expert ids]} to evaluate the layer on a given
     selection (the weights still come from the fp64 scores).
+    residual: optional fp32 [T,d]; added after the routed and shared sum
+    ([nemotron], "ffai_add3": routed + shared first, then the residual).
     Returns dict(y [n,d] fp64, ids [n,k], w [n,k], margin [n], s [n,E], tokens).
     """
     dims = inp["dims"]
@@ -173,8 +175,10 @@ def forward(inp: dict, tokens=None, ids_override: dict | None = None) -> dict:
     s13 = dequant_q4(inp["s13_qs"], inp["s13_sc"])
     s2 = dequant_q4(inp["s2_qs"], inp["s2_sc"])
     y_shared = swiglu_mlp(x, s13, s2)
-    # Routed sum first, then the shared expert ([nemotron], "ffai_add3").
+    # Routed sum first, then the shared expert ([nemotron], "ffai_add3"), then the residual if any.
     y = y_routed + y_shared
+    if residual is not None:
+        y = y + np.asarray(residual, dtype=np.float64)[tokens]
     return dict(y=y, ids=ids, w=w, margin=margin, s=s, tokens=tokens)
 
 

@@ -306,6 +306,30 @@ def test_shared_only_when_routed_weights_are_zero():
         np.testing.assert_allclose(out["y"][t], naive_mlp(x[t].tolist(), s13, s2), rtol=1e-12, atol=1e-12)
 
 
+def test_residual_alone_when_every_expert_is_zero():
+    """All codes 8 (every routed and shared weight 0): the layer output is the residual itself, exactly,
+    and without a residual it is exactly 0 ([nemotron] "ffai_add3": the residual comes after the
+    routed + shared sum)."""
+    dims = synth.Dims(T=5, d=64, E=6, k=2, I=32, I_shared=64)
+    inp = synth.make_inputs(dims, seed=15)
+    for key in ("w13_qs", "w2_qs", "s13_qs", "s2_qs"):
+        inp[key][:] = 0x88
+    r = np.random.default_rng(16).standard_normal((5, 64)).astype(np.float32)
+    np.testing.assert_array_equal(oracle.forward(inp)["y"], 0.0)
+    np.testing.assert_array_equal(oracle.forward(inp, residual=r)["y"], r.astype(np.float64))
+    sub = oracle.forward(inp, tokens=[3, 1], residual=r)["y"]
+    np.testing.assert_array_equal(sub, r[[3, 1]].astype(np.float64))
+
+
+def test_identity_layer_plus_residual_closed_form():
+    """Identity expert (y = x^2 sigma(x)) plus a residual r: y = x^2 sigma(x) + r."""
+    inp = _identity_layer(64, shared_identity=False)
+    x = x_values(inp)
+    r = np.random.default_rng(17).standard_normal(x.shape).astype(np.float32)
+    np.testing.assert_allclose(oracle.forward(inp, residual=r)["y"], x * x / (1 + np.exp(-x)) + r,
+                               rtol=1e-14, atol=1e-15)
+
+
 def test_doubling_down_scales_doubles_output_exactly():
     dims = synth.Dims(T=6, d=64, E=8, k=3, I=32, I_shared=32)
     inp = synth.make_inputs(dims, seed=14)
