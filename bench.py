@@ -215,7 +215,7 @@ def recorded_traffic(profile: str, sources) -> int | None:
     return int(fields["traffic_bytes_per_launch"])
 
 
-def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_sample=False):
+def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_sample=False, residual=False):
     cfg = synth.CONFIGS[name]
     dims = cfg.dims
     device = "cuda"
@@ -231,18 +231,20 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
         weights.append(dw)
         xs.append(x)
     spaces = [layer.Workspace(dims, 0) for _ in range(L)]
+    # with `residual`, every step goes through moe_q4_forward_residual with its own fp32 [T][d] residual
+    res = [torch.randn(dims.T, dims.d, device=device) if residual else None for _ in range(L)]
     stream = torch.cuda.Stream()
     sh = stream.cuda_stream
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for c in range(L):  # eager pass: surfaces launch errors outside capture
-            layer.layer_call(xs[c], weights[c], spaces[c], stream=sh)
+            layer.layer_call(xs[c], weights[c], spaces[c], stream=sh, residual=res[c])
     torch.cuda.synchronize()
 
     def capture(copies):
         hip.begin_capture(sh)
         for c in copies:
-            layer.layer_call(xs[c], weights[c], spaces[c], stream=sh)
+            layer.layer_call(xs[c], weights[c], spaces[c], stream=sh, residual=res[c])
         g = hip.end_capture(sh)
         return g, hip.instantiate(g)
 
@@ -306,7 +308,8 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
     path = abi.moe_path(dims, 0)
     tokens_per_s = T / (ms_per_step / 1000.0)
     res = {
-        "workload": name, "dims": dict(T=T, d=d, E=E, k=dims.k, I=dims.I, I_shared=dims.I_shared),
+        "workload": name, "residual": bool(residual),
+        "dims": dict(T=T, d=d, E=E, k=dims.k, I=dims.I, I_shared=dims.I_shared),
         "path": "gemv" if path == 0 else "grouped", "layer_copies": L, "steps": steps, "warmup": warmup,
         "ms_per_step": ms_per_step, "tokens_per_s": tokens_per_s, "distinct_experts": distinct,
         "group_rows": group_stats,
@@ -439,6 +442,8 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "batched_decode", "prefill", "long_prefill"])
     ap.add_argument("--secondary", default="prefill", help="second workload reported alongside ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--residual", action="store_true",
+                    help="every step uses moe_q4_forward_residual (adds an fp32 [T][d] residual after the layer)")
     ap.add_argument("--all", action="store_true",
                     help="measure every workload (tiny excluded) and print one JSON line with a list of them")
     ap.add_argument("--traffic-run", metavar="WORKLOAD", default=None,
@@ -465,7 +470,7 @@ def main():
         rows = []
         for wl, n in (("decode", args.steps), ("batched_decode", max(40, args.steps // 8)),
                       ("prefill", max(20, args.steps // 40)), ("long_prefill", max(10, args.steps // 80))):
-            r = run_workload(wl, n, max(4, n // 10), torch, hip, abi, layer, synth)
+            r = run_workload(wl, n, max(4, n // 10), torch, hip, abi, layer, synth, residual=args.residual)
             r.pop("_inp0", None)
             rows.append(r)
             print(f"[bench] {wl}: {r['ms_per_step'] * 1000:.1f} us/step, {r['tokens_per_s']:.0f} tokens/s",
@@ -473,11 +478,12 @@ def main():
         print(json.dumps({"metric": METRIC, "n_gpus": 1, "workloads": rows,
                           "copy_ceiling": copy_ceiling(torch, [52 << 20, 1 << 30])}), flush=True)
         return
-    prim = run_workload(args.workload, args.steps, args.warmup, torch, hip, abi, layer, synth)
+    prim = run_workload(args.workload, args.steps, args.warmup, torch, hip, abi, layer, synth,
+                        residual=args.residual)
     sec = None
     if args.secondary and args.secondary != "none" and args.secondary != args.workload:
         n = max(20, args.steps // 40)
-        sec = run_workload(args.secondary, n, max(4, n // 10), torch, hip, abi, layer, synth)
+        sec = run_workload(args.secondary, n, max(4, n // 10), torch, hip, abi, layer, synth, residual=args.residual)
     cpu = None if args.no_cpu_baseline else cpu_baseline(prim["_inp0"])
     rl = prim["roofline"]
     if rl["unit"] == "GB/s":
@@ -499,7 +505,8 @@ def main():
         "data": "synthetic (seeded; Q4 codes uniform, fp16 scales U(0.005,0.02), x N(0,1) bf16)",
         "config": {"workload": f"{args.workload}: T={dims['T']} d={dims['d']} E={dims['E']} top-{dims['k']} "
                                f"I={dims['I']} shared I={dims['I_shared']} Q4 block-32",
-                   "path": prim["path"], "layer_copies": prim["layer_copies"], "parallelism": "single GPU"},
+                   "path": prim["path"], "layer_copies": prim["layer_copies"], "parallelism": "single GPU",
+                   "residual": bool(args.residual)},
         "roofline": prim["roofline"],
         "cpu_baseline": cpu,
         "layer": {k: prim[k] for k in ("layer_hbm_frac", "layer_mfma_frac", "layer_algorithmic_bytes",

@@ -28,7 +28,8 @@
  *   w_j  = s[sel_j] / sum_j s[sel_j]    unbiased, normalised to 1
  *   h_e  = silu(W_g[e] x_t) * (W_u[e] x_t),  y_e = W_d[e] h_e
  *   y_t  = (sum_{j=0..k-1} w_j * y_{sel_j}) + y_shared(x_t)
- * Routed terms are summed in j order, then the shared expert is added.
+ * Routed terms are summed in j order, then the shared expert is added
+ * (moe_q4_forward_residual then adds a residual).
  * No float atomics anywhere: results are bitwise reproducible run to run.
  *
  * Conventions for every call
@@ -191,6 +192,19 @@ int moe_q4_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* 
                    const float* topk_w, const void* routing, size_t routing_bytes,
                    const moe_q4_weights* weights, float* y, void* scratch,
                    size_t scratch_bytes, uint32_t flags, void* stream);
+
+/* moe_q4_forward followed by a residual add, in one pass over y:
+ *   y_t = ((sum_j w_j * y_{sel_j}) + y_shared(x_t)) + residual_t
+ * (routed and shared summed first, then the residual: page thewafflehaus/FFAI
+ * pull request 72, "ffai_add3", whose order keeps the routed + shared sum
+ * independent of the residual's magnitude).  `residual` is a DEVICE array
+ * float32 [T][d], 16-byte aligned, never NULL; it may be `y` itself (each
+ * element is read before it is overwritten, by the same thread).  Every
+ * other argument, error and the behaviour are those of moe_q4_forward. */
+int moe_q4_forward_residual(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids,
+                            const float* topk_w, const void* routing, size_t routing_bytes,
+                            const moe_q4_weights* weights, const float* residual, float* y, void* scratch,
+                            size_t scratch_bytes, uint32_t flags, void* stream);
 
 /* Static string for a return code; never NULL. */
 const char* moe_strerror(int code);

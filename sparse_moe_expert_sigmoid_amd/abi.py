@@ -26,7 +26,7 @@ MOE_GEMV_FORCE_MAX_T = 64
 
 EXPORTED_SYMBOLS = (
     "moe_supports", "moe_path", "moe_routing_bytes", "moe_routing_layout_of", "moe_scratch_bytes",
-    "moe_route", "moe_build_descriptors", "moe_q4_forward", "moe_strerror",
+    "moe_route", "moe_build_descriptors", "moe_q4_forward", "moe_q4_forward_residual", "moe_strerror",
 )
 
 
@@ -96,6 +96,9 @@ def lib() -> ctypes.CDLL:
     L.moe_q4_forward.argtypes = [D, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, POINTER(_Weights), c_void_p,
                                  c_void_p, c_size_t, c_uint32, c_void_p]
     L.moe_q4_forward.restype = c_int
+    L.moe_q4_forward_residual.argtypes = [D, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, POINTER(_Weights),
+                                          c_void_p, c_void_p, c_void_p, c_size_t, c_uint32, c_void_p]
+    L.moe_q4_forward_residual.restype = c_int
     L.moe_strerror.argtypes = [c_int]
     L.moe_strerror.restype = c_char_p
     _lib = L
@@ -187,3 +190,13 @@ def moe_q4_forward(dims, x, topk_ids, topk_w, routing, weights, y, scratch, rout
                               _nbytes(routing, routing_bytes), ctypes.byref(ws), _ptr(y), _ptr(scratch),
                               _nbytes(scratch, scratch_bytes), flags, _stream(stream))
     return _done(rc, check, "moe_q4_forward")
+
+
+def moe_q4_forward_residual(dims, x, topk_ids, topk_w, routing, weights, residual, y, scratch, routing_bytes=None,
+                            scratch_bytes=None, flags: int = 0, stream=None, check: bool = True) -> int:
+    ws = weights if isinstance(weights, _Weights) else _weights(weights)
+    rc = lib().moe_q4_forward_residual(ctypes.byref(Dims.of(dims)), _ptr(x), _ptr(topk_ids), _ptr(topk_w),
+                                       _ptr(routing), _nbytes(routing, routing_bytes), ctypes.byref(ws),
+                                       _ptr(residual), _ptr(y), _ptr(scratch), _nbytes(scratch, scratch_bytes),
+                                       flags, _stream(stream))
+    return _done(rc, check, "moe_q4_forward_residual")

@@ -194,9 +194,10 @@ int moe_build_descriptors(const moe_dims* dims, const int32_t* topk_ids, void* r
                                   static_cast<hipStream_t>(stream)));
 }
 
-int moe_q4_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
-                   const void* routing, size_t routing_bytes, const moe_q4_weights* w, float* y, void* scratch,
-                   size_t scratch_bytes, uint32_t flags, void* stream) {
+namespace {
+int forward_impl(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
+                 const void* routing, size_t routing_bytes, const moe_q4_weights* w, const float* residual,
+                 float* y, void* scratch, size_t scratch_bytes, uint32_t flags, void* stream) {
   int rc = check_dims(dims, flags);
   if (rc) return rc;
   const int path = choose_path(dims, flags);
@@ -223,7 +224,7 @@ int moe_q4_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* 
     _Float16* h_r = reinterpret_cast<_Float16*>(sb + S.h_r);
     _Float16* h_s = reinterpret_cast<_Float16*>(sb + S.h_s);
     if (moe::launch_gemv_gateup(s, x_bf16, topk_ids, w13, s13, h_r, h_s, st) != hipSuccess) return MOE_EHIP;
-    return hip_rc(moe::launch_gemv_down_combine(s, topk_ids, topk_w, w2, s2, h_r, h_s, y, st));
+    return hip_rc(moe::launch_gemv_down_combine(s, topk_ids, topk_w, w2, s2, h_r, h_s, residual, y, st));
   }
   const moe::Routing r = routing_ptrs(const_cast<void*>(routing), L);
   moe::GroupedOut o;
@@ -234,7 +235,27 @@ int moe_q4_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* 
   o.y_s = reinterpret_cast<_Float16*>(sb + S.y_s);
   if (moe::launch_grouped_gateup(s, x_bf16, r, w13, s13, o, flags, st) != hipSuccess) return MOE_EHIP;
   if (moe::launch_grouped_down(s, r, w2, s2, o, flags, st) != hipSuccess) return MOE_EHIP;
-  return hip_rc(moe::launch_combine(s, topk_w, r, o, y, st));
+  return hip_rc(moe::launch_combine(s, topk_w, r, o, residual, y, st));
+}
+}  // namespace
+
+int moe_q4_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
+                   const void* routing, size_t routing_bytes, const moe_q4_weights* w, float* y, void* scratch,
+                   size_t scratch_bytes, uint32_t flags, void* stream) {
+  return forward_impl(dims, x_bf16, topk_ids, topk_w, routing, routing_bytes, w, nullptr, y, scratch, scratch_bytes,
+                      flags, stream);
+}
+
+int moe_q4_forward_residual(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids,
+                            const float* topk_w, const void* routing, size_t routing_bytes,
+                            const moe_q4_weights* w, const float* residual, float* y, void* scratch,
+                            size_t scratch_bytes, uint32_t flags, void* stream) {
+  const int rc = check_dims(dims, flags);
+  if (rc) return rc;
+  if (!residual) return MOE_EINVAL;
+  if (!aligned(residual, 16)) return MOE_EALIGN;
+  return forward_impl(dims, x_bf16, topk_ids, topk_w, routing, routing_bytes, w, residual, y, scratch,
+                      scratch_bytes, flags, stream);
 }
 
 const char* moe_strerror(int code) {

@@ -192,7 +192,8 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
 __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __restrict__ ids,
                                                             const float* __restrict__ topk_w, Q4 w2, Q4 s2,
                                                             const _Float16* __restrict__ h_r,
-                                                            const _Float16* __restrict__ h_s, float* __restrict__ y,
+                                                            const _Float16* __restrict__ h_s, const float* residual,
+                                                            float* y,
                                                             int T, int d, int k, int I, int Is, uint32_t mask_lo,
                                                             uint32_t mask_hi, uint32_t magic) {
   // per wavefront: the slot's h, per block 16 dwords of fp16 pairs (the 16x pairs pre-divided by 16)
@@ -291,7 +292,9 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
     const int r = n0 + threadIdx.x;
     float acc = 0.f;
     for (int j = 0; j < k; ++j) acc = fmaf(topk_w[(size_t)t * k + j], part[j][threadIdx.x], acc);
-    y[(size_t)t * d + r] = acc + part[k][threadIdx.x];
+    float v = acc + part[k][threadIdx.x];
+    if (residual) v += residual[(size_t)t * d + r];  // after routed + shared; residual may be y itself
+    y[(size_t)t * d + r] = v;
   }
 }
 
@@ -305,10 +308,11 @@ hipError_t launch_gemv_gateup(const Shape& s, const uint16_t* x, const int32_t* 
 }
 
 hipError_t launch_gemv_down_combine(const Shape& s, const int32_t* topk_ids, const float* topk_w, Q4 w2, Q4 s2,
-                                    const _Float16* h_r, const _Float16* h_s, float* y, hipStream_t st) {
+                                    const _Float16* h_r, const _Float16* h_s, const float* residual, float* y,
+                                    hipStream_t st) {
   const int nw = (s.k + 1) < 16 ? (s.k + 1) : 16;
   dim3 grid(s.d / 16, s.T);
-  hipLaunchKernelGGL(k_gemv_down_combine, grid, dim3(64 * nw), 0, st, topk_ids, topk_w, w2, s2, h_r, h_s, y, s.T, s.d,
+  hipLaunchKernelGGL(k_gemv_down_combine, grid, dim3(64 * nw), 0, st, topk_ids, topk_w, w2, s2, h_r, h_s, residual, y, s.T, s.d,
                      s.k, s.I, s.Is, 0x000F000Fu, 0x00F000F0u, 0x64006400u);
   return hipGetLastError();
 }

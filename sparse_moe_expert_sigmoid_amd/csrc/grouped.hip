@@ -499,7 +499,7 @@ __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x
 // Per-pair and shared outputs arrive in fp16; every thread sums 8 columns in fp32.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ topk_w, const int* __restrict__ pair_pos,
                                                  const _Float16* __restrict__ y_r, const _Float16* __restrict__ y_s,
-                                                 float* __restrict__ y, int d, int k) {
+                                                 const float* residual, float* y, int d, int k) {
   const int per_row = (d + 2047) / 2048;
   const int t = blockIdx.x / per_row;
   const int col = ((blockIdx.x % per_row) * 256 + threadIdx.x) * 8;
@@ -525,6 +525,12 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ topk_
     const half2v h0 = as_half2(sv[0]), h1 = as_half2(sv[1]), h2 = as_half2(sv[2]), h3 = as_half2(sv[3]);
     o0 = make_float4(acc[0] + (float)h0[0], acc[1] + (float)h0[1], acc[2] + (float)h1[0], acc[3] + (float)h1[1]);
     o1 = make_float4(acc[4] + (float)h2[0], acc[5] + (float)h2[1], acc[6] + (float)h3[0], acc[7] + (float)h3[1]);
+  }
+  if (residual) {  // after routed + shared; residual may be y itself (each thread reads what it then writes)
+    const float4* ro = reinterpret_cast<const float4*>(residual + (size_t)t * d + col);
+    const float4 r0 = ro[0], r1 = ro[1];
+    o0 = make_float4(o0.x + r0.x, o0.y + r0.y, o0.z + r0.z, o0.w + r0.w);
+    o1 = make_float4(o1.x + r1.x, o1.y + r1.y, o1.z + r1.z, o1.w + r1.w);
   }
   float4* yo = reinterpret_cast<float4*>(y + (size_t)t * d + col);
   yo[0] = o0;
@@ -591,10 +597,11 @@ hipError_t launch_grouped_down(const Shape& s, const Routing& r, Q4 w2, Q4 s2, c
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const Shape& s, const float* topk_w, const Routing& r, const GroupedOut& o, float* y,
-                          hipStream_t st) {
+hipError_t launch_combine(const Shape& s, const float* topk_w, const Routing& r, const GroupedOut& o,
+                          const float* residual, float* y, hipStream_t st) {
   dim3 grid(((s.d + 2047) / 2048) * s.T);
-  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, st, topk_w, r.pair_pos, o.y_pair, o.y_s, y, s.d, s.k);
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, st, topk_w, r.pair_pos, o.y_pair, o.y_s, residual, y, s.d,
+                     s.k);
   return hipGetLastError();
 }
 

@@ -76,10 +76,15 @@ class Workspace:
         return self.routing[off:off + nbytes].view(dtype)
 
 
-def layer_call(x: torch.Tensor, w: DeviceWeights, ws: Workspace, stream=None) -> torch.Tensor:
-    """Enqueue route, build and forward for tokens x (bf16 bits as int16 [T][d]); returns ws.y."""
+def layer_call(x: torch.Tensor, w: DeviceWeights, ws: Workspace, stream=None, residual=None) -> torch.Tensor:
+    """Enqueue route, build and forward for tokens x (bf16 bits as int16 [T][d]); returns ws.y.
+    With `residual` (fp32 [T][d] on the device, may be ws.y) the forward adds it after routed + shared."""
     dims, f = ws.dims, ws.flags
     abi.moe_route(dims, x, w["w_router"], w["bias"], ws.topk_ids, ws.topk_w, ws.routing, flags=f, stream=stream)
     abi.moe_build_descriptors(dims, ws.topk_ids, ws.routing, flags=f, stream=stream)
-    abi.moe_q4_forward(dims, x, ws.topk_ids, ws.topk_w, ws.routing, w, ws.y, ws.scratch, flags=f, stream=stream)
+    if residual is None:
+        abi.moe_q4_forward(dims, x, ws.topk_ids, ws.topk_w, ws.routing, w, ws.y, ws.scratch, flags=f, stream=stream)
+    else:
+        abi.moe_q4_forward_residual(dims, x, ws.topk_ids, ws.topk_w, ws.routing, w, residual, ws.y, ws.scratch,
+                                    flags=f, stream=stream)
     return ws.y

@@ -41,7 +41,7 @@ def routing_arrays(ws: Workspace) -> dict:
     return out
 
 
-def check_parity(inp: dict, ws: Workspace, tokens=None, label: str = "") -> dict:
+def check_parity(inp: dict, ws: Workspace, tokens=None, label: str = "", residual=None) -> dict:
     """Parity rule: selection sets exact where margin > MARGIN; else the oracle is re-run on the GPU's
     selection; then max-abs and relative-L2 bounds over all checked tokens."""
     dims = inp["dims"]
@@ -49,13 +49,13 @@ def check_parity(inp: dict, ws: Workspace, tokens=None, label: str = "") -> dict
     ids_gpu = ws.topk_ids.cpu().numpy()[tokens]
     w_gpu = ws.topk_w.cpu().numpy()[tokens]
     y_gpu = ws.y.cpu().numpy()[tokens].astype(np.float64)
-    ref = oracle.forward(inp, tokens=tokens)
+    ref = oracle.forward(inp, tokens=tokens, residual=residual)
     close = ~(ref["margin"] > MARGIN)
     for i in np.nonzero(~close)[0]:
         assert sorted(ids_gpu[i]) == sorted(ref["ids"][i]), (label, int(tokens[i]), ids_gpu[i], ref["ids"][i])
     if close.any():
         ov = {int(tokens[i]): ids_gpu[i] for i in np.nonzero(close)[0]}
-        ref = oracle.forward(inp, tokens=tokens, ids_override=ov)
+        ref = oracle.forward(inp, tokens=tokens, ids_override=ov, residual=residual)
     # weights: compare by expert id
     for i in range(len(tokens)):
         ref_w = dict(zip(ref["ids"][i].tolist(), ref["w"][i].tolist()))

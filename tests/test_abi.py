@@ -159,6 +159,24 @@ def test_forward_validation():
     assert forward(flags=0, routing=0, scratch=0) == abi.MOE_EINVAL  # scratch is still required
 
 
+def forward_residual(dims=TINY, flags=abi.MOE_FLAG_FORCE_GROUPED, **kw):
+    args = dict(x=FAKE, topk_ids=FAKE, topk_w=FAKE, routing=FAKE, residual=FAKE, y=FAKE, scratch=FAKE,
+                routing_bytes=R, scratch_bytes=1 << 30)
+    args.update(kw)
+    return moe.moe_q4_forward_residual(dims, weights=dict(WEIGHTS), **args, flags=flags, stream=0, check=False)
+
+
+def test_forward_residual_validation():
+    assert forward_residual(residual=0) == abi.MOE_EINVAL
+    assert forward_residual(residual=FAKE + 4) == abi.MOE_EALIGN
+    assert forward_residual(dims=d(d=40)) == abi.MOE_EUNSUPPORTED  # shape errors come first
+    # every other argument is checked as for moe_q4_forward
+    for name in ("x", "topk_ids", "topk_w", "y", "scratch", "routing"):
+        assert forward_residual(**{name: 0}) == abi.MOE_EINVAL, name
+    assert forward_residual(y=FAKE + 4) == abi.MOE_EALIGN
+    assert forward_residual(routing_bytes=100) == abi.MOE_ENOSPACE
+
+
 def test_header_documents_every_code():
     text = open(HEADER).read()
     for name, value in [("MOE_OK", 0), ("MOE_EINVAL", -1), ("MOE_EALIGN", -2), ("MOE_EUNSUPPORTED", -3),

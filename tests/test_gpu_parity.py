@@ -54,6 +54,28 @@ def test_tiny_paths_agree_and_are_deterministic():
     assert rel < 5e-3
 
 
+@pytest.mark.parametrize("flags", [GROUPED, GEMV], ids=["grouped", "gemv"])
+@pytest.mark.parametrize("in_place", [False, True], ids=["separate", "in_place"])
+def test_residual_fused_output(flags, in_place):
+    """moe_q4_forward_residual: parity with the oracle's (routed + shared) + residual, and bit for bit the
+    plain forward's output plus the residual in fp32 (the add comes last); the residual may be y itself."""
+    dims, bias = SMALL["ragged"]
+    say(f"[case] residual flags={flags} in_place={in_place} dims={dims}")
+    inp = synth.make_inputs(dims, seed=121, bias=bias)
+    res = (np.random.default_rng(122).standard_normal((dims.T, dims.d)) * 3).astype(np.float32)
+    w = DeviceWeights.upload(inp)
+    x = to_device(inp["x"], "cuda")
+    plain, _ = run(inp, flags, w, x)
+    ws = Workspace(dims, flags)
+    r_dev = torch.from_numpy(res).cuda()
+    if in_place:
+        ws.y.copy_(r_dev)
+    layer_call(x, w, ws, residual=ws.y if in_place else r_dev)
+    torch.cuda.synchronize()
+    check_parity(inp, ws, label=f"residual/{flags}/{in_place}", residual=res)
+    assert torch.equal(ws.y, plain.y + r_dev)
+
+
 @pytest.mark.parametrize("flags", [GROUPED | abi.MOE_FLAG_ID_ORDER, GROUPED | abi.MOE_FLAG_NO_BANDING,
                                    GROUPED | abi.MOE_FLAG_ID_ORDER | abi.MOE_FLAG_NO_BANDING,
                                    GROUPED | abi.MOE_FLAG_BAND_MAJOR])
