@@ -507,19 +507,30 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ topk_
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int pp = pair_pos[(size_t)t * k + j];
-    if (pp < 0) continue;
-    const float w = topk_w[(size_t)t * k + j];
-    const u32x4 v = ld16(y_r + (size_t)pp * d + col);
+  const u32x4 sv = ld16(y_s + (size_t)t * d + col);
+  // up to kCombineBatch pair rows in flight at once; slots past k (and pairs without a row) read a real
+  // row of y_pair and weigh 0, so the sum over j stays in slot order and no load is conditional
+  constexpr int kCombineBatch = 16;
+  for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+    u32x4 v[kCombineBatch];
+    float wj[kCombineBatch];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const half2v h = as_half2(v[m]);
-      acc[2 * m] = fmaf(w, (float)h[0], acc[2 * m]);
-      acc[2 * m + 1] = fmaf(w, (float)h[1], acc[2 * m + 1]);
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const int j = min(j0 + u, k - 1);
+      const int pp = pair_pos[(size_t)t * k + j];
+      wj[u] = (j0 + u < k && pp >= 0) ? topk_w[(size_t)t * k + j] : 0.f;
+      v[u] = ld16(y_r + (size_t)(pp < 0 ? 0 : pp) * d + col);
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const half2v h = as_half2(v[u][m]);
+        acc[2 * m] = fmaf(wj[u], (float)h[0], acc[2 * m]);
+        acc[2 * m + 1] = fmaf(wj[u], (float)h[1], acc[2 * m + 1]);
+      }
     }
   }
-  const u32x4 sv = ld16(y_s + (size_t)t * d + col);
   float4 o0, o1;
   {
     const half2v h0 = as_half2(sv[0]), h1 = as_half2(sv[1]), h2 = as_half2(sv[2]), h3 = as_half2(sv[3]);
