@@ -3,7 +3,7 @@
 The selection rule (sigmoid scores, bias added for selection only, the k largest keys listed by
 descending key, equal keys to the lower expert id, weights = unbiased scores normalised to 1) is
 the oracle's select_experts / routing_weights.  Both router forms are covered: the GEMV router
-(one logit array) and the MFMA router (four partial logit arrays), and every key-register count
+(one logit array) and the MFMA router (eight partial logit arrays), and every key-register count
 of the top-k (E up to 1024, k up to 32).
 """
 import numpy as np
