@@ -484,11 +484,11 @@ def main():
     if args.secondary and args.secondary != "none" and args.secondary != args.workload:
         n = max(20, args.steps // 40)
         sec = run_workload(args.secondary, n, max(4, n // 10), torch, hip, abi, layer, synth, residual=args.residual)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(prim["_inp0"])
     rl = prim["roofline"]
-    if rl["unit"] == "GB/s":
+    if rl["unit"] == "GB/s":  # measured right after the GPU work, before the host-only oracle timing
         ceil = copy_ceiling(torch, [rl["algorithmic_bytes_per_launch"]])
         rl["copy_ceiling"] = next(iter(ceil.values())) | {"bytes": int(next(iter(ceil)))}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(prim["_inp0"])
     dims = prim["dims"]
     out = {
         "metric": METRIC,
