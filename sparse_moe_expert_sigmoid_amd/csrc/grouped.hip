@@ -24,8 +24,9 @@
 // rows x 128 columns as fp16 in LDS (double-buffered); each wavefront owns
 // four 16-column weight slices, loads one 16-byte Q4 block per slice and
 // lane, dequantises it in registers straight into the B-operand layout of
-// v_mfma_f32_16x16x32_f16 and multiplies it against every 16-row slice of
-// the activation tile.  K is permuted consistently: MFMA k-lane group G of
+// v_mfma_f32_16x16x32_f16 (as weight / 16, undone in the epilogue) and
+// multiplies it against every 16-row slice of the activation tile, whose
+// fragments are read from LDS two slices ahead.  K is permuted consistently: MFMA k-lane group G of
 // step s holds elements 32G + 8s .. 32G + 8s + 7 of the 128-wide chunk, which
 // are exactly dword s of Q4 block G.
 #include <type_traits>
@@ -148,36 +149,42 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
   // fragment of each 16-row slice is read from LDS just before its four MFMAs (one slice ahead), and
   // the four weight fragments of the next K-step are dequantised between the MFMAs.  The loop body has
   // no branches around the MFMAs, so the accumulators keep their registers across iterations.
-  auto compute = [&](int buf, const u32x4* q, const half2v* d2, bool large) __attribute__((always_inline)) {
+  auto compute = [&](int buf, const u32x4* q, const half2v* d2, bool general) __attribute__((always_inline)) {
     const char* At = As + buf * kTileBytes;
     SmallScale ss[4];
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) ss[ns] = small_scale(d2[ns]);
-    // small-scale form; redone in the general form when a scale of this iteration is too large for it
-    // (`large` is uniform, so this is a scalar branch that is normally not taken)
+    // common form; redone in the general form when a scale of this iteration is outside its range
+    // (`general` is uniform, so this is a scalar branch that is normally not taken)
     auto deq = [&](uint32_t w, int ns) __attribute__((always_inline)) {
       half8 r = dequant8_small(w, ss[ns]);
-      if (__builtin_expect(large, 0)) r = dequant8_general(w, d2[ns], c.dq_mask, c.dq_magic);
+      if (__builtin_expect(general, 0)) r = dequant8_general(w, d2[ns], c.dq_mask, c.dq_magic);
       return r;
     };
     half8 b_cur[4];
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) b_cur[ns] = deq(q[ns][0], ns);
+    // activation fragments are read two 16-row slices ahead, across K-step boundaries
+    constexpr int NI = 4 * NMT;
+    auto aread = [&](int idx) __attribute__((always_inline)) {
+      return *reinterpret_cast<const half8*>(At + c.rdo + 16 * (c.gx ^ (idx / NMT)) + (idx % NMT) * 16 * kRowBytes);
+    };
+    half8 a0 = aread(0), a1 = aread(NI > 1 ? 1 : 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const char* Ar = At + c.rdo + 16 * (c.gx ^ s);
       half8 b_nxt[4];
-      half8 a_cur = *reinterpret_cast<const half8*>(Ar);
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
-        half8 a_nxt;
-        if (mt + 1 < NMT) a_nxt = *reinterpret_cast<const half8*>(Ar + (mt + 1) * 16 * kRowBytes);
+        const int idx = s * NMT + mt;
+        half8 a2;
+        if (idx + 2 < NI) a2 = aread(idx + 2);
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns)
           // weights as the A operand: the tile comes out transposed (see the epilogue)
-          acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b_cur[ns], a_cur, acc[mt][ns], 0, 0, 0);
+          acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b_cur[ns], a0, acc[mt][ns], 0, 0, 0);
         if (s < 3 && mt < 4) b_nxt[mt] = deq(q[mt][s + 1], mt);
-        if (mt + 1 < NMT) a_cur = a_nxt;
+        a0 = a1;
+        if (idx + 2 < NI) a1 = a2;
       }
       if (s < 3) {
 #pragma unroll
@@ -188,7 +195,7 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
     }
   };
   // Scales of iteration `it` (the K tail's blocks weigh zero), and whether any scale the wavefront uses
-  // in this iteration is too large for the small-scale form.
+  // in this iteration is outside the range of the common dequantisation form.
   auto run_step = [&](int buf, const u32x4* q, const uint32_t* sc_in, int it) __attribute__((always_inline)) {
     half2v d2[4];
     const bool tail = c.ktail && it == c.nit - 1;  // uniform
@@ -252,7 +259,8 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
   }
 
   // ---- epilogue.  With the weights as the A operand, lane (n, G) holds, for activation row
-  // mt*16 + n, the four consecutive output columns 4G .. 4G+3 of each 16-column slice.
+  // mt*16 + n, the four consecutive output columns 4G .. 4G+3 of each 16-column slice, divided by 16
+  // (the dequantised weights are weight / 16; the products and sums scale exactly).
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
     const int row = mt * 16 + c.n;
@@ -268,7 +276,7 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
           float hv[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const float gv = acc[mt][xh][2 * j + e], uv = acc[mt][2 + xh][2 * j + e];
+            const float gv = 16.f * acc[mt][xh][2 * j + e], uv = 16.f * acc[mt][2 + xh][2 * j + e];
             hv[e] = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;
           }
           h[j] = half2v{(_Float16)hv[0], (_Float16)hv[1]};
@@ -301,8 +309,8 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
       const int row = mt * 16 + c.n;
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns) {
-        const half2v p0 = {(_Float16)acc[mt][ns][0], (_Float16)acc[mt][ns][1]};
-        const half2v p1 = {(_Float16)acc[mt][ns][2], (_Float16)acc[mt][ns][3]};
+        const half2v p0 = {(_Float16)(16.f * acc[mt][ns][0]), (_Float16)(16.f * acc[mt][ns][1])};
+        const half2v p1 = {(_Float16)(16.f * acc[mt][ns][2]), (_Float16)(16.f * acc[mt][ns][3])};
         const int chunk = 8 * c.wave + 2 * ns + (c.G >> 1);
         *reinterpret_cast<uint2*>(As + row * (kDownBandCols * 2) + ((chunk ^ (row & 31)) * 16) + 8 * (c.G & 1)) =
             uint2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};

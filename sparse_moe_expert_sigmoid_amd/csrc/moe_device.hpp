@@ -56,48 +56,56 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask_s, uint32_t
 
 // ---------------------------------------------------------------- dequant to fp16 (MFMA operand)
 // Eight codes of one dword (element m in bits 4m..4m+3) -> eight fp16
-// weights (q - 8) * d, in the pair order (e0,e4) (e1,e5) (e2,e6) (e3,e7):
-// each pair needs one mask (after at most one shift).  The activation
-// operands are stored in the same order within every group of 8 (see
-// perm_slot).  Both forms below round (q - 8) * d once, so they give the
-// same bits.
+// weights (q - 8) * d / 16, in the pair order (e0,e4) (e1,e5) (e2,e6)
+// (e3,e7): each pair needs one mask (after at most one shift).  The
+// activation operands are stored in the same order within every group of 8
+// (see perm_slot).  The factor 1/16 keeps the common form at one shift per
+// dword; the GEMM multiplies its fp32 accumulators by 16 (exact) before use.
+// Both forms below give round((q - 8) * d) / 16, the same bits, while that
+// value is an fp16 normal (always, for 2^-10 <= |d| < 2^-4).
 //
 // General form: the pair's nibbles placed in the low mantissa of 1024.0
 // (v_and_or_b32 with 0x64006400) are exactly 1024 + q; minus 1032 (exact),
-// times d (one rounding).
+// times d (one rounding), times 1/16 (exact unless the result is subnormal).
 __device__ __forceinline__ half8 dequant8_general(uint32_t w, half2v d2, uint32_t M, uint32_t C) {
   // M = 0x000F000F (SGPR), C = 0x64006400 (VGPR): p_j = (1024 + e_j, 1024 + e_{j+4}) as fp16 bits
   const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const uint32_t t = w >> 4;
   const uint32_t p0 = and_or(w, M, C), p1 = and_or(t, M, C), p2 = and_or(w >> 8, M, C), p3 = and_or(t >> 8, M, C);
-  const half2v r0 = (__builtin_bit_cast(half2v, p0) - off) * d2;
-  const half2v r1 = (__builtin_bit_cast(half2v, p1) - off) * d2;
-  const half2v r2 = (__builtin_bit_cast(half2v, p2) - off) * d2;
-  const half2v r3 = (__builtin_bit_cast(half2v, p3) - off) * d2;
+  const half2v r0 = ((__builtin_bit_cast(half2v, p0) - off) * d2) * sixteenth;
+  const half2v r1 = ((__builtin_bit_cast(half2v, p1) - off) * d2) * sixteenth;
+  const half2v r2 = ((__builtin_bit_cast(half2v, p2) - off) * d2) * sixteenth;
+  const half2v r3 = ((__builtin_bit_cast(half2v, p3) - off) * d2) * sixteenth;
   return half8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 
-// Small-scale form, for |d| < 2^-4: a nibble masked into bits 4..7 of an
-// fp16 with zero exponent is the subnormal q * 2^-20 (exact), and one packed
-// FMA with (d * 2^20, -8d) -- both exact, d * 2^20 <= 65504 -- gives
-// (q - 8) * d with a single rounding.  Three shifts, four ands, four FMAs.
+// Common form, for 2^-10 <= |d| < 2^-4 (and d = 0): a pair of nibbles masked
+// in place into an fp16 with zero exponent is a pair of subnormals, exactly
+// q * 2^-24 (bits 0..3 of each half) or q * 2^-20 (bits 4..7).  One packed
+// FMA with (d * 2^20, -d/2) or (d * 2^16, -d/2) -- all exact, d * 2^20 <=
+// 65504 -- gives (q - 8) * d / 16 with a single rounding, an fp16 normal for
+// q != 8.  One shift, four ands, four FMAs per eight weights.
 struct SmallScale {
-  half2v mul, add;  // (d * 2^20, d * 2^20), (-8d, -8d)
+  half2v mul_lo, mul_hi, add;  // (d * 2^20, ..), (d * 2^16, ..), (-d/2, ..)
 };
 __device__ __forceinline__ SmallScale small_scale(half2v d2) {
-  const half2v k = {(_Float16)1024.0f, (_Float16)1024.0f};
-  return SmallScale{d2 * k * k, d2 * half2v{(_Float16)-8.0f, (_Float16)-8.0f}};
+  const half2v k = {(_Float16)256.0f, (_Float16)256.0f};
+  const half2v hi = d2 * k * k;
+  return SmallScale{hi * half2v{(_Float16)16.0f, (_Float16)16.0f}, hi, d2 * half2v{(_Float16)-0.5f, (_Float16)-0.5f}};
 }
-// |d| < 2^-4 (also false for inf and NaN)
-__device__ __forceinline__ bool small_scale_ok(uint32_t d_bits) { return (d_bits & 0x7FFFu) < 0x2C00u; }
+// 2^-10 <= |d| < 2^-4, or d = 0 (false for inf and NaN)
+__device__ __forceinline__ bool small_scale_ok(uint32_t d_bits) {
+  const uint32_t m = d_bits & 0x7FFFu;
+  return m - 0x1400u < 0x1800u || m == 0u;
+}
 
 __device__ __forceinline__ half8 dequant8_small(uint32_t w, const SmallScale& s) {
-  const uint32_t M = 0x00F000F0u;
-  const uint32_t p0 = (w << 4) & M, p1 = w & M, p2 = (w >> 4) & M, p3 = (w >> 8) & M;
-  const half2v r0 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p0), s.mul, s.add);
-  const half2v r1 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p1), s.mul, s.add);
-  const half2v r2 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p2), s.mul, s.add);
-  const half2v r3 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, p3), s.mul, s.add);
+  const uint32_t w8 = w >> 8;
+  const half2v r0 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, w & 0x000F000Fu), s.mul_lo, s.add);
+  const half2v r1 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, w & 0x00F000F0u), s.mul_hi, s.add);
+  const half2v r2 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, w8 & 0x000F000Fu), s.mul_lo, s.add);
+  const half2v r3 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, w8 & 0x00F000F0u), s.mul_hi, s.add);
   return half8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 
