@@ -75,14 +75,13 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
   const int ntile = (nkb + 3) / 4;
   const int tw0 = (ntile * wave) / 4, tw1 = (ntile * (wave + 1)) / 4;  // this wavefront's tiles
   const int b0 = 4 * tw0;                                               // its first block
-  const int nbw = min(4 * tw1, nkb) - b0;                               // its valid blocks (<= 64)
   const size_t grp_bytes = (size_t)nkb * 256;  // one 16-row group of codes
   const uint8_t* qg = qs + (size_t)(i0 >> 4) * grp_bytes;          // gate rows i0 .. i0+15
   const uint8_t* qu = qs + (size_t)((Iw + i0) >> 4) * grp_bytes;   // up rows Iw+i0 ..
   const uint16_t* sg = sc + (size_t)(i0 >> 4) * nkb * 16;
   const uint16_t* su = sc + (size_t)((Iw + i0) >> 4) * nkb * 16;
-  // stage x: lane l takes block b0 + l (clamped; never read when past nbw; a quarter of K holds at
-  // most 64 blocks as d <= 8192)
+  // stage x: lane l takes block b0 + l (clamped; blocks past the wavefront's last one are never read;
+  // a quarter of K holds at most 64 blocks as d <= 8192)
   {
     const int bl = min(b0 + lane, nkb - 1);
     const uint16_t* xb = x + (size_t)t * d + 32 * bl;

@@ -72,3 +72,19 @@ def test_slot_order_matches_oracle(E, k, path):
         np.testing.assert_allclose(w[t], ref_w, rtol=0, atol=W_ABS)
     say(f"[route] E={E} k={k} {path}: order checked on {ordered}/{dims.T} tokens")
     assert ordered > 0 or k == 1
+
+
+@pytest.mark.parametrize("T", [4096, 4100])
+def test_large_t_router_tile(T):
+    """T >= 4096 takes the 128-token router tile (4096: whole tiles; 4100: a ragged last tile of 4 tokens)."""
+    dims = synth.Dims(T=T, d=512, E=256, k=10, I=32, I_shared=32)
+    inp = synth.make_inputs(dims, seed=T, weights=False)
+    say(f"[case] large-T router T={T}")
+    ids, w = route(inp, abi.MOE_FLAG_FORCE_GROUPED)
+    s = oracle.sigmoid(oracle.router_logits(inp["x"], inp["w_router"]))
+    ref_ids, margin = oracle.select_experts(s, inp["bias"], dims.k)
+    clear = margin > MARGIN
+    assert clear.mean() > 0.9
+    np.testing.assert_array_equal(np.sort(ids[clear], 1), np.sort(ref_ids[clear], 1))
+    ref_w = oracle.routing_weights(s, ids)
+    np.testing.assert_allclose(w, ref_w, rtol=0, atol=W_ABS)
