@@ -48,6 +48,7 @@ __all__ = [
     "bf16_bits_to_f64", "fp16_bits_to_f64", "dequant_q4",
     "router_logits", "sigmoid", "select_experts", "routing_weights",
     "swiglu_mlp", "forward", "routing_build", "group_order",
+    "f64_to_bf16_bits", "decode_chain",
 ]
 
 
@@ -57,6 +58,40 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns (uint16) -> float64.  A bf16 value is the top half of a float32."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """float64 -> bf16 bit patterns (uint16), rounding to nearest with ties to even.
+
+    bf16 is float32 with the low 16 bits dropped: 8 exponent bits and 7
+    fraction bits.  The value is rounded once, straight from float64, by
+    comparing it with the two neighbouring bf16 values.  NaN -> 0x7FC0.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    flat_v, flat_o = v.ravel(), out.ravel()
+    for i, x in enumerate(flat_v):
+        if np.isnan(x):
+            flat_o[i] = 0x7FC0
+            continue
+        # candidates: truncate the float32 nearest below |x|, and the next bf16 up
+        lo = int(np.array(np.float32(min(abs(x), 3.4028234663852886e38))).view(np.uint32)) >> 16
+        while lo > 0 and bf16_bits_to_f64(np.uint16(lo))[()] > abs(x):
+            lo -= 1
+        hi = lo + 1
+        vlo = bf16_bits_to_f64(np.uint16(lo))[()]
+        # above the largest finite bf16 the next step up is 2^128, which is infinity
+        vhi = bf16_bits_to_f64(np.uint16(hi))[()] if hi < 0x7F80 else 2.0 ** 128
+        if abs(x) == np.inf:
+            m = 0x7F80
+        elif abs(x) - vlo < vhi - abs(x):
+            m = lo
+        elif abs(x) - vlo > vhi - abs(x):
+            m = hi
+        else:
+            m = lo if lo % 2 == 0 else hi
+        flat_o[i] = m | (0x8000 if np.signbit(x) else 0)
+    return out
 
 
 def fp16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -213,3 +248,30 @@ def group_order(counts: np.ndarray, T: int) -> np.ndarray:
     """
     c = np.concatenate([np.asarray(counts, dtype=np.int64), [T]])
     return np.array(sorted(range(c.size), key=lambda g: (-c[g], g)), dtype=np.int32)
+
+
+# ----------------------------------------------------------------------------- multi-layer decode
+
+def decode_chain(layers: list, h0) -> dict:
+    """A residual stream through a stack of MoE layers, one after another.
+
+    [decode] runs single-stream decode as one captured graph over every layer
+    with a persistent workspace (the LagunaDecodeCtx of "feat(laguna):
+    Laguna-S-2.1 decode on the CUDA engine"); between two MoE layers of the
+    model sit attention and norms, which are out of scope here, so each layer
+    takes its input straight from the stream:
+        x = bf16(h)                (round to nearest even; the layer's input is bf16)
+        h = (routed + shared)(x) + h
+    the residual added after the routed and shared sum ([nemotron], "ffai_add3").
+    layers: input dicts as for forward() (their "x" is ignored); h0: [T,d].
+    Returns dict(h [T,d] fp64, margins [L,T]: each layer's selection margin).
+    """
+    h = np.asarray(h0, dtype=np.float64)
+    margins = []
+    for inp in layers:
+        lay = dict(inp)
+        lay["x"] = f64_to_bf16_bits(h)
+        out = forward(lay, residual=h)
+        h = out["y"]
+        margins.append(out["margin"])
+    return dict(h=h, margins=np.array(margins))

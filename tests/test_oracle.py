@@ -424,3 +424,74 @@ def test_generator_zipf_and_outliers():
     assert b[0] == pytest.approx(1.0 / sum(i ** -1.2 for i in range(1, 257)), rel=1e-6)
     o = synth.make_inputs(synth.Dims(T=8192, d=32, E=4, k=1, I=32, I_shared=32), outlier_frac=0.01, weights=False)
     assert len(o["outlier_rows"]) == 82
+
+
+# ----------------------------------------------------------------------------- multi-layer decode chain
+
+def bf16_carry(f32: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even float32 -> bf16 by the bit-carry rule on the float32 pattern (written here
+    from the format definition: add 0x7FFF plus the lowest kept bit, keep the top 16 bits)."""
+    u = np.asarray(f32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_bf16_rounding_matches_the_carry_rule_on_float32_inputs():
+    rng = np.random.default_rng(21)
+    f = (rng.standard_normal(20000) * np.exp(rng.uniform(-60, 60, 20000))).astype(np.float32)
+    f[:4] = [0.0, -0.0, 1.0, -2.5]
+    np.testing.assert_array_equal(oracle.f64_to_bf16_bits(f.astype(np.float64)), bf16_carry(f))
+
+
+def test_bf16_rounding_ties_and_ends():
+    # bf16 spacing at 1 is 2^-7: halfway points go to the even neighbour
+    vals = [1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 2.0 ** -133 * 1.5, 3.5e38, -1e39]
+    want = [0x3F80, 0x3F82, 0xBF80, 0x0002, 0x7F80, 0xFF80]
+    np.testing.assert_array_equal(oracle.f64_to_bf16_bits(np.array(vals)), np.array(want, dtype=np.uint16))
+    assert oracle.f64_to_bf16_bits(np.array([np.nan]))[0] == 0x7FC0
+
+
+def _stream(T, d, seed):
+    return np.random.default_rng(seed).standard_normal((T, d)).astype(np.float32) * 2
+
+
+def test_decode_chain_with_zero_experts_keeps_the_stream():
+    """Every code 8 in every layer: each layer adds exactly zero, so the stream passes through unchanged."""
+    dims = synth.Dims(T=4, d=64, E=6, k=2, I=32, I_shared=64)
+    layers = []
+    for s in range(3):
+        inp = synth.make_inputs(dims, seed=30 + s)
+        for key in ("w13_qs", "w2_qs", "s13_qs", "s2_qs"):
+            inp[key][:] = 0x88
+        layers.append(inp)
+    h0 = _stream(4, 64, 31)
+    out = oracle.decode_chain(layers, h0)
+    np.testing.assert_array_equal(out["h"], h0.astype(np.float64))
+    assert out["margins"].shape == (3, 4)
+
+
+def test_decode_chain_identity_expert_recurrence():
+    """One identity expert per layer and no shared expert: every element follows
+    h <- h + x^2 sigma(x) with x = bf16(h), a scalar recurrence evaluated here element by element."""
+    d = 32
+    base = _identity_layer(d, shared_identity=False)
+    T = base["dims"].T
+    h0 = _stream(T, d, 33)
+    out = oracle.decode_chain([base, base, base], h0)
+    for t in range(T):
+        for c in range(d):
+            h = float(h0[t, c])
+            for _ in range(3):
+                x = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(np.array([h])))[0]
+                h = h + x * x / (1.0 + math.exp(-x))
+            assert abs(out["h"][t, c] - h) <= 1e-12 * max(1.0, abs(h)), (t, c)
+
+
+def test_decode_chain_tokens_are_independent():
+    """The chain never mixes tokens: permuting the stream's rows permutes the result exactly."""
+    dims = synth.Dims(T=5, d=64, E=8, k=2, I=32, I_shared=32)
+    layers = [synth.make_inputs(dims, seed=40 + s) for s in range(2)]
+    h0 = _stream(5, 64, 41)
+    perm = np.array([3, 0, 4, 1, 2])
+    a = oracle.decode_chain(layers, h0)["h"]
+    b = oracle.decode_chain(layers, h0[perm])["h"]
+    np.testing.assert_array_equal(b, a[perm])
