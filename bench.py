@@ -21,6 +21,11 @@ For an HBM-bound dominant kernel the roofline object also carries the rate
 of torch's device copy kernel moving the same number of bytes
 (`copy_ceiling`): the practical streaming ceiling beside the nominal peak.
 
+`decode_ctx` times the library's multi-layer decode context on the decode
+shape: 8 independent layer copies recorded once into one HIP graph by
+moe_decode_ctx_create, a pass taking a residual stream through all of them
+(x = bf16(h), h = layer(x) + h); reported per layer.
+
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -434,6 +439,49 @@ def traffic_run(name, torch, layer, synth):
     print(json.dumps({"traffic_run": name, "layer_calls": 3, "copy_bytes": 256 << 20, "copies": 2}), flush=True)
 
 
+def run_decode_ctx(passes, torch, abi, layer, synth, n_layers=8):
+    """The single-token decode layer as a stack of n_layers independent layer copies recorded once by the
+    library (moe_decode_ctx_*): a pass takes a residual stream h through every layer (x = bf16(h),
+    h = layer(x) + h).  Nothing in a bare MoE stack keeps the stream's scale, so every timed pass starts
+    again from the same small h0 (a 16 KiB device copy, timed alone and subtracted)."""
+    cfg = synth.CONFIGS["decode"]
+    dims = cfg.dims
+    weights = [layer.DeviceWeights.upload(synth.make_inputs(cfg))]
+    for c in range(1, n_layers):
+        _, w = device_copy(cfg, 7000 + 100 * c + cfg.index, torch, "cuda")
+        dw = layer.DeviceWeights()
+        dw.update(w)
+        weights.append(dw)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242)
+    h0 = torch.randn((dims.T, dims.d), device="cuda", generator=g) * 0.1
+    h = h0.clone()
+    ctx = layer.DecodeContext(dims, weights, h)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        def timed(n, with_ctx):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(n):
+                h.copy_(h0)
+                if with_ctx:
+                    ctx.run(stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1000.0 / n
+        timed(max(4, passes // 10), True)
+        total = timed(passes, True)
+        reset = timed(passes, False)
+    finite = bool(torch.isfinite(h).all().item())
+    ctx.close()
+    per_pass = total - reset
+    return {"workload": f"decode stack: {n_layers} layers of T=1 d={dims.d} E={dims.E} top-{dims.k} I={dims.I}",
+            "layers": n_layers, "passes": passes, "us_per_pass": round(per_pass, 3),
+            "us_per_layer": round(per_pass / n_layers, 3), "reset_copy_us": round(reset, 3),
+            "tokens_per_s_per_layer": round(1e6 / (per_pass / n_layers), 1), "stream_finite": finite}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -475,7 +523,9 @@ def main():
             rows.append(r)
             print(f"[bench] {wl}: {r['ms_per_step'] * 1000:.1f} us/step, {r['tokens_per_s']:.0f} tokens/s",
                   file=sys.stderr, flush=True)
-        print(json.dumps({"metric": METRIC, "n_gpus": 1, "workloads": rows,
+        ctx = run_decode_ctx(max(50, args.steps // 4), torch, abi, layer, synth)
+        print(f"[bench] decode stack context: {ctx['us_per_layer']:.1f} us/layer", file=sys.stderr, flush=True)
+        print(json.dumps({"metric": METRIC, "n_gpus": 1, "workloads": rows, "decode_ctx": ctx,
                           "copy_ceiling": copy_ceiling(torch, [52 << 20, 1 << 30])}), flush=True)
         return
     prim = run_workload(args.workload, args.steps, args.warmup, torch, hip, abi, layer, synth,
@@ -484,6 +534,7 @@ def main():
     if args.secondary and args.secondary != "none" and args.secondary != args.workload:
         n = max(20, args.steps // 40)
         sec = run_workload(args.secondary, n, max(4, n // 10), torch, hip, abi, layer, synth, residual=args.residual)
+    ctx = run_decode_ctx(max(50, args.steps // 4), torch, abi, layer, synth) if args.workload == "decode" else None
     rl = prim["roofline"]
     if rl["unit"] == "GB/s":  # measured right after the GPU work, before the host-only oracle timing
         ceil = copy_ceiling(torch, [rl["algorithmic_bytes_per_launch"]])
@@ -517,6 +568,8 @@ def main():
     if sec is not None:
         sec.pop("_inp0", None)
         out["secondary"] = sec
+    if ctx is not None:
+        out["decode_ctx"] = ctx
     print(json.dumps(out), flush=True)
 
 

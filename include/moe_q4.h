@@ -206,6 +206,54 @@ int moe_q4_forward_residual(const moe_dims* dims, const uint16_t* x_bf16, const 
                             const moe_q4_weights* weights, const float* residual, float* y, void* scratch,
                             size_t scratch_bytes, uint32_t flags, void* stream);
 
+/* ---- Multi-layer decode context ------------------------------------------
+ * Page "feat(laguna): Laguna-S-2.1 decode on the CUDA engine" runs decode as
+ * one captured graph over every layer, replayed each step, with a persistent
+ * workspace.  A context does that for a stack of MoE layers of one shape:
+ * the layer input is taken from a residual stream h (float32 [T][d]) and the
+ * layer output is added back to it,
+ *     for l in 0 .. n_layers-1:   x = bf16(h);   h = moe_layer_l(x) + h
+ * with bf16() rounding to nearest even and the residual added after the
+ * routed + shared sum (as moe_q4_forward_residual).  The attention blocks
+ * and norms a model has between its MoE layers are not part of it. */
+typedef struct moe_layer {
+  const float* w_router;   /* DEVICE float32 [E][d], 16-byte aligned        */
+  const float* bias;       /* DEVICE float32 [E]                              */
+  moe_q4_weights weights;  /* DEVICE Q4 stacks as for moe_q4_forward           */
+} moe_layer;
+
+typedef struct moe_decode_ctx moe_decode_ctx;  /* opaque */
+
+/* Bytes of the caller-owned device workspace a context needs (0 if the
+ * shape or flags are unsupported): the bf16 layer input, the selection, one
+ * routing workspace and one scratch buffer, shared by the layers, which run
+ * one after another. */
+size_t moe_decode_ctx_workspace_bytes(const moe_dims* dims, uint32_t flags);
+
+/* Record the whole stack once into a HIP graph.  `layers` (n_layers >= 1,
+ * host array, read during the call only) and every device pointer in it,
+ * `h` (DEVICE float32 [T][d], 16-byte aligned) and `workspace` (DEVICE, 16-
+ * byte aligned, at least moe_decode_ctx_workspace_bytes) stay owned by the
+ * caller and must outlive the context; the graph keeps their addresses.
+ * The library allocates no device memory: the context holds only host-side
+ * objects (the graph and its executable form).  Every argument is checked
+ * before the first HIP call (MOE_EINVAL, MOE_EALIGN, MOE_EUNSUPPORTED,
+ * MOE_ENOSPACE as for the layer calls; n_layers outside 1..4096 is
+ * MOE_EINVAL); a HIP failure while recording gives MOE_EHIP.  Nothing runs
+ * until moe_decode_ctx_run.  On success *out receives the context. */
+int moe_decode_ctx_create(const moe_dims* dims, int n_layers, const moe_layer* layers, float* h, void* workspace,
+                          size_t workspace_bytes, uint32_t flags, moe_decode_ctx** out);
+
+/* Enqueue one pass of the recorded stack on `stream` (any stream, also the
+ * null stream): h is updated in place.  Passes on one context must not
+ * overlap (they share the workspace and h).  MOE_EINVAL for a NULL context,
+ * MOE_EHIP if the launch fails. */
+int moe_decode_ctx_run(moe_decode_ctx* ctx, void* stream);
+
+/* Release the context's host objects (NULL is allowed).  Work already
+ * enqueued by moe_decode_ctx_run completes normally. */
+int moe_decode_ctx_destroy(moe_decode_ctx* ctx);
+
 /* Static string for a return code; never NULL. */
 const char* moe_strerror(int code);
 

@@ -27,6 +27,7 @@ MOE_GEMV_FORCE_MAX_T = 64
 EXPORTED_SYMBOLS = (
     "moe_supports", "moe_path", "moe_routing_bytes", "moe_routing_layout_of", "moe_scratch_bytes",
     "moe_route", "moe_build_descriptors", "moe_q4_forward", "moe_q4_forward_residual", "moe_strerror",
+    "moe_decode_ctx_workspace_bytes", "moe_decode_ctx_create", "moe_decode_ctx_run", "moe_decode_ctx_destroy",
 )
 
 
@@ -47,6 +48,10 @@ class _Q4(Structure):
 
 class _Weights(Structure):
     _fields_ = [("w13", _Q4), ("w2", _Q4), ("s13", _Q4), ("s2", _Q4)]
+
+
+class _Layer(Structure):
+    _fields_ = [("w_router", c_void_p), ("bias", c_void_p), ("weights", _Weights)]
 
 
 _LAYOUT_FIELDS = ("logits", "counts", "offsets", "sorted_pair", "pair_pos", "row_expert", "group_order",
@@ -99,6 +104,15 @@ def lib() -> ctypes.CDLL:
     L.moe_q4_forward_residual.argtypes = [D, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, POINTER(_Weights),
                                           c_void_p, c_void_p, c_void_p, c_size_t, c_uint32, c_void_p]
     L.moe_q4_forward_residual.restype = c_int
+    L.moe_decode_ctx_workspace_bytes.argtypes = [D, c_uint32]
+    L.moe_decode_ctx_workspace_bytes.restype = c_size_t
+    L.moe_decode_ctx_create.argtypes = [D, c_int, POINTER(_Layer), c_void_p, c_void_p, c_size_t, c_uint32,
+                                        POINTER(c_void_p)]
+    L.moe_decode_ctx_create.restype = c_int
+    L.moe_decode_ctx_run.argtypes = [c_void_p, c_void_p]
+    L.moe_decode_ctx_run.restype = c_int
+    L.moe_decode_ctx_destroy.argtypes = [c_void_p]
+    L.moe_decode_ctx_destroy.restype = c_int
     L.moe_strerror.argtypes = [c_int]
     L.moe_strerror.restype = c_char_p
     _lib = L
@@ -200,3 +214,33 @@ def moe_q4_forward_residual(dims, x, topk_ids, topk_w, routing, weights, residua
                                        _ptr(residual), _ptr(y), _ptr(scratch), _nbytes(scratch, scratch_bytes),
                                        flags, _stream(stream))
     return _done(rc, check, "moe_q4_forward_residual")
+
+
+def moe_decode_ctx_workspace_bytes(dims, flags: int = 0) -> int:
+    return lib().moe_decode_ctx_workspace_bytes(ctypes.byref(Dims.of(dims)), flags)
+
+
+def _layer(layer) -> _Layer:
+    """layer: mapping with w_router, bias and the Q4 weight arrays (as for moe_q4_forward)."""
+    return _Layer(_ptr(layer["w_router"]), _ptr(layer["bias"]), _weights(layer))
+
+
+def moe_decode_ctx_create(dims, layers, h, workspace, workspace_bytes=None, flags: int = 0,
+                          check: bool = True):
+    """Returns the context handle (an int), or (when check=False) the return code if creation failed."""
+    arr = (_Layer * max(len(layers), 1))(*[_layer(l) for l in layers])
+    out = c_void_p()
+    rc = lib().moe_decode_ctx_create(ctypes.byref(Dims.of(dims)), len(layers), arr, _ptr(h), _ptr(workspace),
+                                     _nbytes(workspace, workspace_bytes), flags, ctypes.byref(out))
+    if rc != MOE_OK:
+        _done(rc, check, "moe_decode_ctx_create")
+        return rc
+    return out.value
+
+
+def moe_decode_ctx_run(ctx: int, stream=None, check: bool = True) -> int:
+    return _done(lib().moe_decode_ctx_run(ctx, _stream(stream)), check, "moe_decode_ctx_run")
+
+
+def moe_decode_ctx_destroy(ctx) -> int:
+    return lib().moe_decode_ctx_destroy(ctx)

@@ -195,9 +195,11 @@ int moe_build_descriptors(const moe_dims* dims, const int32_t* topk_ids, void* r
 }
 
 namespace {
+// y_bf16 (internal, may be nullptr): also write y rounded to bf16, in the pass that writes y
 int forward_impl(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
                  const void* routing, size_t routing_bytes, const moe_q4_weights* w, const float* residual,
-                 float* y, void* scratch, size_t scratch_bytes, uint32_t flags, void* stream) {
+                 float* y, void* scratch, size_t scratch_bytes, uint32_t flags, void* stream,
+                 uint16_t* y_bf16 = nullptr) {
   int rc = check_dims(dims, flags);
   if (rc) return rc;
   const int path = choose_path(dims, flags);
@@ -224,7 +226,7 @@ int forward_impl(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* to
     _Float16* h_r = reinterpret_cast<_Float16*>(sb + S.h_r);
     _Float16* h_s = reinterpret_cast<_Float16*>(sb + S.h_s);
     if (moe::launch_gemv_gateup(s, x_bf16, topk_ids, w13, s13, h_r, h_s, st) != hipSuccess) return MOE_EHIP;
-    return hip_rc(moe::launch_gemv_down_combine(s, topk_ids, topk_w, w2, s2, h_r, h_s, residual, y, st));
+    return hip_rc(moe::launch_gemv_down_combine(s, topk_ids, topk_w, w2, s2, h_r, h_s, residual, y, y_bf16, st));
   }
   const moe::Routing r = routing_ptrs(const_cast<void*>(routing), L);
   moe::GroupedOut o;
@@ -235,7 +237,7 @@ int forward_impl(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* to
   o.y_s = reinterpret_cast<_Float16*>(sb + S.y_s);
   if (moe::launch_grouped_gateup(s, x_bf16, r, w13, s13, o, flags, st) != hipSuccess) return MOE_EHIP;
   if (moe::launch_grouped_down(s, r, w2, s2, o, flags, st) != hipSuccess) return MOE_EHIP;
-  return hip_rc(moe::launch_combine(s, topk_w, r, o, residual, y, st));
+  return hip_rc(moe::launch_combine(s, topk_w, r, o, residual, y, y_bf16, st));
 }
 }  // namespace
 
@@ -256,6 +258,120 @@ int moe_q4_forward_residual(const moe_dims* dims, const uint16_t* x_bf16, const 
   if (!aligned(residual, 16)) return MOE_EALIGN;
   return forward_impl(dims, x_bf16, topk_ids, topk_w, routing, routing_bytes, w, residual, y, scratch,
                       scratch_bytes, flags, stream);
+}
+
+}  // extern "C"
+
+struct moe_decode_ctx {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+namespace {
+
+struct CtxLayout {
+  size_t x, ids, w, routing, scratch, total;
+};
+
+CtxLayout ctx_layout(const moe_dims* d, uint32_t flags) {
+  const size_t T = d->T, P = (size_t)d->T * d->k;
+  CtxLayout C{};
+  size_t off = 0;
+  C.x = off;       off += align256(T * d->d * 2);
+  C.ids = off;     off += align256(P * 4);
+  C.w = off;       off += align256(P * 4);
+  C.routing = off; off += align256(routing_layout(d).total);
+  C.scratch = off; off += align256(scratch_layout(d, choose_path(d, flags)).total);
+  C.total = off;
+  return C;
+}
+
+bool weights_ok(const moe_q4_weights& w) { return q4_ok(w.w13) && q4_ok(w.w2) && q4_ok(w.s13) && q4_ok(w.s2); }
+bool weights_aligned(const moe_q4_weights& w) {
+  return q4_aligned(w.w13) && q4_aligned(w.w2) && q4_aligned(w.s13) && q4_aligned(w.s2);
+}
+
+// Enqueue the whole stack on `st` (the stream being recorded).
+int enqueue_stack(const moe_dims* dims, int n_layers, const moe_layer* layers, float* h, char* ws,
+                  const CtxLayout& C, uint32_t flags, hipStream_t st) {
+  uint16_t* x = reinterpret_cast<uint16_t*>(ws + C.x);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + C.ids);
+  float* tw = reinterpret_cast<float*>(ws + C.w);
+  void* routing = ws + C.routing;
+  void* scratch = ws + C.scratch;
+  const size_t rbytes = C.scratch - C.routing, sbytes = C.total - C.scratch;
+  (void)hipGetLastError();
+  if (moe::launch_f32_to_bf16(h, x, (size_t)dims->T * dims->d, st) != hipSuccess) return MOE_EHIP;
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_layer& L = layers[l];
+    int rc = moe_route(dims, x, L.w_router, L.bias, ids, tw, routing, rbytes, flags, st);
+    if (rc == MOE_OK) rc = moe_build_descriptors(dims, ids, routing, rbytes, flags, st);
+    // h = layer(x) + h; the last pass also writes the next layer's x = bf16(h)
+    if (rc == MOE_OK)
+      rc = forward_impl(dims, x, ids, tw, routing, rbytes, &L.weights, h, h, scratch, sbytes, flags, st,
+                        l + 1 < n_layers ? x : nullptr);
+    if (rc != MOE_OK) return rc;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_decode_ctx_workspace_bytes(const moe_dims* dims, uint32_t flags) {
+  if (check_dims(dims, flags)) return 0;
+  return ctx_layout(dims, flags).total;
+}
+
+int moe_decode_ctx_create(const moe_dims* dims, int n_layers, const moe_layer* layers, float* h, void* workspace,
+                          size_t workspace_bytes, uint32_t flags, moe_decode_ctx** out) {
+  const int rc0 = check_dims(dims, flags);
+  if (rc0) return rc0;
+  if (!layers || !h || !workspace || !out || n_layers < 1 || n_layers > 4096) return MOE_EINVAL;
+  for (int l = 0; l < n_layers; ++l)
+    if (!layers[l].w_router || !layers[l].bias || !weights_ok(layers[l].weights)) return MOE_EINVAL;
+  if (!aligned(h, 16) || !aligned(workspace, 16)) return MOE_EALIGN;
+  for (int l = 0; l < n_layers; ++l)
+    if (!aligned(layers[l].w_router, 16) || !aligned(layers[l].bias, 4) || !weights_aligned(layers[l].weights))
+      return MOE_EALIGN;
+  const CtxLayout C = ctx_layout(dims, flags);
+  if (workspace_bytes < C.total) return MOE_ENOSPACE;
+
+  hipStream_t cs = nullptr;
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return MOE_EHIP;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int rc = MOE_OK;
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    rc = MOE_EHIP;
+  } else {
+    rc = enqueue_stack(dims, n_layers, layers, h, static_cast<char*>(workspace), C, flags, cs);
+    const hipError_t e = hipStreamEndCapture(cs, &graph);  // ends the recording whatever happened
+    if (rc == MOE_OK && e != hipSuccess) rc = MOE_EHIP;
+    if (rc == MOE_OK && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess) rc = MOE_EHIP;
+  }
+  (void)hipStreamDestroy(cs);
+  if (rc != MOE_OK) {
+    if (exec) (void)hipGraphExecDestroy(exec);
+    if (graph) (void)hipGraphDestroy(graph);
+    return rc;
+  }
+  *out = new moe_decode_ctx{graph, exec};
+  return MOE_OK;
+}
+
+int moe_decode_ctx_run(moe_decode_ctx* ctx, void* stream) {
+  if (!ctx) return MOE_EINVAL;
+  return hip_rc(hipGraphLaunch(ctx->exec, static_cast<hipStream_t>(stream)));
+}
+
+int moe_decode_ctx_destroy(moe_decode_ctx* ctx) {
+  if (!ctx) return MOE_OK;
+  (void)hipGraphExecDestroy(ctx->exec);
+  (void)hipGraphDestroy(ctx->graph);
+  delete ctx;
+  return MOE_OK;
 }
 
 const char* moe_strerror(int code) {

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
                                                             const float* __restrict__ topk_w, Q4 w2, Q4 s2,
                                                             const _Float16* __restrict__ h_r,
                                                             const _Float16* __restrict__ h_s, const float* residual,
-                                                            float* y,
+                                                            float* y, uint16_t* __restrict__ y_bf16,
                                                             int T, int d, int k, int I, int Is, uint32_t mask_lo,
                                                             uint32_t mask_hi, uint32_t magic) {
   // per wavefront: the slot's h, per block 16 dwords of fp16 pairs (the 16x pairs pre-divided by 16)
@@ -294,6 +294,7 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
     float v = acc + part[k][threadIdx.x];
     if (residual) v += residual[(size_t)t * d + r];  // after routed + shared; residual may be y itself
     y[(size_t)t * d + r] = v;
+    if (y_bf16) y_bf16[(size_t)t * d + r] = float_to_bf16_bits(v);
   }
 }
 
@@ -308,10 +309,10 @@ hipError_t launch_gemv_gateup(const Shape& s, const uint16_t* x, const int32_t* 
 
 hipError_t launch_gemv_down_combine(const Shape& s, const int32_t* topk_ids, const float* topk_w, Q4 w2, Q4 s2,
                                     const _Float16* h_r, const _Float16* h_s, const float* residual, float* y,
-                                    hipStream_t st) {
+                                    uint16_t* y_bf16, hipStream_t st) {
   const int nw = (s.k + 1) < 16 ? (s.k + 1) : 16;
   dim3 grid(s.d / 16, s.T);
-  hipLaunchKernelGGL(k_gemv_down_combine, grid, dim3(64 * nw), 0, st, topk_ids, topk_w, w2, s2, h_r, h_s, residual, y, s.T, s.d,
+  hipLaunchKernelGGL(k_gemv_down_combine, grid, dim3(64 * nw), 0, st, topk_ids, topk_w, w2, s2, h_r, h_s, residual, y, y_bf16, s.T, s.d,
                      s.k, s.I, s.Is, 0x000F000Fu, 0x00F000F0u, 0x64006400u);
   return hipGetLastError();
 }

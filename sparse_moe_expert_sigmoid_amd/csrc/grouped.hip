@@ -507,7 +507,8 @@ __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x
 // Per-pair and shared outputs arrive in fp16; every thread sums 8 columns in fp32.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ topk_w, const int* __restrict__ pair_pos,
                                                  const _Float16* __restrict__ y_r, const _Float16* __restrict__ y_s,
-                                                 const float* residual, float* y, int d, int k) {
+                                                 const float* residual, float* y, uint16_t* __restrict__ y_bf16,
+                                                 int d, int k) {
   const int per_row = (d + 2047) / 2048;
   const int t = blockIdx.x / per_row;
   const int col = ((blockIdx.x % per_row) * 256 + threadIdx.x) * 8;
@@ -554,6 +555,34 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ topk_
   float4* yo = reinterpret_cast<float4*>(y + (size_t)t * d + col);
   yo[0] = o0;
   yo[1] = o1;
+  if (y_bf16) {
+    const uint32_t b0 = float_to_bf16_bits(o0.x) | ((uint32_t)float_to_bf16_bits(o0.y) << 16);
+    const uint32_t b1 = float_to_bf16_bits(o0.z) | ((uint32_t)float_to_bf16_bits(o0.w) << 16);
+    const uint32_t b2 = float_to_bf16_bits(o1.x) | ((uint32_t)float_to_bf16_bits(o1.y) << 16);
+    const uint32_t b3 = float_to_bf16_bits(o1.z) | ((uint32_t)float_to_bf16_bits(o1.w) << 16);
+    *reinterpret_cast<u32x4*>(y_bf16 + (size_t)t * d + col) = u32x4{b0, b1, b2, b3};
+  }
+}
+
+// fp32 -> bf16 (round to nearest even) of n8 groups of 8 values: the input of a layer taken from a
+// residual stream.
+__global__ __launch_bounds__(256) void k_f32_to_bf16(const float* __restrict__ h, uint16_t* __restrict__ x,
+                                                     size_t n8) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const float4* hp = reinterpret_cast<const float4*>(h + 8 * i);
+  const float4 a = hp[0], b = hp[1];
+  *reinterpret_cast<u32x4*>(x + 8 * i) =
+      u32x4{float_to_bf16_bits(a.x) | ((uint32_t)float_to_bf16_bits(a.y) << 16),
+            float_to_bf16_bits(a.z) | ((uint32_t)float_to_bf16_bits(a.w) << 16),
+            float_to_bf16_bits(b.x) | ((uint32_t)float_to_bf16_bits(b.y) << 16),
+            float_to_bf16_bits(b.z) | ((uint32_t)float_to_bf16_bits(b.w) << 16)};
+}
+
+hipError_t launch_f32_to_bf16(const float* h, uint16_t* x, size_t n, hipStream_t st) {
+  const size_t n8 = n / 8;
+  hipLaunchKernelGGL(k_f32_to_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, h, x, n8);
+  return hipGetLastError();
 }
 
 int grouped_max_mtiles(const Shape& s) {
@@ -617,9 +646,9 @@ hipError_t launch_grouped_down(const Shape& s, const Routing& r, Q4 w2, Q4 s2, c
 }
 
 hipError_t launch_combine(const Shape& s, const float* topk_w, const Routing& r, const GroupedOut& o,
-                          const float* residual, float* y, hipStream_t st) {
+                          const float* residual, float* y, uint16_t* y_bf16, hipStream_t st) {
   dim3 grid(((s.d + 2047) / 2048) * s.T);
-  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, st, topk_w, r.pair_pos, o.y_pair, o.y_s, residual, y, s.d,
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, st, topk_w, r.pair_pos, o.y_pair, o.y_s, residual, y, y_bf16, s.d,
                      s.k);
   return hipGetLastError();
 }

@@ -45,6 +45,13 @@ __device__ __forceinline__ float fp16_bits_to_float(uint32_t bits16) {
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }
+// fp32 -> bf16 bits, round to nearest with ties to even (add 0x7FFF plus the lowest kept bit, keep the
+// top half; a carry into the exponent gives the next binade or infinity).  NaN -> 0x7FC0.
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
 
 // (a & mask) | bits in one v_and_or_b32.  gfx9 VOP3 encodings take at most one scalar or literal
 // operand, so the mask travels in an SGPR and `bits` in a VGPR.

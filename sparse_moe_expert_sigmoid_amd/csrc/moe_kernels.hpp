@@ -47,10 +47,11 @@ hipError_t launch_build(const Shape& s, const int32_t* topk_ids, const Routing& 
 // gemv.hip  (small-T path)
 hipError_t launch_gemv_gateup(const Shape& s, const uint16_t* x, const int32_t* topk_ids, Q4 w13, Q4 s13,
                               _Float16* h_r, _Float16* h_s, hipStream_t st);
-// residual: optional fp32 [T][d] added after the routed + shared sum (may be y itself; nullptr = none)
+// residual: optional fp32 [T][d] added after the routed + shared sum (may be y itself; nullptr = none);
+// y_bf16: optional bf16 [T][d] copy of y, rounded to nearest even (nullptr = none)
 hipError_t launch_gemv_down_combine(const Shape& s, const int32_t* topk_ids, const float* topk_w, Q4 w2, Q4 s2,
                                     const _Float16* h_r, const _Float16* h_s, const float* residual, float* y,
-                                    hipStream_t st);
+                                    uint16_t* y_bf16, hipStream_t st);
 
 // grouped.hip  (grouped path)
 struct GroupedOut {
@@ -65,7 +66,10 @@ hipError_t launch_grouped_gateup(const Shape& s, const uint16_t* x, const Routin
                                  const GroupedOut& o, uint32_t flags, hipStream_t st);
 hipError_t launch_grouped_down(const Shape& s, const Routing& r, Q4 w2, Q4 s2, const GroupedOut& o,
                                uint32_t flags, hipStream_t st);
+// residual and y_bf16 as for launch_gemv_down_combine
 hipError_t launch_combine(const Shape& s, const float* topk_w, const Routing& r, const GroupedOut& o,
-                          const float* residual, float* y, hipStream_t st);
+                          const float* residual, float* y, uint16_t* y_bf16, hipStream_t st);
+// x[i] = bf16(h[i]) for n values (n % 8 == 0), round to nearest even
+hipError_t launch_f32_to_bf16(const float* h, uint16_t* x, size_t n, hipStream_t st);
 
 }  // namespace moe

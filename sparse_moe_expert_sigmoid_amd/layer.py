@@ -88,3 +88,30 @@ def layer_call(x: torch.Tensor, w: DeviceWeights, ws: Workspace, stream=None, re
         abi.moe_q4_forward_residual(dims, x, ws.topk_ids, ws.topk_w, ws.routing, w, residual, ws.y, ws.scratch,
                                     flags=f, stream=stream)
     return ws.y
+
+
+class DecodeContext:
+    """A stack of MoE layers recorded once into a HIP graph by the library (moe_decode_ctx_*):
+    every run() passes the residual stream h (fp32 [T][d], updated in place) through all layers,
+    x = bf16(h), h = layer(x) + h.  Holds the device buffers the context's graph addresses."""
+
+    def __init__(self, dims, layers: list, h: torch.Tensor, flags: int = 0):
+        self.dims, self.flags, self.layers, self.h = dims, flags, layers, h
+        self.workspace = torch.zeros(max(abi.moe_decode_ctx_workspace_bytes(dims, flags), 256), dtype=torch.uint8,
+                                     device=h.device)
+        self.ctx = abi.moe_decode_ctx_create(dims, layers, h, self.workspace, flags=flags)
+
+    def run(self, stream=None) -> torch.Tensor:
+        abi.moe_decode_ctx_run(self.ctx, stream)
+        return self.h
+
+    def close(self) -> None:
+        if self.ctx:
+            abi.moe_decode_ctx_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -188,3 +188,42 @@ def test_header_documents_every_code():
         m = re.search(rf"#define {name}\s+(\d+)u?", text)
         assert m and int(m.group(1)) == getattr(abi, name), name
     assert ctypes.sizeof(abi.Dims) == 24
+
+
+# ----------------------------------------------------------------------------- multi-layer decode context
+
+def test_decode_ctx_workspace_closed_form():
+    for dims, flags in [(TINY, 0), (TINY, abi.MOE_FLAG_FORCE_GROUPED), (synth.CONFIGS["decode"].dims, 0)]:
+        T, k, dd = dims.T, dims.k, dims.d
+        want = (align(T * dd * 2) + 2 * align(T * k * 4) + align(moe.moe_routing_bytes(dims, flags))
+                + align(moe.moe_scratch_bytes(dims, flags)))
+        assert moe.moe_decode_ctx_workspace_bytes(dims, flags) == want
+    assert moe.moe_decode_ctx_workspace_bytes(d(d=40)) == 0
+
+
+def ctx_create(dims=TINY, n=2, layers=None, flags=0, **kw):
+    lay = layers if layers is not None else [dict(WEIGHTS, w_router=FAKE, bias=FAKE) for _ in range(n)]
+    args = dict(h=FAKE, workspace=FAKE, workspace_bytes=1 << 30)
+    args.update(kw)
+    return moe.moe_decode_ctx_create(dims, lay, flags=flags, check=False, **args)
+
+
+def test_decode_ctx_validation_before_any_hip_call():
+    # every rejection below happens on the host, before a stream is created or anything is recorded
+    assert ctx_create(dims=d(k=0)) == abi.MOE_EINVAL
+    assert ctx_create(dims=d(d=40)) == abi.MOE_EUNSUPPORTED
+    assert ctx_create(n=0) == abi.MOE_EINVAL
+    assert ctx_create(n=4097) == abi.MOE_EINVAL
+    assert ctx_create(h=0) == abi.MOE_EINVAL
+    assert ctx_create(workspace=0) == abi.MOE_EINVAL
+    assert ctx_create(h=FAKE + 4) == abi.MOE_EALIGN
+    assert ctx_create(workspace=FAKE + 8) == abi.MOE_EALIGN
+    assert ctx_create(workspace_bytes=moe.moe_decode_ctx_workspace_bytes(TINY) - 1) == abi.MOE_ENOSPACE
+    good = dict(WEIGHTS, w_router=FAKE, bias=FAKE)
+    for name in list(WEIGHTS) + ["w_router", "bias"]:
+        assert ctx_create(layers=[good, dict(good, **{name: 0})]) == abi.MOE_EINVAL, name
+    for name in list(WEIGHTS) + ["w_router"]:
+        assert ctx_create(layers=[dict(good, **{name: FAKE + 8}), good]) == abi.MOE_EALIGN, name
+    assert ctx_create(layers=[dict(good, bias=FAKE + 2)]) == abi.MOE_EALIGN
+    assert moe.moe_decode_ctx_run(0, stream=0, check=False) == abi.MOE_EINVAL
+    assert moe.moe_decode_ctx_destroy(None) == abi.MOE_OK
