@@ -15,8 +15,9 @@
 //   group_order[E+1]               schedule order of the groups
 //   mt_prefix[E+2]                 exclusive prefix of M-tiles along group_order
 //
-// Two launches over chunks of 256 tokens (the second with one more workgroup
-// that builds the group schedule while the others scatter).  Every token picks k distinct
+// One workgroup when every expert's token bitmask fits in LDS (k_build_small);
+// otherwise two launches over chunks of 256 tokens (the second with one more
+// workgroup that builds the group schedule while the others scatter).  Every token picks k distinct
 // experts, so inside an expert the stable order is token order: the rank of
 // token i of a chunk within expert e is the number of set bits below i in
 // the chunk's bitmask of e, plus the counts of the earlier chunks.  The
@@ -44,12 +45,13 @@ __global__ __launch_bounds__(256) void k_build_count(const int32_t* __restrict__
   for (int e = tid; e < E; e += 256) chunk_counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
 
-// Exclusive scan of v[0..n) in place (n <= 1024+2), 256 threads: each thread sums a run of
+// Exclusive scan of v[0..n) in place (n <= 1024+2) by NT threads: each thread sums a run of
 // consecutive elements, the run sums are scanned inside each wavefront with lane shifts and across
-// the 4 wavefronts through LDS, then every run is rewritten from its offset (two barriers).
-__device__ void block_exclusive_scan(int* v, int n, int* tmp /* [256] */) {
+// the NT/64 wavefronts through LDS, then every run is rewritten from its offset (two barriers).
+template <int NT = 256>
+__device__ void block_exclusive_scan(int* v, int n, int* tmp /* [NT/64] */) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (n + 255) / 256;
+  const int per = (n + NT - 1) / NT;
   const int lo = tid * per;
   int local = 0;
   for (int i = 0; i < per; ++i)
@@ -186,8 +188,127 @@ __global__ __launch_bounds__(256) void k_build_scatter(const int32_t* __restrict
   for (int q = tid; q <= ng; q += 256) r.mt_prefix[q] = off[q];
 }
 
+
+// ---------------------------------------------------------------------------
+// The whole build in one workgroup of 1024 threads, for few pairs (T * k <= 4096) whose experts'
+// token bitmasks fit in LDS (E * ceil(T/32) <= kBuildSmallWords words).  Bit t of expert e's mask is
+// set when token t picked e, so the stable (expert, pair) order ranks a pair of token t inside its
+// expert by the set bits before bit t: a per-word prefix (uint16, T < 65536) plus one popcount.
+// Counts, offsets, ranks and the group schedule never leave the workgroup: one launch, no global
+// histogram.
+constexpr int kBuildSmallThreads = 1024;
+constexpr int kBuildSmallWords = 20480;
+
+__global__ __launch_bounds__(kBuildSmallThreads) void k_build_small(const int32_t* __restrict__ ids, int T, int k,
+                                                                    int E, uint32_t flags, Routing r) {
+  __shared__ uint32_t masks[kBuildSmallWords];
+  __shared__ uint16_t pre[kBuildSmallWords];  // set bits of the expert's earlier words
+  __shared__ int cnt[kMaxExperts + 2];
+  __shared__ int off[kMaxExperts + 2];
+  __shared__ __attribute__((aligned(16))) uint32_t key[kMaxExperts + 4];
+  __shared__ int tmp[kBuildSmallThreads / 64];
+  constexpr int NT = kBuildSmallThreads;
+  const int tid = threadIdx.x;
+  const int W = (T + 31) >> 5;
+  const int P = T * k;
+  const int ng = E + 1;
+  for (int i = tid; i < E * W; i += NT) masks[i] = 0u;
+  for (int e = tid; e <= E; e += NT) cnt[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += NT) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) {
+      const int t = p / k;
+      atomicAdd(&cnt[e], 1);
+      atomicOr(&masks[e * W + (t >> 5)], 1u << (t & 31));
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += NT) off[e] = e < E ? cnt[e] : 0;
+  if (tid == 0) cnt[E] = T;
+  // per-word prefix of set bits inside each expert's mask
+  for (int e = tid; e < E; e += NT) {
+    int run = 0;
+    for (int w = 0; w < W; ++w) {
+      pre[e * W + w] = (uint16_t)run;
+      run += __popc(masks[e * W + w]);
+    }
+  }
+  // schedule keys: count * 2^11 + (2047 - g), one compare per group (counts <= T < 2^21)
+  const int ng4 = (ng + 3) & ~3;  // padded with zero keys, below every real one
+  for (int g = tid; g < ng4; g += NT)
+    key[g] = g < ng ? ((uint32_t)(g < E ? cnt[g] : T) << 11) | (uint32_t)(2047 - g) : 0u;
+  __syncthreads();
+  block_exclusive_scan<NT>(off, E + 1, tmp);  // off[E] = number of valid pairs
+  // ranks of the groups (larger count first, ties to the lower id; or id order)
+  int my_rank = 0, my_tiles = 0;
+  const int g = tid;
+  if (g < ng) {
+    if (flags & MOE_FLAG_ID_ORDER) {
+      my_rank = g;
+    } else {
+      const uint32_t kg = key[g];
+#pragma unroll 4
+      for (int h4 = 0; h4 < ng4 / 4; ++h4) {
+        const u32x4 k4 = reinterpret_cast<const u32x4*>(key)[h4];
+        my_rank += (int)(k4[0] > kg) + (int)(k4[1] > kg) + (int)(k4[2] > kg) + (int)(k4[3] > kg);
+      }
+    }
+    my_tiles = ((g < E ? cnt[g] : T) + kGroupedBM - 1) / kGroupedBM;
+  }
+  // scatter: position of a pair = offset of its expert + earlier pairs of the expert in token order
+  for (int p = tid; p < P; p += NT) {
+    const int e = ids[p];
+    if ((unsigned)e >= (unsigned)E) {
+      r.pair_pos[p] = -1;  // out-of-range id: the pair contributes nothing
+      continue;
+    }
+    const int t = p / k, w = t >> 5;
+    const int pos = off[e] + pre[e * W + w] + __popc(masks[e * W + w] & ((1u << (t & 31)) - 1u));
+    r.sorted_pair[pos] = p;
+    r.pair_pos[p] = pos;
+    r.row_expert[pos] = e;
+  }
+  for (int e = tid; e < E; e += NT) {
+    r.counts[e] = cnt[e];
+    r.offsets[e] = off[e];
+  }
+  if (tid == 0) {
+    r.counts[E] = T;
+    r.offsets[E] = off[E];
+  }
+  __syncthreads();  // every read of off and cnt above is done: off takes the M-tiles in rank order
+  for (int q = tid; q <= ng; q += NT) off[q] = 0;
+  __syncthreads();
+  if (g < ng) {
+    r.group_order[my_rank] = g;
+    off[my_rank] = my_tiles;
+  }
+  if (ng > NT) {  // E = 1024: the last group, by thread 0 (ranks are a permutation, no write collides)
+    if (tid == 0) {
+      const int gl = ng - 1;
+      int rank = gl;
+      if (!(flags & MOE_FLAG_ID_ORDER)) {
+        rank = 0;
+        for (int h = 0; h < ng; ++h) rank += (int)(key[h] > key[gl]);
+      }
+      r.group_order[rank] = gl;
+      off[rank] = (T + kGroupedBM - 1) / kGroupedBM;
+    }
+  }
+  __syncthreads();
+  block_exclusive_scan<NT>(off, ng + 1, tmp);  // off[ng] = total M-tiles
+  for (int q = tid; q <= ng; q += NT) r.mt_prefix[q] = off[q];
+}
+
 hipError_t launch_build(const Shape& s, const int32_t* topk_ids, const Routing& r, uint32_t flags,
                         hipStream_t st) {
+  // one workgroup while the pairs are few (at most 4 per thread: 8.6 against 13 us at 640 pairs; at
+  // 20480 pairs the two parallel launches take 22 us and one workgroup 47) and the masks fit
+  if ((long long)s.E * ((s.T + 31) / 32) <= kBuildSmallWords && (long long)s.T * s.k <= 4LL * kBuildSmallThreads) {
+    hipLaunchKernelGGL(k_build_small, dim3(1), dim3(kBuildSmallThreads), 0, st, topk_ids, s.T, s.k, s.E, flags, r);
+    return hipGetLastError();
+  }
   const int nchunks = (s.T + kBuildChunk - 1) / kBuildChunk;
   hipLaunchKernelGGL(k_build_count, dim3(nchunks), dim3(256), 0, st, topk_ids, s.T, s.k, s.E, r.chunk_counts);
   hipError_t e = hipGetLastError();

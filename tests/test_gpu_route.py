@@ -88,3 +88,26 @@ def test_large_t_router_tile(T):
     np.testing.assert_array_equal(np.sort(ids[clear], 1), np.sort(ref_ids[clear], 1))
     ref_w = oracle.routing_weights(s, ids)
     np.testing.assert_allclose(w, ref_w, rtol=0, atol=W_ABS)
+
+
+BUILDS = [(40, 1024, 32, 0), (40, 1024, 32, abi.MOE_FLAG_ID_ORDER), (700, 1024, 2, 0), (2000, 16, 2, 0),
+          (64, 256, 10, abi.MOE_FLAG_ID_ORDER), (2048, 256, 10, 0)]
+
+
+@pytest.mark.parametrize("T,E,k,extra", BUILDS, ids=[f"T{t}E{e}k{k}f{f}" for t, e, k, f in BUILDS])
+def test_routing_build_forms(T, E, k, extra):
+    """The routing build in one workgroup (at most 4096 pairs, token bitmasks in LDS: E * ceil(T/32) <=
+    20480 words) and in two launches (700 tokens x 1024 experts; 20480 pairs), against the oracle's
+    CSR construction bit for bit, including E = 1024 (1025 groups for 1024 threads) and the id-order
+    schedule."""
+    from gpu_util import check_routing_build
+    flags = abi.MOE_FLAG_FORCE_GROUPED | extra
+    dims = synth.Dims(T=T, d=64, E=E, k=k, I=32, I_shared=32)
+    inp = synth.make_inputs(dims, seed=T + E + k, weights=False)
+    say(f"[case] build T={T} E={E} k={k} flags={flags}")
+    ws = Workspace(dims, flags)
+    abi.moe_route(dims, to_device(inp["x"], "cuda"), to_device(inp["w_router"], "cuda"),
+                  to_device(inp["bias"], "cuda"), ws.topk_ids, ws.topk_w, ws.routing, flags=flags)
+    abi.moe_build_descriptors(dims, ws.topk_ids, ws.routing, flags=flags)
+    torch.cuda.synchronize()
+    check_routing_build(ws)
