@@ -64,6 +64,13 @@ def test_flags_validation():
     assert moe.moe_supports(d(T=64, d=4096, E=256, k=10, I=1024, I_shared=1024), abi.MOE_FLAG_FORCE_GEMV) == 0
     assert moe.moe_supports(d(d=16384), abi.MOE_FLAG_FORCE_GEMV) == abi.MOE_EUNSUPPORTED
     assert moe.moe_supports(d(d=16384), abi.MOE_FLAG_FORCE_GROUPED) == 0
+    # the small-T path's exact limits: d <= 8192, I and I_shared <= 2048
+    g = abi.MOE_FLAG_FORCE_GEMV
+    assert moe.moe_supports(d(d=8192, I=2048, I_shared=2048), g) == 0
+    assert moe.moe_supports(d(d=8224), g) == abi.MOE_EUNSUPPORTED
+    assert moe.moe_supports(d(I=2080), g) == abi.MOE_EUNSUPPORTED
+    assert moe.moe_supports(d(I_shared=2080), g) == abi.MOE_EUNSUPPORTED
+    assert moe.moe_supports(d(T=64), g) == 0 and moe.moe_supports(d(T=65), g) == abi.MOE_EUNSUPPORTED
 
 
 def test_path_selection():

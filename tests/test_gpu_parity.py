@@ -178,3 +178,15 @@ def test_full_size_workloads(name):
         gemv, _ = run(inp, GEMV, w, x)
         assert torch.equal(gemv.topk_ids, ws.topk_ids)
         check_parity(inp, gemv, tokens=tokens, label=name + "/gemv")
+
+
+@pytest.mark.parametrize("flags", [GEMV, GROUPED], ids=["gemv", "grouped"])
+def test_small_t_path_at_its_size_limits(flags):
+    """d = 8192 and I = I_shared = 2048, the largest shape the small-T path takes: a wavefront's quarter of
+    K in the gate+up GEMV is then exactly 64 Q4 blocks, and the down GEMV stages exactly 64 blocks of h.
+    The grouped path on the same shape for comparison."""
+    dims = synth.Dims(T=3, d=8192, E=4, k=2, I=2048, I_shared=2048)
+    say(f"[case] size limits flags={flags} dims={dims}")
+    inp = synth.make_inputs(dims, seed=131)
+    ws, _ = run(inp, flags)
+    check_parity(inp, ws, label=f"limits/{flags}")
