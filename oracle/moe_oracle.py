@@ -23,7 +23,7 @@ What it computes, and where the pages say so
     "ffai_add3" commit, where routed and shared outputs are summed first
     because the other order changed an argmax.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * router logits l = x . W_r^T, no router bias term, no temperature; s = 1/(1+exp(-l));
   * the score-correction bias b is added to s for *selection only*: key = s + b;
   * the k experts with the largest key are chosen, ties going to the lower
