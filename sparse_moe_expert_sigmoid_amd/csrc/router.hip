@@ -92,10 +92,12 @@ hipError_t launch_router_gemv(const Shape& s, const uint16_t* x, const float* w_
 // tokens x 256 experts over one of kRouterParts contiguous parts of K with 8
 // wavefronts: wavefront w takes the 64-expert block w % 4 and half w / 4 of
 // every chunk's K steps, and the two halves are added in LDS at the end
-// (lower half first).  Every workgroup streams its whole part of the router
-// weights, so for large T (enough workgroups to fill the GPU) it takes 128
-// tokens with 4 wavefronts and whole K steps instead, reading the weights
-// half as often.  When that gives few workgroups (small T) a workgroup
+// (lower half first).  Every workgroup streams its part of the router
+// weights for all of its experts, so where 128-token tiles still give 256
+// workgroups the token tile is 128: over all 256 experts with 4 wavefronts
+// and whole K steps (T >= 4096 at E = 256), or over 128 experts with 4
+// wavefronts and two K halves (T = 2048), reading the weights half as often
+// as 64-token tiles.  When that gives few workgroups (small T) a workgroup
 // takes one 64-expert block and splits every chunk's K steps over 8
 // wavefronts instead, whose sums are added in LDS in wavefront order.  The token tile is brought into LDS first, 1 KiB of
 // every token row per chunk of 16 K steps, with buffer loads straight into
@@ -417,6 +419,8 @@ hipError_t launch_router_mfma(const Shape& s, const uint16_t* x, const float* w_
   const int ntt4 = (s.T + 63) / 64, ntt8 = (s.T + 127) / 128, neb4 = (s.E + 4 * kRtExp - 1) / (4 * kRtExp);
   if (ntt8 * neb4 * kRouterParts >= 256)
     router_mfma_cfg<8, 4, 1>(s, x, w_router, logits, st);  // 128 tokens x 256 experts per workgroup
+  else if (ntt8 * ((s.E + 2 * kRtExp - 1) / (2 * kRtExp)) * kRouterParts >= 256)
+    router_mfma_cfg<8, 2, 2>(s, x, w_router, logits, st);  // 128 tokens x 128 experts x 2 K halves
   else if (ntt4 * neb4 * kRouterParts >= 128)
     router_mfma_cfg<4, 4, 2>(s, x, w_router, logits, st);  // 64 tokens x 256 experts x 2 K halves
   else

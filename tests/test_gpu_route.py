@@ -74,9 +74,10 @@ def test_slot_order_matches_oracle(E, k, path):
     assert ordered > 0 or k == 1
 
 
-@pytest.mark.parametrize("T", [4096, 4100])
+@pytest.mark.parametrize("T", [2000, 2048, 4096, 4100])
 def test_large_t_router_tile(T):
-    """T >= 4096 takes the 128-token router tile (4096: whole tiles; 4100: a ragged last tile of 4 tokens)."""
+    """The 128-token router tiles: over 128 experts with two K halves (T = 2048; 2000: a ragged last tile)
+    and over all 256 experts (T = 4096; 4100: a ragged last tile of 4 tokens)."""
     dims = synth.Dims(T=T, d=512, E=256, k=10, I=32, I_shared=32)
     inp = synth.make_inputs(dims, seed=T, weights=False)
     say(f"[case] large-T router T={T}")
