@@ -3,6 +3,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from sparse_moe_expert_sigmoid_amd import abi
 from sparse_moe_expert_sigmoid_amd.layer import DeviceWeights, Workspace, layer_call, to_device
@@ -190,3 +191,36 @@ def test_small_t_path_at_its_size_limits(flags):
     inp = synth.make_inputs(dims, seed=131)
     ws, _ = run(inp, flags)
     check_parity(inp, ws, label=f"limits/{flags}")
+
+
+SCALE_RANGES = {
+    # the grouped GEMM dequantises in its common form for 2^-10 <= |d| < 2^-4 and in the general form
+    # otherwise (chosen per K iteration and wavefront); the small-T path has a single form
+    "large": (0.07, 0.5),          # every block past 2^-4
+    "tiny": (1.0e-4, 9.0e-4),      # every block below 2^-10
+    "mixed": (2.0e-4, 0.2),        # both forms inside one launch, often inside one iteration
+}
+
+
+@pytest.mark.parametrize("flags", [GROUPED, GEMV], ids=["grouped", "gemv"])
+@pytest.mark.parametrize("rng_name", list(SCALE_RANGES))
+def test_scales_outside_the_common_dequant_range(rng_name, flags):
+    """Parity with Q4 scales drawn outside U(0.005, 0.02): the grouped GEMM's general dequantisation form,
+    and both forms mixed, held to the oracle like the common one.  Activations are scaled with the
+    weights (down for large scales, up for tiny ones) so that every fp16 intermediate of the grouped
+    path (h, the per-pair down outputs) stays in the fp16 normal range."""
+    lo, hi = SCALE_RANGES[rng_name]
+    dims = synth.Dims(T=40, d=256, E=8, k=2, I=128, I_shared=64)
+    inp = synth.make_inputs(dims, seed=140 + len(rng_name))
+    rng = np.random.default_rng(141)
+    for key in ("w13_sc", "w2_sc", "s13_sc", "s2_sc"):
+        d = rng.uniform(lo, hi, size=inp[key].shape)
+        if rng_name == "mixed":
+            d = np.exp(rng.uniform(np.log(lo), np.log(hi), size=inp[key].shape))
+        inp[key] = d.astype(np.float16).view(np.uint16)
+    x_scale = {"large": 0.05, "tiny": 64.0, "mixed": 1.0}[rng_name]
+    x = oracle.bf16_bits_to_f64(inp["x"]) * x_scale
+    inp["x"] = synth.bf16_bits_from_f32(x.astype(np.float32))
+    say(f"[case] scales {rng_name} flags={flags}")
+    ws, _ = run(inp, flags)
+    check_parity(inp, ws, label=f"scales/{rng_name}/{flags}")
