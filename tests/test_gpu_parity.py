@@ -224,3 +224,21 @@ def test_scales_outside_the_common_dequant_range(rng_name, flags):
     say(f"[case] scales {rng_name} flags={flags}")
     ws, _ = run(inp, flags)
     check_parity(inp, ws, label=f"scales/{rng_name}/{flags}")
+
+
+@pytest.mark.parametrize("flags", [GROUPED, GEMV], ids=["grouped", "gemv"])
+def test_zero_experts_give_exact_zero_and_exact_residual(flags):
+    """Every code 8 (every routed and shared weight 0): y is exactly 0, and with a residual exactly the
+    residual (added after the routed + shared sum), whatever the scales."""
+    dims = synth.Dims(T=21, d=96, E=12, k=3, I=64, I_shared=96)
+    inp = synth.make_inputs(dims, seed=151)
+    for key in ("w13_qs", "w2_qs", "s13_qs", "s2_qs"):
+        inp[key][:] = 0x88
+    say(f"[case] zero experts flags={flags}")
+    ws, w = run(inp, flags)
+    assert torch.count_nonzero(ws.y) == 0
+    res = torch.randn(dims.T, dims.d, device="cuda")
+    ws2 = Workspace(dims, flags)
+    layer_call(to_device(inp["x"], "cuda"), w, ws2, residual=res)
+    torch.cuda.synchronize()
+    assert torch.equal(ws2.y, res)
