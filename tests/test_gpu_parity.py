@@ -242,3 +242,38 @@ def test_zero_experts_give_exact_zero_and_exact_residual(flags):
     layer_call(to_device(inp["x"], "cuda"), w, ws2, residual=res)
     torch.cuda.synchronize()
     assert torch.equal(ws2.y, res)
+
+
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        E = int(rng.integers(1, 301))
+        k = int(rng.integers(1, min(E, 32) + 1))
+        T = int(rng.integers(1, 201))
+        d = 32 * int(rng.integers(1, 25))       # 32 .. 768
+        I = 32 * int(rng.integers(1, 17))       # 32 .. 512
+        Is = 32 * int(rng.integers(1, 17))
+        out.append(synth.Dims(T=T, d=d, E=E, k=k, I=I, I_shared=Is))
+    return out
+
+
+SWEEP = _random_shapes(12, 2024)
+
+
+@pytest.mark.parametrize("dims", SWEEP, ids=[f"T{s.T}d{s.d}E{s.E}k{s.k}I{s.I}Is{s.I_shared}" for s in SWEEP])
+def test_random_shape_sweep(dims):
+    """Seeded random shapes inside the supported range (any T, E, k <= min(E, 32), d, I, I_shared
+    multiples of 32): the default path, the grouped path and, where T <= 64, the small-T path, each held
+    to the oracle, with the routing build checked bit for bit on the grouped path."""
+    inp = synth.make_inputs(dims, seed=dims.T * 7 + dims.E)
+    w = DeviceWeights.upload(inp)
+    x = to_device(inp["x"], "cuda")
+    for flags in (0, GROUPED, GEMV):
+        if flags == GEMV and dims.T > abi.MOE_GEMV_FORCE_MAX_T:
+            continue
+        say(f"[case] sweep {dims} flags={flags}")
+        ws, _ = run(inp, flags, w, x)
+        check_parity(inp, ws, label=f"sweep/{flags}")
+        if abi.moe_path(dims, flags) == 1:
+            check_routing_build(ws)
