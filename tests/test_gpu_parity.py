@@ -259,6 +259,9 @@ def _random_shapes(n, seed):
 
 
 SWEEP = _random_shapes(12, 2024)
+# many experts: up to 1025 groups (with the shared one) in one grouped launch, most of them tiny
+SWEEP += [synth.Dims(T=t, d=d, E=e, k=k, I=i, I_shared=s)
+          for t, d, e, k, i, s in [(90, 128, 1024, 32, 64, 96), (33, 96, 777, 5, 160, 32), (64, 64, 640, 17, 96, 64)]]
 
 
 @pytest.mark.parametrize("dims", SWEEP, ids=[f"T{s.T}d{s.d}E{s.E}k{s.k}I{s.I}Is{s.I_shared}" for s in SWEEP])
