@@ -48,7 +48,7 @@ __all__ = [
     "bf16_bits_to_f64", "fp16_bits_to_f64", "dequant_q4",
     "router_logits", "sigmoid", "select_experts", "routing_weights",
     "swiglu_mlp", "forward", "routing_build", "group_order",
-    "f64_to_bf16_bits", "decode_chain",
+    "f64_to_bf16_bits", "decode_chain", "rms_norm",
 ]
 
 
@@ -250,6 +250,21 @@ def group_order(counts: np.ndarray, T: int) -> np.ndarray:
     return np.array(sorted(range(c.size), key=lambda g: (-c[g], g)), dtype=np.int32)
 
 
+# ----------------------------------------------------------------------------- pre-MoE norm
+
+def rms_norm(h, gamma, eps: float) -> np.ndarray:
+    """RMSNorm of each row: h / sqrt(mean(h^2) + eps) * gamma, in float64.
+
+    The pages name RMSNorm (per-head QK RMSNorm in [decode]'s attention, a
+    fused add-RMSNorm op) but never define the norm in front of the MoE
+    block; this is the standard definition of RMSNorm (Zhang and Sennrich,
+    2019), with the caller's per-channel gamma and eps.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    ms = np.mean(h * h, axis=-1, keepdims=True)
+    return h / np.sqrt(ms + float(eps)) * np.asarray(gamma, dtype=np.float64)
+
+
 # ----------------------------------------------------------------------------- multi-layer decode
 
 def decode_chain(layers: list, h0) -> dict:
@@ -258,11 +273,13 @@ def decode_chain(layers: list, h0) -> dict:
     [decode] runs single-stream decode as one captured graph over every layer
     with a persistent workspace (the LagunaDecodeCtx of "feat(laguna):
     Laguna-S-2.1 decode on the CUDA engine"); between two MoE layers of the
-    model sit attention and norms, which are out of scope here, so each layer
-    takes its input straight from the stream:
+    model sit attention and norms; attention is out of scope here, so each
+    layer takes its input straight from the stream:
         x = bf16(h)                (round to nearest even; the layer's input is bf16)
         h = (routed + shared)(x) + h
     the residual added after the routed and shared sum ([nemotron], "ffai_add3").
+    A layer dict with "norm_weight" (gamma [d]) and "norm_eps" takes its input
+    through the pre-MoE norm instead: x = bf16(rms_norm(h, gamma, eps)).
     layers: input dicts as for forward() (their "x" is ignored); h0: [T,d].
     Returns dict(h [T,d] fp64, margins [L,T]: each layer's selection margin).
     """
@@ -270,7 +287,10 @@ def decode_chain(layers: list, h0) -> dict:
     margins = []
     for inp in layers:
         lay = dict(inp)
-        lay["x"] = f64_to_bf16_bits(h)
+        if inp.get("norm_weight") is not None:
+            lay["x"] = f64_to_bf16_bits(rms_norm(h, inp["norm_weight"], inp["norm_eps"]))
+        else:
+            lay["x"] = f64_to_bf16_bits(h)
         out = forward(lay, residual=h)
         h = out["y"]
         margins.append(out["margin"])

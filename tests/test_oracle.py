@@ -495,3 +495,57 @@ def test_decode_chain_tokens_are_independent():
     a = oracle.decode_chain(layers, h0)["h"]
     b = oracle.decode_chain(layers, h0[perm])["h"]
     np.testing.assert_array_equal(b, a[perm])
+
+
+# ----------------------------------------------------------------------------- pre-MoE norm
+
+def test_rms_norm_closed_forms():
+    # a row of equal values c: mean square c^2, so every output is c / sqrt(c^2 + eps) * gamma
+    g = np.linspace(0.5, 2.0, 16)
+    for c, eps in [(3.0, 0.0), (0.25, 1e-6), (-2.0, 0.5)]:
+        out = oracle.rms_norm(np.full((1, 16), c), g, eps)
+        np.testing.assert_allclose(out[0], c / math.sqrt(c * c + eps) * g, rtol=1e-15)
+    # a row with mean square 1 and gamma 1, eps 0: unchanged
+    h = np.array([[1.0, -1.0, 1.0, -1.0, math.sqrt(2), 0.0, 1.0, -1.0]])
+    assert abs(np.mean(h * h) - 1.0) < 1e-15
+    np.testing.assert_allclose(oracle.rms_norm(h, np.ones(8), 0.0), h, rtol=1e-15, atol=1e-15)
+
+
+def test_rms_norm_invariances():
+    rng = np.random.default_rng(61)
+    h = rng.standard_normal((5, 64))
+    g = rng.uniform(0.5, 1.5, 64)
+    base = oracle.rms_norm(h, g, 0.0)
+    # positive scaling of a row leaves it unchanged (eps = 0); a negative one flips its sign
+    np.testing.assert_allclose(oracle.rms_norm(7.5 * h, g, 0.0), base, rtol=1e-13)
+    np.testing.assert_allclose(oracle.rms_norm(-h, g, 0.0), -base, rtol=1e-13)
+    # every output row has mean square mean(gamma^2 * (normalised)^2) -> with gamma = 1 exactly 1
+    unit = oracle.rms_norm(h, np.ones(64), 0.0)
+    np.testing.assert_allclose(np.mean(unit * unit, axis=1), 1.0, rtol=1e-13)
+    # rows are independent: a permutation of rows permutes the result
+    perm = np.array([4, 2, 0, 1, 3])
+    np.testing.assert_array_equal(oracle.rms_norm(h[perm], g, 1e-5), oracle.rms_norm(h, g, 1e-5)[perm])
+
+
+def test_decode_chain_with_norm_keeps_zero_layers_identity_and_normalises_input():
+    """With the pre-MoE norm and zero experts the stream still passes unchanged; with identity experts
+    each element follows h <- h + x^2 sigma(x), now with x = bf16(rms_norm(h) * gamma)."""
+    dims = synth.Dims(T=3, d=32, E=1, k=1, I=32, I_shared=32)
+    base = _identity_layer(32, shared_identity=False)
+    T = base["dims"].T
+    gamma = np.random.default_rng(62).uniform(0.5, 1.5, 32)
+    lay = dict(base, norm_weight=gamma, norm_eps=1e-5)
+    h0 = _stream(T, 32, 63)
+    out = oracle.decode_chain([lay, lay], h0)
+    h = h0.astype(np.float64)
+    for _ in range(2):
+        xn = h / np.sqrt(np.mean(h * h, axis=1, keepdims=True) + 1e-5) * gamma
+        x = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(xn))
+        h = h + x * x / (1.0 + np.exp(-x))
+    np.testing.assert_allclose(out["h"], h, rtol=1e-12, atol=1e-12)
+    zero = synth.make_inputs(synth.Dims(T=3, d=64, E=4, k=2, I=32, I_shared=32), seed=64)
+    for key in ("w13_qs", "w2_qs", "s13_qs", "s2_qs"):
+        zero[key][:] = 0x88
+    zero = dict(zero, norm_weight=np.ones(64), norm_eps=1e-6)
+    h1 = _stream(3, 64, 65)
+    np.testing.assert_array_equal(oracle.decode_chain([zero, zero], h1)["h"], h1.astype(np.float64))
