@@ -24,7 +24,8 @@ of torch's device copy kernel moving the same number of bytes
 `decode_ctx` times the library's multi-layer decode context on the decode
 shape: 8 independent layer copies recorded once into one HIP graph by
 moe_decode_ctx_create, a pass taking a residual stream through all of them
-(x = bf16(h), h = layer(x) + h); reported per layer.
+(x = bf16(h), h = layer(x) + h); reported per layer, and again with the
+pre-MoE RMSNorm in front of every layer (`decode_ctx_norm`).
 
 Prints one JSON line.
 """
@@ -439,11 +440,12 @@ def traffic_run(name, torch, layer, synth):
     print(json.dumps({"traffic_run": name, "layer_calls": 3, "copy_bytes": 256 << 20, "copies": 2}), flush=True)
 
 
-def run_decode_ctx(passes, torch, abi, layer, synth, n_layers=8):
+def run_decode_ctx(passes, torch, abi, layer, synth, n_layers=8, norm=False):
     """The single-token decode layer as a stack of n_layers independent layer copies recorded once by the
-    library (moe_decode_ctx_*): a pass takes a residual stream h through every layer (x = bf16(h),
-    h = layer(x) + h).  Nothing in a bare MoE stack keeps the stream's scale, so every timed pass starts
-    again from the same small h0 (a 16 KiB device copy, timed alone and subtracted)."""
+    library (moe_decode_ctx_*): a pass takes a residual stream h through every layer (x = bf16(h), or
+    with `norm` x = bf16(rmsnorm(h) * gamma), then h = layer(x) + h).  Without the norm nothing keeps the
+    stream's scale, so every timed pass starts again from the same small h0 (a 16 KiB device copy, timed
+    alone and subtracted; done the same way with the norm)."""
     cfg = synth.CONFIGS["decode"]
     dims = cfg.dims
     weights = [layer.DeviceWeights.upload(synth.make_inputs(cfg))]
@@ -454,6 +456,10 @@ def run_decode_ctx(passes, torch, abi, layer, synth, n_layers=8):
         weights.append(dw)
     g = torch.Generator(device="cuda")
     g.manual_seed(4242)
+    if norm:
+        for w in weights:
+            w["norm_weight"] = torch.rand(dims.d, device="cuda", generator=g) + 0.5
+            w["norm_eps"] = 1e-6
     h0 = torch.randn((dims.T, dims.d), device="cuda", generator=g) * 0.1
     h = h0.clone()
     ctx = layer.DecodeContext(dims, weights, h)
@@ -476,7 +482,8 @@ def run_decode_ctx(passes, torch, abi, layer, synth, n_layers=8):
     finite = bool(torch.isfinite(h).all().item())
     ctx.close()
     per_pass = total - reset
-    return {"workload": f"decode stack: {n_layers} layers of T=1 d={dims.d} E={dims.E} top-{dims.k} I={dims.I}",
+    return {"workload": f"decode stack: {n_layers} layers of T=1 d={dims.d} E={dims.E} top-{dims.k} I={dims.I}"
+                        + (", pre-MoE RMSNorm" if norm else ""),
             "layers": n_layers, "passes": passes, "us_per_pass": round(per_pass, 3),
             "us_per_layer": round(per_pass / n_layers, 3), "reset_copy_us": round(reset, 3),
             "tokens_per_s_per_layer": round(1e6 / (per_pass / n_layers), 1), "stream_finite": finite}
@@ -524,8 +531,10 @@ def main():
             print(f"[bench] {wl}: {r['ms_per_step'] * 1000:.1f} us/step, {r['tokens_per_s']:.0f} tokens/s",
                   file=sys.stderr, flush=True)
         ctx = run_decode_ctx(max(50, args.steps // 4), torch, abi, layer, synth)
-        print(f"[bench] decode stack context: {ctx['us_per_layer']:.1f} us/layer", file=sys.stderr, flush=True)
-        print(json.dumps({"metric": METRIC, "n_gpus": 1, "workloads": rows, "decode_ctx": ctx,
+        ctxn = run_decode_ctx(max(50, args.steps // 4), torch, abi, layer, synth, norm=True)
+        print(f"[bench] decode stack context: {ctx['us_per_layer']:.1f} us/layer, with the norm "
+              f"{ctxn['us_per_layer']:.1f}", file=sys.stderr, flush=True)
+        print(json.dumps({"metric": METRIC, "n_gpus": 1, "workloads": rows, "decode_ctx": ctx, "decode_ctx_norm": ctxn,
                           "copy_ceiling": copy_ceiling(torch, [52 << 20, 1 << 30])}), flush=True)
         return
     prim = run_workload(args.workload, args.steps, args.warmup, torch, hip, abi, layer, synth,
@@ -535,6 +544,8 @@ def main():
         n = max(20, args.steps // 40)
         sec = run_workload(args.secondary, n, max(4, n // 10), torch, hip, abi, layer, synth, residual=args.residual)
     ctx = run_decode_ctx(max(50, args.steps // 4), torch, abi, layer, synth) if args.workload == "decode" else None
+    ctxn = (run_decode_ctx(max(50, args.steps // 4), torch, abi, layer, synth, norm=True)
+            if args.workload == "decode" else None)
     rl = prim["roofline"]
     if rl["unit"] == "GB/s":  # measured right after the GPU work, before the host-only oracle timing
         ceil = copy_ceiling(torch, [rl["algorithmic_bytes_per_launch"]])
@@ -570,6 +581,7 @@ def main():
         out["secondary"] = sec
     if ctx is not None:
         out["decode_ctx"] = ctx
+        out["decode_ctx_norm"] = ctxn
     print(json.dumps(out), flush=True)
 
 

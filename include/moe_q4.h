@@ -206,6 +206,20 @@ int moe_q4_forward_residual(const moe_dims* dims, const uint16_t* x_bf16, const 
                             const moe_q4_weights* weights, const float* residual, float* y, void* scratch,
                             size_t scratch_bytes, uint32_t flags, void* stream);
 
+/* Pre-MoE norm (the step in front of the layer): for each of T rows of d
+ * values (d % 8 == 0),
+ *     x_t = bf16( h_t / sqrt(mean(h_t^2) + eps) * gamma )
+ * rounded to nearest even: the standard RMSNorm.  The pages name RMSNorm
+ * (per-head QK RMSNorm in "feat(laguna): Laguna-S-2.1 decode on the CUDA
+ * engine", a fused add-RMSNorm op) without defining the norm in front of
+ * the MoE block; this is the plain reading.  h float32 [T][d], gamma
+ * float32 [d] and x_bf16 uint16 [T][d] are DEVICE arrays, 16-byte aligned;
+ * the mean of squares is summed in fp32 in a fixed order (deterministic).
+ * MOE_EINVAL: T or d < 1, a NULL pointer, eps negative or not finite;
+ * MOE_EUNSUPPORTED: d % 8 != 0 or d > 2^20; MOE_EALIGN; MOE_EHIP. */
+int moe_rmsnorm_bf16(int T, int d, const float* h, const float* gamma, float eps, uint16_t* x_bf16,
+                     void* stream);
+
 /* ---- Multi-layer decode context ------------------------------------------
  * Page "feat(laguna): Laguna-S-2.1 decode on the CUDA engine" runs decode as
  * one captured graph over every layer, replayed each step, with a persistent
@@ -214,12 +228,18 @@ int moe_q4_forward_residual(const moe_dims* dims, const uint16_t* x_bf16, const 
  * layer output is added back to it,
  *     for l in 0 .. n_layers-1:   x = bf16(h);   h = moe_layer_l(x) + h
  * with bf16() rounding to nearest even and the residual added after the
- * routed + shared sum (as moe_q4_forward_residual).  The attention blocks
- * and norms a model has between its MoE layers are not part of it. */
+ * routed + shared sum (as moe_q4_forward_residual); a layer with a norm
+ * weight takes x through the pre-MoE norm instead (moe_rmsnorm_bf16).  The
+ * attention blocks a model has between its MoE layers are not part of it. */
 typedef struct moe_layer {
   const float* w_router;   /* DEVICE float32 [E][d], 16-byte aligned        */
   const float* bias;       /* DEVICE float32 [E]                              */
   moe_q4_weights weights;  /* DEVICE Q4 stacks as for moe_q4_forward           */
+  const float* norm_weight;  /* DEVICE float32 [d] (16-byte aligned), or NULL:
+                                with it the layer's input is the pre-MoE norm
+                                x = bf16(rmsnorm(h) * norm_weight), see
+                                moe_rmsnorm_bf16; without it x = bf16(h)      */
+  float norm_eps;          /* eps of that norm (>= 0, finite)                 */
 } moe_layer;
 
 typedef struct moe_decode_ctx moe_decode_ctx;  /* opaque */
@@ -238,8 +258,8 @@ size_t moe_decode_ctx_workspace_bytes(const moe_dims* dims, uint32_t flags);
  * The library allocates no device memory: the context holds only host-side
  * objects (the graph and its executable form).  Every argument is checked
  * before the first HIP call (MOE_EINVAL, MOE_EALIGN, MOE_EUNSUPPORTED,
- * MOE_ENOSPACE as for the layer calls; n_layers outside 1..4096 is
- * MOE_EINVAL); a HIP failure while recording gives MOE_EHIP.  Nothing runs
+ * MOE_ENOSPACE as for the layer calls; n_layers outside 1..4096 or a norm
+ * eps that is negative or not finite is MOE_EINVAL); a HIP failure while recording gives MOE_EHIP.  Nothing runs
  * until moe_decode_ctx_run.  On success *out receives the context. */
 int moe_decode_ctx_create(const moe_dims* dims, int n_layers, const moe_layer* layers, float* h, void* workspace,
                           size_t workspace_bytes, uint32_t flags, moe_decode_ctx** out);

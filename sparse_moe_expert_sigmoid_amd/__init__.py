@@ -14,4 +14,5 @@ from .abi import (  # noqa: F401
     moe_supports, moe_path, moe_routing_bytes, moe_routing_layout_of, moe_scratch_bytes,
     moe_route, moe_build_descriptors, moe_q4_forward, moe_q4_forward_residual, moe_strerror, EXPORTED_SYMBOLS,
     moe_decode_ctx_workspace_bytes, moe_decode_ctx_create, moe_decode_ctx_run, moe_decode_ctx_destroy,
+    moe_rmsnorm_bf16,
 )

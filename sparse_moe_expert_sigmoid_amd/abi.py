@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, Structure, c_char_p, c_int, c_int32, c_size_t, c_uint32, c_void_p
+from ctypes import POINTER, Structure, c_char_p, c_float, c_int, c_int32, c_size_t, c_uint32, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(HERE, "libmoe_q4.so")
@@ -28,6 +28,7 @@ EXPORTED_SYMBOLS = (
     "moe_supports", "moe_path", "moe_routing_bytes", "moe_routing_layout_of", "moe_scratch_bytes",
     "moe_route", "moe_build_descriptors", "moe_q4_forward", "moe_q4_forward_residual", "moe_strerror",
     "moe_decode_ctx_workspace_bytes", "moe_decode_ctx_create", "moe_decode_ctx_run", "moe_decode_ctx_destroy",
+    "moe_rmsnorm_bf16",
 )
 
 
@@ -51,7 +52,8 @@ class _Weights(Structure):
 
 
 class _Layer(Structure):
-    _fields_ = [("w_router", c_void_p), ("bias", c_void_p), ("weights", _Weights)]
+    _fields_ = [("w_router", c_void_p), ("bias", c_void_p), ("weights", _Weights), ("norm_weight", c_void_p),
+                ("norm_eps", c_float)]
 
 
 _LAYOUT_FIELDS = ("logits", "counts", "offsets", "sorted_pair", "pair_pos", "row_expert", "group_order",
@@ -113,6 +115,8 @@ def lib() -> ctypes.CDLL:
     L.moe_decode_ctx_run.restype = c_int
     L.moe_decode_ctx_destroy.argtypes = [c_void_p]
     L.moe_decode_ctx_destroy.restype = c_int
+    L.moe_rmsnorm_bf16.argtypes = [c_int, c_int, c_void_p, c_void_p, c_float, c_void_p, c_void_p]
+    L.moe_rmsnorm_bf16.restype = c_int
     L.moe_strerror.argtypes = [c_int]
     L.moe_strerror.restype = c_char_p
     _lib = L
@@ -221,8 +225,10 @@ def moe_decode_ctx_workspace_bytes(dims, flags: int = 0) -> int:
 
 
 def _layer(layer) -> _Layer:
-    """layer: mapping with w_router, bias and the Q4 weight arrays (as for moe_q4_forward)."""
-    return _Layer(_ptr(layer["w_router"]), _ptr(layer["bias"]), _weights(layer))
+    """layer: mapping with w_router, bias and the Q4 weight arrays (as for moe_q4_forward), and optionally
+    norm_weight (gamma of the pre-MoE norm) with norm_eps."""
+    return _Layer(_ptr(layer["w_router"]), _ptr(layer["bias"]), _weights(layer), _ptr(layer.get("norm_weight")),
+                  float(layer.get("norm_eps", 0.0)))
 
 
 def moe_decode_ctx_create(dims, layers, h, workspace, workspace_bytes=None, flags: int = 0,
@@ -244,3 +250,8 @@ def moe_decode_ctx_run(ctx: int, stream=None, check: bool = True) -> int:
 
 def moe_decode_ctx_destroy(ctx) -> int:
     return lib().moe_decode_ctx_destroy(ctx)
+
+
+def moe_rmsnorm_bf16(T: int, d: int, h, gamma, eps: float, x, stream=None, check: bool = True) -> int:
+    rc = lib().moe_rmsnorm_bf16(T, d, _ptr(h), _ptr(gamma), float(eps), _ptr(x), _stream(stream))
+    return _done(rc, check, "moe_rmsnorm_bf16")

@@ -8,6 +8,7 @@
 // device-to-host copy), which keeps them capturable into a HIP graph.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -301,15 +302,23 @@ int enqueue_stack(const moe_dims* dims, int n_layers, const moe_layer* layers, f
   void* scratch = ws + C.scratch;
   const size_t rbytes = C.scratch - C.routing, sbytes = C.total - C.scratch;
   (void)hipGetLastError();
-  if (moe::launch_f32_to_bf16(h, x, (size_t)dims->T * dims->d, st) != hipSuccess) return MOE_EHIP;
   for (int l = 0; l < n_layers; ++l) {
     const moe_layer& L = layers[l];
+    // the layer's input: through the norm, or bf16(h) (written by the previous layer's last pass)
+    hipError_t e = hipSuccess;
+    if (L.norm_weight)
+      e = moe::launch_rmsnorm_bf16(h, L.norm_weight, L.norm_eps, x, dims->T, dims->d, st);
+    else if (l == 0)
+      e = moe::launch_f32_to_bf16(h, x, (size_t)dims->T * dims->d, st);
+    if (e != hipSuccess) return MOE_EHIP;
     int rc = moe_route(dims, x, L.w_router, L.bias, ids, tw, routing, rbytes, flags, st);
     if (rc == MOE_OK) rc = moe_build_descriptors(dims, ids, routing, rbytes, flags, st);
-    // h = layer(x) + h; the last pass also writes the next layer's x = bf16(h)
+    // h = layer(x) + h; the last pass also writes the next layer's x = bf16(h) unless that layer's
+    // input goes through the norm
+    const bool fused_next = l + 1 < n_layers && !layers[l + 1].norm_weight;
     if (rc == MOE_OK)
       rc = forward_impl(dims, x, ids, tw, routing, rbytes, &L.weights, h, h, scratch, sbytes, flags, st,
-                        l + 1 < n_layers ? x : nullptr);
+                        fused_next ? x : nullptr);
     if (rc != MOE_OK) return rc;
   }
   return MOE_OK;
@@ -318,6 +327,15 @@ int enqueue_stack(const moe_dims* dims, int n_layers, const moe_layer* layers, f
 }  // namespace
 
 extern "C" {
+
+int moe_rmsnorm_bf16(int T, int d, const float* h, const float* gamma, float eps, uint16_t* x_bf16,
+                     void* stream) {
+  if (T < 1 || d < 1 || !h || !gamma || !x_bf16 || !(isfinite(eps) && eps >= 0.f)) return MOE_EINVAL;
+  if (d % 8 || d > (1 << 20)) return MOE_EUNSUPPORTED;
+  if (!aligned(h, 16) || !aligned(gamma, 16) || !aligned(x_bf16, 16)) return MOE_EALIGN;
+  (void)hipGetLastError();
+  return hip_rc(moe::launch_rmsnorm_bf16(h, gamma, eps, x_bf16, T, d, static_cast<hipStream_t>(stream)));
+}
 
 size_t moe_decode_ctx_workspace_bytes(const moe_dims* dims, uint32_t flags) {
   if (check_dims(dims, flags)) return 0;
@@ -329,11 +347,14 @@ int moe_decode_ctx_create(const moe_dims* dims, int n_layers, const moe_layer* l
   const int rc0 = check_dims(dims, flags);
   if (rc0) return rc0;
   if (!layers || !h || !workspace || !out || n_layers < 1 || n_layers > 4096) return MOE_EINVAL;
-  for (int l = 0; l < n_layers; ++l)
+  for (int l = 0; l < n_layers; ++l) {
     if (!layers[l].w_router || !layers[l].bias || !weights_ok(layers[l].weights)) return MOE_EINVAL;
+    if (layers[l].norm_weight && !(isfinite(layers[l].norm_eps) && layers[l].norm_eps >= 0.f)) return MOE_EINVAL;
+  }
   if (!aligned(h, 16) || !aligned(workspace, 16)) return MOE_EALIGN;
   for (int l = 0; l < n_layers; ++l)
-    if (!aligned(layers[l].w_router, 16) || !aligned(layers[l].bias, 4) || !weights_aligned(layers[l].weights))
+    if (!aligned(layers[l].w_router, 16) || !aligned(layers[l].bias, 4) || !weights_aligned(layers[l].weights) ||
+        !aligned(layers[l].norm_weight, 16))
       return MOE_EALIGN;
   const CtxLayout C = ctx_layout(dims, flags);
   if (workspace_bytes < C.total) return MOE_ENOSPACE;

@@ -564,26 +564,6 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ topk_
   }
 }
 
-// fp32 -> bf16 (round to nearest even) of n8 groups of 8 values: the input of a layer taken from a
-// residual stream.
-__global__ __launch_bounds__(256) void k_f32_to_bf16(const float* __restrict__ h, uint16_t* __restrict__ x,
-                                                     size_t n8) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const float4* hp = reinterpret_cast<const float4*>(h + 8 * i);
-  const float4 a = hp[0], b = hp[1];
-  *reinterpret_cast<u32x4*>(x + 8 * i) =
-      u32x4{float_to_bf16_bits(a.x) | ((uint32_t)float_to_bf16_bits(a.y) << 16),
-            float_to_bf16_bits(a.z) | ((uint32_t)float_to_bf16_bits(a.w) << 16),
-            float_to_bf16_bits(b.x) | ((uint32_t)float_to_bf16_bits(b.y) << 16),
-            float_to_bf16_bits(b.z) | ((uint32_t)float_to_bf16_bits(b.w) << 16)};
-}
-
-hipError_t launch_f32_to_bf16(const float* h, uint16_t* x, size_t n, hipStream_t st) {
-  const size_t n8 = n / 8;
-  hipLaunchKernelGGL(k_f32_to_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, h, x, n8);
-  return hipGetLastError();
-}
 
 int grouped_max_mtiles(const Shape& s) {
   // sum_e ceil(c_e / BM) <= floor(P / BM) + min(E, P), plus the shared group

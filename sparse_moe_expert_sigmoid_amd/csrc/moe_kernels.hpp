@@ -69,7 +69,12 @@ hipError_t launch_grouped_down(const Shape& s, const Routing& r, Q4 w2, Q4 s2, c
 // residual and y_bf16 as for launch_gemv_down_combine
 hipError_t launch_combine(const Shape& s, const float* topk_w, const Routing& r, const GroupedOut& o,
                           const float* residual, float* y, uint16_t* y_bf16, hipStream_t st);
+
+// norm.hip
 // x[i] = bf16(h[i]) for n values (n % 8 == 0), round to nearest even
 hipError_t launch_f32_to_bf16(const float* h, uint16_t* x, size_t n, hipStream_t st);
+// x[t] = bf16(h[t] / sqrt(mean(h[t]^2) + eps) * gamma) for T rows of d values (d % 8 == 0)
+hipError_t launch_rmsnorm_bf16(const float* h, const float* gamma, float eps, uint16_t* x, int T, int d,
+                               hipStream_t st);
 
 }  // namespace moe

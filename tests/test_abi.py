@@ -234,3 +234,28 @@ def test_decode_ctx_validation_before_any_hip_call():
     assert ctx_create(layers=[dict(good, bias=FAKE + 2)]) == abi.MOE_EALIGN
     assert moe.moe_decode_ctx_run(0, stream=0, check=False) == abi.MOE_EINVAL
     assert moe.moe_decode_ctx_destroy(None) == abi.MOE_OK
+
+
+def test_rmsnorm_validation_before_any_hip_call():
+    def norm(**kw):
+        args = dict(T=4, d=256, h=FAKE, gamma=FAKE, eps=1e-6, x=FAKE)
+        args.update(kw)
+        return moe.moe_rmsnorm_bf16(args["T"], args["d"], args["h"], args["gamma"], args["eps"], args["x"],
+                                    stream=0, check=False)
+    assert norm(T=0) == abi.MOE_EINVAL and norm(d=0) == abi.MOE_EINVAL
+    for name in ("h", "gamma", "x"):
+        assert norm(**{name: 0}) == abi.MOE_EINVAL, name
+        assert norm(**{name: FAKE + 4}) == abi.MOE_EALIGN, name
+    assert norm(eps=-1.0) == abi.MOE_EINVAL
+    assert norm(eps=float("nan")) == abi.MOE_EINVAL and norm(eps=float("inf")) == abi.MOE_EINVAL
+    assert norm(d=100) == abi.MOE_EUNSUPPORTED
+    assert norm(d=(1 << 20) + 8) == abi.MOE_EUNSUPPORTED
+
+
+def test_decode_ctx_norm_validation():
+    good = dict(WEIGHTS, w_router=FAKE, bias=FAKE)
+    assert ctx_create(layers=[good, dict(good, norm_weight=FAKE + 8, norm_eps=1e-6)]) == abi.MOE_EALIGN
+    assert ctx_create(layers=[dict(good, norm_weight=FAKE, norm_eps=-1.0)]) == abi.MOE_EINVAL
+    assert ctx_create(layers=[dict(good, norm_weight=FAKE, norm_eps=float("nan"))]) == abi.MOE_EINVAL
+    # eps is not looked at without a norm weight
+    assert ctx_create(layers=[dict(good, norm_eps=-1.0)], workspace_bytes=1) == abi.MOE_ENOSPACE

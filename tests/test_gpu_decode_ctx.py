@@ -114,3 +114,64 @@ def test_two_passes_compose():
     assert clear.any()
     r, g = ref["h"][clear], got[clear]
     assert np.linalg.norm(g - r) / np.linalg.norm(r) <= 5e-3
+
+
+# ----------------------------------------------------------------------------- pre-MoE norm
+
+@pytest.mark.parametrize("T,d,scale", [(1, 4096, 1.0), (5, 96, 30.0), (64, 2048, 0.01)])
+def test_rmsnorm_matches_oracle_to_one_bf16_step(T, d, scale):
+    """moe_rmsnorm_bf16 against the fp64 oracle rounded once to bf16: the GPU sums in fp32, so a value
+    within an fp32 rounding of a bf16 halfway point may land on the other neighbour (one step); every
+    other value is the same bits.  Run twice: the same bits (fixed reduction order)."""
+    rng = np.random.default_rng(T + d)
+    h = (rng.standard_normal((T, d)) * scale).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    eps = 1e-6
+    say(f"[case] rmsnorm T={T} d={d}")
+    x = torch.empty((T, d), dtype=torch.int16, device="cuda")
+    hd, gd = torch.from_numpy(h).cuda(), torch.from_numpy(gamma).cuda()
+    abi.moe_rmsnorm_bf16(T, d, hd, gd, eps, x)
+    again = torch.empty_like(x)
+    abi.moe_rmsnorm_bf16(T, d, hd, gd, eps, again)
+    torch.cuda.synchronize()
+    assert torch.equal(x, again)
+    got = x.cpu().numpy().view(np.uint16)
+    ref = oracle.f64_to_bf16_bits(oracle.rms_norm(h, gamma, eps))
+    step = np.abs(got.astype(np.int64) - ref.astype(np.int64))
+    assert step.max() <= 1, step.max()
+    assert (step == 0).mean() >= 0.99
+
+
+@pytest.mark.parametrize("name", ["gemv_T1", "grouped_ragged"])
+def test_chain_with_norm_matches_oracle(name):
+    """Every layer takes its input through the pre-MoE norm: parity with the oracle's chain, and the
+    stream stays bounded over many passes (the norm keeps every layer's input at unit scale)."""
+    dims, flags, n = CASES[name]
+    inputs, weights = make_stack(dims, n, 600)
+    rng = np.random.default_rng(601)
+    for inp, w in zip(inputs, weights):
+        gamma = rng.uniform(0.5, 1.5, dims.d).astype(np.float32)
+        inp["norm_weight"], inp["norm_eps"] = gamma, 1e-6
+        w["norm_weight"], w["norm_eps"] = torch.from_numpy(gamma).cuda(), 1e-6
+    for seed in range(602, 642):
+        h0 = start_stream(dims, seed, amp=3.0)
+        ref = oracle.decode_chain(inputs, h0)
+        clear = np.all(ref["margins"] > MARGIN, axis=0)
+        if clear.sum() >= max(1, int(0.8 * dims.T)):
+            break
+    else:
+        raise AssertionError("no seeded start with clear selections")
+    say(f"[case] decode ctx with norm {name} start seed {seed}")
+    h = torch.from_numpy(h0).cuda()
+    ctx = DecodeContext(dims, weights, h, flags=flags)
+    ctx.run()
+    torch.cuda.synchronize()
+    got = h.cpu().numpy().astype(np.float64)
+    r, g = ref["h"][clear], got[clear]
+    assert np.abs(g - r).max() <= 1e-2 * np.abs(r).max()
+    assert np.linalg.norm(g - r) / np.linalg.norm(r) <= 5e-3
+    for _ in range(20):
+        ctx.run()
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(h).all())
+    ctx.close()
