@@ -118,7 +118,7 @@ def test_two_passes_compose():
 
 # ----------------------------------------------------------------------------- pre-MoE norm
 
-@pytest.mark.parametrize("T,d,scale", [(1, 4096, 1.0), (5, 96, 30.0), (64, 2048, 0.01)])
+@pytest.mark.parametrize("T,d,scale", [(1, 4096, 1.0), (5, 96, 30.0), (64, 2048, 0.01), (2, 16384, 2.0)])
 def test_rmsnorm_matches_oracle_to_one_bf16_step(T, d, scale):
     """moe_rmsnorm_bf16 against the fp64 oracle rounded once to bf16: the GPU sums in fp32, so a value
     within an fp32 rounding of a bf16 halfway point may land on the other neighbour (one step); every
