@@ -259,8 +259,11 @@ size_t moe_decode_ctx_workspace_bytes(const moe_dims* dims, uint32_t flags);
  * objects (the graph and its executable form).  Every argument is checked
  * before the first HIP call (MOE_EINVAL, MOE_EALIGN, MOE_EUNSUPPORTED,
  * MOE_ENOSPACE as for the layer calls; n_layers outside 1..4096 or a norm
- * eps that is negative or not finite is MOE_EINVAL); a HIP failure while recording gives MOE_EHIP.  Nothing runs
- * until moe_decode_ctx_run.  On success *out receives the context. */
+ * eps that is negative or not finite is MOE_EINVAL); a HIP failure while
+ * recording gives MOE_EHIP.  The stack is recorded on a stream of the
+ * context's own in thread-local capture mode, so the calling thread must not
+ * be recording a graph itself.  Nothing runs until moe_decode_ctx_run.  On
+ * success *out receives the context. */
 int moe_decode_ctx_create(const moe_dims* dims, int n_layers, const moe_layer* layers, float* h, void* workspace,
                           size_t workspace_bytes, uint32_t flags, moe_decode_ctx** out);
 
