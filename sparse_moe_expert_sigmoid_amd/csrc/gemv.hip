@@ -20,7 +20,12 @@
 
 namespace moe {
 
-constexpr int kGemvTiles = 8;  // 4-block tiles per row group loaded together by a wavefront
+// 4-block tiles per row group a wavefront loads together before any arithmetic: the gate+up takes its
+// whole quarter of K (8 tiles at d = 4096) at once; the down pass (8 tiles at I = 1024) goes in two
+// batches of 4, so that the first batch's arithmetic overlaps the second's loads (0.26 us less per
+// decode step on MI355X; the gate+up loses 1.3 us the same way)
+constexpr int kGemvTiles = 8;
+constexpr int kDownTiles = 4;
 static_assert(kMaxGemvBlocksPerWave == kWave, "activation staging gives every lane one block");
 
 // ---------------------------------------------------------------------------
@@ -248,12 +253,12 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
       }
       hc0[wave][lane] = -(1032.f * sa + 72.f * sb);
     }
-    // codes and scales of up to kGemvTiles tiles per batch, all in flight before any arithmetic
-    u32x4 cq[kGemvTiles];
-    uint32_t dq[kGemvTiles];
-    int blk[kGemvTiles];
+    // codes and scales of up to kDownTiles tiles per batch, all in flight before any arithmetic
+    u32x4 cq[kDownTiles];
+    uint32_t dq[kDownTiles];
+    int blk[kDownTiles];
 #define MOE_DN_LOAD(TB)                                                        \
-    _Pragma("unroll") for (int j = 0; j < kGemvTiles; ++j) {                   \
+    _Pragma("unroll") for (int j = 0; j < kDownTiles; ++j) {                   \
       const int b = min(4 * min((TB) + j, ntile - 1) + G, nkb - 1);           \
       blk[j] = b;                                                              \
       cq[j] = ld16(qg + (size_t)b * 256 + 16 * n);                             \
@@ -261,10 +266,10 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
     }
     // the wavefront reads back only what its own lanes wrote: LDS operations of one wavefront are ordered
     float acc = 0.f;
-    for (int tb = 0; tb < ntile; tb += kGemvTiles) {
+    for (int tb = 0; tb < ntile; tb += kDownTiles) {
       MOE_DN_LOAD(tb);
 #pragma unroll
-      for (int j = 0; j < kGemvTiles; ++j) {
+      for (int j = 0; j < kDownTiles; ++j) {
         const float use = (tb + j < ntile && 4 * (tb + j) + G < nkb) ? 1.f : 0.f;
         const u32x4* hp = reinterpret_cast<const u32x4*>(hsm[wave][blk[j]]);
         float dot = hc0[wave][blk[j]];
