@@ -328,7 +328,10 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t
     const uint32_t valid = lane + 64 * i < E ? 0xFFFFFFFFu : 0u;
     key[i] = ordered_bits(sc[i] + bs[i]) & valid;
   }
-  // tau: the largest value with at least k keys >= it, i.e. the k-th largest key
+  // tau: the largest value with at least k keys >= it, i.e. the k-th largest key, found bit by bit from
+  // the top.  A candidate with exactly k keys at or above it already splits the k largest from the rest
+  // (the k-th largest key is >= it, the next one below it): the search stops there with tau just under
+  // the candidate, so that the keys above tau are those k and no tie is left to break.
   uint32_t tau = 0u;
 #pragma unroll 4
   for (int bit = 31; bit >= 0; --bit) {
@@ -336,7 +339,11 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t
     int cnt = 0;
 #pragma unroll
     for (int i = 0; i < NPER; ++i) cnt += popc(__builtin_amdgcn_ballot_w64(key[i] >= cand));
-    tau = cnt >= k ? cand : tau;
+    if (cnt == k) {  // uniform over the wavefront
+      tau = cand - 1u;
+      break;
+    }
+    tau = cnt > k ? cand : tau;
   }
   // chosen: every key above tau (fewer than k), then the lowest ids among the keys equal to tau
   uint64_t chosen[NPER];
