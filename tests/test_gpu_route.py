@@ -49,6 +49,31 @@ def test_exact_ties_go_to_the_lower_id(E, k, path):
     np.testing.assert_allclose(w, oracle.routing_weights(s, ref_ids), rtol=0, atol=W_ABS)
 
 
+@pytest.mark.parametrize("tie", [False, True], ids=["distinct", "tie_at_k"])
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("E,k", [(64, 10), (256, 10), (1024, 32)], ids=["E64k10", "E256k10", "E1024k32"])
+def test_one_ulp_apart_at_the_kth_place(E, k, path, tie):
+    # W_r = 0 again (every score exactly 1/2) and biases j * 2^-24 for a permutation j of 0 .. E-1: the
+    # keys 1/2 + j * 2^-24 are exact in fp32 and fp64 and neighbours are one fp32 ulp apart, so the
+    # k-th and (k+1)-th largest keys differ only in the last bit.  With tie, the (k+1)-th largest key is
+    # raised to equal the k-th, so that two keys share the k-th place (the lower id is taken).
+    dims = synth.Dims(T=6, d=64, E=E, k=k, I=32, I_shared=32)
+    inp = synth.make_inputs(dims, seed=17 + E + k, weights=False)
+    rng = np.random.default_rng(E * 7 + k + tie)
+    j = rng.permutation(E).astype(np.float64)
+    if tie:
+        j[np.argsort(-j)[k]] += 1.0
+    inp["w_router"] = np.zeros((E, dims.d), dtype=np.float32)
+    inp["bias"] = (j * 2.0 ** -24).astype(np.float32)
+    assert np.array_equal(inp["bias"].astype(np.float64), j * 2.0 ** -24)
+    say(f"[case] one-ulp gaps E={E} k={k} {path} tie={tie}")
+    ids, w = route(inp, PATHS[path])
+    s = np.full((dims.T, E), 0.5)
+    ref_ids, _ = oracle.select_experts(s, inp["bias"], k)
+    np.testing.assert_array_equal(ids, ref_ids)
+    np.testing.assert_allclose(w, oracle.routing_weights(s, ref_ids), rtol=0, atol=W_ABS)
+
+
 @pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("E,k", SHAPES, ids=[f"E{e}k{k}" for e, k in SHAPES])
 def test_slot_order_matches_oracle(E, k, path):
