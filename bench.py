@@ -203,7 +203,8 @@ def source_hash(*files):
     return h.hexdigest()[:16]
 
 
-GEMV_SOURCES = ("sparse_moe_expert_sigmoid_amd/csrc/gemv.hip", "sparse_moe_expert_sigmoid_amd/csrc/moe_device.hpp")
+GEMV_SOURCES = ("sparse_moe_expert_sigmoid_amd/csrc/gemv.hip", "sparse_moe_expert_sigmoid_amd/csrc/moe_device.hpp",
+                "sparse_moe_expert_sigmoid_amd/csrc/topk.hpp")
 GROUPED_SOURCES = ("sparse_moe_expert_sigmoid_amd/csrc/grouped.hip", "sparse_moe_expert_sigmoid_amd/csrc/moe_device.hpp")
 
 
@@ -221,11 +222,14 @@ def recorded_traffic(profile: str, sources) -> int | None:
     return int(fields["traffic_bytes_per_launch"])
 
 
-def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_sample=False, residual=False):
+def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_sample=False, residual=False,
+                 separate=False):
     cfg = synth.CONFIGS[name]
     dims = cfg.dims
     device = "cuda"
     L = COPIES[name]
+    # one layer call: moe_layer_forward, or with `separate` moe_route + moe_build_descriptors + moe_q4_forward
+    call = layer.layer_call if separate else layer.layer_call_fused
     inp0 = synth.make_inputs(cfg)
     weights = [layer.DeviceWeights.upload(inp0)]
     xs = [layer.to_device(inp0["x"], device)]
@@ -244,13 +248,13 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for c in range(L):  # eager pass: surfaces launch errors outside capture
-            layer.layer_call(xs[c], weights[c], spaces[c], stream=sh, residual=res[c])
+            call(xs[c], weights[c], spaces[c], stream=sh, residual=res[c])
     torch.cuda.synchronize()
 
     def capture(copies):
         hip.begin_capture(sh)
         for c in copies:
-            layer.layer_call(xs[c], weights[c], spaces[c], stream=sh, residual=res[c])
+            call(xs[c], weights[c], spaces[c], stream=sh, residual=res[c])
         g = hip.end_capture(sh)
         return g, hip.instantiate(g)
 
@@ -429,7 +433,7 @@ def traffic_run(name, torch, layer, synth):
     x = layer.to_device(inp["x"], "cuda")
     ws = layer.Workspace(inp["dims"], 0)
     for _ in range(3):
-        layer.layer_call(x, w, ws)
+        layer.layer_call_fused(x, w, ws)
     a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     a.fill_(1)
     b = torch.empty_like(a)
@@ -497,6 +501,9 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "batched_decode", "prefill", "long_prefill"])
     ap.add_argument("--secondary", default="prefill", help="second workload reported alongside ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="time each layer as moe_route + moe_build_descriptors + moe_q4_forward instead of "
+                         "moe_layer_forward (the same results)")
     ap.add_argument("--residual", action="store_true",
                     help="every step uses moe_q4_forward_residual (adds an fp32 [T][d] residual after the layer)")
     ap.add_argument("--all", action="store_true",
@@ -525,7 +532,8 @@ def main():
         rows = []
         for wl, n in (("decode", args.steps), ("batched_decode", max(40, args.steps // 8)),
                       ("prefill", max(20, args.steps // 40)), ("long_prefill", max(10, args.steps // 80))):
-            r = run_workload(wl, n, max(4, n // 10), torch, hip, abi, layer, synth, residual=args.residual)
+            r = run_workload(wl, n, max(4, n // 10), torch, hip, abi, layer, synth, residual=args.residual,
+                             separate=args.separate_calls)
             r.pop("_inp0", None)
             rows.append(r)
             print(f"[bench] {wl}: {r['ms_per_step'] * 1000:.1f} us/step, {r['tokens_per_s']:.0f} tokens/s",
@@ -538,11 +546,12 @@ def main():
                           "copy_ceiling": copy_ceiling(torch, [52 << 20, 1 << 30])}), flush=True)
         return
     prim = run_workload(args.workload, args.steps, args.warmup, torch, hip, abi, layer, synth,
-                        residual=args.residual)
+                        residual=args.residual, separate=args.separate_calls)
     sec = None
     if args.secondary and args.secondary != "none" and args.secondary != args.workload:
         n = max(20, args.steps // 40)
-        sec = run_workload(args.secondary, n, max(4, n // 10), torch, hip, abi, layer, synth, residual=args.residual)
+        sec = run_workload(args.secondary, n, max(4, n // 10), torch, hip, abi, layer, synth, residual=args.residual,
+                           separate=args.separate_calls)
     ctx = run_decode_ctx(max(50, args.steps // 4), torch, abi, layer, synth) if args.workload == "decode" else None
     ctxn = (run_decode_ctx(max(50, args.steps // 4), torch, abi, layer, synth, norm=True)
             if args.workload == "decode" else None)

@@ -206,6 +206,24 @@ int moe_q4_forward_residual(const moe_dims* dims, const uint16_t* x_bf16, const 
                             const moe_q4_weights* weights, const float* residual, float* y, void* scratch,
                             size_t scratch_bytes, uint32_t flags, void* stream);
 
+/* The whole layer in one call: moe_route, moe_build_descriptors and
+ * moe_q4_forward (residual NULL) or moe_q4_forward_residual (residual given,
+ * same rules) with the same arguments, giving the same topk_ids, topk_w and
+ * y bit for bit.  Page "feat(laguna): Laguna-S-2.1 decode on the CUDA engine"
+ * runs the decode layer as one recorded sequence of launches; here, on the
+ * small-T (GEMV) path, the top-k is not a launch of its own: every gate+up
+ * workgroup of a routed pair selects its token's experts from the router's
+ * logits itself (the same selection), and one of them per token writes
+ * topk_ids / topk_w, so a decode layer is three launches.  Every argument is
+ * checked before the first launch (MOE_EINVAL, MOE_EALIGN, MOE_EUNSUPPORTED,
+ * MOE_ENOSPACE as for the separate calls); MOE_EHIP if a launch fails.
+ * topk_ids / topk_w are outputs, as for moe_route; routing and scratch are
+ * sized by moe_routing_bytes / moe_scratch_bytes. */
+int moe_layer_forward(const moe_dims* dims, const uint16_t* x_bf16, const float* w_router, const float* bias,
+                      const moe_q4_weights* weights, const float* residual, float* y, int32_t* topk_ids,
+                      float* topk_w, void* routing, size_t routing_bytes, void* scratch, size_t scratch_bytes,
+                      uint32_t flags, void* stream);
+
 /* Pre-MoE norm (the step in front of the layer): for each of T rows of d
  * values (d % 8 == 0),
  *     x_t = bf16( h_t / sqrt(mean(h_t^2) + eps) * gamma )

@@ -12,7 +12,8 @@ from .abi import (  # noqa: F401
     MOE_FLAG_DEFAULT, MOE_FLAG_FORCE_GROUPED, MOE_FLAG_FORCE_GEMV, MOE_FLAG_ID_ORDER,
     MOE_FLAG_NO_BANDING, MOE_GEMV_MAX_T, MoeError, Dims, lib, lib_path,
     moe_supports, moe_path, moe_routing_bytes, moe_routing_layout_of, moe_scratch_bytes,
-    moe_route, moe_build_descriptors, moe_q4_forward, moe_q4_forward_residual, moe_strerror, EXPORTED_SYMBOLS,
+    moe_route, moe_build_descriptors, moe_q4_forward, moe_q4_forward_residual, moe_layer_forward, moe_strerror,
+    EXPORTED_SYMBOLS,
     moe_decode_ctx_workspace_bytes, moe_decode_ctx_create, moe_decode_ctx_run, moe_decode_ctx_destroy,
     moe_rmsnorm_bf16,
 )

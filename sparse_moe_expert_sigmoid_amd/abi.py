@@ -26,7 +26,7 @@ MOE_GEMV_FORCE_MAX_T = 64
 
 EXPORTED_SYMBOLS = (
     "moe_supports", "moe_path", "moe_routing_bytes", "moe_routing_layout_of", "moe_scratch_bytes",
-    "moe_route", "moe_build_descriptors", "moe_q4_forward", "moe_q4_forward_residual", "moe_strerror",
+    "moe_route", "moe_build_descriptors", "moe_q4_forward", "moe_q4_forward_residual", "moe_layer_forward", "moe_strerror",
     "moe_decode_ctx_workspace_bytes", "moe_decode_ctx_create", "moe_decode_ctx_run", "moe_decode_ctx_destroy",
     "moe_rmsnorm_bf16",
 )
@@ -106,6 +106,9 @@ def lib() -> ctypes.CDLL:
     L.moe_q4_forward_residual.argtypes = [D, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, POINTER(_Weights),
                                           c_void_p, c_void_p, c_void_p, c_size_t, c_uint32, c_void_p]
     L.moe_q4_forward_residual.restype = c_int
+    L.moe_layer_forward.argtypes = [D, c_void_p, c_void_p, c_void_p, POINTER(_Weights), c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_size_t, c_void_p, c_size_t, c_uint32, c_void_p]
+    L.moe_layer_forward.restype = c_int
     L.moe_decode_ctx_workspace_bytes.argtypes = [D, c_uint32]
     L.moe_decode_ctx_workspace_bytes.restype = c_size_t
     L.moe_decode_ctx_create.argtypes = [D, c_int, POINTER(_Layer), c_void_p, c_void_p, c_size_t, c_uint32,
@@ -218,6 +221,16 @@ def moe_q4_forward_residual(dims, x, topk_ids, topk_w, routing, weights, residua
                                        _ptr(residual), _ptr(y), _ptr(scratch), _nbytes(scratch, scratch_bytes),
                                        flags, _stream(stream))
     return _done(rc, check, "moe_q4_forward_residual")
+
+
+def moe_layer_forward(dims, x, w_router, bias, weights, y, topk_ids, topk_w, routing, scratch, residual=None,
+                      routing_bytes=None, scratch_bytes=None, flags: int = 0, stream=None, check: bool = True) -> int:
+    ws = weights if isinstance(weights, _Weights) else _weights(weights)
+    rc = lib().moe_layer_forward(ctypes.byref(Dims.of(dims)), _ptr(x), _ptr(w_router), _ptr(bias), ctypes.byref(ws),
+                                 _ptr(residual), _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(routing),
+                                 _nbytes(routing, routing_bytes), _ptr(scratch), _nbytes(scratch, scratch_bytes),
+                                 flags, _stream(stream))
+    return _done(rc, check, "moe_layer_forward")
 
 
 def moe_decode_ctx_workspace_bytes(dims, flags: int = 0) -> int:

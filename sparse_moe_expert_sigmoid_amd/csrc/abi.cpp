@@ -263,6 +263,63 @@ int moe_q4_forward_residual(const moe_dims* dims, const uint16_t* x_bf16, const 
 
 }  // extern "C"
 
+namespace {
+// The whole layer in one call.  Every argument is checked before the first launch; on the small-T
+// path the router GEMV is followed by the gate+up GEMV that selects its own experts (no top-k
+// launch), then the down + combine pass.  y_bf16 as for forward_impl.
+int layer_impl(const moe_dims* dims, const uint16_t* x_bf16, const float* w_router, const float* bias,
+               const moe_q4_weights* w, const float* residual, float* y, int32_t* topk_ids, float* topk_w,
+               void* routing, size_t routing_bytes, void* scratch, size_t scratch_bytes, uint32_t flags,
+               void* stream, uint16_t* y_bf16 = nullptr) {
+  int rc = check_dims(dims, flags);
+  if (rc) return rc;
+  if (!x_bf16 || !w_router || !bias || !w || !y || !topk_ids || !topk_w || !routing || !scratch) return MOE_EINVAL;
+  if (!q4_ok(w->w13) || !q4_ok(w->w2) || !q4_ok(w->s13) || !q4_ok(w->s2)) return MOE_EINVAL;
+  if (!aligned(x_bf16, 16) || !aligned(w_router, 16) || !aligned(bias, 4) || !aligned(y, 16) ||
+      !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(routing, 16) || !aligned(scratch, 16) ||
+      (residual && !aligned(residual, 16)))
+    return MOE_EALIGN;
+  if (!q4_aligned(w->w13) || !q4_aligned(w->w2) || !q4_aligned(w->s13) || !q4_aligned(w->s2)) return MOE_EALIGN;
+  const int path = choose_path(dims, flags);
+  const Layout L = routing_layout(dims);
+  if (routing_bytes < L.total) return MOE_ENOSPACE;
+  const ScratchLayout S = scratch_layout(dims, path);
+  if (scratch_bytes < S.total) return MOE_ENOSPACE;
+  if (path == 1) {
+    rc = moe_route(dims, x_bf16, w_router, bias, topk_ids, topk_w, routing, routing_bytes, flags, stream);
+    if (rc == MOE_OK) rc = moe_build_descriptors(dims, topk_ids, routing, routing_bytes, flags, stream);
+    if (rc == MOE_OK)
+      rc = forward_impl(dims, x_bf16, topk_ids, topk_w, routing, routing_bytes, w, residual, y, scratch,
+                        scratch_bytes, flags, stream, y_bf16);
+    return rc;
+  }
+  const moe::Shape s = shape_of(dims);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const moe::Routing r = routing_ptrs(routing, L);
+  char* sb = static_cast<char*>(scratch);
+  _Float16* h_r = reinterpret_cast<_Float16*>(sb + S.h_r);
+  _Float16* h_s = reinterpret_cast<_Float16*>(sb + S.h_s);
+  const moe::Q4 w13{w->w13.qs, w->w13.scales}, w2{w->w2.qs, w->w2.scales};
+  const moe::Q4 s13{w->s13.qs, w->s13.scales}, s2{w->s2.qs, w->s2.scales};
+  (void)hipGetLastError();
+  if (moe::launch_router_gemv(s, x_bf16, w_router, r.logits, st) != hipSuccess) return MOE_EHIP;
+  if (moe::launch_gemv_gateup_select(s, x_bf16, r.logits, bias, topk_ids, topk_w, w13, s13, h_r, h_s, st) !=
+      hipSuccess)
+    return MOE_EHIP;
+  return hip_rc(moe::launch_gemv_down_combine(s, topk_ids, topk_w, w2, s2, h_r, h_s, residual, y, y_bf16, st));
+}
+}  // namespace
+
+extern "C" {
+int moe_layer_forward(const moe_dims* dims, const uint16_t* x_bf16, const float* w_router, const float* bias,
+                      const moe_q4_weights* w, const float* residual, float* y, int32_t* topk_ids, float* topk_w,
+                      void* routing, size_t routing_bytes, void* scratch, size_t scratch_bytes, uint32_t flags,
+                      void* stream) {
+  return layer_impl(dims, x_bf16, w_router, bias, w, residual, y, topk_ids, topk_w, routing, routing_bytes, scratch,
+                    scratch_bytes, flags, stream);
+}
+}  // extern "C"
+
 struct moe_decode_ctx {
   hipGraph_t graph;
   hipGraphExec_t exec;
@@ -311,14 +368,11 @@ int enqueue_stack(const moe_dims* dims, int n_layers, const moe_layer* layers, f
     else if (l == 0)
       e = moe::launch_f32_to_bf16(h, x, (size_t)dims->T * dims->d, st);
     if (e != hipSuccess) return MOE_EHIP;
-    int rc = moe_route(dims, x, L.w_router, L.bias, ids, tw, routing, rbytes, flags, st);
-    if (rc == MOE_OK) rc = moe_build_descriptors(dims, ids, routing, rbytes, flags, st);
     // h = layer(x) + h; the last pass also writes the next layer's x = bf16(h) unless that layer's
     // input goes through the norm
     const bool fused_next = l + 1 < n_layers && !layers[l + 1].norm_weight;
-    if (rc == MOE_OK)
-      rc = forward_impl(dims, x, ids, tw, routing, rbytes, &L.weights, h, h, scratch, sbytes, flags, st,
-                        fused_next ? x : nullptr);
+    const int rc = layer_impl(dims, x, L.w_router, L.bias, &L.weights, h, h, ids, tw, routing, rbytes, scratch,
+                              sbytes, flags, st, fused_next ? x : nullptr);
     if (rc != MOE_OK) return rc;
   }
   return MOE_OK;

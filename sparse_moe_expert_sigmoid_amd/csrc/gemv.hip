@@ -17,6 +17,7 @@
 // read topk_ids directly.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
+#include "topk.hpp"
 
 namespace moe {
 
@@ -44,10 +45,18 @@ static_assert(kMaxGemvBlocksPerWave == kWave, "activation staging gives every la
 // h is written in fp16 (h_r[p][I] for pair p, h_s[t][Is] for the shared
 // expert), each group of 8 stored in the pair order of the down kernel: slot
 // i of a group holds element 0,4,1,5,2,6,3,7 [i].
-__global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
+//
+// NPER = 0: the expert of each pair comes from ids.  NPER > 0 (the key registers per lane of the
+// selection, ceil(E/64)): a routed workgroup selects its token's experts itself from the router's
+// logits with one wavefront (the same selection as the top-k launch, so the same experts, order and
+// weights), and the workgroup of row group 0 and slot 0 writes the selection to ids and topk_w for
+// the down pass; this takes the top-k launch off the decode step.
+template <int NPER>
+__global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict__ x, int32_t* __restrict__ ids,
                                                      Q4 w13, Q4 s13, _Float16* __restrict__ h_r, _Float16* __restrict__ h_s,
                                                      int T, int d, int k, int I, int Is, uint32_t mask_lo, uint32_t mask_hi,
-                                                     uint32_t magic) {
+                                                     uint32_t magic, const float* __restrict__ logits,
+                                                     const float* __restrict__ bias, float* __restrict__ topk_w, int E) {
   // x of this wavefront's quarter of K, per block: 16 dwords of fp16 pairs and the block's starting value
   __shared__ __attribute__((aligned(16))) uint32_t xs[4][kMaxGemvBlocksPerWave][16];
   __shared__ float xsum[4][kMaxGemvBlocksPerWave];
@@ -56,44 +65,48 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
   const int n = lane & 15, G = lane >> 4;
   const int job = blockIdx.y;
   const int P = T * k;
-  int t, Iw;
-  const uint8_t* qs;
-  const uint16_t* sc;
-  _Float16* out;
-  if (job < P) {
-    t = job / k;
-    const int e = ids[job];
-    Iw = I;
-    qs = w13.qs + (size_t)e * (2 * (size_t)I) * (d / 2);
-    sc = w13.sc + (size_t)e * (2 * (size_t)I) * (d / 32);
-    out = h_r + (size_t)job * I;
-  } else {
-    t = job - P;
-    Iw = Is;
-    qs = s13.qs;
-    sc = s13.sc;
-    out = h_s + (size_t)t * Is;
-  }
   const int i0 = blockIdx.x * 16;
+  const bool routed = job < P;  // uniform over the workgroup
+  const int Iw = routed ? I : Is;
   if (i0 >= Iw) return;  // uniform over the workgroup (Iw % 32 == 0): no barrier is skipped by part of it
+  const int t = routed ? job / k : job - P;
   const int nkb = d / 32;
   const int ntile = (nkb + 3) / 4;
   const int tw0 = (ntile * wave) / 4, tw1 = (ntile * (wave + 1)) / 4;  // this wavefront's tiles
   const int b0 = 4 * tw0;                                               // its first block
+  // x of this wavefront's blocks: lane l takes block b0 + l (clamped; blocks past the wavefront's last
+  // one are never read; a quarter of K holds at most 64 blocks as d <= 8192).  The loads go out first,
+  // so that with NPER > 0 the selection's logit loads are in flight with them.
+  const int bl = min(b0 + lane, nkb - 1);
+  const uint16_t* xb = x + (size_t)t * d + 32 * bl;
+  u32x4 xr[4];
+#pragma unroll
+  for (int dw = 0; dw < 4; ++dw) xr[dw] = ld16(xb + 8 * dw);
+  int e = 0;
+  if constexpr (NPER > 0) {
+    __shared__ TopkLds tsm;
+    if (routed && wave == 0)
+      topk_wave<NPER, 1>(logits + (size_t)t * E, 0, bias, ids + (size_t)t * k, topk_w + (size_t)t * k, E, k, lane,
+                         tsm, blockIdx.x == 0 && job % k == 0);
+    __syncthreads();
+    if (routed) e = __builtin_amdgcn_readfirstlane(tsm.slot_id[job % k]);
+  } else {
+    if (routed) e = ids[job];
+  }
+  const uint8_t* qs = routed ? w13.qs + (size_t)e * (2 * (size_t)I) * (d / 2) : s13.qs;
+  const uint16_t* sc = routed ? w13.sc + (size_t)e * (2 * (size_t)I) * (d / 32) : s13.sc;
+  _Float16* out = routed ? h_r + (size_t)job * I : h_s + (size_t)t * Is;
   const size_t grp_bytes = (size_t)nkb * 256;  // one 16-row group of codes
   const uint8_t* qg = qs + (size_t)(i0 >> 4) * grp_bytes;          // gate rows i0 .. i0+15
   const uint8_t* qu = qs + (size_t)((Iw + i0) >> 4) * grp_bytes;   // up rows Iw+i0 ..
   const uint16_t* sg = sc + (size_t)(i0 >> 4) * nkb * 16;
   const uint16_t* su = sc + (size_t)((Iw + i0) >> 4) * nkb * 16;
-  // stage x: lane l takes block b0 + l (clamped; blocks past the wavefront's last one are never read;
-  // a quarter of K holds at most 64 blocks as d <= 8192)
+  // stage x as fp16 pairs in the dot-product order, with each block's starting value
   {
-    const int bl = min(b0 + lane, nkb - 1);
-    const uint16_t* xb = x + (size_t)t * d + 32 * bl;
     float sa = 0.f, sb = 0.f;
 #pragma unroll
     for (int dw = 0; dw < 4; ++dw) {
-      const u32x4 u = ld16(xb + 8 * dw);
+      const u32x4 u = xr[dw];
       float xf[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -307,8 +320,30 @@ hipError_t launch_gemv_gateup(const Shape& s, const uint16_t* x, const int32_t* 
                               _Float16* h_r, _Float16* h_s, hipStream_t st) {
   const int Imax = s.I > s.Is ? s.I : s.Is;
   dim3 grid((Imax + 15) / 16, s.T * s.k + s.T);
-  hipLaunchKernelGGL(k_gemv_gateup, grid, dim3(256), 0, st, x, topk_ids, w13, s13, h_r, h_s, s.T, s.d, s.k, s.I, s.Is,
-                     0x000F000Fu, 0x00F000F0u, 0x64006400u);
+  hipLaunchKernelGGL(k_gemv_gateup<0>, grid, dim3(256), 0, st, x, const_cast<int32_t*>(topk_ids), w13, s13, h_r, h_s,
+                     s.T, s.d, s.k, s.I, s.Is, 0x000F000Fu, 0x00F000F0u, 0x64006400u, nullptr, nullptr, nullptr, s.E);
+  return hipGetLastError();
+}
+
+template <int NPER>
+static void gateup_select_nper(const Shape& s, const uint16_t* x, const float* logits, const float* bias,
+                               int32_t* topk_ids, float* topk_w, Q4 w13, Q4 s13, _Float16* h_r, _Float16* h_s,
+                               hipStream_t st) {
+  const int Imax = s.I > s.Is ? s.I : s.Is;
+  dim3 grid((Imax + 15) / 16, s.T * s.k + s.T);
+  hipLaunchKernelGGL(k_gemv_gateup<NPER>, grid, dim3(256), 0, st, x, topk_ids, w13, s13, h_r, h_s, s.T, s.d, s.k, s.I,
+                     s.Is, 0x000F000Fu, 0x00F000F0u, 0x64006400u, logits, bias, topk_w, s.E);
+}
+
+hipError_t launch_gemv_gateup_select(const Shape& s, const uint16_t* x, const float* logits, const float* bias,
+                                     int32_t* topk_ids, float* topk_w, Q4 w13, Q4 s13, _Float16* h_r, _Float16* h_s,
+                                     hipStream_t st) {
+  const int nper = (s.E + 63) / 64;
+  if (nper <= 1) gateup_select_nper<1>(s, x, logits, bias, topk_ids, topk_w, w13, s13, h_r, h_s, st);
+  else if (nper <= 2) gateup_select_nper<2>(s, x, logits, bias, topk_ids, topk_w, w13, s13, h_r, h_s, st);
+  else if (nper <= 4) gateup_select_nper<4>(s, x, logits, bias, topk_ids, topk_w, w13, s13, h_r, h_s, st);
+  else if (nper <= 8) gateup_select_nper<8>(s, x, logits, bias, topk_ids, topk_w, w13, s13, h_r, h_s, st);
+  else gateup_select_nper<16>(s, x, logits, bias, topk_ids, topk_w, w13, s13, h_r, h_s, st);
   return hipGetLastError();
 }
 

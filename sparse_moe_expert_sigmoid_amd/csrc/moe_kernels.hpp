@@ -47,6 +47,11 @@ hipError_t launch_build(const Shape& s, const int32_t* topk_ids, const Routing& 
 // gemv.hip  (small-T path)
 hipError_t launch_gemv_gateup(const Shape& s, const uint16_t* x, const int32_t* topk_ids, Q4 w13, Q4 s13,
                               _Float16* h_r, _Float16* h_s, hipStream_t st);
+// the same, each routed workgroup selecting its token's experts from the router's logits [T][E] (one
+// part) and the bias; the selection is also written to topk_ids / topk_w [T][k] for the down pass
+hipError_t launch_gemv_gateup_select(const Shape& s, const uint16_t* x, const float* logits, const float* bias,
+                                     int32_t* topk_ids, float* topk_w, Q4 w13, Q4 s13, _Float16* h_r, _Float16* h_s,
+                                     hipStream_t st);
 // residual: optional fp32 [T][d] added after the routed + shared sum (may be y itself; nullptr = none);
 // y_bf16: optional bf16 [T][d] copy of y, rounded to nearest even (nullptr = none)
 hipError_t launch_gemv_down_combine(const Shape& s, const int32_t* topk_ids, const float* topk_w, Q4 w2, Q4 s2,

@@ -1,0 +1,148 @@
+// Expert selection by one wavefront (sigmoid top-k with a selection-only
+// bias), shared by the top-k launch and the small-T gate+up GEMV that selects
+// its own experts.
+//
+// Page "feat(laguna): Laguna-S-2.1 decode on the CUDA engine"
+// (thewafflehaus/butter pull request 69): a sigmoid top-10 router with a
+// score-correction bias.  The bias only ranks (key = s + b); the weights are
+// the chosen experts' sigmoid scores normalised to sum to 1; ties go to the
+// lower expert id and the k choices are listed by descending key.
+#pragma once
+#include "moe_device.hpp"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Top-k: one wavefront per token.  Lane l holds experts l, l+64, ... as
+// order-preserving unsigned keys of s + b (lanes past E hold 0, below every
+// real key).  The k-th largest key tau is found bit by bit from the top: a
+// candidate bit stays set when at least k keys are >= the candidate (one
+// ballot and popcount per key register), so the search costs at most 32
+// short steps whatever k is (it stops once a candidate splits off exactly k
+// keys).  The chosen experts are the keys above tau and, of the keys equal
+// to tau, the lowest ids (ties go to the lower id).  They are compacted
+// into LDS; each finds its slot by counting the chosen keys that rank before
+// it (a larger key, or an equal key and a lower id), and the weights are
+// normalised by the sum of the chosen scores taken in slot order.
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  if (f != f) return 1u;  // NaN ranks below every number but above empty slots
+  if (f == 0.f) f = 0.f;  // -0 and +0 are the same key (then the lower id wins)
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+struct TopkLds {  // one wavefront's staging: the chosen entries in id order, then in slot order
+  uint32_t key[kMaxTopK];
+  int32_t id[kMaxTopK];
+  float s[kMaxTopK];
+  int32_t slot_id[kMaxTopK];
+  float slot_s[kMaxTopK];
+};
+
+__device__ __forceinline__ int popc(uint64_t m) { return __builtin_popcountll(m); }
+
+// Selection for one token by one wavefront: writes ids[0..k) and w[0..k) (unless write is false) and
+// leaves the ids and scores in slot order in sm.slot_id / sm.slot_s.  The wavefront reads back only
+// what its own lanes wrote to LDS: LDS operations of one wavefront are ordered.
+template <int NPER, int NPARTS>
+__device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t part_stride,
+                                          const float* __restrict__ bias, int32_t* __restrict__ ids,
+                                          float* __restrict__ w, int E, int k, int lane, TopkLds& sm,
+                                          bool write = true) {
+  // every load first, from clamped indices: one memory round trip
+  float lg[NPARTS][NPER], bs[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = min(lane + 64 * i, E - 1);
+    bs[i] = bias[e];
+#pragma unroll
+    for (int p = 0; p < NPARTS; ++p) lg[p][i] = lrow[p * part_stride + e];
+  }
+  uint32_t key[NPER];
+  float sc[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    float l = lg[0][i];
+#pragma unroll
+    for (int p = 1; p < NPARTS; ++p) l += lg[p][i];  // partial logits, in order
+    sc[i] = sigmoidf_(l);
+    const uint32_t valid = lane + 64 * i < E ? 0xFFFFFFFFu : 0u;
+    key[i] = ordered_bits(sc[i] + bs[i]) & valid;
+  }
+  // tau: the largest value with at least k keys >= it, i.e. the k-th largest key, found bit by bit from
+  // the top.  A candidate with exactly k keys at or above it already splits the k largest from the rest
+  // (the k-th largest key is >= it, the next one below it): the search stops there with tau just under
+  // the candidate, so that the keys above tau are those k and no tie is left to break.
+  uint32_t tau = 0u;
+#pragma unroll 4
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) cnt += popc(__builtin_amdgcn_ballot_w64(key[i] >= cand));
+    if (cnt == k) {  // uniform over the wavefront
+      tau = cand - 1u;
+      break;
+    }
+    tau = cnt > k ? cand : tau;
+  }
+  // chosen: every key above tau (fewer than k), then the lowest ids among the keys equal to tau
+  uint64_t chosen[NPER];
+  int need = k;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    chosen[i] = __builtin_amdgcn_ballot_w64(key[i] > tau);
+    need -= popc(chosen[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    uint64_t eq = __builtin_amdgcn_ballot_w64(key[i] == tau);
+    while (need > 0 && eq != 0) {
+      const uint64_t low = eq & (~eq + 1u);
+      chosen[i] |= low;
+      eq ^= low;
+      --need;
+    }
+  }
+  // compact the k chosen entries into LDS in id order
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const uint64_t m = chosen[i];
+    if ((m >> lane) & 1u) {
+      const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      sm.key[pos] = key[i];
+      sm.id[pos] = lane + 64 * i;
+      sm.s[pos] = sc[i];
+    }
+    base += popc(m);
+  }
+  // lane r < k takes entry r and counts the entries that rank before it: its slot
+  const int r = min(lane, k - 1);
+  const uint32_t K = sm.key[r];
+  const int I = sm.id[r];
+  const float S = sm.s[r];
+  int slot = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t Kj = (uint32_t)__builtin_amdgcn_readlane((int)K, j);
+    const int Ij = __builtin_amdgcn_readlane(I, j);
+    slot += (Kj > K || (Kj == K && Ij < I)) ? 1 : 0;
+  }
+  if (lane < k) {
+    sm.slot_id[slot] = I;
+    sm.slot_s[slot] = S;
+  }
+  const int q = min(lane, k - 1);
+  const int my_id = sm.slot_id[q];
+  const float my_s = sm.slot_s[q];
+  float tot = 0.f;
+  for (int j = 0; j < k; ++j)  // slot order, same value in every lane
+    tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_s), j));
+  if (write && lane < k) {
+    ids[lane] = my_id;
+    w[lane] = my_s / tot;
+  }
+}
+
+}  // namespace moe

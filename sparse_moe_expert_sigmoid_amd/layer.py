@@ -90,6 +90,13 @@ def layer_call(x: torch.Tensor, w: DeviceWeights, ws: Workspace, stream=None, re
     return ws.y
 
 
+def layer_call_fused(x: torch.Tensor, w: DeviceWeights, ws: Workspace, stream=None, residual=None) -> torch.Tensor:
+    """The same layer through the single entry point moe_layer_forward (same results); returns ws.y."""
+    abi.moe_layer_forward(ws.dims, x, w["w_router"], w["bias"], w, ws.y, ws.topk_ids, ws.topk_w, ws.routing,
+                          ws.scratch, residual=residual, flags=ws.flags, stream=stream)
+    return ws.y
+
+
 class DecodeContext:
     """A stack of MoE layers recorded once into a HIP graph by the library (moe_decode_ctx_*):
     every run() passes the residual stream h (fp32 [T][d], updated in place) through all layers,

@@ -259,3 +259,29 @@ def test_decode_ctx_norm_validation():
     assert ctx_create(layers=[dict(good, norm_weight=FAKE, norm_eps=float("nan"))]) == abi.MOE_EINVAL
     # eps is not looked at without a norm weight
     assert ctx_create(layers=[dict(good, norm_eps=-1.0)], workspace_bytes=1) == abi.MOE_ENOSPACE
+
+
+# ----------------------------------------------------------------------------- whole layer in one call
+
+def layer_fwd(dims=TINY, flags=0, **kw):
+    args = dict(x=FAKE, w_router=FAKE, bias=FAKE, weights=WEIGHTS, y=FAKE, topk_ids=FAKE, topk_w=FAKE, routing=FAKE,
+                scratch=FAKE, routing_bytes=1 << 30, scratch_bytes=1 << 30, stream=0)
+    args.update(kw)
+    return moe.moe_layer_forward(dims, flags=flags, check=False, **args)
+
+
+@pytest.mark.parametrize("flags", [0, abi.MOE_FLAG_FORCE_GROUPED, abi.MOE_FLAG_FORCE_GEMV])
+def test_layer_forward_validation_before_any_launch(flags):
+    # every rejection happens on the host before the first launch (no GPU is touched here)
+    assert layer_fwd(dims=d(k=0), flags=flags) == abi.MOE_EINVAL
+    assert layer_fwd(dims=d(d=40), flags=flags) == abi.MOE_EUNSUPPORTED
+    for name in ["x", "w_router", "bias", "y", "topk_ids", "topk_w", "routing", "scratch"]:
+        assert layer_fwd(flags=flags, **{name: 0}) == abi.MOE_EINVAL, name
+    for name in WEIGHTS:
+        assert layer_fwd(flags=flags, weights=dict(WEIGHTS, **{name: 0})) == abi.MOE_EINVAL, name
+    for name in ["x", "w_router", "y", "routing", "scratch", "residual"]:
+        assert layer_fwd(flags=flags, **{name: FAKE + 4}) == abi.MOE_EALIGN, name
+    for name in ["bias", "topk_ids", "topk_w"]:
+        assert layer_fwd(flags=flags, **{name: FAKE + 2}) == abi.MOE_EALIGN, name
+    assert layer_fwd(flags=flags, routing_bytes=moe.moe_routing_bytes(TINY, flags) - 1) == abi.MOE_ENOSPACE
+    assert layer_fwd(flags=flags, scratch_bytes=moe.moe_scratch_bytes(TINY, flags) - 1) == abi.MOE_ENOSPACE
