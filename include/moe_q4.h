@@ -61,7 +61,7 @@
  *             r, block b is element ((r/16)*(K/32) + b)*16 + r%16
  *     value = (q - 8) * scale          (q the 4-bit code, 0..15)
  *   Both are index permutations of the row-major arrays [rows][K/2] and
- *   [rows][K/32] (the Python binding's pack_codes / pack_scales).
+ *   [rows][K/32]; moe_q4_pack (below) performs it on the device.
  *   w13  [E][2I][d]  gate rows 0..I-1, up rows I..2I-1 of every expert
  *   w2   [E][d][I]
  *   s13  [2*I_shared][d], s2 [d][I_shared]   (shared expert, same split)
@@ -80,7 +80,13 @@
  *   Both paths round x to fp16 for the expert projections and keep the
  *   SwiGLU outputs in fp16 between the two projections; the grouped path
  *   also stores every expert's down-projection output in fp16 before the
- *   combine: those values must stay within the fp16 range (65504).
+ *   combine.  On both paths the same three quantities -- x as the experts
+ *   see it, h, and each expert's output before the routing weight -- are
+ *   saturated to the fp16 range: a value beyond +-65504 becomes +-65504,
+ *   one inside it is rounded to nearest even.  Finite inputs never give Inf
+ *   or NaN; results are accurate while those values stay inside the range
+ *   (the router always sees the unsaturated bf16 x).  Inf/NaN inputs are
+ *   outside the contract.
  */
 #ifndef MOE_Q4_H
 #define MOE_Q4_H
@@ -97,7 +103,11 @@ extern "C" {
 #define MOE_EINVAL       (-1)  /* null pointer, non-positive size, k > E          */
 #define MOE_EALIGN       (-2)  /* an array not 16-byte aligned                    */
 #define MOE_EUNSUPPORTED (-3)  /* d, I or I_shared not a multiple of 32, E > 1024,
-                                  k > 32, or a size beyond the chosen path's range */
+                                  k > 32, or a size beyond the chosen path's range:
+                                  small-T path d <= 8192, I, I_shared <= 2048, T <= 64;
+                                  grouped path max(I, I_shared) * d < 2^31 (32-bit
+                                  offsets into one expert's weights); both paths
+                                  (T*k + T) * max(d, I) < 2^31 */
 #define MOE_ENOSPACE     (-4)  /* routing workspace or scratch smaller than needed */
 #define MOE_EHIP         (-5)  /* the HIP runtime rejected a kernel launch          */
 
@@ -168,26 +178,54 @@ int moe_routing_layout_of(const moe_dims* dims, uint32_t flags, moe_routing_layo
 /* Scratch size in bytes needed by moe_q4_forward (0 if unsupported). */
 size_t moe_scratch_bytes(const moe_dims* dims, uint32_t flags);
 
-/* Router and expert selection.
- * Writes topk_ids int32 [T][k] and topk_w float [T][k] (descending s + b;
- * weights sum to 1).  Uses the logits region of `routing` as scratch. */
+/* Router and expert selection: page "feat(laguna): Laguna-S-2.1 decode on
+ * the CUDA engine" (thewafflehaus/butter pull request 69), the sigmoid
+ * top-10 router with a score-correction bias that only ranks the experts.
+ * For every token t: l = W_r x_t (fp32 accumulate), s = sigmoid(l), the k
+ * experts with the largest s + b (ties to the lower id) listed by descending
+ * s + b, and weights s_j / sum s_j.
+ * x_bf16 [T][d] (16-byte aligned), w_router float [E][d] (16-byte aligned),
+ * bias float [E]: inputs.  topk_ids int32 [T][k], topk_w float [T][k]:
+ * outputs.  routing: the caller's routing workspace (moe_routing_bytes); its
+ * logits region is used as scratch.  MOE_EINVAL (NULL pointer, bad dims or
+ * flags), MOE_EALIGN, MOE_EUNSUPPORTED, MOE_ENOSPACE, MOE_EHIP. */
 int moe_route(const moe_dims* dims, const uint16_t* x_bf16, const float* w_router,
               const float* bias, int32_t* topk_ids, float* topk_w,
               void* routing, size_t routing_bytes, uint32_t flags, void* stream);
 
-/* Routing build for the grouped path: per-expert counts, CSR offsets, the
- * stable (expert, token) order of the pairs and its inverse, the expert of
- * every sorted row, the group schedule order (largest first, ties to the
- * lower id; MOE_FLAG_ID_ORDER: id order) and the M-tile prefix.  On the
- * small-T path it enqueues nothing and returns MOE_OK. */
+/* Routing build for the grouped path: page "feat(laguna): batched prefill
+ * with tensor-core projections, fused MoE, CTA scheduling" (grouped-GEMM MoE
+ * with descriptors built on the device, descending-size expert order) and
+ * the Nemotron MoE commits of thewafflehaus/FFAI pull request 72 (one
+ * device-side fill from the router's CSR offsets; router-sorted token
+ * indices; the expert id of every sorted row expanded from the offsets).
+ * Writes into `routing`: per-expert counts, CSR offsets, the stable (expert,
+ * token) order of the pairs and its inverse, the expert of every sorted row,
+ * the group schedule order (largest first, ties to the lower id;
+ * MOE_FLAG_ID_ORDER: id order) and the M-tile prefix (layout:
+ * moe_routing_layout_of).  topk_ids int32 [T][k] is the input (values in
+ * [0, E)).  On the small-T path it enqueues nothing and returns MOE_OK.
+ * MOE_EINVAL, MOE_EALIGN, MOE_EUNSUPPORTED, MOE_ENOSPACE, MOE_EHIP. */
 int moe_build_descriptors(const moe_dims* dims, const int32_t* topk_ids,
                           void* routing, size_t routing_bytes, uint32_t flags,
                           void* stream);
 
-/* Expert computation and combine: writes y float [T][d].
+/* Expert computation and combine: page "feat(laguna): Laguna-S-2.1 decode on
+ * the CUDA engine" (SwiGLU experts over Q4 weights, gate and up fused, the
+ * shared expert always on) and the Nemotron MoE commits of
+ * thewafflehaus/FFAI pull request 72 (gather-on-read through the sorted
+ * token indices, a deterministic scatter-add, "ffai_add3": routed terms
+ * summed first, then the shared expert).  For every token
+ *   y_t = (sum_{j=0..k-1} w_tj * W_d[e] (silu(W_g[e] x_t) * (W_u[e] x_t)))
+ *         + W_sd (silu(W_sg x_t) * (W_su x_t)),  e = topk_ids[t][j],
+ * summed in j order without atomics (bitwise reproducible).
+ * x_bf16 [T][d], topk_ids, topk_w [T][k] (as written by moe_route) and the
+ * Q4 weights are inputs; y float [T][d] (16-byte aligned) is the output.
  * `routing` must hold what moe_build_descriptors wrote for the same
- * topk_ids (grouped path only); `scratch` holds intermediate activations
- * and per-pair outputs and needs moe_scratch_bytes() bytes. */
+ * topk_ids (grouped path only; may be NULL on the small-T path); `scratch`
+ * holds intermediate activations and per-pair outputs and needs
+ * moe_scratch_bytes() bytes.  MOE_EINVAL, MOE_EALIGN, MOE_EUNSUPPORTED,
+ * MOE_ENOSPACE, MOE_EHIP. */
 int moe_q4_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids,
                    const float* topk_w, const void* routing, size_t routing_bytes,
                    const moe_q4_weights* weights, float* y, void* scratch,
@@ -294,6 +332,27 @@ int moe_decode_ctx_run(moe_decode_ctx* ctx, void* stream);
 /* Release the context's host objects (NULL is allowed).  Work already
  * enqueued by moe_decode_ctx_run completes normally. */
 int moe_decode_ctx_destroy(moe_decode_ctx* ctx);
+
+/* Repack Q4 matrices from the plain row-major layout into the 16-row groups
+ * every other call reads, on the device (page "feat(laguna): Laguna-S-2.1
+ * decode on the CUDA engine" loads its Q4-requantised weights once and keeps
+ * them resident; this is the one-time step at load).  n_mats matrices of
+ * shape [rows][K], stacked (an expert stack [E][rows][K] is n_mats = E):
+ *   qs_in       uint8  [n_mats][rows][K/2]   row-major codes: byte i of a row
+ *               holds element 2i (low nibble) and 2i+1 (high nibble)
+ *   scales_in   uint16 [n_mats][rows][K/32]  row-major fp16 scale bits
+ *   qs_out      uint8  [n_mats][rows/16][K/32][16][16]
+ *   scales_out  uint16 [n_mats][rows/16][K/32][16]
+ * (the layout of moe_q4 above, per matrix).  A pure permutation of whole
+ * 16-byte code blocks and of scales; nothing is computed.  All four are
+ * DEVICE arrays owned by the caller; the inputs must not overlap the
+ * outputs (out-of-place only).  Enqueued on `stream`; no allocation.
+ * MOE_EINVAL: a size < 1, a NULL pointer, or overlapping in/out ranges;
+ * MOE_EUNSUPPORTED: rows % 16 != 0, K % 32 != 0, or rows or K > 2^24;
+ * MOE_EALIGN: qs_in, qs_out or scales_out not 16-byte aligned, or scales_in
+ * not 2-byte aligned; MOE_EHIP. */
+int moe_q4_pack(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs_in, const uint16_t* scales_in,
+                uint8_t* qs_out, uint16_t* scales_out, void* stream);
 
 /* Static string for a return code; never NULL. */
 const char* moe_strerror(int code);

@@ -12,7 +12,8 @@ import os
 from ctypes import POINTER, Structure, c_char_p, c_float, c_int, c_int32, c_size_t, c_uint32, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(HERE, "libmoe_q4.so")
+# MOE_Q4_LIB names another build of the same library (the host-sanitized one the CPU tests load)
+lib_path = os.environ.get("MOE_Q4_LIB") or os.path.join(HERE, "libmoe_q4.so")
 
 MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EUNSUPPORTED, MOE_ENOSPACE, MOE_EHIP = 0, -1, -2, -3, -4, -5
 MOE_FLAG_DEFAULT = 0
@@ -28,7 +29,7 @@ EXPORTED_SYMBOLS = (
     "moe_supports", "moe_path", "moe_routing_bytes", "moe_routing_layout_of", "moe_scratch_bytes",
     "moe_route", "moe_build_descriptors", "moe_q4_forward", "moe_q4_forward_residual", "moe_layer_forward", "moe_strerror",
     "moe_decode_ctx_workspace_bytes", "moe_decode_ctx_create", "moe_decode_ctx_run", "moe_decode_ctx_destroy",
-    "moe_rmsnorm_bf16",
+    "moe_rmsnorm_bf16", "moe_q4_pack",
 )
 
 
@@ -120,6 +121,8 @@ def lib() -> ctypes.CDLL:
     L.moe_decode_ctx_destroy.restype = c_int
     L.moe_rmsnorm_bf16.argtypes = [c_int, c_int, c_void_p, c_void_p, c_float, c_void_p, c_void_p]
     L.moe_rmsnorm_bf16.restype = c_int
+    L.moe_q4_pack.argtypes = [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+    L.moe_q4_pack.restype = c_int
     L.moe_strerror.argtypes = [c_int]
     L.moe_strerror.restype = c_char_p
     _lib = L
@@ -268,3 +271,12 @@ def moe_decode_ctx_destroy(ctx) -> int:
 def moe_rmsnorm_bf16(T: int, d: int, h, gamma, eps: float, x, stream=None, check: bool = True) -> int:
     rc = lib().moe_rmsnorm_bf16(T, d, _ptr(h), _ptr(gamma), float(eps), _ptr(x), _stream(stream))
     return _done(rc, check, "moe_rmsnorm_bf16")
+
+
+def moe_q4_pack(n_mats: int, rows: int, K: int, qs_in, scales_in, qs_out, scales_out, stream=None,
+                check: bool = True) -> int:
+    """Row-major Q4 codes [n_mats][rows][K/2] and scales [n_mats][rows][K/32] -> the library's 16-row
+    groups, on the device (out of place)."""
+    rc = lib().moe_q4_pack(n_mats, rows, K, _ptr(qs_in), _ptr(scales_in), _ptr(qs_out), _ptr(scales_out),
+                           _stream(stream))
+    return _done(rc, check, "moe_q4_pack")

@@ -50,6 +50,11 @@ int check_dims(const moe_dims* d, uint32_t flags) {
   if (choose_path(d, flags) == 0) {
     if (d->d > 8192 || d->I > 2048 || d->I_shared > 2048) return MOE_EUNSUPPORTED;
     if (d->T > MOE_GEMV_FORCE_MAX_T) return MOE_EUNSUPPORTED;
+  } else {
+    // The grouped GEMMs address one expert's weights through 32-bit buffer offsets: a gate+up stack of
+    // 2*I rows by d/2 code bytes (I*d bytes) or a down matrix (d*I/2 bytes) must stay below 2^31.
+    const long long Imax = d->I > d->I_shared ? d->I : d->I_shared;
+    if (Imax * d->d >= (1LL << 31)) return MOE_EUNSUPPORTED;
   }
   return MOE_OK;
 }
@@ -447,6 +452,25 @@ int moe_decode_ctx_destroy(moe_decode_ctx* ctx) {
   (void)hipGraphDestroy(ctx->graph);
   delete ctx;
   return MOE_OK;
+}
+
+int moe_q4_pack(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs_in, const uint16_t* scales_in,
+                uint8_t* qs_out, uint16_t* scales_out, void* stream) {
+  if (n_mats < 1 || rows < 1 || K < 1 || !qs_in || !scales_in || !qs_out || !scales_out) return MOE_EINVAL;
+  if (rows % 16 || K % 32 || rows > (1 << 24) || K > (1 << 24)) return MOE_EUNSUPPORTED;
+  if (!aligned(qs_in, 16) || !aligned(qs_out, 16) || !aligned(scales_out, 16) || !aligned(scales_in, 2))
+    return MOE_EALIGN;
+  const size_t nblocks = (size_t)n_mats * (size_t)rows * (size_t)(K / 32);
+  const uintptr_t qi = (uintptr_t)qs_in, qo = (uintptr_t)qs_out, si = (uintptr_t)scales_in,
+                  so = (uintptr_t)scales_out;
+  const size_t qb = 16 * nblocks, sb = 2 * nblocks;
+  auto overlap = [](uintptr_t a, size_t na, uintptr_t b, size_t nb) { return a < b + nb && b < a + na; };
+  if (overlap(qo, qb, qi, qb) || overlap(qo, qb, si, sb) || overlap(so, sb, qi, qb) || overlap(so, sb, si, sb) ||
+      overlap(qo, qb, so, sb))
+    return MOE_EINVAL;
+  (void)hipGetLastError();
+  return hip_rc(moe::launch_q4_pack((size_t)n_mats, rows, K, qs_in, scales_in, qs_out, scales_out,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 const char* moe_strerror(int code) {

@@ -110,8 +110,8 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
       float xf[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        xf[2 * m] = bf16_bits_to_float(u[m] & 0xFFFFu);
-        xf[2 * m + 1] = bf16_bits_to_float(u[m] >> 16);
+        xf[2 * m] = clamp_f16_range(bf16_bits_to_float(u[m] & 0xFFFFu));  // saturated to the fp16 range
+        xf[2 * m + 1] = clamp_f16_range(bf16_bits_to_float(u[m] >> 16));
       }
       const half2v p0 = {(_Float16)xf[0], (_Float16)xf[4]};
       const half2v p1 = {(_Float16)(0.0625f * xf[1]), (_Float16)(0.0625f * xf[5])};
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
     const float g = ((red[0][0][r] + red[1][0][r]) + red[2][0][r]) + red[3][0][r];
     const float u = ((red[0][1][r] + red[1][1][r]) + red[2][1][r]) + red[3][1][r];
     const int i = i0 + r;
-    out[(i & ~7) + perm_slot(i & 7)] = (_Float16)(siluf_(g) * u);
+    out[(i & ~7) + perm_slot(i & 7)] = to_f16_sat(siluf_(g) * u);
   }
 }
 
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
 #undef MOE_DN_LOAD
     acc += __shfl_xor(acc, 16, kWave);
     acc += __shfl_xor(acc, 32, kWave);
-    if (lane < 16) part[slot][lane] = acc;
+    if (lane < 16) part[slot][lane] = clamp_f16_range(acc);  // each expert's output saturates as on the grouped path
   }
   __syncthreads();
   if (threadIdx.x < 16) {

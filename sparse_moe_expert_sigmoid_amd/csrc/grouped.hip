@@ -279,7 +279,7 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
             const float gv = 16.f * acc[mt][xh][2 * j + e], uv = 16.f * acc[mt][2 + xh][2 * j + e];
             hv[e] = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;
           }
-          h[j] = half2v{(_Float16)hv[0], (_Float16)hv[1]};
+          h[j] = half2v{to_f16_sat(hv[0]), to_f16_sat(hv[1])};
         }
         // h is stored in the dequant pair order inside each group of 8 columns (slot 2m holds column
         // m, slot 2m+1 column m+4): lanes G and G^1 (16 lanes apart) hold the two halves of a group.
@@ -309,8 +309,8 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
       const int row = mt * 16 + c.n;
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns) {
-        const half2v p0 = {(_Float16)(16.f * acc[mt][ns][0]), (_Float16)(16.f * acc[mt][ns][1])};
-        const half2v p1 = {(_Float16)(16.f * acc[mt][ns][2]), (_Float16)(16.f * acc[mt][ns][3])};
+        const half2v p0 = {to_f16_sat(16.f * acc[mt][ns][0]), to_f16_sat(16.f * acc[mt][ns][1])};
+        const half2v p1 = {to_f16_sat(16.f * acc[mt][ns][2]), to_f16_sat(16.f * acc[mt][ns][3])};
         const int chunk = 8 * c.wave + 2 * ns + (c.G >> 1);
         *reinterpret_cast<uint2*>(As + row * (kDownBandCols * 2) + ((chunk ^ (row & 31)) * 16) + 8 * (c.G & 1)) =
             uint2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
@@ -485,8 +485,9 @@ __global__ __launch_bounds__(kGroupedThreads, 8 / kGroupedWaves) void k_grouped(
 
 // bf16 -> fp16 copy of the activations for the gate+up A operand, stored in
 // the dequant pair order inside every group of 8 (x0 x4 x1 x5 x2 x6 x3 x7).
-// The conversion is exact inside the fp16 range; round-toward-zero
-// saturates values beyond it to +-65504.
+// The conversion is exact inside the fp16 normal range, rounds to nearest
+// even in the subnormal range and saturates values beyond it to +-65504
+// (the same conversion as the small-T path's staging).
 __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, _Float16* __restrict__ x16,
                                                   size_t n8) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -496,7 +497,7 @@ __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x
   for (int m = 0; m < 4; ++m) {
     const float lo = __builtin_bit_cast(float, v[m] << 16);
     const float hi = __builtin_bit_cast(float, v[m] & 0xFFFF0000u);
-    v[m] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    v[m] = __builtin_bit_cast(uint32_t, half2v{to_f16_sat(lo), to_f16_sat(hi)});
   }
   uint32_t o[4];
   x_bf16_pairs(v, o);  // same 16-bit lane shuffle as for bf16 pairs

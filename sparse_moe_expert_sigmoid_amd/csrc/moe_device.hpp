@@ -45,6 +45,13 @@ __device__ __forceinline__ float fp16_bits_to_float(uint32_t bits16) {
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }
+// The fp16 activations of both paths (x for the expert projections, the SwiGLU output h, each
+// expert's down-projection output) saturate: a value beyond the fp16 range becomes +-65504, one inside
+// it rounds to nearest even.  Finite inputs therefore never give Inf or NaN.
+constexpr float kF16Max = 65504.0f;
+__device__ __forceinline__ float clamp_f16_range(float v) { return __builtin_amdgcn_fmed3f(v, -kF16Max, kF16Max); }
+__device__ __forceinline__ _Float16 to_f16_sat(float v) { return (_Float16)clamp_f16_range(v); }
+
 // fp32 -> bf16 bits, round to nearest with ties to even (add 0x7FFF plus the lowest kept bit, keep the
 // top half; a carry into the exponent gives the next binade or infinity).  NaN -> 0x7FC0.
 __device__ __forceinline__ uint16_t float_to_bf16_bits(float v) {

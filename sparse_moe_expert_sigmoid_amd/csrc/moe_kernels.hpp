@@ -75,6 +75,10 @@ hipError_t launch_grouped_down(const Shape& s, const Routing& r, Q4 w2, Q4 s2, c
 hipError_t launch_combine(const Shape& s, const float* topk_w, const Routing& r, const GroupedOut& o,
                           const float* residual, float* y, uint16_t* y_bf16, hipStream_t st);
 
+// pack.hip: n_mats row-major Q4 matrices [rows][K] -> the 16-row-group layout (rows % 16 == 0, K % 32 == 0)
+hipError_t launch_q4_pack(size_t n_mats, int rows, int K, const uint8_t* qs_in, const uint16_t* sc_in,
+                          uint8_t* qs_out, uint16_t* sc_out, hipStream_t st);
+
 // norm.hip
 // x[i] = bf16(h[i]) for n values (n % 8 == 0), round to nearest even
 hipError_t launch_f32_to_bf16(const float* h, uint16_t* x, size_t n, hipStream_t st);

@@ -12,24 +12,6 @@ from . import abi
 WEIGHT_KEYS = ("w13_qs", "w13_sc", "w2_qs", "w2_sc", "s13_qs", "s13_sc", "s2_qs", "s2_sc")
 
 
-def pack_scales(sc: np.ndarray) -> np.ndarray:
-    """Q4 scales [..., rows, K/32] -> the library's layout [..., rows/16, K/32, 16] (an index
-    permutation: the scale of row r, block b moves to ((r/16)*(K/32) + b)*16 + r%16)."""
-    *lead, rows, nkb = sc.shape
-    assert rows % 16 == 0, rows
-    return np.ascontiguousarray(sc.reshape(*lead, rows // 16, 16, nkb).swapaxes(-1, -2))
-
-
-def pack_codes(qs: np.ndarray) -> np.ndarray:
-    """Q4 codes [..., rows, K/2] (row-major, byte i = elements 2i, 2i+1) -> the library's layout
-    [..., rows/16, K/32, 16, 16]: the 16-byte block b of row r moves to byte ((r/16)*(K/32) + b)*256 +
-    (r%16)*16 (an index permutation of whole blocks)."""
-    *lead, rows, half_k = qs.shape
-    assert rows % 16 == 0 and half_k % 16 == 0, qs.shape
-    nkb = half_k // 16
-    return np.ascontiguousarray(qs.reshape(*lead, rows // 16, 16, nkb, 16).swapaxes(-3, -2))
-
-
 def to_device(a: np.ndarray, device) -> torch.Tensor:
     """numpy -> torch on `device`; uint16 bit patterns travel as int16 (same bytes)."""
     a = np.ascontiguousarray(a)
@@ -47,9 +29,16 @@ class DeviceWeights(dict):
         w.dims = inp["dims"]
         w["w_router"] = to_device(inp["w_router"], device)
         w["bias"] = to_device(inp["bias"], device)
-        for key in WEIGHT_KEYS:
-            pack = pack_scales if key.endswith("_sc") else pack_codes
-            w[key] = to_device(pack(inp[key]), device)
+        # row-major Q4 arrays go up as they are; the library regroups them on the device (moe_q4_pack)
+        for name in ("w13", "w2", "s13", "s2"):
+            qs, sc = inp[name + "_qs"], inp[name + "_sc"]
+            n_mats = qs.shape[0] if qs.ndim == 3 else 1
+            rows, K = qs.shape[-2], 2 * qs.shape[-1]
+            qs_in, sc_in = to_device(qs, device), to_device(sc, device)
+            w[name + "_qs"] = torch.empty_like(qs_in)
+            w[name + "_sc"] = torch.empty_like(sc_in)
+            abi.moe_q4_pack(n_mats, rows, K, qs_in, sc_in, w[name + "_qs"], w[name + "_sc"],
+                            stream=torch.cuda.current_stream(qs_in.device))
         return w
 
 

@@ -285,3 +285,57 @@ def test_layer_forward_validation_before_any_launch(flags):
         assert layer_fwd(flags=flags, **{name: FAKE + 2}) == abi.MOE_EALIGN, name
     assert layer_fwd(flags=flags, routing_bytes=moe.moe_routing_bytes(TINY, flags) - 1) == abi.MOE_ENOSPACE
     assert layer_fwd(flags=flags, scratch_bytes=moe.moe_scratch_bytes(TINY, flags) - 1) == abi.MOE_ENOSPACE
+
+
+# ----------------------------------------------------------------------------- 32-bit offsets of the grouped path
+
+@pytest.mark.parametrize("dd,I,Is", [(65536, 32768, 32), (65536, 32, 32768), (32768, 65536, 32)])
+def test_grouped_path_rejects_shapes_whose_weight_offsets_leave_31_bits(dd, I, Is):
+    """max(I, I_shared) * d reaching 2^31 is rejected on the grouped path (one expert's gate+up stack is
+    I*d bytes of codes, addressed through 32-bit buffer offsets); 32 less in the larger size is accepted.
+    Host only: no such shape is ever launched."""
+    T = 9  # the grouped path by default
+    assert max(I, Is) * dd == 1 << 31
+    assert moe.moe_supports(d(T=T, d=dd, I=I, I_shared=Is, E=4, k=1)) == abi.MOE_EUNSUPPORTED
+    assert moe.moe_routing_bytes(d(T=T, d=dd, I=I, I_shared=Is, E=4, k=1)) == 0
+    if I >= Is:
+        I -= 32
+    else:
+        Is -= 32
+    assert max(I, Is) * dd < 1 << 31
+    assert moe.moe_supports(d(T=T, d=dd, I=I, I_shared=Is, E=4, k=1)) == abi.MOE_OK
+    # the small-T path never gets there: its own limits (d <= 8192, I <= 2048) reject it first
+    assert moe.moe_supports(d(T=1, d=dd, I=I, I_shared=Is, E=4, k=1)) == abi.MOE_EUNSUPPORTED
+
+
+# ----------------------------------------------------------------------------- Q4 repack
+
+def q4pack(**kw):
+    args = dict(n_mats=2, rows=32, K=64, qs_in=FAKE, scales_in=FAKE + (1 << 16), qs_out=FAKE + (2 << 16),
+                scales_out=FAKE + (3 << 16))
+    args.update(kw)
+    return moe.moe_q4_pack(args["n_mats"], args["rows"], args["K"], args["qs_in"], args["scales_in"],
+                           args["qs_out"], args["scales_out"], stream=0, check=False)
+
+
+def test_q4_pack_validation_before_any_hip_call():
+    for name in ("n_mats", "rows", "K"):
+        assert q4pack(**{name: 0}) == abi.MOE_EINVAL, name
+        assert q4pack(**{name: -16}) == abi.MOE_EINVAL, name
+    for name in ("qs_in", "scales_in", "qs_out", "scales_out"):
+        assert q4pack(**{name: 0}) == abi.MOE_EINVAL, name
+    assert q4pack(rows=24) == abi.MOE_EUNSUPPORTED
+    assert q4pack(K=48) == abi.MOE_EUNSUPPORTED
+    assert q4pack(rows=(1 << 24) + 16) == abi.MOE_EUNSUPPORTED
+    for name in ("qs_in", "qs_out", "scales_out"):
+        assert q4pack(**{name: FAKE + (5 << 16) + 8}) == abi.MOE_EALIGN, name
+    assert q4pack(scales_in=FAKE + (1 << 16) + 1) == abi.MOE_EALIGN
+    # 2-byte aligned input scales pass the alignment check (this call is then rejected for overlapping the
+    # output codes, still before any HIP call)
+    assert q4pack(scales_in=FAKE + (2 << 16) + 2) == abi.MOE_EINVAL
+    # outputs overlapping inputs (codes: 2 * 32 * 64 / 2 = 2048 bytes, scales 2 * 32 * 2 * 2 = 256)
+    assert q4pack(qs_out=FAKE) == abi.MOE_EINVAL
+    assert q4pack(qs_out=FAKE + 2032) == abi.MOE_EINVAL
+    assert q4pack(scales_out=FAKE + (1 << 16)) == abi.MOE_EINVAL
+    assert q4pack(scales_out=FAKE + 1024) == abi.MOE_EINVAL     # inside the input codes
+    assert q4pack(qs_out=FAKE + (3 << 16) - 1024) == abi.MOE_EINVAL  # output codes run into output scales

@@ -9,7 +9,7 @@ import torch
 import synth
 from sparse_moe_expert_sigmoid_amd import abi
 from sparse_moe_expert_sigmoid_amd.layer import DeviceWeights, Workspace, layer_call, layer_call_fused, to_device
-from gpu_util import say
+from gpu_util import check_parity, say
 
 pytestmark = pytest.mark.gpu
 
@@ -22,6 +22,9 @@ CASES = [  # (T, d, E, k, I, Is, flags): every key-register count of the selecti
     (5, 256, 1024, 10, 64, 64, abi.MOE_FLAG_FORCE_GEMV),
     (37, 96, 20, 3, 160, 96, abi.MOE_FLAG_FORCE_GROUPED),
     (64, 256, 256, 10, 128, 128, 0),
+    # the decode workload bench.py times (d = 4096, E = 256, top-10, I = I_shared = 1024) at T = 1 and 8
+    (1, 4096, 256, 10, 1024, 1024, 0),
+    (8, 4096, 256, 10, 1024, 1024, 0),
 ]
 
 
@@ -42,6 +45,8 @@ def test_layer_forward_equals_the_separate_calls(case, residual):
     assert torch.equal(a.topk_ids, b.topk_ids)
     assert torch.equal(a.topk_w.view(torch.int32), b.topk_w.view(torch.int32))
     assert torch.equal(a.y.view(torch.int32), b.y.view(torch.int32))
+    if d == 4096 and not residual:  # the decode workload's shape: the single call held to the oracle too
+        check_parity(inp, b, label=f"layer_forward T={T}")
     # again, with the outputs of the first call still in place: nothing depends on stale contents
     layer_call_fused(x, w, b, residual=res if residual else None)
     torch.cuda.synchronize()

@@ -6,7 +6,7 @@ import torch
 import oracle
 import synth
 from sparse_moe_expert_sigmoid_amd import abi
-from sparse_moe_expert_sigmoid_amd.layer import DeviceWeights, Workspace, layer_call, to_device
+from sparse_moe_expert_sigmoid_amd.layer import DeviceWeights, Workspace, layer_call, layer_call_fused, to_device
 from gpu_util import check_parity, check_routing_build, run, say
 
 pytestmark = pytest.mark.gpu
@@ -150,31 +150,56 @@ def test_graph_capture_replays_match_eager(flags):
 
 # ----------------------------------------------------------------------------- full-size workloads
 
-def sample_tokens(T, n, seed, extra=()):
-    rng = np.random.default_rng(seed)
-    pick = set(rng.choice(T, size=min(n, T), replace=False).tolist()) | {0, T - 1} | set(int(e) for e in extra)
-    return np.array(sorted(pick))
+def long_prefill_tokens(ws, inp, n_tiles=4):
+    """Tokens to compare at T = 8192: every row of n_tiles whole 96-row M-tiles of the largest group
+    (its first, last -- ragged -- and two in between), and every outlier row."""
+    dims = ws.dims
+    counts = ws.routing_view("counts", dims.E).cpu().numpy()
+    offsets = ws.routing_view("offsets", dims.E + 1).cpu().numpy()
+    sorted_pair = ws.routing_view("sorted_pair", dims.T * dims.k).cpu().numpy()
+    g = int(np.argmax(counts))
+    nmt = (int(counts[g]) + 95) // 96
+    tiles = sorted({0, nmt - 1, nmt // 3, (2 * nmt) // 3})[:n_tiles]
+    toks = set()
+    for m in tiles:
+        lo = int(offsets[g]) + 96 * m
+        hi = min(lo + 96, int(offsets[g]) + int(counts[g]))
+        toks |= set((sorted_pair[lo:hi] // dims.k).tolist())
+    toks |= set(int(t) for t in inp["outlier_rows"])
+    say(f"[tokens] long prefill: group {g} ({counts[g]} rows, {nmt} M-tiles), tiles {tiles}, "
+        f"{len(inp['outlier_rows'])} outlier rows, {len(toks)} tokens")
+    return np.array(sorted(toks))
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["decode", "batched_decode", "prefill", "long_prefill"])
 def test_full_size_workloads(name):
+    """The four full-size workloads through moe_layer_forward, the call bench.py times, in its default
+    launch configuration: every token compared at T = 1, 64 and 2048; at T = 8192 every row of four whole
+    M-tiles of the largest group and every outlier row.  Bit-reproducible; the separate calls give the
+    same bits; at T = 64 the small-T path too."""
     cfg = synth.CONFIGS[name]
     say(f"[case] full {name} dims={cfg.dims}")
     inp = synth.make_inputs(cfg)
-    ws, w = run(inp, 0)
+    w = DeviceWeights.upload(inp)
+    x = to_device(inp["x"], "cuda")
+    ws = Workspace(cfg.dims, 0)
+    layer_call_fused(x, w, ws)
+    torch.cuda.synchronize()
     T = cfg.dims.T
-    extra = inp["outlier_rows"][:4] if len(inp["outlier_rows"]) else ()
-    tokens = np.arange(T) if T <= 1 else sample_tokens(T, 12, 5, extra)
+    tokens = long_prefill_tokens(ws, inp) if name == "long_prefill" else np.arange(T)
     check_parity(inp, ws, tokens=tokens, label=name)
     if abi.moe_path(cfg.dims) == 1:
         check_routing_build(ws)
         counts = ws.routing_view("counts", cfg.dims.E).cpu().numpy()
         say(f"[groups] {name}: distinct={int((counts > 0).sum())} max={counts.max()} median={int(np.median(counts))}")
-    # bitwise reproducible
-    x = to_device(inp["x"], "cuda")
-    again, _ = run(inp, 0, w, x)
+    # bitwise reproducible, and the separate calls give the same bits
+    again = Workspace(cfg.dims, 0)
+    layer_call_fused(x, w, again)
+    sep, _ = run(inp, 0, w, x)
+    torch.cuda.synchronize()
     assert torch.equal(again.y, ws.y)
+    assert torch.equal(sep.y, ws.y) and torch.equal(sep.topk_ids, ws.topk_ids)
     if T == 64:
         gemv, _ = run(inp, GEMV, w, x)
         assert torch.equal(gemv.topk_ids, ws.topk_ids)
@@ -280,3 +305,90 @@ def test_random_shape_sweep(dims):
         check_parity(inp, ws, label=f"sweep/{flags}")
         if abi.moe_path(dims, flags) == 1:
             check_routing_build(ws)
+
+
+# ----------------------------------------------------------------------------- fp16 range of the activations
+
+def _oracle_h_and_expert_max(inp, X):
+    """max |h| and max |expert output| over every expert (routed and shared) on the rows X, from the
+    oracle's own dequantisation: shows a case really reaches the values it is meant to."""
+    dims = inp["dims"]
+    mats = [(inp["w13_qs"][e], inp["w13_sc"][e], inp["w2_qs"][e], inp["w2_sc"][e]) for e in range(dims.E)]
+    mats.append((inp["s13_qs"], inp["s13_sc"], inp["s2_qs"], inp["s2_sc"]))
+    hmax = ymax = 0.0
+    for a, b, c, d in mats:
+        w13, w2 = oracle.dequant_q4(a, b), oracle.dequant_q4(c, d)
+        I = w13.shape[0] // 2
+        g, u = X @ w13[:I].T, X @ w13[I:].T
+        h = g * oracle.sigmoid(g) * u
+        hmax, ymax = max(hmax, float(np.abs(h).max())), max(ymax, float(np.abs(h @ w2.T).max()))
+    return hmax, ymax
+
+
+@pytest.mark.parametrize("flags", [GROUPED, GEMV], ids=["grouped", "gemv"])
+def test_large_activations_inside_the_fp16_range(flags):
+    """Activations scaled so that the SwiGLU output h reaches about 1e4 (inside fp16, where both paths
+    keep it): parity with the oracle on both paths.  The down scales are divided by 16 so that every
+    expert's output stays inside the fp16 range as well."""
+    dims = synth.Dims(T=40, d=512, E=8, k=2, I=128, I_shared=128)
+    inp = synth.make_inputs(dims, seed=161)
+    x = oracle.bf16_bits_to_f64(inp["x"]) * 24.0
+    inp["x"] = synth.bf16_bits_from_f32(x.astype(np.float32))
+    for key in ("w2_sc", "s2_sc"):
+        inp[key] = (inp[key].view(np.float16) / np.float16(16)).view(np.uint16)
+    hmax, ymax = _oracle_h_and_expert_max(inp, oracle.bf16_bits_to_f64(inp["x"]))
+    assert 5e3 <= hmax < 6e4 and ymax < 6e4, (hmax, ymax)
+    say(f"[case] large activations flags={flags}: max|h| {hmax:.3g}, max|expert out| {ymax:.3g}")
+    ws, _ = run(inp, flags)
+    check_parity(inp, ws, label=f"large_h/{flags}")
+
+
+def test_x_beyond_the_fp16_range_saturates_alike_on_both_paths():
+    """Layer inputs beyond the fp16 range (bf16 holds them) are saturated to +-65504 for the expert
+    projections on both paths, while the router sees them unchanged.  Here one input column holds
+    +-2^17 and the router ignores that column (its W_r column is zero), so the oracle's selection and
+    weights are exact; the expected output is the oracle's layer with that column saturated to
+    +-65504, built from the oracle's dequantisation and expert MLP.  The column's gate/up codes are 7
+    or 9 (weight -+scale) with scales near 1e-3, so h stays inside fp16; the unsaturated input (2^17)
+    would give about twice the output and fail the bound."""
+    dims = synth.Dims(T=24, d=256, E=8, k=2, I=64, I_shared=64)
+    inp = synth.make_inputs(dims, seed=171)
+    rng = np.random.default_rng(172)
+    c0 = 77
+    inp["w_router"][:, c0] = 0.0
+    x = oracle.bf16_bits_to_f64(inp["x"])
+    x[:, c0] = rng.choice([-1.0, 1.0], size=dims.T) * 2.0 ** 17
+    inp["x"] = synth.bf16_bits_from_f32(x.astype(np.float32))
+    for qk, sk in (("w13_qs", "w13_sc"), ("s13_qs", "s13_sc")):
+        q = inp[qk]
+        code = rng.choice([7, 9], size=q.shape[:-1]).astype(np.uint8)  # weight -scale or +scale
+        byte = q[..., c0 // 2]
+        q[..., c0 // 2] = (byte & 0xF0) | code if c0 % 2 == 0 else (byte & 0x0F) | (code << 4)
+        inp[sk] = rng.uniform(1.0e-3, 1.5e-3, size=inp[sk].shape).astype(np.float16).view(np.uint16)
+    x_sat = np.clip(oracle.bf16_bits_to_f64(inp["x"]), -65504.0, 65504.0)
+    sel = oracle.forward(inp)  # selection and weights: the router never sees column c0
+    ref = np.zeros((dims.T, dims.d))
+    for t in range(dims.T):
+        for j in range(dims.k):
+            e = sel["ids"][t, j]
+            ref[t] += sel["w"][t, j] * oracle.swiglu_mlp(
+                x_sat[t:t + 1], oracle.dequant_q4(inp["w13_qs"][e], inp["w13_sc"][e]),
+                oracle.dequant_q4(inp["w2_qs"][e], inp["w2_sc"][e]))[0]
+    ref += oracle.swiglu_mlp(x_sat, oracle.dequant_q4(inp["s13_qs"], inp["s13_sc"]),
+                             oracle.dequant_q4(inp["s2_qs"], inp["s2_sc"]))
+    hmax, ymax = _oracle_h_and_expert_max(inp, x_sat)
+    assert 1e3 <= hmax < 6e4 and ymax < 6e4, (hmax, ymax)
+    outs = []
+    for flags in (GEMV, GROUPED):
+        ws, _ = run(inp, flags)
+        ids = ws.topk_ids.cpu().numpy()
+        for t in range(dims.T):
+            assert sorted(ids[t]) == sorted(sel["ids"][t]), (flags, t)
+        y = ws.y.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(y)), flags
+        max_rel = np.abs(y - ref).max() / np.abs(ref).max()
+        l2_rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+        say(f"[parity] saturated x flags={flags}: max|h| {hmax:.3g} max_rel={max_rel:.3e} l2_rel={l2_rel:.3e}")
+        assert max_rel <= 1e-2 and l2_rel <= 5e-3, (flags, max_rel, l2_rel)
+        outs.append(y)
+    assert np.linalg.norm(outs[0] - outs[1]) <= 5e-3 * np.linalg.norm(ref)

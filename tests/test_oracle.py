@@ -400,6 +400,20 @@ def test_routing_build_bruteforce():
     assert sorted(order.tolist()) == list(range(E + 1))
 
 
+def test_group_order_ties_go_to_the_lower_id():
+    """Hand-built sizes with ties at every level, the expected schedule written out: descending size,
+    equal sizes in ascending group id, the shared group (id E, T rows) ranked by its size like any other
+    group, empty groups last.  A 'ties to the higher id' or 'shared first' slip gives another order."""
+    counts = np.array([3, 5, 3, 0, 5, 3, 0, 7])   # groups 0..7; group 8 is the shared one
+    T = 5                                        # ties the shared group with groups 1 and 4
+    want = [7, 1, 4, 8, 0, 2, 5, 3, 6]
+    np.testing.assert_array_equal(oracle.group_order(counts, T), want)
+    # every group the same size: plain id order, shared last
+    np.testing.assert_array_equal(oracle.group_order(np.full(4, 2), 2), [0, 1, 2, 3, 4])
+    # a shared group larger than every expert comes first
+    np.testing.assert_array_equal(oracle.group_order(np.array([1, 2, 2]), 9), [3, 1, 2, 0])
+
+
 # ----------------------------------------------------------------------------- generator
 
 def test_generator_deterministic_and_distributions():
