@@ -262,6 +262,26 @@ int moe_layer_forward(const moe_dims* dims, const uint16_t* x_bf16, const float*
                       float* topk_w, void* routing, size_t routing_bytes, void* scratch, size_t scratch_bytes,
                       uint32_t flags, void* stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call without the routing and scratch arguments.  The
+ * routing workspace and the scratch live in one device array of the
+ * library's own, MOE_NOALLOC_MAX_BYTES per GPU, reserved when the library is
+ * loaded and held until the process ends; nothing is allocated or freed.
+ * The shape must fit: moe_routing_bytes + moe_scratch_bytes (each rounded
+ * up to a multiple of 256) <= MOE_NOALLOC_MAX_BYTES, else MOE_ENOSPACE
+ * (64 MiB holds the d = 4096, E = 256, top-10, I = 1024 layer up to about
+ * T = 480 tokens).  Every other argument, check, error and result is that of
+ * moe_layer_forward, bit for bit.  All calls on one GPU share the array, so
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and give undefined results; calls on different GPUs do not interact.  The
+ * first call on a device looks the array up for that device (a HIP runtime
+ * query, no allocation); MOE_EHIP if that fails. */
+#define MOE_NOALLOC_MAX_BYTES (64ull << 20)
+int moe_layer_forward_noalloc(const moe_dims* dims, const uint16_t* x_bf16, const float* w_router,
+                              const float* bias, const moe_q4_weights* weights, const float* residual, float* y,
+                              int32_t* topk_ids, float* topk_w, uint32_t flags, void* stream);
+
 /* Pre-MoE norm (the step in front of the layer): for each of T rows of d
  * values (d % 8 == 0),
  *     x_t = bf16( h_t / sqrt(mean(h_t^2) + eps) * gamma )

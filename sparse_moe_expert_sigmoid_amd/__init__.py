@@ -15,5 +15,5 @@ from .abi import (  # noqa: F401
     moe_route, moe_build_descriptors, moe_q4_forward, moe_q4_forward_residual, moe_layer_forward, moe_strerror,
     EXPORTED_SYMBOLS,
     moe_decode_ctx_workspace_bytes, moe_decode_ctx_create, moe_decode_ctx_run, moe_decode_ctx_destroy,
-    moe_rmsnorm_bf16, moe_q4_pack,
+    moe_rmsnorm_bf16, moe_q4_pack, moe_layer_forward_noalloc, MOE_NOALLOC_MAX_BYTES,
 )

@@ -29,8 +29,9 @@ EXPORTED_SYMBOLS = (
     "moe_supports", "moe_path", "moe_routing_bytes", "moe_routing_layout_of", "moe_scratch_bytes",
     "moe_route", "moe_build_descriptors", "moe_q4_forward", "moe_q4_forward_residual", "moe_layer_forward", "moe_strerror",
     "moe_decode_ctx_workspace_bytes", "moe_decode_ctx_create", "moe_decode_ctx_run", "moe_decode_ctx_destroy",
-    "moe_rmsnorm_bf16", "moe_q4_pack",
+    "moe_rmsnorm_bf16", "moe_q4_pack", "moe_layer_forward_noalloc",
 )
+MOE_NOALLOC_MAX_BYTES = 64 << 20
 
 
 class Dims(Structure):
@@ -121,6 +122,9 @@ def lib() -> ctypes.CDLL:
     L.moe_decode_ctx_destroy.restype = c_int
     L.moe_rmsnorm_bf16.argtypes = [c_int, c_int, c_void_p, c_void_p, c_float, c_void_p, c_void_p]
     L.moe_rmsnorm_bf16.restype = c_int
+    L.moe_layer_forward_noalloc.argtypes = [D, c_void_p, c_void_p, c_void_p, POINTER(_Weights), c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_uint32, c_void_p]
+    L.moe_layer_forward_noalloc.restype = c_int
     L.moe_q4_pack.argtypes = [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     L.moe_q4_pack.restype = c_int
     L.moe_strerror.argtypes = [c_int]
@@ -280,3 +284,13 @@ def moe_q4_pack(n_mats: int, rows: int, K: int, qs_in, scales_in, qs_out, scales
     rc = lib().moe_q4_pack(n_mats, rows, K, _ptr(qs_in), _ptr(scales_in), _ptr(qs_out), _ptr(scales_out),
                            _stream(stream))
     return _done(rc, check, "moe_q4_pack")
+
+
+def moe_layer_forward_noalloc(dims, x, w_router, bias, weights, y, topk_ids, topk_w, residual=None, flags: int = 0,
+                              stream=None, check: bool = True) -> int:
+    """moe_layer_forward with the routing workspace and scratch in the library's own device array."""
+    ws = weights if isinstance(weights, _Weights) else _weights(weights)
+    rc = lib().moe_layer_forward_noalloc(ctypes.byref(Dims.of(dims)), _ptr(x), _ptr(w_router), _ptr(bias),
+                                         ctypes.byref(ws), _ptr(residual), _ptr(y), _ptr(topk_ids), _ptr(topk_w),
+                                         flags, _stream(stream))
+    return _done(rc, check, "moe_layer_forward_noalloc")

@@ -315,6 +315,38 @@ int layer_impl(const moe_dims* dims, const uint16_t* x_bf16, const float* w_rout
 }
 }  // namespace
 
+// Sizes and the entry for the variant that keeps its routing workspace and scratch in device memory of
+// the library's own (noalloc.hip).
+namespace moe_abi {
+int layer_sizes(const moe_dims* dims, uint32_t flags, size_t* routing_bytes, size_t* scratch_bytes) {
+  const int rc = check_dims(dims, flags);
+  if (rc) return rc;
+  *routing_bytes = align256(routing_layout(dims).total);
+  *scratch_bytes = align256(scratch_layout(dims, choose_path(dims, flags)).total);
+  return MOE_OK;
+}
+int layer_forward(const moe_dims* dims, const uint16_t* x_bf16, const float* w_router, const float* bias,
+                  const moe_q4_weights* w, const float* residual, float* y, int32_t* topk_ids, float* topk_w,
+                  void* routing, size_t routing_bytes, void* scratch, size_t scratch_bytes, uint32_t flags,
+                  void* stream) {
+  return layer_impl(dims, x_bf16, w_router, bias, w, residual, y, topk_ids, topk_w, routing, routing_bytes, scratch,
+                    scratch_bytes, flags, stream);
+}
+int check_layer_args(const moe_dims* dims, const uint16_t* x_bf16, const float* w_router, const float* bias,
+                     const moe_q4_weights* w, const float* residual, const float* y, const int32_t* topk_ids,
+                     const float* topk_w, uint32_t flags) {
+  const int rc = check_dims(dims, flags);
+  if (rc) return rc;
+  if (!x_bf16 || !w_router || !bias || !w || !y || !topk_ids || !topk_w) return MOE_EINVAL;
+  if (!q4_ok(w->w13) || !q4_ok(w->w2) || !q4_ok(w->s13) || !q4_ok(w->s2)) return MOE_EINVAL;
+  if (!aligned(x_bf16, 16) || !aligned(w_router, 16) || !aligned(bias, 4) || !aligned(y, 16) ||
+      !aligned(topk_ids, 4) || !aligned(topk_w, 4) || (residual && !aligned(residual, 16)))
+    return MOE_EALIGN;
+  if (!q4_aligned(w->w13) || !q4_aligned(w->w2) || !q4_aligned(w->s13) || !q4_aligned(w->s2)) return MOE_EALIGN;
+  return MOE_OK;
+}
+}  // namespace moe_abi
+
 extern "C" {
 int moe_layer_forward(const moe_dims* dims, const uint16_t* x_bf16, const float* w_router, const float* bias,
                       const moe_q4_weights* w, const float* residual, float* y, int32_t* topk_ids, float* topk_w,

@@ -339,3 +339,41 @@ def test_q4_pack_validation_before_any_hip_call():
     assert q4pack(scales_out=FAKE + (1 << 16)) == abi.MOE_EINVAL
     assert q4pack(scales_out=FAKE + 1024) == abi.MOE_EINVAL     # inside the input codes
     assert q4pack(qs_out=FAKE + (3 << 16) - 1024) == abi.MOE_EINVAL  # output codes run into output scales
+
+
+# ----------------------------------------------------------------------------- layer call without allocation
+
+def noalloc(dims=TINY, flags=0, **kw):
+    args = dict(x=FAKE, w_router=FAKE, bias=FAKE, weights=WEIGHTS, y=FAKE, topk_ids=FAKE, topk_w=FAKE, stream=0)
+    args.update(kw)
+    return moe.moe_layer_forward_noalloc(dims, flags=flags, check=False, **args)
+
+
+@pytest.mark.parametrize("flags", [0, abi.MOE_FLAG_FORCE_GROUPED])
+def test_layer_forward_noalloc_validation_before_any_hip_call(flags):
+    assert noalloc(dims=d(k=0), flags=flags) == abi.MOE_EINVAL
+    assert noalloc(dims=d(d=40), flags=flags) == abi.MOE_EUNSUPPORTED
+    for name in ["x", "w_router", "bias", "y", "topk_ids", "topk_w"]:
+        assert noalloc(flags=flags, **{name: 0}) == abi.MOE_EINVAL, name
+    for name in WEIGHTS:
+        assert noalloc(flags=flags, weights=dict(WEIGHTS, **{name: 0})) == abi.MOE_EINVAL, name
+    for name in ["x", "w_router", "y", "residual"]:
+        assert noalloc(flags=flags, **{name: FAKE + 4}) == abi.MOE_EALIGN, name
+    for name in ["bias", "topk_ids", "topk_w"]:
+        assert noalloc(flags=flags, **{name: FAKE + 2}) == abi.MOE_EALIGN, name
+
+
+def test_layer_forward_noalloc_size_limit():
+    """Shapes whose routing workspace plus scratch exceed the fixed array are rejected before any HIP call;
+    the limit is stated in the header and in the binding."""
+    assert abi.MOE_NOALLOC_MAX_BYTES == 64 << 20
+    assert re.search(r"#define MOE_NOALLOC_MAX_BYTES \(64ull << 20\)", open(HEADER).read())
+
+    def need(dims, flags=0):
+        return (align(moe.moe_routing_bytes(dims, flags)) + align(moe.moe_scratch_bytes(dims, flags)))
+    prefill = synth.CONFIGS["prefill"].dims
+    assert need(prefill) > abi.MOE_NOALLOC_MAX_BYTES
+    assert noalloc(dims=prefill) == abi.MOE_ENOSPACE
+    big = d(T=480, d=4096, E=256, k=10, I=1024, I_shared=1024)
+    assert need(big) <= abi.MOE_NOALLOC_MAX_BYTES < need(d(T=520, d=4096, E=256, k=10, I=1024, I_shared=1024))
+    assert noalloc(dims=d(T=520, d=4096, E=256, k=10, I=1024, I_shared=1024)) == abi.MOE_ENOSPACE

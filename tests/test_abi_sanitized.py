@@ -14,7 +14,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CLANG = "/opt/rocm/llvm/bin/clang++"
-OBJS = ["router.o", "build.o", "gemv.o", "grouped.o", "norm.o", "pack.o"]
+OBJS = ["router.o", "build.o", "gemv.o", "grouped.o", "norm.o", "pack.o", "noalloc.o"]
 OUT = os.path.join(ROOT, "_build", "host_sanitized")
 
 
