@@ -46,6 +46,10 @@ static_assert(kMaxGemvBlocksPerWave == kWave, "activation staging gives every la
 // expert), each group of 8 stored in the pair order of the down kernel: slot
 // i of a group holds element 0,4,1,5,2,6,3,7 [i].
 //
+// Both kernels are compiled without floating-point contraction (the multiply-adds meant as one FMA are
+// written as fmaf): the instantiations used by the separate calls and by moe_layer_forward then round
+// alike, bit for bit.
+//
 // NPER = 0: the expert of each pair comes from ids.  NPER > 0 (the key registers per lane of the
 // selection, ceil(E/64)): a routed workgroup selects its token's experts itself from the router's
 // logits with one wavefront (the same selection as the top-k launch, so the same experts, order and
@@ -57,6 +61,7 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
                                                      int T, int d, int k, int I, int Is, uint32_t mask_lo, uint32_t mask_hi,
                                                      uint32_t magic, const float* __restrict__ logits,
                                                      const float* __restrict__ bias, float* __restrict__ topk_w, int E) {
+#pragma clang fp contract(off)
   // x of this wavefront's quarter of K, per block: 16 dwords of fp16 pairs and the block's starting value
   __shared__ __attribute__((aligned(16))) uint32_t xs[4][kMaxGemvBlocksPerWave][16];
   __shared__ float xsum[4][kMaxGemvBlocksPerWave];
@@ -123,8 +128,9 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
           u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
                 __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
     }
-    xsum[wave][lane] = -(1032.f * sa + 1152.f * sb);
+    xsum[wave][lane] = -fmaf(1032.f, sa, 1152.f * sb);
   }
+  wave_lds_sync();  // the tiles below read the blocks other lanes staged
   // codes and scales of up to kGemvTiles tiles per batch, all in flight before any arithmetic; blocks
   // past the row end (last tile) re-read the row's last block and weigh zero.
   u32x4 cg[kGemvTiles], cu[kGemvTiles];
@@ -139,7 +145,6 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
     dg[j] = sg[(size_t)b * 16 + n];                                            \
     du[j] = su[(size_t)b * 16 + n];                                            \
   }
-  // the wavefront reads back only what its own lanes wrote: LDS operations of one wavefront are ordered
   float accg = 0.f, accu = 0.f;
   for (int tb = tw0; tb < tw1; tb += kGemvTiles) {
     MOE_GU_LOAD(tb);
@@ -213,6 +218,7 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
                                                             float* y, uint16_t* __restrict__ y_bf16,
                                                             int T, int d, int k, int I, int Is, uint32_t mask_lo,
                                                             uint32_t mask_hi, uint32_t magic) {
+#pragma clang fp contract(off)
   // per wavefront: the slot's h, per block 16 dwords of fp16 pairs (the 16x pairs pre-divided by 16)
   // and the block's starting value -(1032 A + 72 B)
   __shared__ __attribute__((aligned(16))) uint32_t hsm[16][kMaxGemvBlocksPerWave][16];
@@ -264,8 +270,9 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
         }
         *reinterpret_cast<u32x4*>(hsm[wave][lane] + 4 * g) = v;
       }
-      hc0[wave][lane] = -(1032.f * sa + 72.f * sb);
+      hc0[wave][lane] = -fmaf(1032.f, sa, 72.f * sb);
     }
+    wave_lds_sync();  // the tiles below read the blocks other lanes staged
     // codes and scales of up to kDownTiles tiles per batch, all in flight before any arithmetic
     u32x4 cq[kDownTiles];
     uint32_t dq[kDownTiles];
@@ -277,8 +284,7 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
       cq[j] = ld16(qg + (size_t)b * 256 + 16 * n);                             \
       dq[j] = sg[(size_t)b * 16 + n];                                          \
     }
-    // the wavefront reads back only what its own lanes wrote: LDS operations of one wavefront are ordered
-    float acc = 0.f;
+      float acc = 0.f;
     for (int tb = 0; tb < ntile; tb += kDownTiles) {
       MOE_DN_LOAD(tb);
 #pragma unroll

@@ -144,6 +144,15 @@ __device__ __forceinline__ void vm_lgkm_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
+// One wavefront hands data to its other lanes through LDS.  The hardware keeps a wavefront's LDS
+// operations in order, but the compiler treats the lanes as separate threads and may move a read of
+// another lane's slot above the write that fills it: this fence (wavefront scope, no barrier
+// instruction) keeps every LDS access where the program puts it.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Workgroup barrier without a memory fence.  The ordering it needs comes from explicit waits: every
 // wavefront waits for its own loads into LDS (and its LDS reads) before arriving, so after the barrier
 // the new tile is in LDS and nobody still reads the buffer that is refilled next.

@@ -42,8 +42,8 @@ struct TopkLds {  // one wavefront's staging: the chosen entries in id order, th
 __device__ __forceinline__ int popc(uint64_t m) { return __builtin_popcountll(m); }
 
 // Selection for one token by one wavefront: writes ids[0..k) and w[0..k) (unless write is false) and
-// leaves the ids and scores in slot order in sm.slot_id / sm.slot_s.  The wavefront reads back only
-// what its own lanes wrote to LDS: LDS operations of one wavefront are ordered.
+// leaves the ids and scores in slot order in sm.slot_id / sm.slot_s.  The lanes exchange entries
+// through LDS, with wave_lds_sync between each write and the reads of other lanes.
 template <int NPER, int NPARTS>
 __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t part_stride,
                                           const float* __restrict__ bias, int32_t* __restrict__ ids,
@@ -118,6 +118,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t
     }
     base += popc(m);
   }
+  wave_lds_sync();
   // lane r < k takes entry r and counts the entries that rank before it: its slot
   const int r = min(lane, k - 1);
   const uint32_t K = sm.key[r];
@@ -133,6 +134,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t
     sm.slot_id[slot] = I;
     sm.slot_s[slot] = S;
   }
+  wave_lds_sync();
   const int q = min(lane, k - 1);
   const int my_id = sm.slot_id[q];
   const float my_s = sm.slot_s[q];
@@ -143,6 +145,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t
     ids[lane] = my_id;
     w[lane] = my_s / tot;
   }
+  wave_lds_sync();  // callers read sm.slot_id / sm.slot_s in any lane
 }
 
 }  // namespace moe

@@ -14,7 +14,6 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CLANG = "/opt/rocm/llvm/bin/clang++"
-OBJS = ["router.o", "build.o", "gemv.o", "grouped.o", "norm.o", "pack.o", "noalloc.o"]
 OUT = os.path.join(ROOT, "_build", "host_sanitized")
 
 
@@ -26,7 +25,7 @@ def _run(cmd, **kw):
 
 def _sanitized_library() -> str:
     from sparse_moe_expert_sigmoid_amd import build as B
-    objs = [os.path.join(B.BUILD_DIR, o) for o in OBJS]
+    objs = [os.path.join(B.BUILD_DIR, os.path.splitext(src)[0] + ".o") for src in B.SOURCES if src != "abi.cpp"]
     if not all(os.path.exists(o) for o in objs):
         B.build()
     os.makedirs(OUT, exist_ok=True)
