@@ -5,7 +5,8 @@
     python bench.py --all          (every workload, one JSON line with a list of them)
 
 One step is one call of the whole layer on one batch of synthetic tokens:
-moe_route + moe_build_descriptors + moe_q4_forward.  Steps are captured in
+moe_layer_forward (with --separate-calls: moe_route + moe_build_descriptors +
+moe_q4_forward, the same results).  Steps are captured in
 a HIP graph that cycles through L independent layer copies (weights and
 tokens), so that successive steps do not find the previous step's weights
 in the 256 MB MALL, as in a model with many layers.  W warm-up steps run
@@ -16,8 +17,10 @@ The primary workload (default: single-token decode, d=4096, E=256, top-10,
 I=1024, shared I=1024) gives `value`; the 2048-token prefill chunk is
 measured the same way and reported under `secondary`.  Per-kernel average
 durations come from graphs that replay only that kernel's nodes, extracted
-from the captured layer graph, timed with HIP events on the same stream.
-For an HBM-bound dominant kernel the roofline object also carries the rate
+from the captured layer graph, timed with HIP events on the same stream
+(every launch of the layer is idempotent, so replaying one alone is valid).
+`cpu_baseline` (primary and secondary line) times the CPU oracle on a
+bounded sample of the same workload's tokens.  For an HBM-bound dominant kernel the roofline object also carries the rate
 of torch's device copy kernel moving the same number of bytes
 (`copy_ceiling`): the practical streaming ceiling beside the nominal peak.
 
@@ -281,7 +284,9 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
     ms = t0.elapsed_time(t1)
     ms_per_step = ms / steps
 
-    # per-kernel average durations from graphs of that kernel's nodes alone
+    # per-kernel average durations from graphs of that kernel's nodes alone.  This needs every launch of
+    # the layer to be idempotent: replayed alone, a kernel must rewrite the same values (a launch that
+    # accumulated into state cleared by an earlier one would corrupt what later replays read).
     nodes = hip.kernel_nodes(full_graph, sh)
     by_kernel = {}
     for kname, p in nodes:
@@ -425,13 +430,14 @@ def cpu_baseline(inp, budget_s=15.0):
                       f"{el:.1f} s wall on the host", **host_info()}
 
 
-def traffic_run(name, torch, layer, synth):
+def traffic_run(name, torch, layer, synth, flags=0):
     """Three layer calls and two 256 MiB copies, nothing else: the run that rocprofv3 --pmc FETCH_SIZE /
-    WRITE_SIZE records for the traffic summaries under profiles/ (the copy calibrates the counters)."""
+    WRITE_SIZE records for the traffic summaries under profiles/ (the copy calibrates the counters).
+    `flags` are the layer's MOE_FLAG_* bits (e.g. the grouped GEMMs' work order)."""
     inp = synth.make_inputs(synth.CONFIGS[name])
     w = layer.DeviceWeights.upload(inp)
     x = layer.to_device(inp["x"], "cuda")
-    ws = layer.Workspace(inp["dims"], 0)
+    ws = layer.Workspace(inp["dims"], flags)
     for _ in range(3):
         layer.layer_call_fused(x, w, ws)
     a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -441,7 +447,8 @@ def traffic_run(name, torch, layer, synth):
     for _ in range(2):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps({"traffic_run": name, "layer_calls": 3, "copy_bytes": 256 << 20, "copies": 2}), flush=True)
+    print(json.dumps({"traffic_run": name, "flags": flags, "layer_calls": 3, "copy_bytes": 256 << 20, "copies": 2}),
+          flush=True)
 
 
 def run_decode_ctx(passes, torch, abi, layer, synth, n_layers=8, norm=False):
@@ -511,6 +518,9 @@ def main():
     ap.add_argument("--traffic-run", metavar="WORKLOAD", default=None,
                     help="for hardware-counter collection only: run WORKLOAD's layer 3 times, then copy a 256 MiB "
                          "device buffer twice (the calibration of FETCH_SIZE / WRITE_SIZE), print one line, exit")
+    ap.add_argument("--flags", type=int, default=0,
+                    help="MOE_FLAG_* bits for --traffic-run (4 = expert-id group order, 8 = items in launch "
+                         "order, 16 = band-major items)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this layer is built and measured on a single MI355X; "
@@ -525,7 +535,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(3)
     if args.traffic_run:
-        traffic_run(args.traffic_run, torch, layer, synth)
+        traffic_run(args.traffic_run, torch, layer, synth, flags=args.flags)
         return
     hip = Hip()
     if args.all:
@@ -560,6 +570,8 @@ def main():
         ceil = copy_ceiling(torch, [rl["algorithmic_bytes_per_launch"]])
         rl["copy_ceiling"] = next(iter(ceil.values())) | {"bytes": int(next(iter(ceil)))}
     cpu = None if args.no_cpu_baseline else cpu_baseline(prim["_inp0"])
+    if sec is not None and not args.no_cpu_baseline:  # the oracle on the secondary workload too (one sample)
+        sec["cpu_baseline"] = cpu_baseline(sec["_inp0"], budget_s=10.0)
     dims = prim["dims"]
     out = {
         "metric": METRIC,

@@ -164,8 +164,13 @@ size_t moe_scratch_bytes(const moe_dims* dims, uint32_t flags) {
   return scratch_layout(dims, choose_path(dims, flags)).total;
 }
 
-int moe_route(const moe_dims* dims, const uint16_t* x_bf16, const float* w_router, const float* bias,
-              int32_t* topk_ids, float* topk_w, void* routing, size_t routing_bytes, uint32_t flags, void* stream) {
+namespace {
+// x16 (internal, may be nullptr): on the grouped path the router also writes the fp16 copy of x that the
+// gate+up reads (the whole-layer call passes its scratch slot and skips that copy's own pass).  Every
+// launch here stays idempotent: replaying any one of them alone rewrites the same values.
+int route_impl(const moe_dims* dims, const uint16_t* x_bf16, const float* w_router, const float* bias,
+               int32_t* topk_ids, float* topk_w, void* routing, size_t routing_bytes, uint32_t flags, void* stream,
+               _Float16* x16) {
   int rc = check_dims(dims, flags);
   if (rc) return rc;
   if (!x_bf16 || !w_router || !bias || !topk_ids || !topk_w || !routing) return MOE_EINVAL;
@@ -180,10 +185,16 @@ int moe_route(const moe_dims* dims, const uint16_t* x_bf16, const float* w_route
   (void)hipGetLastError();
   const bool gemv = choose_path(dims, flags) == 0;
   hipError_t e = gemv ? moe::launch_router_gemv(s, x_bf16, w_router, r.logits, st)
-                      : moe::launch_router_mfma(s, x_bf16, w_router, r.logits, st);
+                      : moe::launch_router_mfma(s, x_bf16, w_router, r.logits, st, x16);
   if (e != hipSuccess) return MOE_EHIP;
   const int nparts = gemv ? 1 : moe::kRouterParts;
   return hip_rc(moe::launch_topk(s, r.logits, nparts, bias, topk_ids, topk_w, st));
+}
+}  // namespace
+
+int moe_route(const moe_dims* dims, const uint16_t* x_bf16, const float* w_router, const float* bias,
+              int32_t* topk_ids, float* topk_w, void* routing, size_t routing_bytes, uint32_t flags, void* stream) {
+  return route_impl(dims, x_bf16, w_router, bias, topk_ids, topk_w, routing, routing_bytes, flags, stream, nullptr);
 }
 
 int moe_build_descriptors(const moe_dims* dims, const int32_t* topk_ids, void* routing, size_t routing_bytes,
@@ -201,11 +212,12 @@ int moe_build_descriptors(const moe_dims* dims, const int32_t* topk_ids, void* r
 }
 
 namespace {
-// y_bf16 (internal, may be nullptr): also write y rounded to bf16, in the pass that writes y
+// y_bf16 (internal, may be nullptr): also write y rounded to bf16, in the pass that writes y.
+// x16_ready (internal): the scratch's fp16 copy of x was written by the router of the same layer call.
 int forward_impl(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
                  const void* routing, size_t routing_bytes, const moe_q4_weights* w, const float* residual,
                  float* y, void* scratch, size_t scratch_bytes, uint32_t flags, void* stream,
-                 uint16_t* y_bf16 = nullptr) {
+                 uint16_t* y_bf16 = nullptr, bool x16_ready = false) {
   int rc = check_dims(dims, flags);
   if (rc) return rc;
   const int path = choose_path(dims, flags);
@@ -241,7 +253,7 @@ int forward_impl(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* to
   o.h_s = reinterpret_cast<_Float16*>(sb + S.h_s);
   o.y_pair = reinterpret_cast<_Float16*>(sb + S.y_pair);
   o.y_s = reinterpret_cast<_Float16*>(sb + S.y_s);
-  if (moe::launch_grouped_gateup(s, x_bf16, r, w13, s13, o, flags, st) != hipSuccess) return MOE_EHIP;
+  if (moe::launch_grouped_gateup(s, x_bf16, r, w13, s13, o, flags, st, x16_ready) != hipSuccess) return MOE_EHIP;
   if (moe::launch_grouped_down(s, r, w2, s2, o, flags, st) != hipSuccess) return MOE_EHIP;
   return hip_rc(moe::launch_combine(s, topk_w, r, o, residual, y, y_bf16, st));
 }
@@ -291,11 +303,12 @@ int layer_impl(const moe_dims* dims, const uint16_t* x_bf16, const float* w_rout
   const ScratchLayout S = scratch_layout(dims, path);
   if (scratch_bytes < S.total) return MOE_ENOSPACE;
   if (path == 1) {
-    rc = moe_route(dims, x_bf16, w_router, bias, topk_ids, topk_w, routing, routing_bytes, flags, stream);
+    _Float16* x16 = reinterpret_cast<_Float16*>(static_cast<char*>(scratch) + S.x16);
+    rc = route_impl(dims, x_bf16, w_router, bias, topk_ids, topk_w, routing, routing_bytes, flags, stream, x16);
     if (rc == MOE_OK) rc = moe_build_descriptors(dims, topk_ids, routing, routing_bytes, flags, stream);
     if (rc == MOE_OK)
       rc = forward_impl(dims, x_bf16, topk_ids, topk_w, routing, routing_bytes, w, residual, y, scratch,
-                        scratch_bytes, flags, stream, y_bf16);
+                        scratch_bytes, flags, stream, y_bf16, true);
     return rc;
   }
   const moe::Shape s = shape_of(dims);

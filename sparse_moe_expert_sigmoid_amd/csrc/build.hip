@@ -28,6 +28,27 @@
 
 namespace moe {
 
+// f(j, e) for the k expert ids of token t, j ascending.  The ids are loaded 16 at a time, all in
+// flight together (a load per id followed by its use would wait out one memory latency per id).
+template <typename F>
+__device__ __forceinline__ void for_each_id(const int32_t* __restrict__ ids, int t, int k, F&& f) {
+  for (int j0 = 0; j0 < k; j0 += 16) {
+    int v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = ids[(size_t)t * k + min(j0 + u, k - 1)];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (j0 + u < k) f(j0 + u, v[u]);
+  }
+}
+
+// The ids of pairs p = p0 + NT*i (i < 4, p < P) for the one-workgroup build (P <= 4*NT), loaded together.
+template <int NT>
+__device__ __forceinline__ void load_pair_ids(const int32_t* __restrict__ ids, int p0, int P, int (&v)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = ids[min(p0 + NT * i, P - 1)];
+}
+
 __global__ __launch_bounds__(256) void k_build_count(const int32_t* __restrict__ ids, int T, int k, int E,
                                                      int* __restrict__ chunk_counts) {
   __shared__ int hist[kMaxExperts];
@@ -35,12 +56,10 @@ __global__ __launch_bounds__(256) void k_build_count(const int32_t* __restrict__
   for (int e = tid; e < E; e += 256) hist[e] = 0;
   __syncthreads();
   const int t = blockIdx.x * kBuildChunk + tid;
-  if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      const int e = ids[(size_t)t * k + j];
+  if (t < T)
+    for_each_id(ids, t, k, [&](int, int e) {
       if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
-    }
-  }
+    });
   __syncthreads();
   for (int e = tid; e < E; e += 256) chunk_counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
@@ -118,20 +137,17 @@ __global__ __launch_bounds__(256) void k_build_scatter(const int32_t* __restrict
   if (!schedule) {
     const int i = tid;
     const int t = chunk * kBuildChunk + i;
-    if (t < T) {
-      for (int j = 0; j < k; ++j) {
-        const int e = ids[(size_t)t * k + j];
+    if (t < T)
+      for_each_id(ids, t, k, [&](int, int e) {
         if ((unsigned)e < (unsigned)E) atomicOr(&masks[e * W + (i >> 5)], 1u << (i & 31));
-      }
-    }
+      });
     __syncthreads();
-    if (t < T) {
-      for (int j = 0; j < k; ++j) {
+    if (t < T)
+      for_each_id(ids, t, k, [&](int j, int e) {
         const int p = t * k + j;
-        const int e = ids[(size_t)p];
         if ((unsigned)e >= (unsigned)E) {
           r.pair_pos[p] = -1;  // out-of-range id: the pair contributes nothing
-          continue;
+          return;
         }
         const int w = i >> 5;
         int rank = __popc(masks[e * W + w] & ((1u << (i & 31)) - 1u));
@@ -140,8 +156,7 @@ __global__ __launch_bounds__(256) void k_build_scatter(const int32_t* __restrict
         r.sorted_pair[pos] = p;
         r.pair_pos[p] = pos;
         r.row_expert[pos] = e;
-      }
-    }
+      });
     return;
   }
   // ---- group schedule -------------------------------------------------------
@@ -215,9 +230,12 @@ __global__ __launch_bounds__(kBuildSmallThreads) void k_build_small(const int32_
   for (int i = tid; i < E * W; i += NT) masks[i] = 0u;
   for (int e = tid; e <= E; e += NT) cnt[e] = 0;
   __syncthreads();
-  for (int p = tid; p < P; p += NT) {
-    const int e = ids[p];
-    if ((unsigned)e < (unsigned)E) {
+  int pid[4];  // P <= 4 * NT: this thread's pairs are tid + NT*i, i < 4
+  load_pair_ids<NT>(ids, tid, P, pid);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + NT * i, e = pid[i];
+    if (p < P && (unsigned)e < (unsigned)E) {
       const int t = p / k;
       atomicAdd(&cnt[e], 1);
       atomicOr(&masks[e * W + (t >> 5)], 1u << (t & 31));
@@ -257,8 +275,10 @@ __global__ __launch_bounds__(kBuildSmallThreads) void k_build_small(const int32_
     my_tiles = ((g < E ? cnt[g] : T) + kGroupedBM - 1) / kGroupedBM;
   }
   // scatter: position of a pair = offset of its expert + earlier pairs of the expert in token order
-  for (int p = tid; p < P; p += NT) {
-    const int e = ids[p];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + NT * i, e = pid[i];
+    if (p >= P) continue;
     if ((unsigned)e >= (unsigned)E) {
       r.pair_pos[p] = -1;  // out-of-range id: the pair contributes nothing
       continue;
@@ -311,7 +331,7 @@ hipError_t launch_build(const Shape& s, const int32_t* topk_ids, const Routing& 
   }
   const int nchunks = (s.T + kBuildChunk - 1) / kBuildChunk;
   hipLaunchKernelGGL(k_build_count, dim3(nchunks), dim3(256), 0, st, topk_ids, s.T, s.k, s.E, r.chunk_counts);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_build_scatter, dim3(nchunks + 1), dim3(256), 0, st, topk_ids, s.T, s.k, s.E, nchunks, flags,
                      r);

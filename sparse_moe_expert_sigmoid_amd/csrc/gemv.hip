@@ -250,6 +250,19 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
     const int ntile = (nkb + 3) / 4;
     const uint8_t* qg = qs + (size_t)(n0 >> 4) * nkb * 256;
     const uint16_t* sg = sc + (size_t)(n0 >> 4) * nkb * 16;
+    // codes and scales of up to kDownTiles tiles per batch, all in flight before any arithmetic;
+    // the first batch is issued before h is staged, so that the two loads overlap
+    u32x4 cq[kDownTiles];
+    uint32_t dq[kDownTiles];
+    int blk[kDownTiles];
+#define MOE_DN_LOAD(TB)                                                        \
+    _Pragma("unroll") for (int j = 0; j < kDownTiles; ++j) {                   \
+      const int b = min(4 * min((TB) + j, ntile - 1) + G, nkb - 1);           \
+      blk[j] = b;                                                              \
+      cq[j] = ld16(qg + (size_t)b * 256 + 16 * n);                             \
+      dq[j] = sg[(size_t)b * 16 + n];                                          \
+    }
+    MOE_DN_LOAD(0);
     // stage h: lane l takes block l (clamped; blocks past nkb are never read; nkb <= 64 as I <= 2048)
     {
       const int bl = min(lane, nkb - 1);
@@ -273,20 +286,9 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
       hc0[wave][lane] = -fmaf(1032.f, sa, 72.f * sb);
     }
     wave_lds_sync();  // the tiles below read the blocks other lanes staged
-    // codes and scales of up to kDownTiles tiles per batch, all in flight before any arithmetic
-    u32x4 cq[kDownTiles];
-    uint32_t dq[kDownTiles];
-    int blk[kDownTiles];
-#define MOE_DN_LOAD(TB)                                                        \
-    _Pragma("unroll") for (int j = 0; j < kDownTiles; ++j) {                   \
-      const int b = min(4 * min((TB) + j, ntile - 1) + G, nkb - 1);           \
-      blk[j] = b;                                                              \
-      cq[j] = ld16(qg + (size_t)b * 256 + 16 * n);                             \
-      dq[j] = sg[(size_t)b * 16 + n];                                          \
-    }
-      float acc = 0.f;
+    float acc = 0.f;
     for (int tb = 0; tb < ntile; tb += kDownTiles) {
-      MOE_DN_LOAD(tb);
+      if (tb != 0) MOE_DN_LOAD(tb);
 #pragma unroll
       for (int j = 0; j < kDownTiles; ++j) {
         const float use = (tb + j < ntile && 4 * (tb + j) + G < nkb) ? 1.f : 0.f;

@@ -619,16 +619,7 @@ __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x
                                                   size_t n8) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
-  u32x4 v = ld16(x + 8 * i);
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const float lo = __builtin_bit_cast(float, v[m] << 16);
-    const float hi = __builtin_bit_cast(float, v[m] & 0xFFFF0000u);
-    v[m] = __builtin_bit_cast(uint32_t, half2v{to_f16_sat(lo), to_f16_sat(hi)});
-  }
-  uint32_t o[4];
-  x_bf16_pairs(v, o);  // same 16-bit lane shuffle as for bf16 pairs
-  *reinterpret_cast<u32x4*>(x16 + 8 * i) = u32x4{o[0], o[1], o[2], o[3]};
+  *reinterpret_cast<u32x4*>(x16 + 8 * i) = x8_bf16_to_f16_pairs(ld16(x + 8 * i));
 }
 
 // Combine: y[t] = (sum_j w[t,j] * y_pair[pair_pos[t*k+j]]) + y_shared[t], j ascending, no atomics.
@@ -716,11 +707,13 @@ static GArgs make_args(const Shape& s, const Routing& r, uint32_t flags) {
 }
 
 hipError_t launch_grouped_gateup(const Shape& s, const uint16_t* x, const Routing& r, Q4 w13, Q4 s13,
-                                 const GroupedOut& o, uint32_t flags, hipStream_t st) {
-  const size_t n8 = (size_t)s.T * s.d / 8;
-  hipLaunchKernelGGL(k_x_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, x, o.x16, n8);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+                                 const GroupedOut& o, uint32_t flags, hipStream_t st, bool x16_ready) {
+  if (!x16_ready) {
+    const size_t n8 = (size_t)s.T * s.d / 8;
+    hipLaunchKernelGGL(k_x_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, x, o.x16, n8);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   GArgs a = make_args(s, r, flags);
   a.a_r = o.x16;
   a.a_s = o.x16;

@@ -179,6 +179,21 @@ __device__ __forceinline__ void x_bf16_pairs(const u32x4 u, uint32_t out[4]) {
   out[3] = __builtin_amdgcn_perm(u[3], u[1], 0x07060302u);
 }
 
+// 8 consecutive bf16 activations -> fp16 in that pair order (x0 x4 x1 x5 x2 x6 x3 x7), each value
+// rounded to nearest even and saturated to +-65504 (exact inside the fp16 normal range).  The
+// grouped path's fp16 activation copy is made with this, by the router or by its own pass.
+__device__ __forceinline__ u32x4 x8_bf16_to_f16_pairs(u32x4 v) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float lo = __builtin_bit_cast(float, v[m] << 16);
+    const float hi = __builtin_bit_cast(float, v[m] & 0xFFFF0000u);
+    v[m] = __builtin_bit_cast(uint32_t, half2v{to_f16_sat(lo), to_f16_sat(hi)});
+  }
+  uint32_t o[4];
+  x_bf16_pairs(v, o);  // the same 16-bit lane shuffle as for bf16 pairs
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+
 // ---------------------------------------------------------------- GEMV helper
 // v_dot2_f32_f16: two fp16 products added to an fp32 accumulator.
 __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {

@@ -34,8 +34,9 @@ hipError_t launch_router_gemv(const Shape& s, const uint16_t* x, const float* w_
                               hipStream_t st);
 // writes kRouterParts partial logit arrays [part][T][E] (K split in that many parts)
 constexpr int kRouterParts = 8;
+// x16 (may be nullptr): also write the fp16 pair-ordered copy of x that launch_grouped_gateup reads
 hipError_t launch_router_mfma(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
-                              hipStream_t st);
+                              hipStream_t st, _Float16* x16 = nullptr);
 // logits: nparts partial arrays [nparts][T][E], summed in order
 hipError_t launch_topk(const Shape& s, const float* logits, int nparts, const float* bias, int32_t* topk_ids,
                        float* topk_w, hipStream_t st);
@@ -67,8 +68,9 @@ struct GroupedOut {
   _Float16* y_s;     // [T][d]
 };
 int grouped_max_mtiles(const Shape& s);
+// x16_ready: o.x16 already holds the fp16 copy of x (written by launch_router_mfma)
 hipError_t launch_grouped_gateup(const Shape& s, const uint16_t* x, const Routing& r, Q4 w13, Q4 s13,
-                                 const GroupedOut& o, uint32_t flags, hipStream_t st);
+                                 const GroupedOut& o, uint32_t flags, hipStream_t st, bool x16_ready = false);
 hipError_t launch_grouped_down(const Shape& s, const Routing& r, Q4 w2, Q4 s2, const GroupedOut& o,
                                uint32_t flags, hipStream_t st);
 // residual and y_bf16 as for launch_gemv_down_combine

@@ -141,10 +141,14 @@ __device__ __forceinline__ void split_hi_lo(const float4 a, const float4 b, bf16
 }
 
 // TA 16-token blocks, EB 64-expert blocks per workgroup, every chunk's K steps split over KS wavefronts
+// x16 (may be nullptr): the workgroups of one token tile and K part also write that part of the fp16
+// pair-ordered copy of x for the grouped gate+up, each a contiguous share of the tile's rows, from the
+// bf16 tile they staged in LDS (every element of x is written once).
 template <int TA, int EB, int KS>
 __global__ __launch_bounds__(64 * EB * KS) void k_router_mfma(const uint16_t* __restrict__ x,
                                                               const float* __restrict__ W,
-                                                              float* __restrict__ logits, int T, int d, int E) {
+                                                              float* __restrict__ logits, int T, int d, int E,
+                                                              _Float16* __restrict__ x16) {
   constexpr int kRtBlocks = EB, kRtWaves = EB * KS;
   static_assert(16 * TA % kRtWaves == 0, "token rows split evenly over the wavefronts");
   static_assert(16 * TA * kRtXRow >= kRtBlocks * 4 * TA * 64 * 16, "the K-part sums fit in the token tile");
@@ -228,6 +232,17 @@ __global__ __launch_bounds__(64 * EB * KS) void k_router_mfma(const uint16_t* __
         }
       }
     }
+    if (x16 != nullptr) {  // uniform; the chunk stays in LDS until the next chunk's barrier
+      const int eb = item % neb;
+      const int r0 = (16 * TA * eb) / neb, r1 = min((16 * TA * (eb + 1)) / neb, rows);
+      const int per_row = cn * (kRtK / 8);  // 16-byte groups of 8 values per row of the chunk
+      for (int i = threadIdx.x; i < (r1 - r0) * per_row; i += 64 * kRtWaves) {
+        const int r = r0 + i / per_row, g = i % per_row;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xs + r * kRtXRow + 16 * g);
+        *reinterpret_cast<u32x4*>(x16 + (size_t)(t0 + r) * d + (size_t)(st0 + c0) * kRtK + 8 * g) =
+            x8_bf16_to_f16_pairs(v);
+      }
+    }
   }
 #undef MOE_RT_LOAD
 #undef MOE_RT_MMA
@@ -288,31 +303,32 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 }
 
 template <int TA, int EB, int KS>
-static void router_mfma_cfg(const Shape& s, const uint16_t* x, const float* w_router, float* logits, hipStream_t st) {
+static void router_mfma_cfg(const Shape& s, const uint16_t* x, const float* w_router, float* logits, hipStream_t st,
+                            _Float16* x16) {
   const int ntt = (s.T + 16 * TA - 1) / (16 * TA), neb = (s.E + EB * kRtExp - 1) / (EB * kRtExp);
   const dim3 grid(ntt * neb * kRouterParts), block(64 * EB * KS);
-  hipLaunchKernelGGL((k_router_mfma<TA, EB, KS>), grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E);
+  hipLaunchKernelGGL((k_router_mfma<TA, EB, KS>), grid, block, 0, st, x, w_router, logits, s.T, s.d, s.E, x16);
 }
 
 hipError_t launch_router_mfma(const Shape& s, const uint16_t* x, const float* w_router, float* logits,
-                              hipStream_t st) {
+                              hipStream_t st, _Float16* x16) {
   const int ntt4 = (s.T + 63) / 64, ntt8 = (s.T + 127) / 128, neb4 = (s.E + 4 * kRtExp - 1) / (4 * kRtExp);
   if (ntt8 * neb4 * kRouterParts >= 256)
-    router_mfma_cfg<8, 4, 1>(s, x, w_router, logits, st);  // 128 tokens x 256 experts per workgroup
+    router_mfma_cfg<8, 4, 1>(s, x, w_router, logits, st, x16);  // 128 tokens x 256 experts per workgroup
   else if (ntt8 * ((s.E + 2 * kRtExp - 1) / (2 * kRtExp)) * kRouterParts >= 256)
-    router_mfma_cfg<8, 2, 2>(s, x, w_router, logits, st);  // 128 tokens x 128 experts x 2 K halves
+    router_mfma_cfg<8, 2, 2>(s, x, w_router, logits, st, x16);  // 128 tokens x 128 experts x 2 K halves
   else if (ntt4 * neb4 * kRouterParts >= 128)
-    router_mfma_cfg<4, 4, 2>(s, x, w_router, logits, st);  // 64 tokens x 256 experts x 2 K halves
+    router_mfma_cfg<4, 4, 2>(s, x, w_router, logits, st, x16);  // 64 tokens x 256 experts x 2 K halves
   else {
     // small T: 64 experts x 8 K parts per workgroup, and the largest token tile (64, 32 or 16) that still
     // gives 128 workgroups (T = 64: 11.7 -> 7.7 us with 16 tokens)
     const int neb1 = (s.E + kRtExp - 1) / kRtExp;
     if (ntt4 * neb1 * kRouterParts >= 128)
-      router_mfma_cfg<4, 1, 8>(s, x, w_router, logits, st);
+      router_mfma_cfg<4, 1, 8>(s, x, w_router, logits, st, x16);
     else if (((s.T + 31) / 32) * neb1 * kRouterParts >= 128)
-      router_mfma_cfg<2, 1, 8>(s, x, w_router, logits, st);
+      router_mfma_cfg<2, 1, 8>(s, x, w_router, logits, st, x16);
     else
-      router_mfma_cfg<1, 1, 8>(s, x, w_router, logits, st);
+      router_mfma_cfg<1, 1, 8>(s, x, w_router, logits, st, x16);
   }
   return hipGetLastError();
 }
