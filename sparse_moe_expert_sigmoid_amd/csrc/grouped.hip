@@ -51,8 +51,6 @@ constexpr int kRowBytes = kGroupedBK * 2;
 constexpr int kTileBytes = kGroupedBM * kRowBytes;  // 24 KB
 constexpr int kStages = 2;        // pipeline depth (LDS ring of kStages activation tiles)
 constexpr int kGroupedThreads = 64 * kGroupedWaves;
-constexpr int kDownOutBytes = kGroupedBM * kDownBandCols * 2;  // down output tile, staged in LDS
-constexpr int kLdsBytes = kStages * kTileBytes > kDownOutBytes ? kStages * kTileBytes : kDownOutBytes;
 constexpr int kTileLoads = kTileBytes / (kGroupedThreads * 16);  // buffer_load ... lds per lane per tile
 constexpr int kLoadsPerStep = kTileLoads + 8;        // vector-memory ops per lane per K step (+4 code blocks, 4 scales)
 constexpr int kRowsPerWave = kGroupedBM / kGroupedWaves;  // activation rows staged by each wavefront
@@ -101,265 +99,163 @@ struct TileCtx {
   bool ktail, shared;
 };
 
-// Scheduling of one unit of a K-step (one 16-row activation slice): its LDS read of the slice two
-// units ahead first, then its four MFMAs with the unit's share of the dequantisation (V VALU
-// instructions) spread between them.  Units are separated by full scheduling barriers, so every LDS
-// read stays two units (eight MFMAs) ahead of its use whatever the register pressure, and a wavefront
-// issues its dequantisation while its own MFMAs occupy the matrix pipe.
-// Materialise a value in registers at this point of the program (no instruction).
-__device__ __forceinline__ void pin_vgprs(half8& v) {
-  u32x4 u = __builtin_bit_cast(u32x4, v);
-  asm volatile("" : "+v"(u));
-  v = __builtin_bit_cast(half8, u);
-}
-
-template <int I, int V>
-__device__ __forceinline__ void unit_schedule() {
-  if constexpr (I < 4) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    constexpr int v = (V * (I + 1)) / 4 - (V * I) / 4;
-    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x002, v, 0);  // VALU
-    unit_schedule<I + 1, V>();
-  }
-}
-
-// Dequantisation of one dword of codes (8 weights) into an MFMA operand, in the common form (scales in
-// [2^-10, 2^-4) or 0, one rounding) or the general one.
-template <bool GENERAL>
-struct Deq {
-  SmallScale ss[4];
-  const half2v* d2;
-  uint32_t mask, magic;
-  __device__ __forceinline__ Deq(const half2v* d2_, uint32_t mask_, uint32_t magic_) : d2(d2_), mask(mask_), magic(magic_) {
-    if constexpr (!GENERAL) {
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) ss[ns] = small_scale(d2_[ns]);
-    }
-  }
-  __device__ __forceinline__ half8 operator()(uint32_t w, int ns) const {
-    if constexpr (GENERAL) return dequant8_general(w, d2[ns], mask, magic);
-    else return dequant8_small(w, ss[ns]);
-  }
-};
-
-// One MFMA K-step S (32 of the iteration's 128 K values) of a tile with NMT slices: for each 16-row slice
-// of activations (read from LDS two slices ahead, across K-step boundaries) four MFMAs against the
-// wavefront's four weight slices; between them, the four weight fragments of step S + 1 are
-// dequantised.  Every K-step is one basic block (no branches), so the hints above can interleave it.
-template <int S, int NMT, bool GENERAL>
-__device__ __forceinline__ void k_step(floatx4 (&acc)[NMT][4], half8 (&b_cur)[4], half8& a0, half8& a1,
-                                       const char* At, const TileCtx& c, const u32x4* q, const Deq<GENERAL>& deq) {
-  constexpr int NI = 4 * NMT;
-  constexpr int kDeqVALU = GENERAL ? 19 : 9;  // VALU instructions per dequantised fragment
-  auto aread = [&](int idx) __attribute__((always_inline)) {
-    return *reinterpret_cast<const half8*>(At + c.rdo + 16 * (c.gx ^ (idx / NMT)) + (idx % NMT) * 16 * kRowBytes);
-  };
-  half8 b_nxt[4];
-#pragma unroll
-  for (int mt = 0; mt < NMT; ++mt) {
-    const int idx = S * NMT + mt;
-    __builtin_amdgcn_sched_barrier(0);
-    half8 a2;
-    if (idx + 2 < NI) a2 = aread(idx + 2);
-#pragma unroll
-    for (int ns = 0; ns < 4; ++ns)
-      // weights as the A operand: the tile comes out transposed (see the epilogue)
-      acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b_cur[ns], a0, acc[mt][ns], 0, 0, 0);
-    // fragments of step S + 1 dequantised in this unit; the empty asm statements keep each one here
-    // (otherwise instruction selection emits pure arithmetic next to its first use, i.e. all of it in
-    // the last unit before the next K-step)
-    int nd = 0;
-    if (S < 3 && mt < 4) {
-      b_nxt[mt] = deq(q[mt][S + 1], mt);
-      pin_vgprs(b_nxt[mt]);
-      nd = 1;
-    }
-    if (S < 3 && mt == NMT - 1) {
-#pragma unroll
-      for (int ns = NMT; ns < 4; ++ns) {
-        b_nxt[ns] = deq(q[ns][S + 1], ns);
-        pin_vgprs(b_nxt[ns]);
-      }
-      nd += NMT < 4 ? 4 - NMT : 0;
-    }
-    a0 = a1;
-    if (idx + 2 < NI) a1 = a2;
-    if (idx + 2 < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the LDS read first
-    if (nd == 0) unit_schedule<0, 0>();
-    else if (nd == 1) unit_schedule<0, kDeqVALU>();
-    else if (nd == 2) unit_schedule<0, 2 * kDeqVALU>();
-    else if (nd == 3) unit_schedule<0, 3 * kDeqVALU>();
-    else unit_schedule<0, 4 * kDeqVALU>();
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (S < 3) {
-#pragma unroll
-    for (int ns = 0; ns < 4; ++ns) b_cur[ns] = b_nxt[ns];
-  }
-}
-
-// One K iteration (4 MFMA K-steps of 32) on the LDS tile At.
-template <int NMT, bool GENERAL>
-__device__ __forceinline__ void mfma_iter(floatx4 (&acc)[NMT][4], const char* At, const TileCtx& c, const u32x4* q,
-                                          const half2v* d2) {
-  const Deq<GENERAL> deq(d2, c.dq_mask, c.dq_magic);
-  half8 b_cur[4];
-#pragma unroll
-  for (int ns = 0; ns < 4; ++ns) b_cur[ns] = deq(q[ns][0], ns);
-  constexpr int NI = 4 * NMT;
-  half8 a0 = *reinterpret_cast<const half8*>(At + c.rdo + 16 * c.gx);
-  half8 a1 = *reinterpret_cast<const half8*>(At + c.rdo + 16 * (c.gx ^ ((NI > 1 ? 1 : 0) / NMT)) +
-                                             ((NI > 1 ? 1 : 0) % NMT) * 16 * kRowBytes);
-  k_step<0, NMT, GENERAL>(acc, b_cur, a0, a1, At, c, q, deq);
-  k_step<1, NMT, GENERAL>(acc, b_cur, a0, a1, At, c, q, deq);
-  k_step<2, NMT, GENERAL>(acc, b_cur, a0, a1, At, c, q, deq);
-  k_step<3, NMT, GENERAL>(acc, b_cur, a0, a1, At, c, q, deq);
-}
-
-// Loads of K iteration `it`: the activation tile into LDS buffer `buf` (this wavefront's rows).
-__device__ __forceinline__ void issue_a(const TileCtx& c, char* As, int it, int buf) {
-  const int kb = it * kGroupedBK * 2;
-  if (c.ktail && it == c.nit - 1) {  // uniform
-#pragma unroll
-    for (int i = 0; i < kTileLoads; ++i) {
-      // a chunk past the row end re-reads the tile's first chunk of the same row: finite data
-      // that meets zero weights (the weights' K tail is masked to zero below)
-      const int chunk = (c.lane & 15) ^ ((kRowsPerWave * c.wave + 4 * i + (c.lane >> 4)) & 15);
-      const uint32_t off = c.aoff[i] - (it * kGroupedBK + 8 * chunk >= c.Kdim ? 16u * (uint32_t)chunk : 0u);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          c.ra, (lds_void*)(As + buf * kTileBytes + (kRowsPerWave * c.wave + 4 * i) * kRowBytes), 16, (int)off, kb,
-          0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kTileLoads; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          c.ra, (lds_void*)(As + buf * kTileBytes + (kRowsPerWave * c.wave + 4 * i) * kRowBytes), 16,
-          (int)c.aoff[i], kb, 0, 0);
-  }
-}
-// ... and this wavefront's four weight slices: one 16-byte code block and its scale per slice and lane.
-__device__ __forceinline__ void load_w(const TileCtx& c, int it, u32x4* qd, uint32_t* sd) {
-  // in the K tail iteration, lanes whose block lies past the row end re-read the row's last block
-  // (their scale is masked to zero): every access stays inside the weight matrix
-  const bool tail = c.ktail && it == c.nit - 1;  // uniform
-  const uint32_t qo = tail ? c.qoff_tail : c.qoff, so = tail ? c.soff_tail : c.soff;
-#pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
-    qd[ns] = __builtin_amdgcn_raw_buffer_load_b128(c.rq, (int)qo, c.qns[ns] + it * 1024, 0);
-    sd[ns] = __builtin_amdgcn_raw_buffer_load_b16(c.rs, (int)so, c.sns[ns] + it * 128, 0);
-  }
-}
-
-// Whether any scale of this wavefront's four weight slices, over the whole K range, is outside the
-// range of the common dequantisation form (uniform).  A slice's scales are one contiguous run of
-// nkb * 16 fp16 values, read here in 1 KB chunks, 16 bytes per lane; lanes past the run read the
-// next slice's scales or nothing (the buffer ends at the matrix) and are ignored.  The first four
-// chunks (K <= 4096) are issued before the tile's first K iteration and checked behind it; longer
-// rows check their remaining chunks four at a time.
-struct ScaleScan {
-  static constexpr int kRound = 4;  // chunks per slice in flight at once
-  u32x4 v[4][kRound];
-  __device__ __forceinline__ void issue(const TileCtx& c, int r0) {
-    const int chunks = (c.nkb * 32 + 1023) >> 10;
-#pragma unroll
-    for (int r = 0; r < kRound; ++r)
-      if (r0 + r < chunks)
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns)
-          v[ns][r] = __builtin_amdgcn_raw_buffer_load_b128(c.rs, 16 * c.lane, c.sns[ns] + 1024 * (r0 + r), 0);
-  }
-  __device__ __forceinline__ bool bad(const TileCtx& c, int r0) const {
-    const int bytes = c.nkb * 32;
-    bool b = false;
-#pragma unroll
-    for (int r = 0; r < kRound; ++r)
-      if (1024 * (r0 + r) + 16 * c.lane < bytes)
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            b = b || !small_scale_ok(v[ns][r][j] & 0xFFFFu) || !small_scale_ok(v[ns][r][j] >> 16);
-    return b;
-  }
-  // after issue(c, 0): the answer for the whole row
-  __device__ __forceinline__ bool general(const TileCtx& c) {
-    bool b = bad(c, 0);
-    const int chunks = (c.nkb * 32 + 1023) >> 10;
-    for (int r0 = kRound; r0 < chunks; r0 += kRound) {
-      issue(c, r0);
-      b = b || bad(c, r0);
-    }
-    return __builtin_amdgcn_ballot_w64(b) != 0;
-  }
-};
-
 // Main loop and epilogue of one tile with NMT active 16-row slices (known
-// at compile time, so the K loop has no per-MFMA conditions) and one
-// dequantisation form for the whole tile.  Slices of the wavefront's four
-// 16-column weight slices that lie past the N edge are computed on a valid
-// row and discarded in the epilogue.  The loads of K iteration 0 were
-// issued by the caller (q0, sc0 and LDS buffer 0).
-template <bool GATEUP, int NMT, bool GENERAL>
-__device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, char* As, const u32x4 (&q0)[4],
-                                             const uint32_t (&sc0)[4]) {
+// at compile time, so the K loop has no per-MFMA conditions).  Slices of the
+// wavefront's four 16-column weight slices that lie past the N edge are
+// computed on a valid row and discarded in the epilogue.
+template <bool GATEUP, int NMT>
+__device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, char* As) {
+  constexpr int BK = kGroupedBK;
+  auto issue_a = [&](int it, int buf) {
+    const int kb = it * BK * 2;
+    if (c.ktail && it == c.nit - 1) {  // uniform
+#pragma unroll
+      for (int i = 0; i < kTileLoads; ++i) {
+        // a chunk past the row end re-reads the tile's first chunk of the same row: finite data
+        // that meets zero weights (the weights' K tail is masked to zero below)
+        const int chunk = (c.lane & 15) ^ ((kRowsPerWave * c.wave + 4 * i + (c.lane >> 4)) & 15);
+        const uint32_t off = c.aoff[i] - (it * BK + 8 * chunk >= c.Kdim ? 16u * (uint32_t)chunk : 0u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            c.ra, (lds_void*)(As + buf * kTileBytes + (kRowsPerWave * c.wave + 4 * i) * kRowBytes), 16, (int)off, kb,
+            0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kTileLoads; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            c.ra, (lds_void*)(As + buf * kTileBytes + (kRowsPerWave * c.wave + 4 * i) * kRowBytes), 16,
+            (int)c.aoff[i], kb, 0, 0);
+    }
+  };
+  auto load_w = [&](int it, u32x4* qd, uint32_t* sd) {
+    // in the K tail iteration, lanes whose block lies past the row end re-read the row's last block
+    // (their scale is masked to zero): every access stays inside the weight matrix
+    const bool tail = c.ktail && it == c.nit - 1;  // uniform
+    const uint32_t qo = tail ? c.qoff_tail : c.qoff, so = tail ? c.soff_tail : c.soff;
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+      qd[ns] = __builtin_amdgcn_raw_buffer_load_b128(c.rq, (int)qo, c.qns[ns] + it * 1024, 0);
+      sd[ns] = __builtin_amdgcn_raw_buffer_load_b16(c.rs, (int)so, c.sns[ns] + it * 128, 0);
+    }
+  };
+
   floatx4 acc[NMT][4];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) acc[mt][ns] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // One K iteration on LDS buffer `buf` with the scales of iteration `it` (the K tail's blocks weigh
-  // zero).  The body has no branches around the MFMAs, so the accumulators keep their registers.
+  // One K iteration (4 MFMA K-steps of 32) on LDS buffer `buf`.  Within a K-step the activation
+  // fragment of each 16-row slice is read from LDS just before its four MFMAs (one slice ahead), and
+  // the four weight fragments of the next K-step are dequantised between the MFMAs.  The loop body has
+  // no branches around the MFMAs, so the accumulators keep their registers across iterations.
+  auto compute = [&](int buf, const u32x4* q, const half2v* d2, bool general) __attribute__((always_inline)) {
+    const char* At = As + buf * kTileBytes;
+    SmallScale ss[4];
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) ss[ns] = small_scale(d2[ns]);
+    // common form; redone in the general form when a scale of this iteration is outside its range
+    // (`general` is uniform, so this is a scalar branch that is normally not taken)
+    auto deq = [&](uint32_t w, int ns) __attribute__((always_inline)) {
+      half8 r = dequant8_small(w, ss[ns]);
+      if (__builtin_expect(general, 0)) r = dequant8_general(w, d2[ns], c.dq_mask, c.dq_magic);
+      return r;
+    };
+    half8 b_cur[4];
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) b_cur[ns] = deq(q[ns][0], ns);
+    // activation fragments are read two 16-row slices ahead, across K-step boundaries
+    constexpr int NI = 4 * NMT;
+    auto aread = [&](int idx) __attribute__((always_inline)) {
+      return *reinterpret_cast<const half8*>(At + c.rdo + 16 * (c.gx ^ (idx / NMT)) + (idx % NMT) * 16 * kRowBytes);
+    };
+    half8 a0 = aread(0), a1 = aread(NI > 1 ? 1 : 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      half8 b_nxt[4];
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const int idx = s * NMT + mt;
+        half8 a2;
+        if (idx + 2 < NI) a2 = aread(idx + 2);
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns)
+          // weights as the A operand: the tile comes out transposed (see the epilogue)
+          acc[mt][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b_cur[ns], a0, acc[mt][ns], 0, 0, 0);
+        if (s < 3 && mt < 4) b_nxt[mt] = deq(q[mt][s + 1], mt);
+        a0 = a1;
+        if (idx + 2 < NI) a1 = a2;
+      }
+      if (s < 3) {
+#pragma unroll
+        for (int ns = NMT; ns < 4; ++ns) b_nxt[ns] = deq(q[ns][s + 1], ns);
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) b_cur[ns] = b_nxt[ns];
+      }
+    }
+  };
+  // Scales of iteration `it` (the K tail's blocks weigh zero), and whether any scale the wavefront uses
+  // in this iteration is outside the range of the common dequantisation form.
   auto run_step = [&](int buf, const u32x4* q, const uint32_t* sc_in, int it) __attribute__((always_inline)) {
     half2v d2[4];
     const bool tail = c.ktail && it == c.nit - 1;  // uniform
+    bool small = true;
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
       // the step's loads have landed: no register in flight is overwritten here
       const uint32_t bits = (tail && it * 4 + c.G >= c.nkb) ? 0u : sc_in[ns];
+      small = small && small_scale_ok(bits);
       const _Float16 dv = __builtin_bit_cast(_Float16, (uint16_t)bits);
       d2[ns] = half2v{dv, dv};
     }
-    mfma_iter<NMT, GENERAL>(acc, As + buf * kTileBytes, c, q, d2);
+    compute(buf, q, d2, __builtin_amdgcn_ballot_w64(!small) != 0);
   };
 
-  // Two-stage pipeline: while step `it` is computed, the activation tile and weight blocks of step
-  // it+1 are in flight (LDS ring of two tiles, weights in registers).
-  static_assert(kStages == 2, "the caller issues exactly the first step");
+  // kStages-deep pipeline: while step `it` is computed, the activation tiles and weight blocks of
+  // steps it+1 .. it+kStages-1 are in flight (LDS ring of kStages tiles, weights in registers).
   constexpr int NS = kStages;
   u32x4 q[NS][4];
   uint32_t sc[NS][4];
 #pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
-    q[0][ns] = q0[ns];
-    sc[0][ns] = sc0[ns];
+  for (int st = 0; st < NS - 1; ++st) {
+    if (st < c.nit) {
+      issue_a(st, st);
+      load_w(st, q[st], sc[st]);
+    }
   }
-  // Wait until step `it` has landed (the younger step stays in flight), then barrier.
+  // Wait until step `it` has landed (younger steps stay in flight), then barrier.
   auto arrive = [&](int it) __attribute__((always_inline)) {
-    vm_lgkm_wait<0>();
+    const int younger = min(NS - 2, c.nit - 1 - it);
+    static_assert(kStages <= 3, "the waits below cover up to two younger steps");
+    if (younger >= 2) vm_lgkm_wait<2 * kLoadsPerStep>();
+    else if (younger == 1) vm_lgkm_wait<kLoadsPerStep>();
+    else vm_lgkm_wait<0>();
     tile_barrier();  // every wavefront's part of tile `it` is in LDS; tile it-1 is no longer read
   };
-  // Main loop over whole pairs of steps: the compute is unconditional (only the load issue depends
-  // on the trip count), so the accumulators stay in their registers.
+  // Main loop over whole groups of NS steps: the compute is unconditional (only the load issue and the
+  // wait depth depend on the trip count), so the accumulators stay in their registers.
   int it0 = 0;
   for (; it0 + NS <= c.nit; it0 += NS) {
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       const int it = it0 + st;
       arrive(it);
-      if (it + 1 < c.nit) {
-        const int nxt = (st + 1) % NS;  // folded: st is an unrolled constant
-        issue_a(c, As, it + 1, nxt);
-        load_w(c, it + 1, q[nxt], sc[nxt]);
+      if (it + NS - 1 < c.nit) {
+        const int nxt = (st + NS - 1) % NS;  // folded: st is an unrolled constant
+        issue_a(it + NS - 1, nxt);
+        load_w(it + NS - 1, q[nxt], sc[nxt]);
       }
       run_step(st, q[st], sc[st], it);
     }
   }
-  // An odd trip count leaves one step (its loads were issued above or by the caller).
-  if (it0 < c.nit) {
-    arrive(it0);
-    run_step(0, q[0], sc[0], it0);
+  // The remaining nit % NS steps (their loads were issued above or in the prologue).
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st) {
+    const int it = it0 + st;
+    if (it < c.nit) {
+      arrive(it);
+      run_step(st, q[st], sc[st], it);
+    }
   }
 
   // ---- epilogue.  With the weights as the A operand, lane (n, G) holds, for activation row
@@ -402,10 +298,10 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
     }
   }
   if (!GATEUP) {
-    // The down tile goes out through LDS so that every store writes whole rows: 96 rows of
-    // kDownBandCols fp16, 16-byte chunk j of row r in slot j ^ (r & 31) (the 16 lanes that write one
-    // column chunk for 16 rows hit 16 different bank groups).
-    static_assert(kLdsBytes >= kDownOutBytes, "the output tile fits in LDS");
+    // The down tile goes out through LDS so that every store writes whole rows: 96 x 256 fp16 = the
+    // activation ring, 512 B per row, 16-byte chunk j of row r in slot j ^ (r & 31) (the 16 lanes that
+    // write one column chunk for 16 rows hit 16 different bank groups).
+    static_assert(kStages * kTileBytes >= kGroupedBM * kDownBandCols * 2, "the output tile fits in the ring");
     vm_lgkm_wait<0>();
     tile_barrier();  // every wavefront is done reading the activation ring
 #pragma unroll
@@ -422,15 +318,13 @@ __device__ __forceinline__ void grouped_tile(const GArgs& a, const TileCtx& c, c
     }
     vm_lgkm_wait<0>();
     tile_barrier();
-    // thread t stores chunk t % C of rows t / C, t / C + R, ... (C chunks per row, R rows per pass)
-    constexpr int C = kDownBandCols / 8, R = kGroupedThreads / C;
-    static_assert(R * C == kGroupedThreads && (16 * kGroupedBM) % R == 0, "whole rows per pass");
+    // thread t stores chunk t % 32 of rows t / 32, t / 32 + 8, ...: one wavefront store covers two rows
     _Float16* out = c.shared ? a.y_s : a.y_r;
-    const int tid = (int)threadIdx.x, chunk = tid % C;
+    const int tid = (int)threadIdx.x, chunk = tid & 31;
     const int col = c.c0 - 64 * c.wave + 8 * chunk;  // d % 32 == 0: a chunk is all inside d or all past it
 #pragma unroll
-    for (int i = 0; i < 16 * NMT / R; ++i) {
-      const int row = R * i + tid / C;
+    for (int i = 0; i < 2 * NMT; ++i) {
+      const int row = 8 * i + (tid >> 5);
       const u32x4 v = *reinterpret_cast<const u32x4*>(As + row * (kDownBandCols * 2) + ((chunk ^ (row & 31)) * 16));
       if (row < c.mlen && col < a.d) *reinterpret_cast<u32x4*>(out + (size_t)(c.rbase + row) * a.d + col) = v;
     }
@@ -441,7 +335,7 @@ template <bool GATEUP>
 __global__ __launch_bounds__(kGroupedThreads, 8 / kGroupedWaves) void k_grouped(GArgs a) {
   constexpr int BM = kGroupedBM, BK = kGroupedBK;
   constexpr int BANDW = GATEUP ? kGateUpBandCols : kDownBandCols;
-  __shared__ __attribute__((aligned(1024))) char As[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char As[kStages * kTileBytes];
   __shared__ int s_prefix[kMaxExperts + 2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = ufl(tid >> 6);
@@ -579,34 +473,13 @@ __global__ __launch_bounds__(kGroupedThreads, 8 / kGroupedWaves) void k_grouped(
   c.G = G; c.n = n; c.lane = lane; c.ktail = ktail; c.shared = shared;
   c.dq_mask = a.dq_mask;
   c.dq_magic = a.dq_magic;
-  // The scan of the tile's scales is issued first, then K iteration 0; the scan's result is needed
-  // once both are in flight.
-  ScaleScan scan;
-  scan.issue(c, 0);
-  u32x4 q0[4];
-  uint32_t sc0[4];
-  issue_a(c, As, 0, 0);
-  load_w(c, 0, q0, sc0);
-  const bool general = scan.general(c);
-  const int nmt = (mlen + 15) >> 4;
-  if (__builtin_expect(general, 0)) {
-    switch (nmt) {
-      case 1: grouped_tile<GATEUP, 1, true>(a, c, As, q0, sc0); break;
-      case 2: grouped_tile<GATEUP, 2, true>(a, c, As, q0, sc0); break;
-      case 3: grouped_tile<GATEUP, 3, true>(a, c, As, q0, sc0); break;
-      case 4: grouped_tile<GATEUP, 4, true>(a, c, As, q0, sc0); break;
-      case 5: grouped_tile<GATEUP, 5, true>(a, c, As, q0, sc0); break;
-      default: grouped_tile<GATEUP, 6, true>(a, c, As, q0, sc0); break;
-    }
-  } else {
-    switch (nmt) {
-      case 1: grouped_tile<GATEUP, 1, false>(a, c, As, q0, sc0); break;
-      case 2: grouped_tile<GATEUP, 2, false>(a, c, As, q0, sc0); break;
-      case 3: grouped_tile<GATEUP, 3, false>(a, c, As, q0, sc0); break;
-      case 4: grouped_tile<GATEUP, 4, false>(a, c, As, q0, sc0); break;
-      case 5: grouped_tile<GATEUP, 5, false>(a, c, As, q0, sc0); break;
-      default: grouped_tile<GATEUP, 6, false>(a, c, As, q0, sc0); break;
-    }
+  switch ((mlen + 15) >> 4) {
+    case 1: grouped_tile<GATEUP, 1>(a, c, As); break;
+    case 2: grouped_tile<GATEUP, 2>(a, c, As); break;
+    case 3: grouped_tile<GATEUP, 3>(a, c, As); break;
+    case 4: grouped_tile<GATEUP, 4>(a, c, As); break;
+    case 5: grouped_tile<GATEUP, 5>(a, c, As); break;
+    default: grouped_tile<GATEUP, 6>(a, c, As); break;
   }
 }
 
