@@ -30,6 +30,7 @@ EXPORTED_SYMBOLS = (
     "moe_route", "moe_build_descriptors", "moe_q4_forward", "moe_q4_forward_residual", "moe_layer_forward", "moe_strerror",
     "moe_decode_ctx_workspace_bytes", "moe_decode_ctx_create", "moe_decode_ctx_run", "moe_decode_ctx_destroy",
     "moe_rmsnorm_bf16", "moe_q4_pack", "moe_layer_forward_noalloc",
+    "moe_q4_to_mxfp4", "moe_rows_to_fp8", "moe_w4a8_scratch_bytes", "moe_w4a8_forward",
 )
 MOE_NOALLOC_MAX_BYTES = 64 << 20
 
@@ -51,6 +52,14 @@ class _Q4(Structure):
 
 class _Weights(Structure):
     _fields_ = [("w13", _Q4), ("w2", _Q4), ("s13", _Q4), ("s2", _Q4)]
+
+
+class _Mx(Structure):
+    _fields_ = [("codes", c_void_p), ("exps", c_void_p)]
+
+
+class _MxWeights(Structure):
+    _fields_ = [("w13", _Mx), ("w2", _Mx), ("s13", _Mx), ("s2", _Mx)]
 
 
 class _Layer(Structure):
@@ -127,6 +136,15 @@ def lib() -> ctypes.CDLL:
     L.moe_layer_forward_noalloc.restype = c_int
     L.moe_q4_pack.argtypes = [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     L.moe_q4_pack.restype = c_int
+    L.moe_q4_to_mxfp4.argtypes = [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+    L.moe_q4_to_mxfp4.restype = c_int
+    L.moe_rows_to_fp8.argtypes = [c_int32, c_int32, c_void_p, c_int, c_void_p, c_void_p, c_void_p]
+    L.moe_rows_to_fp8.restype = c_int
+    L.moe_w4a8_scratch_bytes.argtypes = [D, c_uint32]
+    L.moe_w4a8_scratch_bytes.restype = c_size_t
+    L.moe_w4a8_forward.argtypes = [D, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, POINTER(_MxWeights),
+                                   c_void_p, c_void_p, c_size_t, c_uint32, c_void_p]
+    L.moe_w4a8_forward.restype = c_int
     L.moe_strerror.argtypes = [c_int]
     L.moe_strerror.restype = c_char_p
     _lib = L
@@ -294,3 +312,37 @@ def moe_layer_forward_noalloc(dims, x, w_router, bias, weights, y, topk_ids, top
                                          ctypes.byref(ws), _ptr(residual), _ptr(y), _ptr(topk_ids), _ptr(topk_w),
                                          flags, _stream(stream))
     return _done(rc, check, "moe_layer_forward_noalloc")
+
+
+def moe_q4_to_mxfp4(n_mats: int, rows: int, K: int, qs, scales, codes_out, exps_out, stream=None,
+                    check: bool = True) -> int:
+    """Q4 blocks -> MXFP4 blocks (e2m1 codes, biased block exponents), block for block, on the device."""
+    rc = lib().moe_q4_to_mxfp4(n_mats, rows, K, _ptr(qs), _ptr(scales), _ptr(codes_out), _ptr(exps_out),
+                               _stream(stream))
+    return _done(rc, check, "moe_q4_to_mxfp4")
+
+
+def moe_rows_to_fp8(rows: int, K: int, x, codes_out, scales_out, in_is_fp16: bool = False, stream=None,
+                    check: bool = True) -> int:
+    """Rows of bf16 (or fp16) bits -> e4m3 codes and fp32 row scales, on the device."""
+    rc = lib().moe_rows_to_fp8(rows, K, _ptr(x), 1 if in_is_fp16 else 0, _ptr(codes_out), _ptr(scales_out),
+                               _stream(stream))
+    return _done(rc, check, "moe_rows_to_fp8")
+
+
+def moe_w4a8_scratch_bytes(dims, flags: int = 0) -> int:
+    return lib().moe_w4a8_scratch_bytes(ctypes.byref(Dims.of(dims)), flags)
+
+
+def _mx_weights(w) -> _MxWeights:
+    """w: mapping with w13_codes, w13_exps, w2_codes, w2_exps, s13_codes, s13_exps, s2_codes, s2_exps."""
+    return _MxWeights(*[_Mx(_ptr(w[n + "_codes"]), _ptr(w[n + "_exps"])) for n in ("w13", "w2", "s13", "s2")])
+
+
+def moe_w4a8_forward(dims, x, topk_ids, topk_w, routing, weights, y, scratch, routing_bytes=None,
+                     scratch_bytes=None, flags: int = 0, stream=None, check: bool = True) -> int:
+    ws = weights if isinstance(weights, _MxWeights) else _mx_weights(weights)
+    rc = lib().moe_w4a8_forward(ctypes.byref(Dims.of(dims)), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(routing),
+                                _nbytes(routing, routing_bytes), ctypes.byref(ws), _ptr(y), _ptr(scratch),
+                                _nbytes(scratch, scratch_bytes), flags, _stream(stream))
+    return _done(rc, check, "moe_w4a8_forward")

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libmoe_q4.so")
-SOURCES = ["router.hip", "build.hip", "gemv.hip", "grouped.hip", "norm.hip", "pack.hip", "noalloc.hip", "abi.cpp"]
+SOURCES = ["router.hip", "build.hip", "gemv.hip", "grouped.hip", "w4a8.hip", "norm.hip", "pack.hip", "noalloc.hip", "abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [

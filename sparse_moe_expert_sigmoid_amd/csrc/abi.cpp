@@ -125,6 +125,37 @@ bool q4_aligned(const moe_q4& q) { return aligned(q.qs, 16) && aligned(q.scales,
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// W4A8 variant: grouped path only, every K a whole number of 128-value MFMA steps.
+int check_w4a8(const moe_dims* d, uint32_t flags) {
+  const int rc = check_dims(d, flags);
+  if (rc) return rc;
+  if (choose_path(d, flags) != 1) return MOE_EUNSUPPORTED;
+  if (d->d % 128 || d->I % 128 || d->I_shared % 128) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+struct W4A8Layout {
+  size_t x8, xs, h_r, h_s, h8_r, hs_r, h8_s, hs_s, y_pair, y_s, total;
+};
+
+W4A8Layout w4a8_layout(const moe_dims* d) {
+  const size_t T = d->T, P = (size_t)d->T * d->k;
+  W4A8Layout S{};
+  size_t off = 0;
+  S.x8 = off;     off += align256(T * d->d);
+  S.xs = off;     off += align256(T * 4);
+  S.h_r = off;    off += align256(P * d->I * 2);
+  S.h_s = off;    off += align256(T * d->I_shared * 2);
+  S.h8_r = off;   off += align256(P * d->I);
+  S.hs_r = off;   off += align256(P * 4);
+  S.h8_s = off;   off += align256(T * d->I_shared);
+  S.hs_s = off;   off += align256(T * 4);
+  S.y_pair = off; off += align256(P * d->d * 2);
+  S.y_s = off;    off += align256(T * d->d * 2);
+  S.total = off;
+  return S;
+}
+
 }  // namespace
 
 extern "C" {
@@ -516,6 +547,74 @@ int moe_q4_pack(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs_in, c
   (void)hipGetLastError();
   return hip_rc(moe::launch_q4_pack((size_t)n_mats, rows, K, qs_in, scales_in, qs_out, scales_out,
                                     static_cast<hipStream_t>(stream)));
+}
+
+int moe_q4_to_mxfp4(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs, const uint16_t* scales,
+                    uint8_t* codes_out, uint8_t* exps_out, void* stream) {
+  if (n_mats < 1 || rows < 1 || K < 1 || !qs || !scales || !codes_out || !exps_out) return MOE_EINVAL;
+  if (rows % 16 || K % 32 || rows > (1 << 24) || K > (1 << 24)) return MOE_EUNSUPPORTED;
+  if (!aligned(qs, 16) || !aligned(codes_out, 16) || !aligned(scales, 2)) return MOE_EALIGN;
+  const size_t nblocks = (size_t)n_mats * (size_t)rows * (size_t)(K / 32);
+  const uintptr_t qi = (uintptr_t)qs, si = (uintptr_t)scales, co = (uintptr_t)codes_out, eo = (uintptr_t)exps_out;
+  const size_t qb = 16 * nblocks, sb = 2 * nblocks, eb = nblocks;
+  auto overlap = [](uintptr_t a, size_t na, uintptr_t b, size_t nb) { return a < b + nb && b < a + na; };
+  if (overlap(co, qb, qi, qb) || overlap(co, qb, si, sb) || overlap(eo, eb, qi, qb) || overlap(eo, eb, si, sb) ||
+      overlap(co, qb, eo, eb))
+    return MOE_EINVAL;
+  (void)hipGetLastError();
+  return hip_rc(moe::launch_q4_to_mx(nblocks, qs, scales, codes_out, exps_out, static_cast<hipStream_t>(stream)));
+}
+
+int moe_rows_to_fp8(int32_t rows, int32_t K, const uint16_t* in, int in_is_fp16, uint8_t* codes_out,
+                    float* scales_out, void* stream) {
+  if (rows < 1 || K < 1 || !in || !codes_out || !scales_out) return MOE_EINVAL;
+  if (K % 4 || (long long)rows * K >= (1LL << 31)) return MOE_EUNSUPPORTED;
+  if (!aligned(in, 16) || !aligned(codes_out, 16) || !aligned(scales_out, 4)) return MOE_EALIGN;
+  (void)hipGetLastError();
+  return hip_rc(moe::launch_rows_fp8(in, in_is_fp16 != 0, rows, K, codes_out, scales_out,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_w4a8_scratch_bytes(const moe_dims* dims, uint32_t flags) {
+  if (check_w4a8(dims, flags)) return 0;
+  return w4a8_layout(dims).total;
+}
+
+int moe_w4a8_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
+                     const void* routing, size_t routing_bytes, const moe_mxfp4_weights* w, float* y,
+                     void* scratch, size_t scratch_bytes, uint32_t flags, void* stream) {
+  const int rc = check_w4a8(dims, flags);
+  if (rc) return rc;
+  if (!x_bf16 || !topk_ids || !topk_w || !routing || !w || !y || !scratch) return MOE_EINVAL;
+  const moe_mxfp4* m[4] = {&w->w13, &w->w2, &w->s13, &w->s2};
+  for (const moe_mxfp4* p : m)
+    if (!p->codes || !p->exps) return MOE_EINVAL;
+  if (!aligned(x_bf16, 16) || !aligned(y, 16) || !aligned(scratch, 16) || !aligned(routing, 16) ||
+      !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return MOE_EALIGN;
+  for (const moe_mxfp4* p : m)
+    if (!aligned(p->codes, 16)) return MOE_EALIGN;
+  const Layout L = routing_layout(dims);
+  if (routing_bytes < L.total) return MOE_ENOSPACE;
+  const W4A8Layout S = w4a8_layout(dims);
+  if (scratch_bytes < S.total) return MOE_ENOSPACE;
+  char* sb = static_cast<char*>(scratch);
+  moe::W4A8Scratch o;
+  o.x8 = reinterpret_cast<uint8_t*>(sb + S.x8);
+  o.xs = reinterpret_cast<float*>(sb + S.xs);
+  o.h_r = reinterpret_cast<_Float16*>(sb + S.h_r);
+  o.h_s = reinterpret_cast<_Float16*>(sb + S.h_s);
+  o.h8_r = reinterpret_cast<uint8_t*>(sb + S.h8_r);
+  o.hs_r = reinterpret_cast<float*>(sb + S.hs_r);
+  o.h8_s = reinterpret_cast<uint8_t*>(sb + S.h8_s);
+  o.hs_s = reinterpret_cast<float*>(sb + S.hs_s);
+  o.y_pair = reinterpret_cast<_Float16*>(sb + S.y_pair);
+  o.y_s = reinterpret_cast<_Float16*>(sb + S.y_s);
+  const moe::MxWeights mw{w->w13.codes, w->w13.exps, w->w2.codes, w->w2.exps,
+                          w->s13.codes, w->s13.exps, w->s2.codes, w->s2.exps};
+  (void)hipGetLastError();
+  return hip_rc(moe::launch_w4a8_forward(shape_of(dims), x_bf16, routing_ptrs(const_cast<void*>(routing), L), mw, o,
+                                         topk_w, y, flags, static_cast<hipStream_t>(stream)));
 }
 
 const char* moe_strerror(int code) {

@@ -81,6 +81,32 @@ hipError_t launch_combine(const Shape& s, const float* topk_w, const Routing& r,
 hipError_t launch_q4_pack(size_t n_mats, int rows, int K, const uint8_t* qs_in, const uint16_t* sc_in,
                           uint8_t* qs_out, uint16_t* sc_out, hipStream_t st);
 
+// w4a8.hip: MXFP4 weights x FP8 activations on the grouped path
+struct MxWeights {
+  const uint8_t* w13_codes; const uint8_t* w13_exp;   // e2m1 codes / block exponents, 16-row-group layout
+  const uint8_t* w2_codes;  const uint8_t* w2_exp;
+  const uint8_t* s13_codes; const uint8_t* s13_exp;
+  const uint8_t* s2_codes;  const uint8_t* s2_exp;
+};
+struct W4A8Scratch {
+  uint8_t* x8;  float* xs;     // [T][d] e4m3 codes of x, [T] row scales
+  _Float16* h_r; _Float16* h_s;  // [P][I] (sorted rows), [T][Is]
+  uint8_t* h8_r; float* hs_r;  // [P][I], [P]
+  uint8_t* h8_s; float* hs_s;  // [T][Is], [T]
+  _Float16* y_pair; _Float16* y_s;  // [P][d] (sorted rows), [T][d]
+};
+// nblocks Q4 blocks (16 code bytes + one fp16 scale each) -> e2m1 codes (same nibble order) and
+// biased block exponents, block b to block b
+hipError_t launch_q4_to_mx(size_t nblocks, const uint8_t* qs, const uint16_t* sc, uint8_t* codes, uint8_t* exps,
+                           hipStream_t st);
+// rows x K values (bf16 bits, or fp16 when in_f16; K % 4 == 0) -> e4m3 codes and fp32 row scales
+hipError_t launch_rows_fp8(const uint16_t* in, bool in_f16, int rows, int K, uint8_t* out, float* scale,
+                           hipStream_t st);
+// d, I, Is % 128 == 0; routing built for the grouped path
+hipError_t launch_w4a8_forward(const Shape& s, const uint16_t* x, const Routing& r, const MxWeights& w,
+                               const W4A8Scratch& o, const float* topk_w, float* y, uint32_t flags,
+                               hipStream_t st);
+
 // norm.hip
 // x[i] = bf16(h[i]) for n values (n % 8 == 0), round to nearest even
 hipError_t launch_f32_to_bf16(const float* h, uint16_t* x, size_t n, hipStream_t st);

@@ -1,0 +1,527 @@
+// W4A8 variant of the grouped path: MXFP4 expert weights times FP8 activations on the block-scaled
+// MFMA of gfx950.
+//
+// Page thewafflehaus/FFAI pull request 72 ("Nemotron-Nano-30B GB10 prefill quality + speed wins"):
+// W4A8 grouped MoE (fp8 activations times fp4 weights) beside the Q4 W4A16 path; the fp4 MoE weights
+// are the Q4 weights requantised to a block-scaled fp4 grid, and the fp8 activations carry a
+// per-token scale applied to the product.  Here the fp4 grid is e2m1 in blocks of 32 with a shared
+// power-of-two exponent (one byte, bias 127), the block format that
+// v_mfma_scale_f32_16x16x128_f8f6f4 multiplies directly: one such MFMA takes, per lane, one 32-value
+// block of one weight row as its fp4 operand with that block's exponent as its scale, so the main
+// loop has no dequantisation at all.  Activations (x, then h) are e4m3 with one fp32 scale per row
+// (amax / 448), applied to the fp32 accumulators in the epilogues.
+//
+// Operand layout of the MFMA (16 x 16 x 128, checked on the GPU against a host product): the fp4
+// operand lane (n, G) = (l % 16, l / 16) holds row n, K values 32G .. 32G+31 (value j in nibble j,
+// low nibble first), i.e. block G of the 128-value K step, and supplies block G's scale; the fp8
+// operand lane (n, G) holds column n, K values 16G .. 16G+15 in its first four dwords and
+// 64 + 16G .. 64 + 16G + 15 in the last four; the result is the 16 x 16 fp32 tile with lane (n, G)
+// holding rows 4G .. 4G+3 of column n.  With the weights as the fp4 operand the tile comes out
+// transposed, as on the W4A16 path: lane (n, G) holds, for activation row n, four consecutive
+// output columns.
+//
+// Work items, schedule order, XCD remapping and the launch shape are those of the W4A16 grouped
+// GEMM (grouped.hip); the K loop is 128 values per iteration with a two-stage pipeline (activation
+// tile in LDS, weight blocks in registers).  d, I and I_shared must be multiples of 128.
+#include "moe_device.hpp"
+#include "moe_kernels.hpp"
+#include "moe_q4.h"
+
+namespace moe {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+constexpr int kMxBM = kGroupedBM;            // rows per M-tile
+constexpr int kMxBK = 128;                   // K per iteration: one MFMA
+constexpr int kMxWaves = kGroupedWaves;
+constexpr int kMxThreads = 64 * kMxWaves;
+constexpr int kMxRowBytes = kMxBK;           // fp8 activations: 128 B per row and iteration
+constexpr int kMxTileBytes = kMxBM * kMxRowBytes;             // 12 KB
+constexpr int kMxStages = 2;
+constexpr int kMxTileLoads = kMxTileBytes / (kMxThreads * 16);  // 16-byte loads into LDS per lane per tile
+constexpr int kMxRowsPerWave = kMxBM / kMxWaves;
+constexpr int kMxGateUpBandCols = kGateUpBandCols;
+constexpr int kMxDownBandCols = kDownBandCols;
+constexpr int kMxDownOutBytes = kMxBM * kMxDownBandCols * 2;
+constexpr int kMxLdsBytes = kMxStages * kMxTileBytes > kMxDownOutBytes ? kMxStages * kMxTileBytes : kMxDownOutBytes;
+constexpr uint32_t kMxOffsetOOB = 0xFFFFFFF0u;
+static_assert(kMxTileLoads * kMxThreads * 16 == kMxTileBytes, "whole tile per load round");
+static_assert(kMxRowsPerWave == 8 * kMxTileLoads, "each load instruction fills 8 rows");
+
+// LDS tile: row r holds its 128 fp8 values as 8 chunks of 16 B, chunk c in slot c ^ ((r >> 1) & 7):
+// the 16 lanes that read one chunk of 16 consecutive rows (two rows per 256-byte bank line) hit 16
+// different bank groups.
+__device__ __forceinline__ int mx_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+struct MxArgs {
+  const uint8_t* a_r;       // fp8 rows: gate+up -> x8 [T][d] (gathered); down -> h8_r [P][I] (sorted rows)
+  const uint8_t* a_s;       // shared group: gate+up -> x8; down -> h8_s [T][Is]
+  const float* as_r;        // fp32 row scales of a_r rows: gate+up -> xs [T]; down -> hs_r [P]
+  const float* as_s;        // ... of a_s rows: gate+up -> xs [T]; down -> hs_s [T]
+  uint32_t a_r_bytes, a_s_bytes;
+  const uint8_t* wr_codes;  // routed stack (w13 or w2): e2m1 codes in 16-row groups
+  const uint8_t* wr_exp;    //   and the blocks' biased exponents
+  const uint8_t* ws_codes;  // shared expert
+  const uint8_t* ws_exp;
+  _Float16* h_r;            // gate+up outputs, natural column order
+  _Float16* h_s;
+  _Float16* y_r;            // down outputs
+  _Float16* y_s;
+  const int* counts;
+  const int* offsets;
+  const int* sorted_pair;
+  const int* group_order;
+  const int* mt_prefix;
+  int T, d, E, k, I, Is;
+  int nbands;
+  int order;
+};
+
+__device__ __forceinline__ int ufl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <bool GATEUP, int NMT>
+__device__ __forceinline__ void mx_tile(const MxArgs& a, char* As, const __amdgpu_buffer_rsrc_t& rq,
+                                        const __amdgpu_buffer_rsrc_t& rs, const __amdgpu_buffer_rsrc_t& ra,
+                                        const uint32_t (&aoff)[kMxTileLoads], const int (&qns)[4],
+                                        const int (&sns)[4], const bool (&nok)[4], int nit, int c0, int wave,
+                                        int lane, int mlen, int rbase, int m0, int Iw, bool shared) {
+  const int n = lane & 15, G = lane >> 4;
+  auto issue_a = [&](int it, int buf) {
+#pragma unroll
+    for (int i = 0; i < kMxTileLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (lds_void*)(As + buf * kMxTileBytes + (kMxRowsPerWave * wave + 8 * i) * kMxRowBytes), 16, (int)aoff[i],
+          it * kMxBK, 0, 0);
+  };
+  // this lane's weight block of every slice (row n, block 4it + G: 16 B of codes, one exponent byte)
+  auto load_w = [&](int it, u32x4* qd, uint32_t* sd) {
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+      qd[ns] = __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * lane, qns[ns] + it * 1024, 0);
+      sd[ns] = __builtin_amdgcn_raw_buffer_load_b8(rs, lane, sns[ns] + it * 64, 0);
+    }
+  };
+
+  floatx4 acc[NMT][4];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) acc[mt][ns] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // the fp8 operand of slice mt: chunks G and 4 + G of activation row 16 mt + n
+  const int sw = (n >> 1) & 7;
+  const uint32_t off0 = (uint32_t)(n * kMxRowBytes + 16 * (G ^ sw)), off1 = (uint32_t)(n * kMxRowBytes + 16 * ((4 + G) ^ sw));
+  auto aread = [&](const char* At, int mt) __attribute__((always_inline)) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(At + mt * 16 * kMxRowBytes + off0);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(At + mt * 16 * kMxRowBytes + off1);
+    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto compute = [&](int buf, const u32x4* q, const uint32_t* sc) __attribute__((always_inline)) {
+    const char* At = As + buf * kMxTileBytes;
+    v8i w[4];
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) w[ns] = v8i{(int)q[ns][0], (int)q[ns][1], (int)q[ns][2], (int)q[ns][3], 0, 0, 0, 0};
+    v8i x0 = aread(At, 0);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      v8i x1;
+      if (mt + 1 < NMT) x1 = aread(At, mt + 1);
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns)
+        // weights (e2m1, format 4) as the A operand with their block exponent; activations (e4m3,
+        // format 0) as the B operand with exponent 127 (scale 1)
+        acc[mt][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[ns], x0, acc[mt][ns], 4, 0, 0,
+                                                                         (int)sc[ns], 0, 127);
+      if (mt + 1 < NMT) x0 = x1;
+    }
+  };
+
+  // two-stage pipeline: while step `it` is computed, step it+1's tile and weight blocks are in flight
+  u32x4 q[2][4];
+  uint32_t sc[2][4];
+  issue_a(0, 0);
+  load_w(0, q[0], sc[0]);
+  int it0 = 0;
+  for (; it0 + 2 <= nit; it0 += 2) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int it = it0 + st;
+      vm_lgkm_wait<0>();
+      tile_barrier();  // every wavefront's part of tile `it` is in LDS; tile it-1 is no longer read
+      if (it + 1 < nit) {
+        issue_a(it + 1, st ^ 1);
+        load_w(it + 1, q[st ^ 1], sc[st ^ 1]);
+      }
+      compute(st, q[st], sc[st]);
+    }
+  }
+  if (it0 < nit) {
+    vm_lgkm_wait<0>();
+    tile_barrier();
+    compute(0, q[0], sc[0]);
+  }
+
+  // ---- epilogue: lane (n, G) holds, for activation row 16 mt + n, output columns 4G .. 4G+3 of each
+  // 16-column slice; the row's activation scale multiplies them.
+  const float* rsc = shared ? a.as_s : a.as_r;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    const int row = mt * 16 + n;
+    const bool live = row < mlen;
+    const int rr = live ? row : 0;
+    float s;
+    if (GATEUP)
+      s = shared ? rsc[m0 + rr] : rsc[a.sorted_pair[rbase + rr] / a.k];  // the token's x scale
+    else
+      s = rsc[rbase + rr];  // the h row's scale (token row for the shared group)
+    if (GATEUP) {
+      _Float16* out = shared ? a.h_s : a.h_r;
+#pragma unroll
+      for (int xh = 0; xh < 2; ++xh) {
+        // h columns c0 + 16 xh + 4G + i: SiLU(gate) * up, gate rows in slices 0, 1 and up rows in 2, 3
+        float hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gv = s * acc[mt][xh][i], uv = s * acc[mt][2 + xh][i];
+          hv[i] = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;
+        }
+        const uint2 v = {__builtin_bit_cast(uint32_t, half2v{to_f16_sat(hv[0]), to_f16_sat(hv[1])}),
+                         __builtin_bit_cast(uint32_t, half2v{to_f16_sat(hv[2]), to_f16_sat(hv[3])})};
+        const int col = c0 + 16 * xh + 4 * G;
+        if (live && nok[xh]) *reinterpret_cast<uint2*>(out + (size_t)(rbase + row) * Iw + col) = v;
+      }
+    } else {
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) acc[mt][ns] *= s;
+    }
+  }
+  if (!GATEUP) {
+    // the down tile leaves through LDS so that every store writes whole rows (as on the W4A16 path)
+    static_assert(kMxLdsBytes >= kMxDownOutBytes, "the output tile fits in LDS");
+    vm_lgkm_wait<0>();
+    tile_barrier();  // every wavefront is done reading the activation ring
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int row = mt * 16 + n;
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) {
+        const half2v p0 = {to_f16_sat(acc[mt][ns][0]), to_f16_sat(acc[mt][ns][1])};
+        const half2v p1 = {to_f16_sat(acc[mt][ns][2]), to_f16_sat(acc[mt][ns][3])};
+        const int chunk = 8 * wave + 2 * ns + (G >> 1);
+        *reinterpret_cast<uint2*>(As + row * (kMxDownBandCols * 2) + ((chunk ^ (row & 31)) * 16) + 8 * (G & 1)) =
+            uint2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+      }
+    }
+    vm_lgkm_wait<0>();
+    tile_barrier();
+    constexpr int C = kMxDownBandCols / 8, R = kMxThreads / C;
+    static_assert(R * C == kMxThreads && 16 % R == 0, "whole rows per pass");
+    _Float16* out = shared ? a.y_s : a.y_r;
+    const int tid = (int)threadIdx.x, chunk = tid % C;
+    const int col = c0 - 64 * wave + 8 * chunk;
+#pragma unroll
+    for (int i = 0; i < 16 * NMT / R; ++i) {
+      const int row = R * i + tid / C;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(As + row * (kMxDownBandCols * 2) + ((chunk ^ (row & 31)) * 16));
+      if (row < mlen && col < a.d) *reinterpret_cast<u32x4*>(out + (size_t)(rbase + row) * a.d + col) = v;
+    }
+  }
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(kMxThreads, 8 / kMxWaves) void k_grouped_mx(MxArgs a) {
+  constexpr int BANDW = GATEUP ? kMxGateUpBandCols : kMxDownBandCols;
+  __shared__ __attribute__((aligned(1024))) char As[kMxLdsBytes];
+  __shared__ int s_prefix[kMaxExperts + 2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = ufl(tid >> 6);
+  const int ngroups = a.E + 1;
+  for (int i = tid; i <= ngroups; i += kMxThreads) s_prefix[i] = a.mt_prefix[i];
+  __syncthreads();
+  const int nb = a.nbands;
+  const int n_mt = ufl(s_prefix[ngroups]);
+  // work item -> (group rank, band, M-tile), as on the W4A16 path
+  int rank, band, mtile;
+  {
+    const int bid = blockIdx.x;
+    const int order = (a.order == 1 && nb % 8 != 0) ? 2 : a.order;
+    const int nbx = order == 1 ? nb / 8 : nb;
+    int item;
+    if (order == 0) {
+      const int sl = bid >> 3;
+      item = (((sl >> 3) << 3) + (bid & 7)) * 8 + (sl & 7);
+    } else {
+      item = order == 1 ? bid >> 3 : bid;
+    }
+    if (item >= n_mt * nbx) return;
+    int lo = 0, hi = ngroups;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ufl(s_prefix[mid]) * nbx <= item) lo = mid; else hi = mid;
+    }
+    rank = lo;
+    const int p0 = ufl(s_prefix[rank]);
+    const int nmt = ufl(s_prefix[rank + 1]) - p0;
+    const int local = item - p0 * nbx;
+    if (order == 1) {
+      band = 8 * (local / nmt) + (bid & 7);
+      mtile = local % nmt;
+    } else {
+      mtile = local / nbx;
+      band = local % nbx;
+    }
+  }
+  const int g = ufl(a.group_order[rank]);
+  const bool shared = (g == a.E);
+  const int cnt = shared ? a.T : ufl(a.counts[g]);
+  const int Iw = shared ? a.Is : a.I;
+  const int Kdim = GATEUP ? a.d : Iw;
+  const int Ndim = GATEUP ? Iw : a.d;
+  if (band * BANDW >= Ndim) return;
+  const int m0 = mtile * kMxBM;
+  const int mlen = min(kMxBM, cnt - m0);
+  const int gbase = shared ? 0 : ufl(a.offsets[g]);
+  const int rbase = gbase + m0;
+  const uint32_t wrows = GATEUP ? 2u * (uint32_t)Iw : (uint32_t)a.d;
+  const uint32_t qstride = (uint32_t)Kdim / 2, nkb = (uint32_t)Kdim / 32;
+  const uint8_t* Wq = shared ? a.ws_codes : a.wr_codes + (size_t)g * wrows * qstride;
+  const uint8_t* We = shared ? a.ws_exp : a.wr_exp + (size_t)g * wrows * nkb;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Wq, wrows * qstride);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(We, wrows * nkb);
+  const __amdgpu_buffer_rsrc_t ra = shared ? make_rsrc(a.a_s, a.a_s_bytes) : make_rsrc(a.a_r, a.a_r_bytes);
+
+  // activation rows staged by this wavefront: rows kMxRowsPerWave*wave + 8i + lane/8, slot lane%8
+  uint32_t aoff[kMxTileLoads];
+#pragma unroll
+  for (int i = 0; i < kMxTileLoads; ++i) {
+    const int row = kMxRowsPerWave * wave + 8 * i + (lane >> 3);
+    const int rr = row < mlen ? row : 0;
+    uint32_t arow;
+    if (GATEUP)
+      arow = shared ? (uint32_t)(m0 + rr) : (uint32_t)(a.sorted_pair[rbase + rr] / a.k);
+    else
+      arow = (uint32_t)(rbase + rr);
+    // the chunk that belongs in slot lane % 8 of this row; rows past the group read nothing (zeros)
+    const int chunk = mx_slot(row, lane & 7);
+    aoff[i] = row < mlen ? arow * (uint32_t)Kdim + 16u * (uint32_t)chunk : kMxOffsetOOB;
+  }
+  const int nit = Kdim / kMxBK;
+  // this wavefront's weight rows: four 16-row slices (gate+up: gate columns c0.., c0+16.., then the
+  // matching up rows; down: output columns c0 + 16 ns)
+  int rowbase[4];
+  bool nok[4];
+  int c0;
+  if (GATEUP) {
+    c0 = band * BANDW + wave * 32;
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+      const int col = c0 + 16 * (ns & 1);
+      nok[ns] = col < Iw;
+      rowbase[ns] = (ns < 2 ? 0 : Iw) + (nok[ns] ? col : 0);
+    }
+  } else {
+    c0 = band * BANDW + wave * 64;
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+      const int col = c0 + 16 * ns;
+      nok[ns] = col < a.d;
+      rowbase[ns] = nok[ns] ? col : 0;
+    }
+  }
+  // codes [rows/16][K/32][16][16 B] and exponents [rows/16][K/32][16]: slice ns's iteration `it` is
+  // one KiB of codes from ((rowbase/16)*(K/32) + 4 it)*256 and 64 exponent bytes from
+  // ((rowbase/16)*(K/32) + 4 it)*16; lane l takes code bytes 16 l and exponent byte l
+  int qns[4], sns[4];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) {
+    qns[ns] = ufl((int)((uint32_t)(rowbase[ns] / 16) * nkb * 256u));
+    sns[ns] = ufl((int)((uint32_t)(rowbase[ns] / 16) * nkb * 16u));
+  }
+  switch ((mlen + 15) >> 4) {
+    case 1: mx_tile<GATEUP, 1>(a, As, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
+    case 2: mx_tile<GATEUP, 2>(a, As, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
+    case 3: mx_tile<GATEUP, 3>(a, As, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
+    case 4: mx_tile<GATEUP, 4>(a, As, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
+    case 5: mx_tile<GATEUP, 5>(a, As, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
+    default: mx_tile<GATEUP, 6>(a, As, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
+  }
+}
+
+// ---------------------------------------------------------------------------- requantisation
+// One Q4 block (16 code bytes, fp16 scale) -> 16 bytes of e2m1 codes and the biased shared
+// exponent: values w = (q - 8) * d (exact in fp32), E = floor(log2 max|w|) - 2 (E = -127 for an
+// all-zero block), codes = w / 2^E rounded to the nearest e2m1 value, ties to the even mantissa,
+// saturating at +-6.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return c | (__builtin_signbit(v) ? 8u : 0u);
+}
+
+__global__ __launch_bounds__(256) void k_q4_to_mx(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ sc,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ exps,
+                                                  size_t nblocks) {
+  for (size_t b = (size_t)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += (size_t)gridDim.x * 256) {
+    const u32x4 v = ld16(qs + 16 * b);
+    const float d = (float)__builtin_bit_cast(_Float16, sc[b]);
+    int qmax = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int q = (int)((v[w] >> (4 * j)) & 0xF) - 8;
+        qmax = max(qmax, q < 0 ? -q : q);
+      }
+    const float amax = (float)qmax * fabsf(d);
+    int e = -127;
+    if (amax > 0.f) {
+      int ex;
+      (void)frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1
+      e = min(max(ex - 3, -127), 127);
+    }
+    u32x4 out = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t o = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int q = (int)((v[w] >> (4 * j)) & 0xF) - 8;
+        const float val = ldexpf((float)q * d, -e);  // exact: a power-of-two scaling of an exact product
+        o |= e2m1_code(val) << (4 * j);
+      }
+      out[w] = o;
+    }
+    *reinterpret_cast<u32x4*>(codes + 16 * b) = out;
+    exps[b] = (uint8_t)(e + 127);
+  }
+}
+
+// ---------------------------------------------------------------------------- row quantisation
+// e4m3 code of a finite fp32 value: nearest e4m3 value, ties to the even mantissa, saturating at
+// +-448; the sign bit is kept for values that round to zero.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const float a = fabsf(v);
+  uint32_t c;
+  if (!(a < 448.f)) {
+    c = 0x7E;
+  } else if (a < 0.015625f) {                  // subnormal range: steps of 2^-9
+    c = (uint32_t)rintf(a * 512.f);            // 0 .. 8 (8 is the smallest normal, code 0x08)
+  } else {
+    int ex;
+    (void)frexpf(a, &ex);                      // a = m * 2^ex, m in [0.5, 1): exponent e = ex - 1
+    const int e = ex - 1;
+    const uint32_t r = (uint32_t)rintf(ldexpf(a, 3 - e));  // 8 .. 16 (16 carries into the next exponent)
+    c = (uint32_t)(8 * e + 48) + r;
+    c = c > 0x7Eu ? 0x7Eu : c;
+  }
+  return c | (__builtin_signbit(v) ? 0x80u : 0u);
+}
+
+// One workgroup per row: s = amax / 448 (1 for an all-zero row), codes = e4m3(x / s), both divisions
+// correctly rounded in fp32.  IN_F16: the input row is fp16 (h), else bf16 (x).
+template <bool IN_F16>
+__global__ __launch_bounds__(256) void k_rows_fp8(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
+                                                  float* __restrict__ scale, int K) {
+  __shared__ float red[4];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint16_t* src = in + (size_t)r * K;
+  auto val = [&](uint16_t b) { return IN_F16 ? (float)__builtin_bit_cast(_Float16, b) : bf16_bits_to_float(b); };
+  float m = 0.f;
+  for (int i = 4 * tid; i < K; i += 4 * 256) {
+    const uint2 u = *reinterpret_cast<const uint2*>(src + i);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(val((uint16_t)(u.x & 0xFFFF))), fabsf(val((uint16_t)(u.x >> 16)))),
+                       fmaxf(fabsf(val((uint16_t)(u.y & 0xFFFF))), fabsf(val((uint16_t)(u.y >> 16))))));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+  if (tid == 0) scale[r] = s;
+  for (int i = 4 * tid; i < K; i += 4 * 256) {
+    const uint2 u = *reinterpret_cast<const uint2*>(src + i);
+    const uint32_t c0 = e4m3_code(__fdiv_rn(val((uint16_t)(u.x & 0xFFFF)), s));
+    const uint32_t c1 = e4m3_code(__fdiv_rn(val((uint16_t)(u.x >> 16)), s));
+    const uint32_t c2 = e4m3_code(__fdiv_rn(val((uint16_t)(u.y & 0xFFFF)), s));
+    const uint32_t c3 = e4m3_code(__fdiv_rn(val((uint16_t)(u.y >> 16)), s));
+    *reinterpret_cast<uint32_t*>(out + (size_t)r * K + i) = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_q4_to_mx(size_t nblocks, const uint8_t* qs, const uint16_t* sc, uint8_t* codes, uint8_t* exps,
+                           hipStream_t st) {
+  if (nblocks == 0) return hipSuccess;
+  const size_t want = (nblocks + 255) / 256;
+  const unsigned grid = (unsigned)(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(k_q4_to_mx, dim3(grid), dim3(256), 0, st, qs, sc, codes, exps, nblocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_fp8(const uint16_t* in, bool in_f16, int rows, int K, uint8_t* out, float* scale,
+                           hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (in_f16) hipLaunchKernelGGL(k_rows_fp8<true>, dim3(rows), dim3(256), 0, st, in, out, scale, K);
+  else hipLaunchKernelGGL(k_rows_fp8<false>, dim3(rows), dim3(256), 0, st, in, out, scale, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a8_forward(const Shape& s, const uint16_t* x, const Routing& r, const MxWeights& w,
+                               const W4A8Scratch& o, const float* topk_w, float* y, uint32_t flags,
+                               hipStream_t st) {
+  const int P = s.T * s.k;
+  hipError_t e = launch_rows_fp8(x, false, s.T, s.d, o.x8, o.xs, st);
+  if (e != hipSuccess) return e;
+  MxArgs a{};
+  a.counts = r.counts;
+  a.offsets = r.offsets;
+  a.sorted_pair = r.sorted_pair;
+  a.group_order = r.group_order;
+  a.mt_prefix = r.mt_prefix;
+  a.T = s.T; a.d = s.d; a.E = s.E; a.k = s.k; a.I = s.I; a.Is = s.Is;
+  a.order = (flags & MOE_FLAG_NO_BANDING) ? 2 : (flags & MOE_FLAG_BAND_MAJOR) ? 1 : 0;
+  const long mtiles = grouped_max_mtiles(s);
+  // gate+up
+  a.a_r = o.x8; a.a_s = o.x8; a.as_r = o.xs; a.as_s = o.xs;
+  a.a_r_bytes = a.a_s_bytes = (uint32_t)((size_t)s.T * s.d);
+  a.wr_codes = w.w13_codes; a.wr_exp = w.w13_exp; a.ws_codes = w.s13_codes; a.ws_exp = w.s13_exp;
+  a.h_r = o.h_r; a.h_s = o.h_s;
+  const int Imax = s.I > s.Is ? s.I : s.Is;
+  a.nbands = (Imax + kMxGateUpBandCols - 1) / kMxGateUpBandCols;
+  long grid = (mtiles * a.nbands + 63) / 64 * 64;
+  hipLaunchKernelGGL(k_grouped_mx<true>, dim3((unsigned)grid), dim3(kMxThreads), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // h rows to fp8 (routed rows by sorted position, then the shared expert's token rows)
+  if ((e = launch_rows_fp8(reinterpret_cast<const uint16_t*>(o.h_r), true, P, s.I, o.h8_r, o.hs_r, st)) != hipSuccess)
+    return e;
+  if ((e = launch_rows_fp8(reinterpret_cast<const uint16_t*>(o.h_s), true, s.T, s.Is, o.h8_s, o.hs_s, st)) !=
+      hipSuccess)
+    return e;
+  // down
+  a.a_r = o.h8_r; a.a_s = o.h8_s; a.as_r = o.hs_r; a.as_s = o.hs_s;
+  a.a_r_bytes = (uint32_t)((size_t)P * s.I);
+  a.a_s_bytes = (uint32_t)((size_t)s.T * s.Is);
+  a.wr_codes = w.w2_codes; a.wr_exp = w.w2_exp; a.ws_codes = w.s2_codes; a.ws_exp = w.s2_exp;
+  a.y_r = o.y_pair; a.y_s = o.y_s;
+  a.nbands = (s.d + kMxDownBandCols - 1) / kMxDownBandCols;
+  grid = (mtiles * a.nbands + 63) / 64 * 64;
+  hipLaunchKernelGGL(k_grouped_mx<false>, dim3((unsigned)grid), dim3(kMxThreads), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  GroupedOut go{};
+  go.y_pair = o.y_pair;
+  go.y_s = o.y_s;
+  return launch_combine(s, topk_w, r, go, nullptr, y, nullptr, st);
+}
+
+}  // namespace moe

@@ -63,16 +63,18 @@ def check_near_tie_selection(sel: dict, ids_gpu: np.ndarray, i: int, label, toke
         assert abs(key[e] - kth) <= MARGIN, (label, token, e, key[e], kth)
 
 
-def check_parity(inp: dict, ws: Workspace, tokens=None, label: str = "", residual=None) -> dict:
+def check_parity(inp: dict, ws: Workspace, tokens=None, label: str = "", residual=None, forward=None,
+                 y=None) -> dict:
     """Parity rule: selection sets exact where margin > MARGIN; elsewhere the GPU's set may differ from
     the oracle's only among experts whose oracle key is within MARGIN of the k-th key, and the oracle is
     evaluated on the GPU's selection (weights from the oracle's fp64 scores); then max-abs and
-    relative-L2 bounds over all checked tokens, and routing weights within W_ABS."""
+    relative-L2 bounds over all checked tokens, and routing weights within W_ABS.
+    forward: the oracle's layer function (default oracle.forward); y: the output tensor (default ws.y)."""
     dims = inp["dims"]
     tokens = np.arange(dims.T) if tokens is None else np.asarray(tokens)
     ids_gpu = ws.topk_ids.cpu().numpy()[tokens]
     w_gpu = ws.topk_w.cpu().numpy()[tokens]
-    y_gpu = ws.y.cpu().numpy()[tokens].astype(np.float64)
+    y_gpu = (ws.y if y is None else y).cpu().numpy()[tokens].astype(np.float64)
     sel = oracle_selection(inp, tokens)
     close = ~(sel["margin"] > MARGIN)
     for i in range(len(tokens)):
@@ -82,7 +84,10 @@ def check_parity(inp: dict, ws: Workspace, tokens=None, label: str = "", residua
             assert sorted(ids_gpu[i]) == sorted(sel["ids"][i]), (label, int(tokens[i]), ids_gpu[i], sel["ids"][i])
     ov = {int(tokens[i]): ids_gpu[i] for i in np.nonzero(close)[0]}
     # one expert pass of the oracle, on the GPU's selection where the margin is too small to decide
-    ref = oracle.forward(inp, tokens=tokens, ids_override=ov or None, residual=residual)
+    if forward is None:
+        ref = oracle.forward(inp, tokens=tokens, ids_override=ov or None, residual=residual)
+    else:
+        ref = forward(inp, tokens=tokens, ids_override=ov or None)
     # weights: compare by expert id
     for i in range(len(tokens)):
         ref_w = dict(zip(ref["ids"][i].tolist(), ref["w"][i].tolist()))

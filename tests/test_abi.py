@@ -377,3 +377,87 @@ def test_layer_forward_noalloc_size_limit():
     big = d(T=480, d=4096, E=256, k=10, I=1024, I_shared=1024)
     assert need(big) <= abi.MOE_NOALLOC_MAX_BYTES < need(d(T=520, d=4096, E=256, k=10, I=1024, I_shared=1024))
     assert noalloc(dims=d(T=520, d=4096, E=256, k=10, I=1024, I_shared=1024)) == abi.MOE_ENOSPACE
+
+
+# ----------------------------------------------------------------------------- W4A8 variant
+
+MX = {k: FAKE for k in ("w13_codes", "w13_exps", "w2_codes", "w2_exps", "s13_codes", "s13_exps", "s2_codes",
+                        "s2_exps")}
+
+
+def w4a8(dims=TINY, flags=abi.MOE_FLAG_FORCE_GROUPED, weights=None, **kw):
+    args = dict(x=FAKE, topk_ids=FAKE, topk_w=FAKE, routing=FAKE, y=FAKE, scratch=FAKE, routing_bytes=R,
+                scratch_bytes=1 << 30)
+    args.update(kw)
+    return moe.moe_w4a8_forward(dims, weights=dict(MX, **(weights or {})), **args, flags=flags, stream=0,
+                                check=False)
+
+
+@pytest.mark.parametrize("dims", [TINY, BIG, synth.CONFIGS["long_prefill"].dims])
+def test_w4a8_scratch_closed_form(dims):
+    T, k, dd, I, Is = dims.T, dims.k, dims.d, dims.I, dims.I_shared
+    P = T * k
+    want = (align(T * dd) + align(T * 4) + align(P * I * 2) + align(T * Is * 2) + align(P * I) + align(P * 4)
+            + align(T * Is) + align(T * 4) + align(P * dd * 2) + align(T * dd * 2))
+    assert moe.moe_w4a8_scratch_bytes(dims, abi.MOE_FLAG_FORCE_GROUPED) == want
+    # only the grouped path has a W4A8 form
+    assert moe.moe_w4a8_scratch_bytes(dims, abi.MOE_FLAG_FORCE_GEMV) == 0
+    assert moe.moe_w4a8_scratch_bytes(d(d=96, I=128, I_shared=128), abi.MOE_FLAG_FORCE_GROUPED) == 0
+
+
+def test_w4a8_forward_validation_before_any_hip_call():
+    for name in ("x", "topk_ids", "topk_w", "y", "scratch", "routing"):
+        assert w4a8(**{name: 0}) == abi.MOE_EINVAL, name
+    for name in MX:
+        assert w4a8(weights={name: 0}) == abi.MOE_EINVAL, name
+    for name in ("w13_codes", "w2_codes", "s13_codes", "s2_codes"):
+        assert w4a8(weights={name: FAKE + 8}, scratch_bytes=0) == abi.MOE_EALIGN, name
+    assert w4a8(x=FAKE + 2, scratch_bytes=0) == abi.MOE_EALIGN
+    assert w4a8(routing=FAKE + 8, scratch_bytes=0) == abi.MOE_EALIGN
+    # block exponents are read one byte at a time: no alignment, so the call gets to the size checks
+    assert w4a8(weights={"w13_exps": FAKE + 1}, scratch_bytes=0) == abi.MOE_ENOSPACE
+    assert w4a8(scratch_bytes=moe.moe_w4a8_scratch_bytes(TINY, abi.MOE_FLAG_FORCE_GROUPED) - 1) == abi.MOE_ENOSPACE
+    assert w4a8(routing_bytes=100) == abi.MOE_ENOSPACE
+    assert w4a8(flags=0) == abi.MOE_EUNSUPPORTED            # T = 8 selects the small-T path
+    assert w4a8(flags=abi.MOE_FLAG_FORCE_GEMV) == abi.MOE_EUNSUPPORTED
+    for kw in (dict(d=96), dict(I=160), dict(I_shared=32)):
+        assert w4a8(dims=d(**kw)) == abi.MOE_EUNSUPPORTED, kw
+    assert w4a8(dims=d(k=0)) == abi.MOE_EINVAL
+
+
+def q4mx(**kw):
+    args = dict(n_mats=2, rows=32, K=64, qs=FAKE, scales=FAKE + (1 << 16), codes_out=FAKE + (2 << 16),
+                exps_out=FAKE + (3 << 16))
+    args.update(kw)
+    return moe.moe_q4_to_mxfp4(args["n_mats"], args["rows"], args["K"], args["qs"], args["scales"],
+                               args["codes_out"], args["exps_out"], stream=0, check=False)
+
+
+def test_q4_to_mxfp4_validation_before_any_hip_call():
+    for name in ("n_mats", "rows", "K"):
+        assert q4mx(**{name: 0}) == abi.MOE_EINVAL, name
+    for name in ("qs", "scales", "codes_out", "exps_out"):
+        assert q4mx(**{name: 0}) == abi.MOE_EINVAL, name
+    assert q4mx(rows=24) == abi.MOE_EUNSUPPORTED
+    assert q4mx(K=48) == abi.MOE_EUNSUPPORTED
+    assert q4mx(qs=FAKE + 8) == abi.MOE_EALIGN
+    assert q4mx(codes_out=FAKE + (2 << 16) + 8) == abi.MOE_EALIGN
+    assert q4mx(scales=FAKE + (1 << 16) + 1) == abi.MOE_EALIGN
+    # overlaps (codes 2 * 32 * 2 * 16 = 2048 bytes, scales 256, exps 128)
+    assert q4mx(codes_out=FAKE) == abi.MOE_EINVAL
+    assert q4mx(exps_out=FAKE + 100) == abi.MOE_EINVAL
+    assert q4mx(exps_out=FAKE + (1 << 16) + 200) == abi.MOE_EINVAL
+    assert q4mx(exps_out=FAKE + (2 << 16) + 1000) == abi.MOE_EINVAL
+
+
+def test_rows_to_fp8_validation_before_any_hip_call():
+    def call(rows=4, K=64, x=FAKE, codes=FAKE + (1 << 16), scales=FAKE + (2 << 16)):
+        return moe.moe_rows_to_fp8(rows, K, x, codes, scales, stream=0, check=False)
+    assert call(rows=0) == abi.MOE_EINVAL
+    assert call(K=0) == abi.MOE_EINVAL
+    assert call(x=0) == abi.MOE_EINVAL and call(codes=0) == abi.MOE_EINVAL and call(scales=0) == abi.MOE_EINVAL
+    assert call(K=66) == abi.MOE_EUNSUPPORTED
+    assert call(rows=1 << 20, K=4096) == abi.MOE_EUNSUPPORTED
+    assert call(x=FAKE + 8) == abi.MOE_EALIGN
+    assert call(codes=FAKE + (1 << 16) + 4) == abi.MOE_EALIGN
+    assert call(scales=FAKE + (2 << 16) + 2) == abi.MOE_EALIGN

@@ -1,0 +1,249 @@
+"""GPU: the W4A8 variant (MXFP4 expert weights x FP8 activations) through the C ABI, against the W4A8
+oracle: the weight requantisation and the activation quantisation bit for bit, the layer under the
+parity rule (selection exact outside the margin, max-abs and relative-L2 bounds)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.moe_w4a8 as w4
+import synth
+from sparse_moe_expert_sigmoid_amd import abi
+from sparse_moe_expert_sigmoid_amd.layer import DeviceWeights, Workspace, layer_call, to_device
+from gpu_util import check_parity, say
+from test_gpu_pack import ref_pack_codes, ref_pack_scales
+
+pytestmark = pytest.mark.gpu
+
+GROUPED = abi.MOE_FLAG_FORCE_GROUPED
+
+
+def mx_upload(w: DeviceWeights) -> dict:
+    """MXFP4 copies of the packed Q4 stacks, made on the device by moe_q4_to_mxfp4."""
+    dims = w.dims
+    shapes = {"w13": (dims.E, 2 * dims.I, dims.d), "w2": (dims.E, dims.d, dims.I),
+              "s13": (1, 2 * dims.I_shared, dims.d), "s2": (1, dims.d, dims.I_shared)}
+    mx = {}
+    for name, (n, rows, K) in shapes.items():
+        codes = torch.empty_like(w[name + "_qs"])
+        exps = torch.empty(n * rows * (K // 32), dtype=torch.uint8, device=codes.device)
+        abi.moe_q4_to_mxfp4(n, rows, K, w[name + "_qs"], w[name + "_sc"], codes, exps)
+        mx[name + "_codes"], mx[name + "_exps"] = codes, exps
+    return mx
+
+
+def w4a8_call(dims, x, ws: Workspace, mx: dict, flags: int) -> torch.Tensor:
+    """route + build (the W4A16 calls) then the W4A8 forward into a fresh output."""
+    y = torch.full((dims.T, dims.d), float("nan"), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(abi.moe_w4a8_scratch_bytes(dims, flags), dtype=torch.uint8, device="cuda")
+    abi.moe_w4a8_forward(dims, x, ws.topk_ids, ws.topk_w, ws.routing, mx, y, scratch, flags=flags)
+    return y
+
+
+# ----------------------------------------------------------------------------- requantisation, bit for bit
+
+def special_q4(rng, rows, K):
+    """Random Q4 codes and scales with hand-placed edge blocks: all-zero values, zero and negative
+    scales, subnormal and largest fp16 scales, a single nonzero element, every code equal."""
+    qs = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    sc = np.float16(rng.uniform(0.005, 0.02, (rows, K // 32))).view(np.uint16)
+    f16 = lambda v: np.float16(v).view(np.uint16)
+    qs[0, 0:16] = 0x88                                   # all values zero
+    qs[1, 0:16] = rng.integers(0, 256, 16); sc[1, 0] = f16(0.0)
+    sc[2, 0] = f16(-0.0113)
+    sc[3, 0] = f16(2.0 ** -24)                           # smallest subnormal
+    sc[4, 0] = f16(65504.0)
+    sc[5, 0] = f16(6.1e-5)                               # around the subnormal edge
+    qs[6, 0:16] = 0x88; qs[6, 3] = 0x8F                  # one nonzero element (+7)
+    qs[7, 0:16] = 0x00                                   # every value -8
+    qs[8, 0:16] = 0xFF                                   # every value +7
+    sc[9, :] = f16(-0.25)
+    return qs, sc
+
+
+@pytest.mark.parametrize("n_mats,rows,K", [(1, 16, 32), (2, 48, 256), (3, 64, 4096), (1, 2048, 1024)])
+def test_q4_to_mxfp4_bit_exact(n_mats, rows, K):
+    say(f"[case] q4_to_mxfp4 n_mats={n_mats} rows={rows} K={K}")
+    rng = np.random.default_rng(rows + K + n_mats)
+    qs = np.empty((n_mats, rows, K // 2), np.uint8)
+    sc = np.empty((n_mats, rows, K // 32), np.uint16)
+    for m in range(n_mats):
+        qs[m], sc[m] = special_q4(rng, rows, K)
+    ref = [w4.mx_requant(qs[m], sc[m]) for m in range(n_mats)]
+    ref_c = np.stack([r[0] for r in ref])
+    ref_e = np.stack([r[1] for r in ref])
+    # row-major in, row-major out (block b to block b)
+    qi, si = to_device(qs, "cuda"), to_device(sc, "cuda")
+    co = torch.full_like(qi, 0x5A)
+    eo = torch.full((n_mats * rows * (K // 32),), 0x5A, dtype=torch.uint8, device="cuda")
+    abi.moe_q4_to_mxfp4(n_mats, rows, K, qi, si, co, eo)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(co.cpu().numpy().reshape(-1), ref_c.reshape(-1))
+    np.testing.assert_array_equal(eo.cpu().numpy().reshape(-1), ref_e.reshape(-1))
+    # the packed 16-row groups in, the same layout out
+    qp, sp = torch.empty_like(qi), torch.empty_like(si)
+    abi.moe_q4_pack(n_mats, rows, K, qi, si, qp, sp)
+    abi.moe_q4_to_mxfp4(n_mats, rows, K, qp, sp, co, eo)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(co.cpu().numpy().reshape(-1), ref_pack_codes(ref_c).reshape(-1))
+    np.testing.assert_array_equal(eo.cpu().numpy().reshape(-1), ref_pack_scales(ref_e).reshape(-1))
+
+
+def special_rows(rng, rows, K, fp16: bool):
+    X = rng.standard_normal((rows, K)).astype(np.float32)
+    X[1] = 0.0                                           # all-zero row: scale 1, zero codes
+    X[2] *= 8.0                                          # outlier row
+    X[3] = 0.0; X[3, K - 1] = -3.0                       # one nonzero element
+    X[4] = np.ldexp(1.0, rng.integers(-30, 0, K)).astype(np.float32) * rng.choice([-1, 1], K)  # wide range:
+    X[4, 0] = 1.0                                        # most elements land in the e4m3 subnormals or zero
+    X[5, ::2] = -0.0
+    if fp16:
+        X[6, 0] = 65504.0; X[6, 1] = -65504.0
+        bits = np.float16(X).view(np.uint16)
+        vals = bits.view(np.float16).astype(np.float32)
+    else:
+        bits = synth.bf16_bits_from_f32(X)
+        vals = (bits.astype(np.uint32) << 16).view(np.float32)
+    return bits, vals
+
+
+@pytest.mark.parametrize("fp16", [False, True], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("rows,K", [(8, 4), (8, 256), (37, 4096), (300, 1024)])
+def test_rows_to_fp8_bit_exact(rows, K, fp16):
+    say(f"[case] rows_to_fp8 rows={rows} K={K} fp16={fp16}")
+    rng = np.random.default_rng(rows * 7 + K)
+    bits, vals = special_rows(rng, rows, K, fp16)
+    codes_ref, s_ref = w4.quant_rows_fp8(vals)
+    xi = to_device(bits, "cuda")
+    codes = torch.full((rows, K), 0x5A, dtype=torch.uint8, device="cuda")
+    s = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+    abi.moe_rows_to_fp8(rows, K, xi, codes, s, in_is_fp16=fp16)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(s.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(codes.cpu().numpy(), codes_ref)
+
+
+# ----------------------------------------------------------------------------- the layer
+
+SMALL = {
+    "tiny": (synth.CONFIGS["tiny"].dims, "uniform"),
+    "ragged": (synth.Dims(T=37, d=384, E=20, k=3, I=256, I_shared=128), "uniform"),
+    "multi_tile": (synth.Dims(T=300, d=512, E=4, k=2, I=256, I_shared=384), "uniform"),
+    "single_expert": (synth.Dims(T=5, d=128, E=1, k=1, I=128, I_shared=128), "uniform"),
+    "one_token": (synth.Dims(T=1, d=256, E=16, k=4, I=128, I_shared=128), "uniform"),
+    "skewed": (synth.Dims(T=200, d=256, E=32, k=4, I=128, I_shared=256), "zipf"),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_w4a8_small_shapes(name):
+    dims, bias = SMALL[name]
+    say(f"[case] w4a8 small {name} dims={dims}")
+    inp = synth.make_inputs(dims, seed=300 + len(name), bias=bias)
+    w = DeviceWeights.upload(inp)
+    x = to_device(inp["x"], "cuda")
+    ws = Workspace(dims, GROUPED)
+    layer_call(x, w, ws)
+    mx = mx_upload(w)
+    y = w4a8_call(dims, x, ws, mx, GROUPED)
+    torch.cuda.synchronize()
+    check_parity(inp, ws, label=f"w4a8/{name}", forward=w4.forward_w4a8, y=y)
+
+
+def test_w4a8_schedule_orders_give_the_same_bits():
+    dims, bias = SMALL["skewed"]
+    inp = synth.make_inputs(dims, seed=9, bias=bias)
+    w = DeviceWeights.upload(inp)
+    x = to_device(inp["x"], "cuda")
+    mx = mx_upload(w)
+    outs = []
+    for flags in (GROUPED, GROUPED | abi.MOE_FLAG_NO_BANDING, GROUPED | abi.MOE_FLAG_BAND_MAJOR,
+                  GROUPED | abi.MOE_FLAG_ID_ORDER):
+        ws = Workspace(dims, flags)
+        layer_call(x, w, ws)
+        outs.append(w4a8_call(dims, x, ws, mx, flags))
+        outs.append(w4a8_call(dims, x, ws, mx, flags))   # and run to run
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_w4a8_doubling_down_scales_doubles_output():
+    """Doubling every Q4 down scale raises each block exponent by one: y doubles exactly."""
+    dims, bias = SMALL["ragged"]
+    inp = synth.make_inputs(dims, seed=21, bias=bias)
+    inp2 = dict(inp)
+    for name in ("w2_sc", "s2_sc"):
+        inp2[name] = (inp[name].view(np.float16) * np.float16(2)).view(np.uint16)
+    x = to_device(inp["x"], "cuda")
+    ys = []
+    for i in (inp, inp2):
+        w = DeviceWeights.upload(i)
+        ws = Workspace(dims, GROUPED)
+        layer_call(x, w, ws)
+        ys.append(w4a8_call(dims, x, ws, mx_upload(w), GROUPED))
+    torch.cuda.synchronize()
+    # exact, except where a per-pair down output (stored in fp16) falls in the fp16 subnormal range, whose
+    # absolute spacing 2^-24 does not scale: at most k + 1 such roundings per output element
+    diff = (ys[1] - 2 * ys[0]).abs()
+    assert float(diff.max()) <= (dims.k + 1) * 2.0 ** -24 * 2, float(diff.max())
+    assert float((diff == 0).float().mean()) > 0.99
+
+
+_MX_CACHE: dict = {}
+
+
+def oracle_mx(inp: dict, key: str, experts) -> dict:
+    """The oracle's requantised matrices for the given experts (and the shared expert), memoised per input
+    set so that a full-size check requantises each matrix once."""
+    out = {}
+    for name in ("w13", "w2"):
+        for e in experts:
+            k = (key, name, int(e))
+            if k not in _MX_CACHE:
+                _MX_CACHE[k] = w4.mx_requant(inp[name + "_qs"][e], inp[name + "_sc"][e])
+            out[(name, int(e))] = _MX_CACHE[k]
+    for name in ("s13", "s2"):
+        k = (key, name, None)
+        if k not in _MX_CACHE:
+            _MX_CACHE[k] = w4.mx_requant(inp[name + "_qs"], inp[name + "_sc"])
+        out[(name, None)] = _MX_CACHE[k]
+    return out
+
+
+def few_expert_tokens(ids: np.ndarray, n: int) -> list:
+    """n tokens chosen greedily so that together they use as few distinct experts as possible."""
+    chosen, used = [], set()
+    for _ in range(n):
+        best = min((len(used | set(ids[t].tolist())), t) for t in range(len(ids)) if t not in chosen)
+        chosen.append(best[1])
+        used |= set(ids[best[1]].tolist())
+    return sorted(chosen)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,ntok", [("decode", 1), ("prefill", 3), ("long_prefill", 3)])
+def test_w4a8_full_size_sampled_tokens(name, ntok):
+    """The full-size workloads (T = 1 on the grouped path), the grouped GEMMs in their default launch
+    configuration; the oracle evaluates a few tokens chosen to share experts, with its own requantised
+    weights."""
+    cfg = synth.CONFIGS[name]
+    dims = cfg.dims
+    say(f"[case] w4a8 full {name} dims={dims}")
+    inp = synth.make_inputs(cfg)
+    w = DeviceWeights.upload(inp)
+    x = to_device(inp["x"], "cuda")
+    ws = Workspace(dims, GROUPED)
+    layer_call(x, w, ws)
+    y = w4a8_call(dims, x, ws, mx_upload(w), GROUPED)
+    y2 = w4a8_call(dims, x, ws, mx_upload(w), GROUPED)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    assert torch.isfinite(y).all()
+    ids = ws.topk_ids.cpu().numpy()
+    tokens = few_expert_tokens(ids, ntok)
+    experts = np.unique(ids[tokens])
+    say(f"[sample] {name}: tokens {tokens}, {len(experts)} experts")
+    mx = oracle_mx(inp, name, experts)
+    fwd = lambda i, tokens, ids_override: w4.forward_w4a8(i, tokens=tokens, ids_override=ids_override, mx=mx)
+    check_parity(inp, ws, tokens=np.array(tokens), label=f"w4a8/{name}", forward=fwd, y=y)
