@@ -15,7 +15,10 @@ bracketed by device synchronisation.
 
 The primary workload (default: single-token decode, d=4096, E=256, top-10,
 I=1024, shared I=1024) gives `value`; the 2048-token prefill chunk is
-measured the same way and reported under `secondary`.  Per-kernel average
+measured the same way and reported under `secondary`, and again as the W4A8
+variant (moe_route + moe_build_descriptors + moe_w4a8_forward on MXFP4 copies
+of the weights, fp8 activations) under `secondary_w4a8`, whose roofline is
+priced against the fp8 MFMA peak.  Per-kernel average
 durations come from graphs that replay only that kernel's nodes, extracted
 from the captured layer graph, timed with HIP events on the same stream
 (every launch of the layer is idempotent, so replaying one alone is valid).
@@ -50,6 +53,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/sec at T=1 and T=2048; % HBM roofline / % bf16 MFMA peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+MFMA_F8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA (fp8 x fp4 runs at the fp8 rate), TFLOP/s
 COPIES = {"decode": 8, "batched_decode": 8, "prefill": 2, "long_prefill": 2}
 
 
@@ -135,7 +139,9 @@ def short_name(mangled: str) -> str:
                       ("k_build_count", "build_count"), ("k_build_scatter", "build_scatter"),
                       ("k_gemv_gateup", "gemv_gateup"), ("k_gemv_down_combine", "gemv_down_combine"),
                       ("k_x_to_f16", "x_to_f16"), ("k_groupedILb1", "grouped_gateup"),
-                      ("k_groupedILb0", "grouped_down"), ("k_combine", "combine")):
+                      ("k_groupedILb0", "grouped_down"), ("k_combine", "combine"),
+                      ("k_grouped_mxILb1", "grouped_mx_gateup"), ("k_grouped_mxILb0", "grouped_mx_down"),
+                      ("k_rows_fp8ILb0", "rows_fp8_x"), ("k_rows_fp8ILb1", "rows_fp8_h")):
         if key in mangled:
             return nice
     return mangled
@@ -225,13 +231,27 @@ def recorded_traffic(profile: str, sources) -> int | None:
     return int(fields["traffic_bytes_per_launch"])
 
 
+def mx_weights(abi, torch, dims, w):
+    """MXFP4 copies (moe_q4_to_mxfp4) of one layer copy's packed Q4 stacks."""
+    shapes = {"w13": (dims.E, 2 * dims.I, dims.d), "w2": (dims.E, dims.d, dims.I),
+              "s13": (1, 2 * dims.I_shared, dims.d), "s2": (1, dims.d, dims.I_shared)}
+    mx = {}
+    for name, (n, rows, K) in shapes.items():
+        codes = torch.empty_like(w[name + "_qs"])
+        exps = torch.empty(n * rows * (K // 32), dtype=torch.uint8, device=codes.device)
+        abi.moe_q4_to_mxfp4(n, rows, K, w[name + "_qs"], w[name + "_sc"], codes, exps)
+        mx[name + "_codes"], mx[name + "_exps"] = codes, exps
+    return mx
+
+
 def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_sample=False, residual=False,
-                 separate=False):
+                 separate=False, variant="w4a16"):
     cfg = synth.CONFIGS[name]
     dims = cfg.dims
     device = "cuda"
     L = COPIES[name]
-    # one layer call: moe_layer_forward, or with `separate` moe_route + moe_build_descriptors + moe_q4_forward
+    # one layer call: moe_layer_forward, or with `separate` moe_route + moe_build_descriptors + moe_q4_forward;
+    # the W4A8 variant: moe_route + moe_build_descriptors + moe_w4a8_forward on MXFP4 copies of the weights
     call = layer.layer_call if separate else layer.layer_call_fused
     inp0 = synth.make_inputs(cfg)
     weights = [layer.DeviceWeights.upload(inp0)]
@@ -244,6 +264,18 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
         weights.append(dw)
         xs.append(x)
     spaces = [layer.Workspace(dims, 0) for _ in range(L)]
+    if variant == "w4a8":
+        if abi.moe_path(dims, 0) != 1 or residual:
+            raise ValueError("the W4A8 variant runs on the grouped path, without a residual")
+        mxs = {id(w): mx_weights(abi, torch, dims, w) for w in weights}
+        w4a8_scratch = {id(ws): torch.empty(abi.moe_w4a8_scratch_bytes(dims, 0), dtype=torch.uint8, device=device)
+                        for ws in spaces}
+
+        def call(x, w, ws, stream=None, residual=None):
+            abi.moe_route(dims, x, w["w_router"], w["bias"], ws.topk_ids, ws.topk_w, ws.routing, stream=stream)
+            abi.moe_build_descriptors(dims, ws.topk_ids, ws.routing, stream=stream)
+            abi.moe_w4a8_forward(dims, x, ws.topk_ids, ws.topk_w, ws.routing, mxs[id(w)], ws.y,
+                                 w4a8_scratch[id(ws)], stream=stream)
     # with `residual`, every step goes through moe_q4_forward_residual with its own fp32 [T][d] residual
     res = [torch.randn(dims.T, dims.d, device=device) if residual else None for _ in range(L)]
     stream = torch.cuda.Stream()
@@ -323,7 +355,7 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
     path = abi.moe_path(dims, 0)
     tokens_per_s = T / (ms_per_step / 1000.0)
     res = {
-        "workload": name, "residual": bool(residual),
+        "workload": name, "variant": variant, "residual": bool(residual),
         "dims": dict(T=T, d=d, E=E, k=dims.k, I=dims.I, I_shared=dims.I_shared),
         "path": "gemv" if path == 0 else "grouped", "layer_copies": L, "steps": steps, "warmup": warmup,
         "ms_per_step": ms_per_step, "tokens_per_s": tokens_per_s, "distinct_experts": distinct,
@@ -343,6 +375,15 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
                            if name == "decode" else None,
                            "algorithmic_bytes_per_launch": per_launch,
                            "avg_launch_us": round(kernel_us[kname], 3)}
+    elif variant == "w4a8":
+        kname = "grouped_mx_gateup"
+        per_launch = 2 * (P * 2 * dims.I + T * 2 * dims.I_shared) * d
+        achieved = per_launch / (kernel_us[kname] * 1e-6) / 1e12
+        res["roofline"] = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),
+                           "peak": MFMA_F8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(achieved / MFMA_F8_PEAK_TFLOPS, 4), "traffic": None,
+                           "algorithmic_flop_per_launch": per_launch, "avg_launch_us": round(kernel_us[kname], 3)}
+        res["layer_mfma_frac_fp8"] = layer_flop / (ms_per_step / 1000.0) / (MFMA_F8_PEAK_TFLOPS * 1e12)
     else:
         kname = "grouped_gateup"
         per_launch = 2 * (P * 2 * dims.I + T * 2 * dims.I_shared) * d
@@ -430,16 +471,27 @@ def cpu_baseline(inp, budget_s=15.0):
                       f"{el:.1f} s wall on the host", **host_info()}
 
 
-def traffic_run(name, torch, layer, synth, flags=0):
+def traffic_run(name, torch, layer, synth, flags=0, variant="w4a16"):
     """Three layer calls and two 256 MiB copies, nothing else: the run that rocprofv3 --pmc FETCH_SIZE /
     WRITE_SIZE records for the traffic summaries under profiles/ (the copy calibrates the counters).
-    `flags` are the layer's MOE_FLAG_* bits (e.g. the grouped GEMMs' work order)."""
+    `flags` are the layer's MOE_FLAG_* bits (e.g. the grouped GEMMs' work order); `variant` w4a8 runs
+    moe_route + moe_build_descriptors + moe_w4a8_forward on MXFP4 copies of the weights instead."""
+    from sparse_moe_expert_sigmoid_amd import abi
     inp = synth.make_inputs(synth.CONFIGS[name])
+    dims = inp["dims"]
     w = layer.DeviceWeights.upload(inp)
     x = layer.to_device(inp["x"], "cuda")
-    ws = layer.Workspace(inp["dims"], flags)
+    ws = layer.Workspace(dims, flags)
+    if variant == "w4a8":
+        mx = mx_weights(abi, torch, dims, w)
+        scratch = torch.empty(abi.moe_w4a8_scratch_bytes(dims, flags), dtype=torch.uint8, device="cuda")
     for _ in range(3):
-        layer.layer_call_fused(x, w, ws)
+        if variant == "w4a8":
+            abi.moe_route(dims, x, w["w_router"], w["bias"], ws.topk_ids, ws.topk_w, ws.routing, flags=flags)
+            abi.moe_build_descriptors(dims, ws.topk_ids, ws.routing, flags=flags)
+            abi.moe_w4a8_forward(dims, x, ws.topk_ids, ws.topk_w, ws.routing, mx, ws.y, scratch, flags=flags)
+        else:
+            layer.layer_call_fused(x, w, ws)
     a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     a.fill_(1)
     b = torch.empty_like(a)
@@ -447,8 +499,8 @@ def traffic_run(name, torch, layer, synth, flags=0):
     for _ in range(2):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps({"traffic_run": name, "flags": flags, "layer_calls": 3, "copy_bytes": 256 << 20, "copies": 2}),
-          flush=True)
+    print(json.dumps({"traffic_run": name, "variant": variant, "flags": flags, "layer_calls": 3,
+                      "copy_bytes": 256 << 20, "copies": 2}), flush=True)
 
 
 def run_decode_ctx(passes, torch, abi, layer, synth, n_layers=8, norm=False):
@@ -508,6 +560,8 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "batched_decode", "prefill", "long_prefill"])
     ap.add_argument("--secondary", default="prefill", help="second workload reported alongside ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-w4a8", action="store_true",
+                    help="skip the W4A8 variant (MXFP4 weights x FP8 activations) of the secondary workload")
     ap.add_argument("--separate-calls", action="store_true",
                     help="time each layer as moe_route + moe_build_descriptors + moe_q4_forward instead of "
                          "moe_layer_forward (the same results)")
@@ -521,6 +575,8 @@ def main():
     ap.add_argument("--flags", type=int, default=0,
                     help="MOE_FLAG_* bits for --traffic-run (4 = expert-id group order, 8 = items in launch "
                          "order, 16 = band-major items)")
+    ap.add_argument("--variant", default="w4a16", choices=["w4a16", "w4a8"],
+                    help="layer variant of --traffic-run")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this layer is built and measured on a single MI355X; "
@@ -535,7 +591,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(3)
     if args.traffic_run:
-        traffic_run(args.traffic_run, torch, layer, synth, flags=args.flags)
+        traffic_run(args.traffic_run, torch, layer, synth, flags=args.flags, variant=args.variant)
         return
     hip = Hip()
     if args.all:
@@ -562,6 +618,11 @@ def main():
         n = max(20, args.steps // 40)
         sec = run_workload(args.secondary, n, max(4, n // 10), torch, hip, abi, layer, synth, residual=args.residual,
                            separate=args.separate_calls)
+    w4a8 = None
+    if sec is not None and not args.no_w4a8 and abi.moe_path(synth.CONFIGS[args.secondary].dims, 0) == 1:
+        n = max(20, args.steps // 40)
+        w4a8 = run_workload(args.secondary, n, max(4, n // 10), torch, hip, abi, layer, synth, variant="w4a8")
+        w4a8.pop("_inp0", None)
     ctx = run_decode_ctx(max(50, args.steps // 4), torch, abi, layer, synth) if args.workload == "decode" else None
     ctxn = (run_decode_ctx(max(50, args.steps // 4), torch, abi, layer, synth, norm=True)
             if args.workload == "decode" else None)
@@ -595,11 +656,14 @@ def main():
         "layer": {k: prim[k] for k in ("layer_hbm_frac", "layer_mfma_frac", "layer_algorithmic_bytes",
                                        "layer_algorithmic_flop", "distinct_experts", "kernel_avg_us")},
         "kernel_sources": source_hash("sparse_moe_expert_sigmoid_amd/csrc/gemv.hip",
-                                      "sparse_moe_expert_sigmoid_amd/csrc/grouped.hip"),
+                                      "sparse_moe_expert_sigmoid_amd/csrc/grouped.hip",
+                                      "sparse_moe_expert_sigmoid_amd/csrc/w4a8.hip"),
     }
     if sec is not None:
         sec.pop("_inp0", None)
         out["secondary"] = sec
+    if w4a8 is not None:
+        out["secondary_w4a8"] = w4a8
     if ctx is not None:
         out["decode_ctx"] = ctx
         out["decode_ctx_norm"] = ctxn

@@ -21,8 +21,10 @@
 // output columns.
 //
 // Work items, schedule order, XCD remapping and the launch shape are those of the W4A16 grouped
-// GEMM (grouped.hip); the K loop is 128 values per iteration with a two-stage pipeline (activation
-// tile in LDS, weight blocks in registers).  d, I and I_shared must be multiples of 128.
+// GEMM (grouped.hip); the K loop is 128 values per iteration with the next step's operands in
+// flight (activation tile in LDS, weight blocks in registers).  d, I and I_shared must be multiples of 128.
+#include <type_traits>
+
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 #include "moe_q4.h"
@@ -39,13 +41,11 @@ constexpr int kMxWaves = kGroupedWaves;
 constexpr int kMxThreads = 64 * kMxWaves;
 constexpr int kMxRowBytes = kMxBK;           // fp8 activations: 128 B per row and iteration
 constexpr int kMxTileBytes = kMxBM * kMxRowBytes;             // 12 KB
-constexpr int kMxStages = 2;
 constexpr int kMxTileLoads = kMxTileBytes / (kMxThreads * 16);  // 16-byte loads into LDS per lane per tile
 constexpr int kMxRowsPerWave = kMxBM / kMxWaves;
 constexpr int kMxGateUpBandCols = kGateUpBandCols;
 constexpr int kMxDownBandCols = kDownBandCols;
 constexpr int kMxDownOutBytes = kMxBM * kMxDownBandCols * 2;
-constexpr int kMxLdsBytes = kMxStages * kMxTileBytes > kMxDownOutBytes ? kMxStages * kMxTileBytes : kMxDownOutBytes;
 constexpr uint32_t kMxOffsetOOB = 0xFFFFFFF0u;
 static_assert(kMxTileLoads * kMxThreads * 16 == kMxTileBytes, "whole tile per load round");
 static_assert(kMxRowsPerWave == 8 * kMxTileLoads, "each load instruction fills 8 rows");
@@ -82,17 +82,22 @@ struct MxArgs {
 __device__ __forceinline__ int ufl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 template <bool GATEUP, int NMT>
-__device__ __forceinline__ void mx_tile(const MxArgs& a, char* As, const __amdgpu_buffer_rsrc_t& rq,
+__device__ __forceinline__ void mx_tile(const MxArgs& a, char* As0, char* As1, char* Aout,
+                                        const __amdgpu_buffer_rsrc_t& rq,
                                         const __amdgpu_buffer_rsrc_t& rs, const __amdgpu_buffer_rsrc_t& ra,
                                         const uint32_t (&aoff)[kMxTileLoads], const int (&qns)[4],
                                         const int (&sns)[4], const bool (&nok)[4], int nit, int c0, int wave,
                                         int lane, int mlen, int rbase, int m0, int Iw, bool shared) {
   const int n = lane & 15, G = lane >> 4;
+  // The ring's stages are separate LDS objects (stage numbers are compile-time constants below), so the
+  // compiler can tell that reading one stage does not depend on the loads still filling the other and
+  // puts no wait for them in front of the reads.
+  auto ring = [&](int buf) __attribute__((always_inline)) { return buf == 0 ? As0 : As1; };
   auto issue_a = [&](int it, int buf) {
 #pragma unroll
     for (int i = 0; i < kMxTileLoads; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_void*)(As + buf * kMxTileBytes + (kMxRowsPerWave * wave + 8 * i) * kMxRowBytes), 16, (int)aoff[i],
+          ra, (lds_void*)(ring(buf) + (kMxRowsPerWave * wave + 8 * i) * kMxRowBytes), 16, (int)aoff[i],
           it * kMxBK, 0, 0);
   };
   // this lane's weight block of every slice (row n, block 4it + G: 16 B of codes, one exponent byte)
@@ -119,7 +124,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As, const __amdgp
     return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
   auto compute = [&](int buf, const u32x4* q, const uint32_t* sc) __attribute__((always_inline)) {
-    const char* At = As + buf * kMxTileBytes;
+    const char* At = ring(buf);
     v8i w[4];
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) w[ns] = v8i{(int)q[ns][0], (int)q[ns][1], (int)q[ns][2], (int)q[ns][3], 0, 0, 0, 0};
@@ -138,30 +143,28 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As, const __amdgp
     }
   };
 
-  // two-stage pipeline: while step `it` is computed, step it+1's tile and weight blocks are in flight
+  // Two-stage pipeline: while step `it` is computed, step it+1's activation tile (LDS) and weight
+  // blocks (registers) are in flight.
   u32x4 q[2][4];
   uint32_t sc[2][4];
   issue_a(0, 0);
   load_w(0, q[0], sc[0]);
+  auto step = [&](int it, auto st_c) __attribute__((always_inline)) {
+    constexpr int st = decltype(st_c)::value;
+    vm_lgkm_wait<0>();
+    tile_barrier();  // every wavefront's part of tile `it` is in LDS; tile it-1 is no longer read
+    if (it + 1 < nit) {
+      issue_a(it + 1, st ^ 1);
+      load_w(it + 1, q[st ^ 1], sc[st ^ 1]);
+    }
+    compute(st, q[st], sc[st]);
+  };
   int it0 = 0;
   for (; it0 + 2 <= nit; it0 += 2) {
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int it = it0 + st;
-      vm_lgkm_wait<0>();
-      tile_barrier();  // every wavefront's part of tile `it` is in LDS; tile it-1 is no longer read
-      if (it + 1 < nit) {
-        issue_a(it + 1, st ^ 1);
-        load_w(it + 1, q[st ^ 1], sc[st ^ 1]);
-      }
-      compute(st, q[st], sc[st]);
-    }
+    step(it0 + 0, std::integral_constant<int, 0>{});
+    step(it0 + 1, std::integral_constant<int, 1>{});
   }
-  if (it0 < nit) {
-    vm_lgkm_wait<0>();
-    tile_barrier();
-    compute(0, q[0], sc[0]);
-  }
+  if (it0 < nit) step(it0, std::integral_constant<int, 0>{});
 
   // ---- epilogue: lane (n, G) holds, for activation row 16 mt + n, output columns 4G .. 4G+3 of each
   // 16-column slice; the row's activation scale multiplies them.
@@ -198,10 +201,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As, const __amdgp
     }
   }
   if (!GATEUP) {
-    // the down tile leaves through LDS so that every store writes whole rows (as on the W4A16 path)
-    static_assert(kMxLdsBytes >= kMxDownOutBytes, "the output tile fits in LDS");
-    vm_lgkm_wait<0>();
-    tile_barrier();  // every wavefront is done reading the activation ring
+    // the down tile leaves through LDS (a region of its own) so that every store writes whole rows
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       const int row = mt * 16 + n;
@@ -210,7 +210,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As, const __amdgp
         const half2v p0 = {to_f16_sat(acc[mt][ns][0]), to_f16_sat(acc[mt][ns][1])};
         const half2v p1 = {to_f16_sat(acc[mt][ns][2]), to_f16_sat(acc[mt][ns][3])};
         const int chunk = 8 * wave + 2 * ns + (G >> 1);
-        *reinterpret_cast<uint2*>(As + row * (kMxDownBandCols * 2) + ((chunk ^ (row & 31)) * 16) + 8 * (G & 1)) =
+        *reinterpret_cast<uint2*>(Aout + row * (kMxDownBandCols * 2) + ((chunk ^ (row & 31)) * 16) + 8 * (G & 1)) =
             uint2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
       }
     }
@@ -224,7 +224,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As, const __amdgp
 #pragma unroll
     for (int i = 0; i < 16 * NMT / R; ++i) {
       const int row = R * i + tid / C;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(As + row * (kMxDownBandCols * 2) + ((chunk ^ (row & 31)) * 16));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Aout + row * (kMxDownBandCols * 2) + ((chunk ^ (row & 31)) * 16));
       if (row < mlen && col < a.d) *reinterpret_cast<u32x4*>(out + (size_t)(rbase + row) * a.d + col) = v;
     }
   }
@@ -233,7 +233,9 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As, const __amdgp
 template <bool GATEUP>
 __global__ __launch_bounds__(kMxThreads, 8 / kMxWaves) void k_grouped_mx(MxArgs a) {
   constexpr int BANDW = GATEUP ? kMxGateUpBandCols : kMxDownBandCols;
-  __shared__ __attribute__((aligned(1024))) char As[kMxLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char As0[kMxTileBytes];
+  __shared__ __attribute__((aligned(1024))) char As1[kMxTileBytes];
+  __shared__ __attribute__((aligned(1024))) char Aout[GATEUP ? 16 : kMxDownOutBytes];
   __shared__ int s_prefix[kMaxExperts + 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = ufl(tid >> 6);
   const int ngroups = a.E + 1;
@@ -339,12 +341,12 @@ __global__ __launch_bounds__(kMxThreads, 8 / kMxWaves) void k_grouped_mx(MxArgs 
     sns[ns] = ufl((int)((uint32_t)(rowbase[ns] / 16) * nkb * 16u));
   }
   switch ((mlen + 15) >> 4) {
-    case 1: mx_tile<GATEUP, 1>(a, As, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
-    case 2: mx_tile<GATEUP, 2>(a, As, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
-    case 3: mx_tile<GATEUP, 3>(a, As, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
-    case 4: mx_tile<GATEUP, 4>(a, As, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
-    case 5: mx_tile<GATEUP, 5>(a, As, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
-    default: mx_tile<GATEUP, 6>(a, As, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
+    case 1: mx_tile<GATEUP, 1>(a, As0, As1, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
+    case 2: mx_tile<GATEUP, 2>(a, As0, As1, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
+    case 3: mx_tile<GATEUP, 3>(a, As0, As1, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
+    case 4: mx_tile<GATEUP, 4>(a, As0, As1, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
+    case 5: mx_tile<GATEUP, 5>(a, As0, As1, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
+    default: mx_tile<GATEUP, 6>(a, As0, As1, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
   }
 }
 
