@@ -1,4 +1,5 @@
-"""Plain CPU oracle of the W4A8 variant of the layer: MXFP4 expert weights times FP8 activations.
+"""Plain CPU oracle of the fp8-activation variants of the layer: W4A8 (MXFP4 expert weights times FP8
+activations) and W8A8 (MXFP8 expert weights times FP8 activations).
 
 TEST INFRASTRUCTURE.  Only tests/, ``__graft_entry__.smoke()`` and the CPU baseline leg of
 ``bench.py`` may import or call this module.  It shares no code with the HIP library.
@@ -11,6 +12,9 @@ What it computes, and where the pages say so
     (a different-but-valid grid, so the deeper reference outputs move), and the fp8 activations
     carry a per-token scale folded back after the product (per-token-act FP8 with the scales
     applied to the GEMM output).
+
+The same page pairs a W8A8 path (fp8 activations times fp8 weights), argmax-exact on its prefill
+with near-lossless fp8 weights.
 
 Readings taken where the pages are silent (stated in the repository's design notes too):
   * fp4 means e2m1 (1 sign, 2 exponent, 1 mantissa bit, exponent bias 1; no inf or NaN): the
@@ -25,6 +29,10 @@ Readings taken where the pages are silent (stated in the repository's design not
     activation row is scaled by s = amax / 448 (float32 division; s = 1 for an all-zero row), each
     element becomes the e4m3 value nearest to fl32(x / s) (ties to the even mantissa, saturating at
     +-448), and the row's product is multiplied back by s;
+  * W8A8's fp8 weights are the Q4 blocks requantised to MXFP8: e4m3 elements in the same blocks of 32
+    with a shared 2^E, E = floor(log2(max_i |w_i|)) - 8 (8 being the largest exponent of an e4m3
+    value), elements w_i / 2^E rounded to the nearest e4m3 value (ties to even, saturating at +-448),
+    E = -127 for an all-zero block;
   * the gate+up result h = silu(g) * u is rounded to fp16 (saturating at +-65504, as on the W4A16
     path) before its own per-row fp8 quantisation for the down projection;
   * routing (router, selection, weights) and the combine order are those of the W4A16 layer.
@@ -38,7 +46,8 @@ from .moe_oracle import (bf16_bits_to_f64, fp16_bits_to_f64, router_logits, sele
                          sigmoid)
 
 __all__ = ["e2m1_value", "e4m3_value", "round_e2m1", "round_e4m3", "mx_requant", "mx_dequant",
-           "quant_rows_fp8", "dequant_rows_fp8", "forward_w4a8", "E4M3_MAX", "FP16_MAX"]
+           "mx8_requant", "mx8_dequant", "quant_rows_fp8", "dequant_rows_fp8", "forward_w4a8", "forward_w8a8",
+           "E4M3_MAX", "FP16_MAX"]
 
 E4M3_MAX = 448.0
 FP16_MAX = 65504.0
@@ -102,19 +111,24 @@ def round_e4m3(v) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- requantisation
 
+def _q4_values(qs: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Row-major Q4 (uint8 [rows, K/2], fp16 bits [rows, K/32]) -> the values (q - 8) * d, float64."""
+    qs = np.asarray(qs, dtype=np.uint8)
+    rows, half = qs.shape
+    q = np.empty((rows, 2 * half), dtype=np.int64)
+    q[:, 0::2] = qs & 0x0F
+    q[:, 1::2] = qs >> 4
+    d = fp16_bits_to_f64(scales)
+    return (q - 8).astype(np.float64) * np.repeat(d, 32, axis=1)
+
+
 def mx_requant(qs: np.ndarray, scales: np.ndarray):
     """Q4 block matrix (row-major: uint8 [rows, K/2], fp16 bits [rows, K/32]) -> MXFP4.
 
     Returns (codes uint8 [rows, K/2], element 2i in the low nibble of byte i as in the Q4 format;
     exp uint8 [rows, K/32], the biased shared exponent E + 127 of each 32-element block)."""
-    qs = np.asarray(qs, dtype=np.uint8)
-    rows, half = qs.shape
-    K = 2 * half
-    q = np.empty((rows, K), dtype=np.int64)
-    q[:, 0::2] = qs & 0x0F
-    q[:, 1::2] = qs >> 4
-    d = fp16_bits_to_f64(scales)
-    w = (q - 8).astype(np.float64) * np.repeat(d, 32, axis=1)
+    w = _q4_values(qs, scales)
+    rows, K = w.shape
     wb = w.reshape(rows, K // 32, 32)
     amax = np.abs(wb).max(axis=2)
     with np.errstate(divide="ignore"):
@@ -135,6 +149,28 @@ def mx_dequant(codes: np.ndarray, exp: np.ndarray) -> np.ndarray:
     c[:, 1::2] = codes >> 4
     scale = np.ldexp(1.0, np.asarray(exp, dtype=np.int64) - 127)
     return e2m1_value(c) * np.repeat(scale, 32, axis=1)
+
+
+def mx8_requant(qs: np.ndarray, scales: np.ndarray):
+    """Q4 block matrix (row-major: uint8 [rows, K/2], fp16 bits [rows, K/32]) -> MXFP8.
+
+    Returns (codes uint8 [rows, K], e4m3 element k of the row at byte k; exp uint8 [rows, K/32], the
+    biased shared exponent E + 127 of each 32-element block)."""
+    w = _q4_values(qs, scales)
+    rows, K = w.shape
+    wb = w.reshape(rows, K // 32, 32)
+    amax = np.abs(wb).max(axis=2)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127).astype(np.int64)
+    e = np.clip(e, -127, 127)
+    codes = round_e4m3(wb / np.ldexp(1.0, e)[:, :, None]).reshape(rows, K)
+    return codes.astype(np.uint8), (e + 127).astype(np.uint8)
+
+
+def mx8_dequant(codes: np.ndarray, exp: np.ndarray) -> np.ndarray:
+    """MXFP8 (codes [rows, K], biased exponents [rows, K/32]) -> float64 [rows, K]."""
+    scale = np.ldexp(1.0, np.asarray(exp, dtype=np.int64) - 127)
+    return e4m3_value(codes) * np.repeat(scale, 32, axis=1)
 
 
 # ----------------------------------------------------------------------------- activations
@@ -170,11 +206,7 @@ def _mlp_w4a8(Xq: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
     return hq @ w2.T
 
 
-def forward_w4a8(inp: dict, tokens=None, ids_override: dict | None = None, mx: dict | None = None) -> dict:
-    """The W4A8 layer for the chosen tokens (all by default), same routing as the W4A16 layer.
-
-    mx: optional precomputed {name: (codes, exp)} of mx_requant for w13/w2 per expert and s13/s2
-    (computed here when absent).  Returns dict(y [n,d], ids, w, margin, tokens)."""
+def _forward_fp8act(inp: dict, tokens, ids_override, mx, requant, dequant) -> dict:
     dims = inp["dims"]
     k, d = dims.k, dims.d
     tokens = np.arange(dims.T) if tokens is None else np.asarray(tokens, dtype=np.int64)
@@ -191,10 +223,10 @@ def forward_w4a8(inp: dict, tokens=None, ids_override: dict | None = None, mx: d
 
     def mat(name, e=None):
         if mx is not None and (name, e) in mx:
-            return mx_dequant(*mx[(name, e)])
+            return dequant(*mx[(name, e)])
         qs = inp[name + "_qs"] if e is None else inp[name + "_qs"][e]
         sc = inp[name + "_sc"] if e is None else inp[name + "_sc"][e]
-        return mx_dequant(*mx_requant(qs, sc))
+        return dequant(*requant(qs, sc))
 
     n = len(tokens)
     y_routed = np.zeros((n, d))
@@ -204,3 +236,16 @@ def forward_w4a8(inp: dict, tokens=None, ids_override: dict | None = None, mx: d
         y_routed[rows] += w[rows, slots][:, None] * Y
     y_shared = _mlp_w4a8(xq, mat("s13"), mat("s2"))
     return dict(y=y_routed + y_shared, ids=ids, w=w, margin=margin, tokens=tokens)
+
+
+def forward_w4a8(inp: dict, tokens=None, ids_override: dict | None = None, mx: dict | None = None) -> dict:
+    """The W4A8 layer for the chosen tokens (all by default), same routing as the W4A16 layer.
+
+    mx: optional precomputed {(name, e): (codes, exp)} of mx_requant for w13/w2 per expert and s13/s2
+    (e None; computed here when absent).  Returns dict(y [n,d], ids, w, margin, tokens)."""
+    return _forward_fp8act(inp, tokens, ids_override, mx, mx_requant, mx_dequant)
+
+
+def forward_w8a8(inp: dict, tokens=None, ids_override: dict | None = None, mx: dict | None = None) -> dict:
+    """The W8A8 layer: as forward_w4a8 with MXFP8 weights (mx8_requant; `mx` holds its outputs)."""
+    return _forward_fp8act(inp, tokens, ids_override, mx, mx8_requant, mx8_dequant)

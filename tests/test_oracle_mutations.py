@@ -132,3 +132,85 @@ def test_planted_mistake_fails_a_pin(name, monkeypatch):
         except Exception:  # an assertion, or a shape error from a transposed operand
             caught.append(pin)
     assert caught, f"mutation {name} of oracle.{fn} passed every pin it should fail: {catching}"
+
+
+# ----------------------------------------------------------------------------- the fp8-activation oracle
+
+import oracle.moe_w4a8 as ow  # noqa: E402
+import test_oracle_w4a8 as pins8  # noqa: E402
+
+_real_mx_requant, _real_mx8_requant, _real_round_e4m3 = ow.mx_requant, ow.mx8_requant, ow.round_e4m3
+
+
+def _mx_requant_exponent_high(qs, scales):
+    codes, exp = _real_mx_requant(qs, scales)       # slip: E = floor(log2 amax) - 1
+    w = ow._q4_values(qs, scales)
+    rows, K = w.shape
+    wb = w.reshape(rows, K // 32, 32)
+    e = exp.astype(np.int64) - 127 + 1
+    c = ow.round_e2m1(wb / np.ldexp(1.0, e)[:, :, None]).reshape(rows, K)
+    return ((c[:, 0::2] & 15) | ((c[:, 1::2] & 15) << 4)).astype(np.uint8), (e + 127).astype(np.uint8)
+
+
+def _mx_requant_nibbles_swapped(qs, scales):
+    codes, exp = _real_mx_requant(qs, scales)
+    return ((codes >> 4) | ((codes & 15) << 4)).astype(np.uint8), exp
+
+
+def _mx8_requant_exponent_low(qs, scales):
+    w = ow._q4_values(qs, scales)                    # slip: E = floor(log2 amax) - 7 (too coarse)
+    rows, K = w.shape
+    wb = w.reshape(rows, K // 32, 32)
+    _, exp = _real_mx8_requant(qs, scales)
+    e = exp.astype(np.int64) - 127 + 1
+    return ow.round_e4m3(wb / np.ldexp(1.0, e)[:, :, None]).reshape(rows, K).astype(np.uint8), (e + 127).astype(np.uint8)
+
+
+def _round_e4m3_ties_away(v):
+    v = np.asarray(v, dtype=np.float64)
+    c = _real_round_e4m3(v)
+    # slip: a value exactly halfway between two codes goes to the larger magnitude
+    lo = ow.e4m3_value(c & 0x7F)
+    nxt = ow.e4m3_value(np.minimum((c & 0x7F) + 1, 0x7E))
+    half = np.abs(np.abs(v) - (lo + nxt) / 2) == 0
+    return np.where(half & ((c & 0x7F) < 0x7E), c + 1, c).astype(np.uint8)
+
+
+def _quant_rows_unscaled(X):
+    X = np.asarray(X, dtype=np.float32)              # slip: no per-row scale
+    return ow.round_e4m3(X.astype(np.float64)), np.ones(X.shape[0], dtype=np.float32)
+
+
+MUTATIONS_FP8 = {
+    "mx_exponent_high": ("mx_requant", _mx_requant_exponent_high, ["test_requant_hand_worked_block"]),
+    "mx_nibbles_swapped": ("mx_requant", _mx_requant_nibbles_swapped, ["test_requant_hand_worked_block"]),
+    "mx8_exponent_low": ("mx8_requant", _mx8_requant_exponent_low, ["test_mx8_requant_hand_worked_block",
+                                                                     "test_mx8_requant_power_of_two_scales_are_exact"]),
+    "e4m3_ties_away": ("round_e4m3", _round_e4m3_ties_away, ["test_e4m3_rounding"]),
+    "quant_rows_unscaled": ("quant_rows_fp8", _quant_rows_unscaled, ["test_quant_rows_fp8"]),
+}
+
+
+def _run_pin(pin):
+    """Run one pin; a parametrized pin runs every one of its cases."""
+    fn = getattr(pins8, pin)
+    marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
+    if not marks:
+        return fn()
+    for case in marks[0].args[1]:
+        fn(*case)
+
+
+@pytest.mark.parametrize("name", list(MUTATIONS_FP8))
+def test_planted_mistake_in_the_fp8_oracle_fails_a_pin(name, monkeypatch):
+    fn, repl, catching = MUTATIONS_FP8[name]
+    for pin in catching:
+        _run_pin(pin)
+    monkeypatch.setattr(ow, fn, repl)
+    caught = []
+    for pin in catching:
+        try:
+            _run_pin(pin)
+        except Exception:
+            caught.append(pin)
+    assert caught, f"mutation {name} of oracle.moe_w4a8.{fn} passed every pin it should fail: {catching}"

@@ -157,3 +157,75 @@ def test_layer_permutation_equivariance_and_token_subsets():
     full = w4.forward_w4a8(inp)
     sub = w4.forward_w4a8(inp, tokens=[5, 1, 3])
     assert np.array_equal(sub["y"], full["y"][[5, 1, 3]])
+
+
+# ----------------------------------------------------------------------------- W8A8 (MXFP8 weights)
+
+def test_mx8_requant_power_of_two_scales_are_exact():
+    # d a power of two: amax = 8d, E = log2(8d) - 8, so the elements are (q - 8) * 2^5 = -256 .. 224,
+    # integers with at most 3 significant bits times a power of two: every one is an e4m3 value
+    for d in (1.0, 0.25, 2.0 ** -14, 2.0 ** -24, 64.0):
+        qs, sc = _q4_block(list(range(16)) * 2, d)
+        codes, exp = w4.mx8_requant(qs, sc)
+        assert exp.tolist() == [[int(np.log2(8 * d)) - 8 + 127]]
+        assert np.array_equal(w4.mx8_dequant(codes, exp), oracle.dequant_q4(qs, sc))
+    qs, sc = _q4_block([8] * 32, 1.0)          # all values zero
+    codes, exp = w4.mx8_requant(qs, sc)
+    assert exp.tolist() == [[0]] and not codes.any()
+
+
+def test_mx8_requant_hand_worked_block():
+    # d = fp16(0.0113) = 0.01129913330078125; amax = 8d = 0.0904 -> floor(log2) = -4, E = -12 (byte 115);
+    # the elements (q - 8) * d * 4096 = -370.25, -323.97, -277.69, -231.41, -185.13, -138.84, -92.56,
+    # -46.28, 0, 46.28, ... round to the nearest e4m3 value: -384 (0xFC), -320 (0xFA), -288 (0xF9),
+    # -224 (0xF6), -192 (0xF4), -144 (0xF1), -96 (0xEC), -48 (0xE4), 0, 48 (0x64), 96 (0x6C),
+    # 144 (0x71), 192 (0x74), 224 (0x76), 288 (0x79), 320 (0x7A)
+    qs, sc = _q4_block(list(range(16)) * 2, 0.0113)
+    codes, exp = w4.mx8_requant(qs, sc)
+    assert exp.tolist() == [[115]]
+    expect = [0xFC, 0xFA, 0xF9, 0xF6, 0xF4, 0xF1, 0xEC, 0xE4, 0x00, 0x64, 0x6C, 0x71, 0x74, 0x76, 0x79, 0x7A]
+    assert codes[0, :16].tolist() == expect and codes[0, 16:].tolist() == expect
+
+
+def test_mx8_requant_error_bound():
+    # below the saturation point each element is within half an e4m3 step of its Q4 value (2^-4 of its
+    # magnitude, or 2^(E-10) in the subnormal range); elements past 448 * 2^E sit at +-448 * 2^E
+    rng = np.random.default_rng(6)
+    qs = rng.integers(0, 256, size=(32, 64), dtype=np.uint8)
+    sc = np.float16(rng.uniform(0.005, 0.02, size=(32, 4)) * rng.choice([-1, 1], size=(32, 4))).view(np.uint16)
+    ref = oracle.dequant_q4(qs, sc).reshape(32, 4, 32)
+    codes, exp = w4.mx8_requant(qs, sc)
+    got = w4.mx8_dequant(codes, exp).reshape(32, 4, 32)
+    scale = np.ldexp(1.0, exp.astype(np.int64) - 127)[:, :, None]
+    sat = np.abs(ref) > 448 * scale
+    inside = ~sat
+    assert np.all(np.abs(got - ref)[inside] <= (2.0 ** -4 * np.abs(ref) + 2.0 ** -10 * scale)[inside] + 1e-15)
+    assert np.array_equal(np.abs(got)[sat], (448 * np.broadcast_to(scale, got.shape))[sat])
+    assert sat.any()   # the test draws blocks whose largest value saturates
+
+
+def test_w8a8_layer_doubling_down_scales_doubles_y():
+    inp = synth.make_inputs(synth.CONFIGS["tiny"])
+    base = w4.forward_w8a8(inp)["y"]
+    inp2 = dict(inp)
+    for name in ("w2_sc", "s2_sc"):
+        inp2[name] = (inp[name].view(np.float16).astype(np.float32) * 2).astype(np.float16).view(np.uint16)
+    assert np.array_equal(w4.forward_w8a8(inp2)["y"], 2 * base)
+
+
+def test_w8a8_layer_matches_w4a16_with_power_of_two_scales():
+    # with power-of-two scales the MXFP8 weights equal the Q4 weights exactly (above), for every code, so
+    # the layers differ only by the fp8 roundings of x and h and the fp16 rounding of h
+    inp = synth.make_inputs(synth.CONFIGS["tiny"])
+    rng = np.random.default_rng(12)
+    for name in ("w13", "w2", "s13", "s2"):
+        e = rng.integers(-9, -5, size=inp[name + "_sc"].shape)
+        inp[name + "_sc"] = np.float16(np.ldexp(1.0, e)).view(np.uint16)
+    r8 = w4.forward_w8a8(inp)
+    r16 = oracle.forward(inp)
+    assert np.array_equal(r8["ids"], r16["ids"])
+    err = np.linalg.norm(r8["y"] - r16["y"]) / np.linalg.norm(r16["y"])
+    assert 0 < err < 0.08
+    # and W8A8 is closer to W4A16 than W4A8 is (the fp4 grid is the coarser one)
+    r4 = w4.forward_w4a8(inp)
+    assert np.linalg.norm(r4["y"] - r16["y"]) > 1.5 * np.linalg.norm(r8["y"] - r16["y"])
