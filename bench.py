@@ -16,9 +16,10 @@ bracketed by device synchronisation.
 The primary workload (default: single-token decode, d=4096, E=256, top-10,
 I=1024, shared I=1024) gives `value`; the 2048-token prefill chunk is
 measured the same way and reported under `secondary`, and again as the W4A8
-variant (moe_route + moe_build_descriptors + moe_w4a8_forward on MXFP4 copies
-of the weights, fp8 activations) under `secondary_w4a8`, whose roofline is
-priced against the fp8 MFMA peak.  Per-kernel average
+and W8A8 variants (moe_route + moe_build_descriptors + moe_w4a8_forward /
+moe_w8a8_forward on MXFP4 / MXFP8 copies of the weights, fp8 activations)
+under `secondary_w4a8` / `secondary_w8a8`, whose rooflines are priced against
+the fp8 MFMA peak.  Per-kernel average
 durations come from graphs that replay only that kernel's nodes, extracted
 from the captured layer graph, timed with HIP events on the same stream
 (every launch of the layer is idempotent, so replaying one alone is valid).
@@ -231,15 +232,16 @@ def recorded_traffic(profile: str, sources) -> int | None:
     return int(fields["traffic_bytes_per_launch"])
 
 
-def mx_weights(abi, torch, dims, w):
-    """MXFP4 copies (moe_q4_to_mxfp4) of one layer copy's packed Q4 stacks."""
+def mx_weights(abi, torch, dims, w, fp8=False):
+    """MXFP4 (moe_q4_to_mxfp4) or MXFP8 (moe_q4_to_mxfp8) copies of one layer copy's packed Q4 stacks."""
     shapes = {"w13": (dims.E, 2 * dims.I, dims.d), "w2": (dims.E, dims.d, dims.I),
               "s13": (1, 2 * dims.I_shared, dims.d), "s2": (1, dims.d, dims.I_shared)}
     mx = {}
+    requant = abi.moe_q4_to_mxfp8 if fp8 else abi.moe_q4_to_mxfp4
     for name, (n, rows, K) in shapes.items():
-        codes = torch.empty_like(w[name + "_qs"])
+        codes = torch.empty(w[name + "_qs"].numel() * (2 if fp8 else 1), dtype=torch.uint8, device="cuda")
         exps = torch.empty(n * rows * (K // 32), dtype=torch.uint8, device=codes.device)
-        abi.moe_q4_to_mxfp4(n, rows, K, w[name + "_qs"], w[name + "_sc"], codes, exps)
+        requant(n, rows, K, w[name + "_qs"], w[name + "_sc"], codes, exps)
         mx[name + "_codes"], mx[name + "_exps"] = codes, exps
     return mx
 
@@ -264,18 +266,19 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
         weights.append(dw)
         xs.append(x)
     spaces = [layer.Workspace(dims, 0) for _ in range(L)]
-    if variant == "w4a8":
+    if variant in ("w4a8", "w8a8"):
         if abi.moe_path(dims, 0) != 1 or residual:
-            raise ValueError("the W4A8 variant runs on the grouped path, without a residual")
-        mxs = {id(w): mx_weights(abi, torch, dims, w) for w in weights}
-        w4a8_scratch = {id(ws): torch.empty(abi.moe_w4a8_scratch_bytes(dims, 0), dtype=torch.uint8, device=device)
-                        for ws in spaces}
+            raise ValueError("the fp8-activation variants run on the grouped path, without a residual")
+        fp8w = variant == "w8a8"
+        mxs = {id(w): mx_weights(abi, torch, dims, w, fp8w) for w in weights}
+        scratch_bytes = abi.moe_w8a8_scratch_bytes if fp8w else abi.moe_w4a8_scratch_bytes
+        fwd = abi.moe_w8a8_forward if fp8w else abi.moe_w4a8_forward
+        fp8_scratch = {id(ws): torch.empty(scratch_bytes(dims, 0), dtype=torch.uint8, device=device) for ws in spaces}
 
         def call(x, w, ws, stream=None, residual=None):
             abi.moe_route(dims, x, w["w_router"], w["bias"], ws.topk_ids, ws.topk_w, ws.routing, stream=stream)
             abi.moe_build_descriptors(dims, ws.topk_ids, ws.routing, stream=stream)
-            abi.moe_w4a8_forward(dims, x, ws.topk_ids, ws.topk_w, ws.routing, mxs[id(w)], ws.y,
-                                 w4a8_scratch[id(ws)], stream=stream)
+            fwd(dims, x, ws.topk_ids, ws.topk_w, ws.routing, mxs[id(w)], ws.y, fp8_scratch[id(ws)], stream=stream)
     # with `residual`, every step goes through moe_q4_forward_residual with its own fp32 [T][d] residual
     res = [torch.randn(dims.T, dims.d, device=device) if residual else None for _ in range(L)]
     stream = torch.cuda.Stream()
@@ -375,7 +378,7 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
                            if name == "decode" else None,
                            "algorithmic_bytes_per_launch": per_launch,
                            "avg_launch_us": round(kernel_us[kname], 3)}
-    elif variant == "w4a8":
+    elif variant in ("w4a8", "w8a8"):
         kname = "grouped_mx_gateup"
         per_launch = 2 * (P * 2 * dims.I + T * 2 * dims.I_shared) * d
         achieved = per_launch / (kernel_us[kname] * 1e-6) / 1e12
@@ -475,21 +478,25 @@ def traffic_run(name, torch, layer, synth, flags=0, variant="w4a16"):
     """Three layer calls and two 256 MiB copies, nothing else: the run that rocprofv3 --pmc FETCH_SIZE /
     WRITE_SIZE records for the traffic summaries under profiles/ (the copy calibrates the counters).
     `flags` are the layer's MOE_FLAG_* bits (e.g. the grouped GEMMs' work order); `variant` w4a8 runs
-    moe_route + moe_build_descriptors + moe_w4a8_forward on MXFP4 copies of the weights instead."""
+    moe_route + moe_build_descriptors + moe_w4a8_forward on MXFP4 copies of the weights instead, w8a8
+    moe_w8a8_forward on MXFP8 copies."""
     from sparse_moe_expert_sigmoid_amd import abi
     inp = synth.make_inputs(synth.CONFIGS[name])
     dims = inp["dims"]
     w = layer.DeviceWeights.upload(inp)
     x = layer.to_device(inp["x"], "cuda")
     ws = layer.Workspace(dims, flags)
-    if variant == "w4a8":
-        mx = mx_weights(abi, torch, dims, w)
-        scratch = torch.empty(abi.moe_w4a8_scratch_bytes(dims, flags), dtype=torch.uint8, device="cuda")
+    if variant != "w4a16":
+        fp8w = variant == "w8a8"
+        mx = mx_weights(abi, torch, dims, w, fp8w)
+        scratch = torch.empty((abi.moe_w8a8_scratch_bytes if fp8w else abi.moe_w4a8_scratch_bytes)(dims, flags),
+                              dtype=torch.uint8, device="cuda")
+        fwd = abi.moe_w8a8_forward if fp8w else abi.moe_w4a8_forward
     for _ in range(3):
-        if variant == "w4a8":
+        if variant != "w4a16":
             abi.moe_route(dims, x, w["w_router"], w["bias"], ws.topk_ids, ws.topk_w, ws.routing, flags=flags)
             abi.moe_build_descriptors(dims, ws.topk_ids, ws.routing, flags=flags)
-            abi.moe_w4a8_forward(dims, x, ws.topk_ids, ws.topk_w, ws.routing, mx, ws.y, scratch, flags=flags)
+            fwd(dims, x, ws.topk_ids, ws.topk_w, ws.routing, mx, ws.y, scratch, flags=flags)
         else:
             layer.layer_call_fused(x, w, ws)
     a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -561,7 +568,8 @@ def main():
     ap.add_argument("--secondary", default="prefill", help="second workload reported alongside ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-w4a8", action="store_true",
-                    help="skip the W4A8 variant (MXFP4 weights x FP8 activations) of the secondary workload")
+                    help="skip the W4A8 / W8A8 variants (MXFP4 / MXFP8 weights x FP8 activations) of the "
+                         "secondary workload")
     ap.add_argument("--separate-calls", action="store_true",
                     help="time each layer as moe_route + moe_build_descriptors + moe_q4_forward instead of "
                          "moe_layer_forward (the same results)")
@@ -575,7 +583,7 @@ def main():
     ap.add_argument("--flags", type=int, default=0,
                     help="MOE_FLAG_* bits for --traffic-run (4 = expert-id group order, 8 = items in launch "
                          "order, 16 = band-major items)")
-    ap.add_argument("--variant", default="w4a16", choices=["w4a16", "w4a8"],
+    ap.add_argument("--variant", default="w4a16", choices=["w4a16", "w4a8", "w8a8"],
                     help="layer variant of --traffic-run")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -618,11 +626,12 @@ def main():
         n = max(20, args.steps // 40)
         sec = run_workload(args.secondary, n, max(4, n // 10), torch, hip, abi, layer, synth, residual=args.residual,
                            separate=args.separate_calls)
-    w4a8 = None
+    fp8act = {}
     if sec is not None and not args.no_w4a8 and abi.moe_path(synth.CONFIGS[args.secondary].dims, 0) == 1:
         n = max(20, args.steps // 40)
-        w4a8 = run_workload(args.secondary, n, max(4, n // 10), torch, hip, abi, layer, synth, variant="w4a8")
-        w4a8.pop("_inp0", None)
+        for v in ("w4a8", "w8a8"):
+            fp8act[v] = run_workload(args.secondary, n, max(4, n // 10), torch, hip, abi, layer, synth, variant=v)
+            fp8act[v].pop("_inp0", None)
     ctx = run_decode_ctx(max(50, args.steps // 4), torch, abi, layer, synth) if args.workload == "decode" else None
     ctxn = (run_decode_ctx(max(50, args.steps // 4), torch, abi, layer, synth, norm=True)
             if args.workload == "decode" else None)
@@ -662,8 +671,8 @@ def main():
     if sec is not None:
         sec.pop("_inp0", None)
         out["secondary"] = sec
-    if w4a8 is not None:
-        out["secondary_w4a8"] = w4a8
+    for v, r in fp8act.items():
+        out["secondary_" + v] = r
     if ctx is not None:
         out["decode_ctx"] = ctx
         out["decode_ctx_norm"] = ctxn

@@ -374,76 +374,92 @@ int moe_decode_ctx_destroy(moe_decode_ctx* ctx);
 int moe_q4_pack(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs_in, const uint16_t* scales_in,
                 uint8_t* qs_out, uint16_t* scales_out, void* stream);
 
-/* ---- W4A8 variant: MXFP4 expert weights x FP8 activations ---------------
+/* ---- fp8-activation variants: W4A8 and W8A8 ----------------------------
  * Page thewafflehaus/FFAI pull request 72 ("Nemotron-Nano-30B GB10 prefill
- * quality + speed wins") adds a W4A8 grouped MoE beside the Q4 W4A16 one:
- * the Q4 weights requantised once to a block-scaled fp4 grid, activations
- * in fp8 with a per-token scale applied to the product.  Here that grid is
- * MXFP4 -- e2m1 elements (0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives) in the
- * same 32-element blocks, each block with a power-of-two scale 2^E stored as
- * the byte E + 127 -- which the gfx950 block-scaled MFMA multiplies as is,
- * and fp8 is e4m3 (largest 448).  Per layer call, for every token t:
+ * quality + speed wins") adds W4A8 (fp8 activations x fp4 weights) and
+ * W8A8 (fp8 activations x fp8 weights) grouped MoE paths beside the Q4
+ * W4A16 one; the fp4 weights are the Q4 weights requantised once to a
+ * block-scaled fp4 grid, the fp8 activations carry a per-token scale
+ * applied to the product.  Here the weight grids are the block formats the
+ * gfx950 block-scaled MFMA multiplies as they are, in the Q4 blocks of 32,
+ * each block with a power-of-two scale 2^E stored as the byte E + 127:
+ *   MXFP4  e2m1 elements (0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives),
+ *          E = floor(log2 max|w|) - 2
+ *   MXFP8  e4m3 elements (largest 448), E = floor(log2 max|w|) - 8
+ * (E = -127 for an all-zero block; elements round to nearest, ties to the
+ * even mantissa, saturating at the largest value).  fp8 activations are
+ * e4m3.  Per layer call, for every token t:
  *   routing  as for moe_q4_forward (the same topk_w and routing build);
  *   x8_t     = e4m3(x_t / sx_t),   sx_t = amax(x_t) / 448   (1 if x_t = 0)
  *   h        = fp16(silu(sx_t * (W_g x8_t)) * (sx_t * (W_u x8_t)))
  *   h8       = e4m3(h / sh),       sh = amax(h) / 448 per h row
- *   y_e      = sh * (W_d h8)       (W the MXFP4 matrices, exact products,
- *                                   fp32 accumulation)
+ *   y_e      = sh * (W_d h8)       (W the requantised matrices, exact
+ *                                   products, fp32 accumulation)
  * then the combine of moe_q4_forward.  Both divisions are correctly rounded
- * fp32; the e4m3 and e2m1 roundings are to nearest, ties to the even
- * mantissa, saturating at +-448 and +-6. */
-typedef struct moe_mxfp4 {
-  const uint8_t* codes;  /* [rows/16][K/32][16][16] e2m1 codes, 16-byte aligned:
-                            the Q4 code layout, element 2i in the low nibble */
+ * fp32. */
+typedef struct moe_mx {
+  const uint8_t* codes;  /* [rows/16][K/32][16][B] element codes, 16-byte
+                            aligned: the Q4 code layout with B bytes per
+                            block, B = 16 for MXFP4 (element 2i in the low
+                            nibble of byte i) and 32 for MXFP8 (element i
+                            at byte i)                                    */
   const uint8_t* exps;   /* [rows/16][K/32][16] biased block exponents, the
                             Q4 scale layout with one byte per block      */
-} moe_mxfp4;
+} moe_mx;
 
-typedef struct moe_mxfp4_weights {
-  moe_mxfp4 w13;  /* [E][2I][d]       */
-  moe_mxfp4 w2;   /* [E][d][I]        */
-  moe_mxfp4 s13;  /* [2*I_shared][d]  */
-  moe_mxfp4 s2;   /* [d][I_shared]    */
-} moe_mxfp4_weights;
+typedef struct moe_mx_weights {
+  moe_mx w13;  /* [E][2I][d]       */
+  moe_mx w2;   /* [E][d][I]        */
+  moe_mx s13;  /* [2*I_shared][d]  */
+  moe_mx s2;   /* [d][I_shared]    */
+} moe_mx_weights;
 
-/* Requantise Q4 blocks to MXFP4 on the device (the one-time load step).
- * Block b of (qs, scales) becomes block b of (codes_out, exps_out), so it
- * works on the packed 16-row groups (giving the moe_mxfp4 layout) and on
- * row-major arrays alike; n_mats * rows * K / 32 blocks in total.  For a
- * block of values w_i = (q_i - 8) * scale: E = floor(log2 max_i |w_i|) - 2
- * (-127 for an all-zero block), element i = e2m1(w_i / 2^E), exponent byte
- * E + 127.  DEVICE arrays owned by the caller: qs and codes_out 16-byte
- * aligned [blocks][16], scales uint16 [blocks] (2-byte aligned), exps_out
- * uint8 [blocks]; outputs must not overlap inputs.
+/* Requantise Q4 blocks to MXFP4 (moe_q4_to_mxfp4) or MXFP8 (moe_q4_to_mxfp8)
+ * on the device (the one-time load step).  Block b of (qs, scales) becomes
+ * block b of (codes_out, exps_out), so it works on the packed 16-row groups
+ * (giving the moe_mx layout) and on row-major arrays alike; n_mats * rows *
+ * K / 32 blocks in total.  DEVICE arrays owned by the caller: qs and
+ * codes_out 16-byte aligned ([blocks][16] in, [blocks][16] or [blocks][32]
+ * out), scales uint16 [blocks] (2-byte aligned), exps_out uint8 [blocks];
+ * outputs must not overlap inputs.
  * MOE_EINVAL: a size < 1, a NULL pointer, overlapping ranges;
  * MOE_EUNSUPPORTED: rows % 16 != 0, K % 32 != 0, or rows or K > 2^24;
  * MOE_EALIGN; MOE_EHIP. */
 int moe_q4_to_mxfp4(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs, const uint16_t* scales,
                     uint8_t* codes_out, uint8_t* exps_out, void* stream);
+int moe_q4_to_mxfp8(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs, const uint16_t* scales,
+                    uint8_t* codes_out, uint8_t* exps_out, void* stream);
 
-/* The activation step of the W4A8 layer on its own: `rows` rows of K values
- * (bf16 bits, or fp16 bits when in_is_fp16 != 0) -> e4m3 codes (uint8
- * [rows][K]) and fp32 row scales s = amax / 448 (1 for an all-zero row),
- * code = e4m3(x / s) as above.  DEVICE arrays owned by the caller, 16-byte
- * aligned (scales 4-byte).  MOE_EINVAL: rows or K < 1, a NULL pointer;
- * MOE_EUNSUPPORTED: K % 4 != 0 or rows * K >= 2^31; MOE_EALIGN; MOE_EHIP. */
+/* The activation step of the fp8 variants on its own: `rows` rows of K
+ * values (bf16 bits, or fp16 bits when in_is_fp16 != 0) -> e4m3 codes
+ * (uint8 [rows][K]) and fp32 row scales s = amax / 448 (1 for an all-zero
+ * row), code = e4m3(x / s) as above.  DEVICE arrays owned by the caller,
+ * 16-byte aligned (scales 4-byte).  MOE_EINVAL: rows or K < 1, a NULL
+ * pointer; MOE_EUNSUPPORTED: K % 4 != 0 or rows * K >= 2^31; MOE_EALIGN;
+ * MOE_EHIP. */
 int moe_rows_to_fp8(int32_t rows, int32_t K, const uint16_t* in, int in_is_fp16, uint8_t* codes_out,
                     float* scales_out, void* stream);
 
-/* Bytes of scratch moe_w4a8_forward needs, 0 if the shape or flags are
- * unsupported (see there). */
+/* Bytes of scratch moe_w4a8_forward / moe_w8a8_forward need (the same for
+ * both), 0 if the shape or flags are unsupported (see there). */
 size_t moe_w4a8_scratch_bytes(const moe_dims* dims, uint32_t flags);
+size_t moe_w8a8_scratch_bytes(const moe_dims* dims, uint32_t flags);
 
-/* The W4A8 expert layer (formula above) on the grouped path.  Arguments as
- * for moe_q4_forward, with MXFP4 weights (from moe_q4_to_mxfp4); the routing
- * workspace must hold moe_build_descriptors' output for the same topk ids
- * and flags.  topk_ids is checked but not read (the routing build holds
- * it).  MOE_EUNSUPPORTED also when flags select the small-T path (pass
- * MOE_FLAG_FORCE_GROUPED for T <= MOE_GEMV_MAX_T) or d, I or I_shared is not
- * a multiple of 128; MOE_EINVAL, MOE_EALIGN (exps need no alignment),
- * MOE_ENOSPACE (scratch below moe_w4a8_scratch_bytes), MOE_EHIP. */
+/* The W4A8 (MXFP4 weights from moe_q4_to_mxfp4) and W8A8 (MXFP8 weights
+ * from moe_q4_to_mxfp8) expert layers (formula above) on the grouped path.
+ * Arguments as for moe_q4_forward; the routing workspace must hold
+ * moe_build_descriptors' output for the same topk ids and flags.  topk_ids
+ * is checked but not read (the routing build holds it).  MOE_EUNSUPPORTED
+ * also when flags select the small-T path (pass MOE_FLAG_FORCE_GROUPED for
+ * T <= MOE_GEMV_MAX_T), when d, I or I_shared is not a multiple of 128, and
+ * for W8A8 when 2 * max(I, I_shared) * d >= 2^31 (32-bit offsets into one
+ * expert's fp8 codes); MOE_EINVAL, MOE_EALIGN (exps need no alignment),
+ * MOE_ENOSPACE (scratch below the _scratch_bytes query), MOE_EHIP. */
 int moe_w4a8_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
-                     const void* routing, size_t routing_bytes, const moe_mxfp4_weights* w, float* y,
+                     const void* routing, size_t routing_bytes, const moe_mx_weights* w, float* y,
+                     void* scratch, size_t scratch_bytes, uint32_t flags, void* stream);
+int moe_w8a8_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
+                     const void* routing, size_t routing_bytes, const moe_mx_weights* w, float* y,
                      void* scratch, size_t scratch_bytes, uint32_t flags, void* stream);
 
 /* Static string for a return code; never NULL. */

@@ -16,5 +16,6 @@ from .abi import (  # noqa: F401
     EXPORTED_SYMBOLS,
     moe_decode_ctx_workspace_bytes, moe_decode_ctx_create, moe_decode_ctx_run, moe_decode_ctx_destroy,
     moe_rmsnorm_bf16, moe_q4_pack, moe_layer_forward_noalloc, MOE_NOALLOC_MAX_BYTES,
-    moe_q4_to_mxfp4, moe_rows_to_fp8, moe_w4a8_scratch_bytes, moe_w4a8_forward,
+    moe_q4_to_mxfp4, moe_q4_to_mxfp8, moe_rows_to_fp8, moe_w4a8_scratch_bytes, moe_w8a8_scratch_bytes,
+    moe_w4a8_forward, moe_w8a8_forward,
 )

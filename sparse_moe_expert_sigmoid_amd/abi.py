@@ -30,7 +30,8 @@ EXPORTED_SYMBOLS = (
     "moe_route", "moe_build_descriptors", "moe_q4_forward", "moe_q4_forward_residual", "moe_layer_forward", "moe_strerror",
     "moe_decode_ctx_workspace_bytes", "moe_decode_ctx_create", "moe_decode_ctx_run", "moe_decode_ctx_destroy",
     "moe_rmsnorm_bf16", "moe_q4_pack", "moe_layer_forward_noalloc",
-    "moe_q4_to_mxfp4", "moe_rows_to_fp8", "moe_w4a8_scratch_bytes", "moe_w4a8_forward",
+    "moe_q4_to_mxfp4", "moe_q4_to_mxfp8", "moe_rows_to_fp8", "moe_w4a8_scratch_bytes", "moe_w8a8_scratch_bytes",
+    "moe_w4a8_forward", "moe_w8a8_forward",
 )
 MOE_NOALLOC_MAX_BYTES = 64 << 20
 
@@ -136,15 +137,18 @@ def lib() -> ctypes.CDLL:
     L.moe_layer_forward_noalloc.restype = c_int
     L.moe_q4_pack.argtypes = [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     L.moe_q4_pack.restype = c_int
-    L.moe_q4_to_mxfp4.argtypes = [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
-    L.moe_q4_to_mxfp4.restype = c_int
+    for name in ("moe_q4_to_mxfp4", "moe_q4_to_mxfp8"):
+        getattr(L, name).argtypes = [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        getattr(L, name).restype = c_int
     L.moe_rows_to_fp8.argtypes = [c_int32, c_int32, c_void_p, c_int, c_void_p, c_void_p, c_void_p]
     L.moe_rows_to_fp8.restype = c_int
-    L.moe_w4a8_scratch_bytes.argtypes = [D, c_uint32]
-    L.moe_w4a8_scratch_bytes.restype = c_size_t
-    L.moe_w4a8_forward.argtypes = [D, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, POINTER(_MxWeights),
-                                   c_void_p, c_void_p, c_size_t, c_uint32, c_void_p]
-    L.moe_w4a8_forward.restype = c_int
+    for v in ("w4a8", "w8a8"):
+        getattr(L, f"moe_{v}_scratch_bytes").argtypes = [D, c_uint32]
+        getattr(L, f"moe_{v}_scratch_bytes").restype = c_size_t
+        getattr(L, f"moe_{v}_forward").argtypes = [D, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                                   POINTER(_MxWeights), c_void_p, c_void_p, c_size_t, c_uint32,
+                                                   c_void_p]
+        getattr(L, f"moe_{v}_forward").restype = c_int
     L.moe_strerror.argtypes = [c_int]
     L.moe_strerror.restype = c_char_p
     _lib = L
@@ -316,10 +320,18 @@ def moe_layer_forward_noalloc(dims, x, w_router, bias, weights, y, topk_ids, top
 
 def moe_q4_to_mxfp4(n_mats: int, rows: int, K: int, qs, scales, codes_out, exps_out, stream=None,
                     check: bool = True) -> int:
-    """Q4 blocks -> MXFP4 blocks (e2m1 codes, biased block exponents), block for block, on the device."""
+    """Q4 blocks -> MXFP4 blocks (16 bytes of e2m1 codes, biased block exponents), block for block."""
     rc = lib().moe_q4_to_mxfp4(n_mats, rows, K, _ptr(qs), _ptr(scales), _ptr(codes_out), _ptr(exps_out),
                                _stream(stream))
     return _done(rc, check, "moe_q4_to_mxfp4")
+
+
+def moe_q4_to_mxfp8(n_mats: int, rows: int, K: int, qs, scales, codes_out, exps_out, stream=None,
+                    check: bool = True) -> int:
+    """Q4 blocks -> MXFP8 blocks (32 bytes of e4m3 codes, biased block exponents), block for block."""
+    rc = lib().moe_q4_to_mxfp8(n_mats, rows, K, _ptr(qs), _ptr(scales), _ptr(codes_out), _ptr(exps_out),
+                               _stream(stream))
+    return _done(rc, check, "moe_q4_to_mxfp8")
 
 
 def moe_rows_to_fp8(rows: int, K: int, x, codes_out, scales_out, in_is_fp16: bool = False, stream=None,
@@ -334,15 +346,34 @@ def moe_w4a8_scratch_bytes(dims, flags: int = 0) -> int:
     return lib().moe_w4a8_scratch_bytes(ctypes.byref(Dims.of(dims)), flags)
 
 
+def moe_w8a8_scratch_bytes(dims, flags: int = 0) -> int:
+    return lib().moe_w8a8_scratch_bytes(ctypes.byref(Dims.of(dims)), flags)
+
+
 def _mx_weights(w) -> _MxWeights:
     """w: mapping with w13_codes, w13_exps, w2_codes, w2_exps, s13_codes, s13_exps, s2_codes, s2_exps."""
     return _MxWeights(*[_Mx(_ptr(w[n + "_codes"]), _ptr(w[n + "_exps"])) for n in ("w13", "w2", "s13", "s2")])
 
 
+def _fp8act_forward(variant, dims, x, topk_ids, topk_w, routing, weights, y, scratch, routing_bytes,
+                    scratch_bytes, flags, stream, check):
+    ws = weights if isinstance(weights, _MxWeights) else _mx_weights(weights)
+    fn = getattr(lib(), f"moe_{variant}_forward")
+    rc = fn(ctypes.byref(Dims.of(dims)), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(routing),
+            _nbytes(routing, routing_bytes), ctypes.byref(ws), _ptr(y), _ptr(scratch), _nbytes(scratch, scratch_bytes),
+            flags, _stream(stream))
+    return _done(rc, check, f"moe_{variant}_forward")
+
+
 def moe_w4a8_forward(dims, x, topk_ids, topk_w, routing, weights, y, scratch, routing_bytes=None,
                      scratch_bytes=None, flags: int = 0, stream=None, check: bool = True) -> int:
-    ws = weights if isinstance(weights, _MxWeights) else _mx_weights(weights)
-    rc = lib().moe_w4a8_forward(ctypes.byref(Dims.of(dims)), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(routing),
-                                _nbytes(routing, routing_bytes), ctypes.byref(ws), _ptr(y), _ptr(scratch),
-                                _nbytes(scratch, scratch_bytes), flags, _stream(stream))
-    return _done(rc, check, "moe_w4a8_forward")
+    """The W4A8 layer (MXFP4 weights from moe_q4_to_mxfp4, fp8 activations)."""
+    return _fp8act_forward("w4a8", dims, x, topk_ids, topk_w, routing, weights, y, scratch, routing_bytes,
+                           scratch_bytes, flags, stream, check)
+
+
+def moe_w8a8_forward(dims, x, topk_ids, topk_w, routing, weights, y, scratch, routing_bytes=None,
+                     scratch_bytes=None, flags: int = 0, stream=None, check: bool = True) -> int:
+    """The W8A8 layer (MXFP8 weights from moe_q4_to_mxfp8, fp8 activations)."""
+    return _fp8act_forward("w8a8", dims, x, topk_ids, topk_w, routing, weights, y, scratch, routing_bytes,
+                           scratch_bytes, flags, stream, check)

@@ -125,12 +125,15 @@ bool q4_aligned(const moe_q4& q) { return aligned(q.qs, 16) && aligned(q.scales,
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
-// W4A8 variant: grouped path only, every K a whole number of 128-value MFMA steps.
-int check_w4a8(const moe_dims* d, uint32_t flags) {
+// fp8-activation variants: grouped path only, every K a whole number of 128-value MFMA steps; MXFP8
+// codes take twice the bytes of Q4 codes, so one expert's gate+up stack (2 I d bytes) must leave 31 bits.
+int check_fp8act(const moe_dims* d, uint32_t flags, bool fp8) {
   const int rc = check_dims(d, flags);
   if (rc) return rc;
   if (choose_path(d, flags) != 1) return MOE_EUNSUPPORTED;
   if (d->d % 128 || d->I % 128 || d->I_shared % 128) return MOE_EUNSUPPORTED;
+  const long long Imax = d->I > d->I_shared ? d->I : d->I_shared;
+  if (fp8 && 2 * Imax * d->d >= (1LL << 31)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -549,20 +552,32 @@ int moe_q4_pack(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs_in, c
                                     static_cast<hipStream_t>(stream)));
 }
 
-int moe_q4_to_mxfp4(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs, const uint16_t* scales,
-                    uint8_t* codes_out, uint8_t* exps_out, void* stream) {
+namespace {
+int q4_to_mx(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs, const uint16_t* scales, uint8_t* codes_out,
+             uint8_t* exps_out, bool fp8, void* stream) {
   if (n_mats < 1 || rows < 1 || K < 1 || !qs || !scales || !codes_out || !exps_out) return MOE_EINVAL;
   if (rows % 16 || K % 32 || rows > (1 << 24) || K > (1 << 24)) return MOE_EUNSUPPORTED;
   if (!aligned(qs, 16) || !aligned(codes_out, 16) || !aligned(scales, 2)) return MOE_EALIGN;
   const size_t nblocks = (size_t)n_mats * (size_t)rows * (size_t)(K / 32);
   const uintptr_t qi = (uintptr_t)qs, si = (uintptr_t)scales, co = (uintptr_t)codes_out, eo = (uintptr_t)exps_out;
-  const size_t qb = 16 * nblocks, sb = 2 * nblocks, eb = nblocks;
+  const size_t qb = 16 * nblocks, sb = 2 * nblocks, cb = (fp8 ? 32 : 16) * nblocks, eb = nblocks;
   auto overlap = [](uintptr_t a, size_t na, uintptr_t b, size_t nb) { return a < b + nb && b < a + na; };
-  if (overlap(co, qb, qi, qb) || overlap(co, qb, si, sb) || overlap(eo, eb, qi, qb) || overlap(eo, eb, si, sb) ||
-      overlap(co, qb, eo, eb))
+  if (overlap(co, cb, qi, qb) || overlap(co, cb, si, sb) || overlap(eo, eb, qi, qb) || overlap(eo, eb, si, sb) ||
+      overlap(co, cb, eo, eb))
     return MOE_EINVAL;
   (void)hipGetLastError();
-  return hip_rc(moe::launch_q4_to_mx(nblocks, qs, scales, codes_out, exps_out, static_cast<hipStream_t>(stream)));
+  return hip_rc(moe::launch_q4_to_mx(nblocks, qs, scales, codes_out, exps_out, fp8, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int moe_q4_to_mxfp4(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs, const uint16_t* scales,
+                    uint8_t* codes_out, uint8_t* exps_out, void* stream) {
+  return q4_to_mx(n_mats, rows, K, qs, scales, codes_out, exps_out, false, stream);
+}
+
+int moe_q4_to_mxfp8(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs, const uint16_t* scales,
+                    uint8_t* codes_out, uint8_t* exps_out, void* stream) {
+  return q4_to_mx(n_mats, rows, K, qs, scales, codes_out, exps_out, true, stream);
 }
 
 int moe_rows_to_fp8(int32_t rows, int32_t K, const uint16_t* in, int in_is_fp16, uint8_t* codes_out,
@@ -576,23 +591,29 @@ int moe_rows_to_fp8(int32_t rows, int32_t K, const uint16_t* in, int in_is_fp16,
 }
 
 size_t moe_w4a8_scratch_bytes(const moe_dims* dims, uint32_t flags) {
-  if (check_w4a8(dims, flags)) return 0;
+  if (check_fp8act(dims, flags, false)) return 0;
   return w4a8_layout(dims).total;
 }
 
-int moe_w4a8_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
-                     const void* routing, size_t routing_bytes, const moe_mxfp4_weights* w, float* y,
-                     void* scratch, size_t scratch_bytes, uint32_t flags, void* stream) {
-  const int rc = check_w4a8(dims, flags);
+size_t moe_w8a8_scratch_bytes(const moe_dims* dims, uint32_t flags) {
+  if (check_fp8act(dims, flags, true)) return 0;
+  return w4a8_layout(dims).total;
+}
+
+namespace {
+int fp8act_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
+                   const void* routing, size_t routing_bytes, const moe_mx_weights* w, float* y, void* scratch,
+                   size_t scratch_bytes, uint32_t flags, bool fp8, void* stream) {
+  const int rc = check_fp8act(dims, flags, fp8);
   if (rc) return rc;
   if (!x_bf16 || !topk_ids || !topk_w || !routing || !w || !y || !scratch) return MOE_EINVAL;
-  const moe_mxfp4* m[4] = {&w->w13, &w->w2, &w->s13, &w->s2};
-  for (const moe_mxfp4* p : m)
+  const moe_mx* m[4] = {&w->w13, &w->w2, &w->s13, &w->s2};
+  for (const moe_mx* p : m)
     if (!p->codes || !p->exps) return MOE_EINVAL;
   if (!aligned(x_bf16, 16) || !aligned(y, 16) || !aligned(scratch, 16) || !aligned(routing, 16) ||
       !aligned(topk_ids, 4) || !aligned(topk_w, 4))
     return MOE_EALIGN;
-  for (const moe_mxfp4* p : m)
+  for (const moe_mx* p : m)
     if (!aligned(p->codes, 16)) return MOE_EALIGN;
   const Layout L = routing_layout(dims);
   if (routing_bytes < L.total) return MOE_ENOSPACE;
@@ -614,7 +635,22 @@ int moe_w4a8_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t
                           w->s13.codes, w->s13.exps, w->s2.codes, w->s2.exps};
   (void)hipGetLastError();
   return hip_rc(moe::launch_w4a8_forward(shape_of(dims), x_bf16, routing_ptrs(const_cast<void*>(routing), L), mw, o,
-                                         topk_w, y, flags, static_cast<hipStream_t>(stream)));
+                                         topk_w, y, flags, fp8, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int moe_w4a8_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
+                     const void* routing, size_t routing_bytes, const moe_mx_weights* w, float* y,
+                     void* scratch, size_t scratch_bytes, uint32_t flags, void* stream) {
+  return fp8act_forward(dims, x_bf16, topk_ids, topk_w, routing, routing_bytes, w, y, scratch, scratch_bytes, flags,
+                        false, stream);
+}
+
+int moe_w8a8_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
+                     const void* routing, size_t routing_bytes, const moe_mx_weights* w, float* y,
+                     void* scratch, size_t scratch_bytes, uint32_t flags, void* stream) {
+  return fp8act_forward(dims, x_bf16, topk_ids, topk_w, routing, routing_bytes, w, y, scratch, scratch_bytes, flags,
+                        true, stream);
 }
 
 const char* moe_strerror(int code) {

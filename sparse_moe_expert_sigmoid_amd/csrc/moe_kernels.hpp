@@ -83,7 +83,7 @@ hipError_t launch_q4_pack(size_t n_mats, int rows, int K, const uint8_t* qs_in, 
 
 // w4a8.hip: MXFP4 weights x FP8 activations on the grouped path
 struct MxWeights {
-  const uint8_t* w13_codes; const uint8_t* w13_exp;   // e2m1 codes / block exponents, 16-row-group layout
+  const uint8_t* w13_codes; const uint8_t* w13_exp;   // MXFP4 or MXFP8 codes / block exponents, 16-row groups
   const uint8_t* w2_codes;  const uint8_t* w2_exp;
   const uint8_t* s13_codes; const uint8_t* s13_exp;
   const uint8_t* s2_codes;  const uint8_t* s2_exp;
@@ -95,16 +95,16 @@ struct W4A8Scratch {
   uint8_t* h8_s; float* hs_s;  // [T][Is], [T]
   _Float16* y_pair; _Float16* y_s;  // [P][d] (sorted rows), [T][d]
 };
-// nblocks Q4 blocks (16 code bytes + one fp16 scale each) -> e2m1 codes (same nibble order) and
-// biased block exponents, block b to block b
+// nblocks Q4 blocks (16 code bytes + one fp16 scale each) -> MXFP4 (16 bytes of e2m1 codes, same nibble
+// order) or with fp8 MXFP8 (32 e4m3 codes), and biased block exponents, block b to block b
 hipError_t launch_q4_to_mx(size_t nblocks, const uint8_t* qs, const uint16_t* sc, uint8_t* codes, uint8_t* exps,
-                           hipStream_t st);
+                           bool fp8, hipStream_t st);
 // rows x K values (bf16 bits, or fp16 when in_f16; K % 4 == 0) -> e4m3 codes and fp32 row scales
 hipError_t launch_rows_fp8(const uint16_t* in, bool in_f16, int rows, int K, uint8_t* out, float* scale,
                            hipStream_t st);
-// d, I, Is % 128 == 0; routing built for the grouped path
+// d, I, Is % 128 == 0; routing built for the grouped path; fp8: MXFP8 weights (W8A8), else MXFP4 (W4A8)
 hipError_t launch_w4a8_forward(const Shape& s, const uint16_t* x, const Routing& r, const MxWeights& w,
-                               const W4A8Scratch& o, const float* topk_w, float* y, uint32_t flags,
+                               const W4A8Scratch& o, const float* topk_w, float* y, uint32_t flags, bool fp8,
                                hipStream_t st);
 
 // norm.hip

@@ -35,20 +35,20 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-constexpr int kMxBM = kGroupedBM;            // rows per M-tile
+constexpr int kMxBM = kGroupedBM;            // rows per M-tile of the routing build
 constexpr int kMxBK = 128;                   // K per iteration: one MFMA
 constexpr int kMxWaves = kGroupedWaves;
 constexpr int kMxThreads = 64 * kMxWaves;
 constexpr int kMxRowBytes = kMxBK;           // fp8 activations: 128 B per row and iteration
-constexpr int kMxTileBytes = kMxBM * kMxRowBytes;             // 12 KB
-constexpr int kMxTileLoads = kMxTileBytes / (kMxThreads * 16);  // 16-byte loads into LDS per lane per tile
-constexpr int kMxRowsPerWave = kMxBM / kMxWaves;
 constexpr int kMxGateUpBandCols = kGateUpBandCols;
 constexpr int kMxDownBandCols = kDownBandCols;
-constexpr int kMxDownOutBytes = kMxBM * kMxDownBandCols * 2;
 constexpr uint32_t kMxOffsetOOB = 0xFFFFFFF0u;
-static_assert(kMxTileLoads * kMxThreads * 16 == kMxTileBytes, "whole tile per load round");
-static_assert(kMxRowsPerWave == 8 * kMxTileLoads, "each load instruction fills 8 rows");
+// Rows a workgroup computes: the whole 96-row M-tile, or (BME = 48) one half of it, so that the MXFP8
+// weights' doubled registers fit beside the accumulators.  The activation tile arrives in BME / 8
+// load instructions of 8 rows x 128 B; wavefront w issues instructions w, w + 4, w + 8.
+template <int BME> constexpr int kMxLoadInst = BME / 8;
+template <int BME> constexpr int kMxLoadsPerWave = (BME / 8 + kMxWaves - 1) / kMxWaves;
+static_assert(64 * 16 == 8 * kMxRowBytes, "one load instruction fills 8 rows");
 
 // LDS tile: row r holds its 128 fp8 values as 8 chunks of 16 B, chunk c in slot c ^ ((r >> 1) & 7):
 // the 16 lanes that read one chunk of 16 consecutive rows (two rows per 256-byte bank line) hit 16
@@ -81,11 +81,18 @@ struct MxArgs {
 
 __device__ __forceinline__ int ufl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <bool GATEUP, int NMT>
+// Weight element formats (the MFMA's operand format codes): e2m1 (MXFP4) or e4m3 (MXFP8).
+constexpr int kFmtFp4 = 4;
+constexpr int kFmtFp8 = 0;
+// Per weight format: bytes of one 32-element block, and the 16-byte loads a lane makes per slice and step.
+template <int WF> constexpr int kBlockBytes = WF == kFmtFp4 ? 16 : 32;
+template <int WF> constexpr int kWLoads = WF == kFmtFp4 ? 1 : 2;
+
+template <bool GATEUP, int WF, int BME, int NMT>
 __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As0, char* As1, char* Aout,
                                         const __amdgpu_buffer_rsrc_t& rq,
                                         const __amdgpu_buffer_rsrc_t& rs, const __amdgpu_buffer_rsrc_t& ra,
-                                        const uint32_t (&aoff)[kMxTileLoads], const int (&qns)[4],
+                                        const uint32_t (&aoff)[kMxLoadsPerWave<BME>], const int (&qns)[4],
                                         const int (&sns)[4], const bool (&nok)[4], int nit, int c0, int wave,
                                         int lane, int mlen, int rbase, int m0, int Iw, bool shared) {
   const int n = lane & 15, G = lane >> 4;
@@ -95,16 +102,26 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As0, char* As1, c
   auto ring = [&](int buf) __attribute__((always_inline)) { return buf == 0 ? As0 : As1; };
   auto issue_a = [&](int it, int buf) {
 #pragma unroll
-    for (int i = 0; i < kMxTileLoads; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_void*)(ring(buf) + (kMxRowsPerWave * wave + 8 * i) * kMxRowBytes), 16, (int)aoff[i],
-          it * kMxBK, 0, 0);
+    for (int i = 0; i < kMxLoadsPerWave<BME>; ++i) {
+      const int inst = wave + kMxWaves * i;  // uniform
+      if (inst < kMxLoadInst<BME>)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(ring(buf) + 8 * inst * kMxRowBytes), 16,
+                                                 (int)aoff[i], it * kMxBK, 0, 0);
+    }
   };
-  // this lane's weight block of every slice (row n, block 4it + G: 16 B of codes, one exponent byte)
-  auto load_w = [&](int it, u32x4* qd, uint32_t* sd) {
+  // This lane's weights of every slice, from the step's 4 blocks of 16 rows (4 KiB-aligned runs of
+  // 4 x 16 x kBlockBytes bytes), and the exponent byte of block G of row n.  MXFP4: lane (n, G) takes
+  // the 16 bytes of block G of row n (its 32 values in order).  MXFP8: lane (n, G) takes values
+  // 16G .. 16G+15 and 64 + 16G .. 64 + 16G + 15 of the 128 (the MFMA's fp8 operand layout): half G % 2
+  // of blocks G / 2 and 2 + G / 2.
+  constexpr int BB = kBlockBytes<WF>, NW = kWLoads<WF>;
+  const int wo0 = WF == kFmtFp4 ? 16 * lane : (G >> 1) * 16 * BB + n * BB + 16 * (G & 1);
+  auto load_w = [&](int it, u32x4 (*qd)[NW], uint32_t* sd) {
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
-      qd[ns] = __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * lane, qns[ns] + it * 1024, 0);
+#pragma unroll
+      for (int h = 0; h < NW; ++h)
+        qd[ns][h] = __builtin_amdgcn_raw_buffer_load_b128(rq, wo0 + h * 2 * 16 * BB, qns[ns] + it * 64 * BB, 0);
       sd[ns] = __builtin_amdgcn_raw_buffer_load_b8(rs, lane, sns[ns] + it * 64, 0);
     }
   };
@@ -123,11 +140,14 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As0, char* As1, c
     const u32x4 hi = *reinterpret_cast<const u32x4*>(At + mt * 16 * kMxRowBytes + off1);
     return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
-  auto compute = [&](int buf, const u32x4* q, const uint32_t* sc) __attribute__((always_inline)) {
+  auto compute = [&](int buf, const u32x4 (*q)[NW], const uint32_t* sc) __attribute__((always_inline)) {
     const char* At = ring(buf);
     v8i w[4];
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) w[ns] = v8i{(int)q[ns][0], (int)q[ns][1], (int)q[ns][2], (int)q[ns][3], 0, 0, 0, 0};
+    for (int ns = 0; ns < 4; ++ns) {
+      const u32x4 lo = q[ns][0], hi = NW > 1 ? q[ns][NW - 1] : u32x4{0u, 0u, 0u, 0u};
+      w[ns] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
     v8i x0 = aread(At, 0);
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
@@ -135,9 +155,9 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As0, char* As1, c
       if (mt + 1 < NMT) x1 = aread(At, mt + 1);
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns)
-        // weights (e2m1, format 4) as the A operand with their block exponent; activations (e4m3,
-        // format 0) as the B operand with exponent 127 (scale 1)
-        acc[mt][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[ns], x0, acc[mt][ns], 4, 0, 0,
+        // weights (format WF) as the A operand with their block exponent; activations (e4m3, format 0)
+        // as the B operand with exponent 127 (scale 1)
+        acc[mt][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[ns], x0, acc[mt][ns], WF, kFmtFp8, 0,
                                                                          (int)sc[ns], 0, 127);
       if (mt + 1 < NMT) x0 = x1;
     }
@@ -145,7 +165,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As0, char* As1, c
 
   // Two-stage pipeline: while step `it` is computed, step it+1's activation tile (LDS) and weight
   // blocks (registers) are in flight.
-  u32x4 q[2][4];
+  u32x4 q[2][4][NW];
   uint32_t sc[2][4];
   issue_a(0, 0);
   load_w(0, q[0], sc[0]);
@@ -230,12 +250,16 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As0, char* As1, c
   }
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int WF>
 __global__ __launch_bounds__(kMxThreads, 8 / kMxWaves) void k_grouped_mx(MxArgs a) {
+  // MXFP8 weights: every M-tile is two work items of 48 rows (launch indices b and b + 8 of the same
+  // XCD, adjacent in time, so the second reads the weight band from L2)
+  constexpr bool HALF = WF == kFmtFp8;
+  constexpr int BME = HALF ? kMxBM / 2 : kMxBM;
   constexpr int BANDW = GATEUP ? kMxGateUpBandCols : kMxDownBandCols;
-  __shared__ __attribute__((aligned(1024))) char As0[kMxTileBytes];
-  __shared__ __attribute__((aligned(1024))) char As1[kMxTileBytes];
-  __shared__ __attribute__((aligned(1024))) char Aout[GATEUP ? 16 : kMxDownOutBytes];
+  __shared__ __attribute__((aligned(1024))) char As0[BME * kMxRowBytes];
+  __shared__ __attribute__((aligned(1024))) char As1[BME * kMxRowBytes];
+  __shared__ __attribute__((aligned(1024))) char Aout[GATEUP ? 16 : BME * kMxDownBandCols * 2];
   __shared__ int s_prefix[kMaxExperts + 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = ufl(tid >> 6);
   const int ngroups = a.E + 1;
@@ -243,10 +267,12 @@ __global__ __launch_bounds__(kMxThreads, 8 / kMxWaves) void k_grouped_mx(MxArgs 
   __syncthreads();
   const int nb = a.nbands;
   const int n_mt = ufl(s_prefix[ngroups]);
+  const int bx = blockIdx.x;
+  const int hsel = HALF ? (bx >> 3) & 1 : 0;
   // work item -> (group rank, band, M-tile), as on the W4A16 path
   int rank, band, mtile;
   {
-    const int bid = blockIdx.x;
+    const int bid = HALF ? (((bx >> 4) << 3) | (bx & 7)) : bx;
     const int order = (a.order == 1 && nb % 8 != 0) ? 2 : a.order;
     const int nbx = order == 1 ? nb / 8 : nb;
     int item;
@@ -281,23 +307,25 @@ __global__ __launch_bounds__(kMxThreads, 8 / kMxWaves) void k_grouped_mx(MxArgs 
   const int Kdim = GATEUP ? a.d : Iw;
   const int Ndim = GATEUP ? Iw : a.d;
   if (band * BANDW >= Ndim) return;
-  const int m0 = mtile * kMxBM;
-  const int mlen = min(kMxBM, cnt - m0);
+  const int m0 = mtile * kMxBM + hsel * BME;
+  if (cnt - m0 <= 0) return;  // the lower half of a tile with at most 48 rows
+  const int mlen = min(BME, cnt - m0);
   const int gbase = shared ? 0 : ufl(a.offsets[g]);
   const int rbase = gbase + m0;
   const uint32_t wrows = GATEUP ? 2u * (uint32_t)Iw : (uint32_t)a.d;
-  const uint32_t qstride = (uint32_t)Kdim / 2, nkb = (uint32_t)Kdim / 32;
+  const uint32_t qstride = (uint32_t)Kdim / 32 * kBlockBytes<WF>, nkb = (uint32_t)Kdim / 32;
   const uint8_t* Wq = shared ? a.ws_codes : a.wr_codes + (size_t)g * wrows * qstride;
   const uint8_t* We = shared ? a.ws_exp : a.wr_exp + (size_t)g * wrows * nkb;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Wq, wrows * qstride);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(We, wrows * nkb);
   const __amdgpu_buffer_rsrc_t ra = shared ? make_rsrc(a.a_s, a.a_s_bytes) : make_rsrc(a.a_r, a.a_r_bytes);
 
-  // activation rows staged by this wavefront: rows kMxRowsPerWave*wave + 8i + lane/8, slot lane%8
-  uint32_t aoff[kMxTileLoads];
+  // activation rows staged by this wavefront: rows 8 inst + lane/8 of its load instructions inst =
+  // wave + 4i, slot lane%8
+  uint32_t aoff[kMxLoadsPerWave<BME>];
 #pragma unroll
-  for (int i = 0; i < kMxTileLoads; ++i) {
-    const int row = kMxRowsPerWave * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < kMxLoadsPerWave<BME>; ++i) {
+    const int row = 8 * (wave + kMxWaves * i) + (lane >> 3);
     const int rr = row < mlen ? row : 0;
     uint32_t arow;
     if (GATEUP)
@@ -331,80 +359,34 @@ __global__ __launch_bounds__(kMxThreads, 8 / kMxWaves) void k_grouped_mx(MxArgs 
       rowbase[ns] = nok[ns] ? col : 0;
     }
   }
-  // codes [rows/16][K/32][16][16 B] and exponents [rows/16][K/32][16]: slice ns's iteration `it` is
-  // one KiB of codes from ((rowbase/16)*(K/32) + 4 it)*256 and 64 exponent bytes from
-  // ((rowbase/16)*(K/32) + 4 it)*16; lane l takes code bytes 16 l and exponent byte l
+  // codes [rows/16][K/32][16][block bytes] and exponents [rows/16][K/32][16]: slice ns's iteration
+  // `it` is 64 blocks' worth of codes from ((rowbase/16)*(K/32) + 4 it)*16 blocks and 64 exponent bytes
+  // from ((rowbase/16)*(K/32) + 4 it)*16; lane l takes exponent byte l
   int qns[4], sns[4];
 #pragma unroll
   for (int ns = 0; ns < 4; ++ns) {
-    qns[ns] = ufl((int)((uint32_t)(rowbase[ns] / 16) * nkb * 256u));
+    qns[ns] = ufl((int)((uint32_t)(rowbase[ns] / 16) * nkb * 16u * (uint32_t)kBlockBytes<WF>));
     sns[ns] = ufl((int)((uint32_t)(rowbase[ns] / 16) * nkb * 16u));
   }
-  switch ((mlen + 15) >> 4) {
-    case 1: mx_tile<GATEUP, 1>(a, As0, As1, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
-    case 2: mx_tile<GATEUP, 2>(a, As0, As1, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
-    case 3: mx_tile<GATEUP, 3>(a, As0, As1, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
-    case 4: mx_tile<GATEUP, 4>(a, As0, As1, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
-    case 5: mx_tile<GATEUP, 5>(a, As0, As1, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
-    default: mx_tile<GATEUP, 6>(a, As0, As1, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, rbase, m0, Iw, shared); break;
-  }
-}
-
-// ---------------------------------------------------------------------------- requantisation
-// One Q4 block (16 code bytes, fp16 scale) -> 16 bytes of e2m1 codes and the biased shared
-// exponent: values w = (q - 8) * d (exact in fp32), E = floor(log2 max|w|) - 2 (E = -127 for an
-// all-zero block), codes = w / 2^E rounded to the nearest e2m1 value, ties to the even mantissa,
-// saturating at +-6.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float a = fabsf(v);
-  uint32_t c;
-  if (a <= 0.25f) c = 0;
-  else if (a < 0.75f) c = 1;
-  else if (a <= 1.25f) c = 2;
-  else if (a < 1.75f) c = 3;
-  else if (a <= 2.5f) c = 4;
-  else if (a < 3.5f) c = 5;
-  else if (a <= 5.0f) c = 6;
-  else c = 7;
-  return c | (__builtin_signbit(v) ? 8u : 0u);
-}
-
-__global__ __launch_bounds__(256) void k_q4_to_mx(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ sc,
-                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ exps,
-                                                  size_t nblocks) {
-  for (size_t b = (size_t)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += (size_t)gridDim.x * 256) {
-    const u32x4 v = ld16(qs + 16 * b);
-    const float d = (float)__builtin_bit_cast(_Float16, sc[b]);
-    int qmax = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int q = (int)((v[w] >> (4 * j)) & 0xF) - 8;
-        qmax = max(qmax, q < 0 ? -q : q);
-      }
-    const float amax = (float)qmax * fabsf(d);
-    int e = -127;
-    if (amax > 0.f) {
-      int ex;
-      (void)frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1
-      e = min(max(ex - 3, -127), 127);
+#define MX_TILE(NMT)                                                                                      \
+  mx_tile<GATEUP, WF, BME, NMT>(a, As0, As1, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, \
+                                rbase, m0, Iw, shared)
+  const int nmt16 = (mlen + 15) >> 4;
+  if constexpr (BME == 48) {
+    if (nmt16 == 1) MX_TILE(1);
+    else if (nmt16 == 2) MX_TILE(2);
+    else MX_TILE(3);
+  } else {
+    switch (nmt16) {
+      case 1: MX_TILE(1); break;
+      case 2: MX_TILE(2); break;
+      case 3: MX_TILE(3); break;
+      case 4: MX_TILE(4); break;
+      case 5: MX_TILE(5); break;
+      default: MX_TILE(6); break;
     }
-    u32x4 out = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t o = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int q = (int)((v[w] >> (4 * j)) & 0xF) - 8;
-        const float val = ldexpf((float)q * d, -e);  // exact: a power-of-two scaling of an exact product
-        o |= e2m1_code(val) << (4 * j);
-      }
-      out[w] = o;
-    }
-    *reinterpret_cast<u32x4*>(codes + 16 * b) = out;
-    exps[b] = (uint8_t)(e + 127);
   }
+#undef MX_TILE
 }
 
 // ---------------------------------------------------------------------------- row quantisation
@@ -426,6 +408,82 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
     c = c > 0x7Eu ? 0x7Eu : c;
   }
   return c | (__builtin_signbit(v) ? 0x80u : 0u);
+}
+
+// ---------------------------------------------------------------------------- requantisation
+// One Q4 block (16 code bytes, fp16 scale) -> 16 bytes of e2m1 codes and the biased shared
+// exponent: values w = (q - 8) * d (exact in fp32), E = floor(log2 max|w|) - 2 (E = -127 for an
+// all-zero block), codes = w / 2^E rounded to the nearest e2m1 value, ties to the even mantissa,
+// saturating at +-6.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return c | (__builtin_signbit(v) ? 8u : 0u);
+}
+
+// WF = fp8 (MXFP8): E = floor(log2 max|w|) - 8, 32 e4m3 codes (value j at byte j), saturating at +-448.
+template <int WF>
+__global__ __launch_bounds__(256) void k_q4_to_mx(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ sc,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ exps,
+                                                  size_t nblocks) {
+  constexpr int emax = WF == kFmtFp4 ? 2 : 8;  // largest exponent of the element format
+  for (size_t b = (size_t)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += (size_t)gridDim.x * 256) {
+    const u32x4 v = ld16(qs + 16 * b);
+    const float d = (float)__builtin_bit_cast(_Float16, sc[b]);
+    int qmax = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int q = (int)((v[w] >> (4 * j)) & 0xF) - 8;
+        qmax = max(qmax, q < 0 ? -q : q);
+      }
+    const float amax = (float)qmax * fabsf(d);
+    int e = -127;
+    if (amax > 0.f) {
+      int ex;
+      (void)frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1
+      e = min(max(ex - 1 - emax, -127), 127);
+    }
+    if constexpr (WF == kFmtFp4) {
+      u32x4 out = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t o = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int q = (int)((v[w] >> (4 * j)) & 0xF) - 8;
+          const float val = ldexpf((float)q * d, -e);  // exact: a power-of-two scaling of an exact product
+          o |= e2m1_code(val) << (4 * j);
+        }
+        out[w] = o;
+      }
+      *reinterpret_cast<u32x4*>(codes + 16 * b) = out;
+    } else {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 out = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int q = (int)((v[2 * half + w] >> (4 * j)) & 0xF) - 8;
+            const float val = ldexpf((float)q * d, -e);
+            out[2 * w + j / 4] |= e4m3_code(val) << (8 * (j % 4));
+          }
+        *reinterpret_cast<u32x4*>(codes + 32 * b + 16 * half) = out;
+      }
+    }
+    exps[b] = (uint8_t)(e + 127);
+  }
 }
 
 // One workgroup per row: s = amax / 448 (1 for an all-zero row), codes = e4m3(x / s), both divisions
@@ -463,11 +521,12 @@ __global__ __launch_bounds__(256) void k_rows_fp8(const uint16_t* __restrict__ i
 }  // namespace
 
 hipError_t launch_q4_to_mx(size_t nblocks, const uint8_t* qs, const uint16_t* sc, uint8_t* codes, uint8_t* exps,
-                           hipStream_t st) {
+                           bool fp8, hipStream_t st) {
   if (nblocks == 0) return hipSuccess;
   const size_t want = (nblocks + 255) / 256;
   const unsigned grid = (unsigned)(want < 8192 ? want : 8192);
-  hipLaunchKernelGGL(k_q4_to_mx, dim3(grid), dim3(256), 0, st, qs, sc, codes, exps, nblocks);
+  if (fp8) hipLaunchKernelGGL(k_q4_to_mx<kFmtFp8>, dim3(grid), dim3(256), 0, st, qs, sc, codes, exps, nblocks);
+  else hipLaunchKernelGGL(k_q4_to_mx<kFmtFp4>, dim3(grid), dim3(256), 0, st, qs, sc, codes, exps, nblocks);
   return hipGetLastError();
 }
 
@@ -480,7 +539,7 @@ hipError_t launch_rows_fp8(const uint16_t* in, bool in_f16, int rows, int K, uin
 }
 
 hipError_t launch_w4a8_forward(const Shape& s, const uint16_t* x, const Routing& r, const MxWeights& w,
-                               const W4A8Scratch& o, const float* topk_w, float* y, uint32_t flags,
+                               const W4A8Scratch& o, const float* topk_w, float* y, uint32_t flags, bool fp8,
                                hipStream_t st) {
   const int P = s.T * s.k;
   hipError_t e = launch_rows_fp8(x, false, s.T, s.d, o.x8, o.xs, st);
@@ -501,8 +560,9 @@ hipError_t launch_w4a8_forward(const Shape& s, const uint16_t* x, const Routing&
   a.h_r = o.h_r; a.h_s = o.h_s;
   const int Imax = s.I > s.Is ? s.I : s.Is;
   a.nbands = (Imax + kMxGateUpBandCols - 1) / kMxGateUpBandCols;
-  long grid = (mtiles * a.nbands + 63) / 64 * 64;
-  hipLaunchKernelGGL(k_grouped_mx<true>, dim3((unsigned)grid), dim3(kMxThreads), 0, st, a);
+  long grid = (mtiles * a.nbands + 63) / 64 * 64;  // MXFP8: two half-tile items per launch-order item
+  if (fp8) hipLaunchKernelGGL((k_grouped_mx<true, kFmtFp8>), dim3((unsigned)(2 * grid)), dim3(kMxThreads), 0, st, a);
+  else hipLaunchKernelGGL((k_grouped_mx<true, kFmtFp4>), dim3((unsigned)grid), dim3(kMxThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // h rows to fp8 (routed rows by sorted position, then the shared expert's token rows)
   if ((e = launch_rows_fp8(reinterpret_cast<const uint16_t*>(o.h_r), true, P, s.I, o.h8_r, o.hs_r, st)) != hipSuccess)
@@ -518,7 +578,8 @@ hipError_t launch_w4a8_forward(const Shape& s, const uint16_t* x, const Routing&
   a.y_r = o.y_pair; a.y_s = o.y_s;
   a.nbands = (s.d + kMxDownBandCols - 1) / kMxDownBandCols;
   grid = (mtiles * a.nbands + 63) / 64 * 64;
-  hipLaunchKernelGGL(k_grouped_mx<false>, dim3((unsigned)grid), dim3(kMxThreads), 0, st, a);
+  if (fp8) hipLaunchKernelGGL((k_grouped_mx<false, kFmtFp8>), dim3((unsigned)(2 * grid)), dim3(kMxThreads), 0, st, a);
+  else hipLaunchKernelGGL((k_grouped_mx<false, kFmtFp4>), dim3((unsigned)grid), dim3(kMxThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   GroupedOut go{};
   go.y_pair = o.y_pair;

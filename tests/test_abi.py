@@ -385,12 +385,12 @@ MX = {k: FAKE for k in ("w13_codes", "w13_exps", "w2_codes", "w2_exps", "s13_cod
                         "s2_exps")}
 
 
-def w4a8(dims=TINY, flags=abi.MOE_FLAG_FORCE_GROUPED, weights=None, **kw):
+def w4a8(dims=TINY, flags=abi.MOE_FLAG_FORCE_GROUPED, weights=None, variant="w4a8", **kw):
     args = dict(x=FAKE, topk_ids=FAKE, topk_w=FAKE, routing=FAKE, y=FAKE, scratch=FAKE, routing_bytes=R,
                 scratch_bytes=1 << 30)
     args.update(kw)
-    return moe.moe_w4a8_forward(dims, weights=dict(MX, **(weights or {})), **args, flags=flags, stream=0,
-                                check=False)
+    fn = moe.moe_w4a8_forward if variant == "w4a8" else moe.moe_w8a8_forward
+    return fn(dims, weights=dict(MX, **(weights or {})), **args, flags=flags, stream=0, check=False)
 
 
 @pytest.mark.parametrize("dims", [TINY, BIG, synth.CONFIGS["long_prefill"].dims])
@@ -399,13 +399,27 @@ def test_w4a8_scratch_closed_form(dims):
     P = T * k
     want = (align(T * dd) + align(T * 4) + align(P * I * 2) + align(T * Is * 2) + align(P * I) + align(P * 4)
             + align(T * Is) + align(T * 4) + align(P * dd * 2) + align(T * dd * 2))
-    assert moe.moe_w4a8_scratch_bytes(dims, abi.MOE_FLAG_FORCE_GROUPED) == want
-    # only the grouped path has a W4A8 form
-    assert moe.moe_w4a8_scratch_bytes(dims, abi.MOE_FLAG_FORCE_GEMV) == 0
-    assert moe.moe_w4a8_scratch_bytes(d(d=96, I=128, I_shared=128), abi.MOE_FLAG_FORCE_GROUPED) == 0
+    for fn in (moe.moe_w4a8_scratch_bytes, moe.moe_w8a8_scratch_bytes):
+        assert fn(dims, abi.MOE_FLAG_FORCE_GROUPED) == want
+        # only the grouped path has the fp8-activation forms
+        assert fn(dims, abi.MOE_FLAG_FORCE_GEMV) == 0
+        assert fn(d(d=96, I=128, I_shared=128), abi.MOE_FLAG_FORCE_GROUPED) == 0
 
 
-def test_w4a8_forward_validation_before_any_hip_call():
+def test_w8a8_rejects_shapes_whose_fp8_code_offsets_leave_31_bits():
+    # one expert's MXFP8 gate+up codes take 2 * I * d bytes: the largest accepted shape and the first
+    # rejected one (W4A8 and the Q4 path still accept the latter: their codes take half the bytes)
+    G = abi.MOE_FLAG_FORCE_GROUPED
+    ok = d(T=16, d=8192, I=131072 - 128, I_shared=128)
+    bad = d(T=16, d=8192, I=131072, I_shared=128)
+    assert moe.moe_w8a8_scratch_bytes(ok, G) > 0 and moe.moe_w8a8_scratch_bytes(bad, G) == 0
+    assert moe.moe_w4a8_scratch_bytes(bad, G) > 0
+    assert w4a8(dims=bad, variant="w8a8") == abi.MOE_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("variant", ["w4a8", "w8a8"])
+def test_w4a8_forward_validation_before_any_hip_call(variant):
+    w4a8 = _variant_call(variant)
     for name in ("x", "topk_ids", "topk_w", "y", "scratch", "routing"):
         assert w4a8(**{name: 0}) == abi.MOE_EINVAL, name
     for name in MX:
@@ -425,12 +439,28 @@ def test_w4a8_forward_validation_before_any_hip_call():
     assert w4a8(dims=d(k=0)) == abi.MOE_EINVAL
 
 
-def q4mx(**kw):
+def _variant_call(variant):
+    return lambda **kw: w4a8(variant=variant, **kw)
+
+
+def q4mx(fp8=False, **kw):
     args = dict(n_mats=2, rows=32, K=64, qs=FAKE, scales=FAKE + (1 << 16), codes_out=FAKE + (2 << 16),
                 exps_out=FAKE + (3 << 16))
     args.update(kw)
-    return moe.moe_q4_to_mxfp4(args["n_mats"], args["rows"], args["K"], args["qs"], args["scales"],
-                               args["codes_out"], args["exps_out"], stream=0, check=False)
+    fn = moe.moe_q4_to_mxfp8 if fp8 else moe.moe_q4_to_mxfp4
+    return fn(args["n_mats"], args["rows"], args["K"], args["qs"], args["scales"], args["codes_out"],
+              args["exps_out"], stream=0, check=False)
+
+
+def test_q4_to_mxfp8_output_overlap_counts_its_32_byte_blocks():
+    # 128 blocks: 4096 bytes of MXFP8 codes, which reach an exponent array placed 3000 bytes in (the
+    # MXFP4 codes, 2048 bytes, do not)
+    assert q4mx(fp8=True, exps_out=FAKE + (2 << 16) + 3000) == abi.MOE_EINVAL
+    assert q4mx(fp8=True, n_mats=0, exps_out=FAKE + (2 << 16) + 3000) == abi.MOE_EINVAL  # size check first
+    for name in ("qs", "scales", "codes_out", "exps_out"):
+        assert q4mx(fp8=True, **{name: 0}) == abi.MOE_EINVAL
+    assert q4mx(fp8=True, rows=24) == abi.MOE_EUNSUPPORTED
+    assert q4mx(fp8=True, codes_out=FAKE + (2 << 16) + 8) == abi.MOE_EALIGN
 
 
 def test_q4_to_mxfp4_validation_before_any_hip_call():

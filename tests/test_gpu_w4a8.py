@@ -1,6 +1,6 @@
-"""GPU: the W4A8 variant (MXFP4 expert weights x FP8 activations) through the C ABI, against the W4A8
-oracle: the weight requantisation and the activation quantisation bit for bit, the layer under the
-parity rule (selection exact outside the margin, max-abs and relative-L2 bounds)."""
+"""GPU: the fp8-activation variants W4A8 (MXFP4 expert weights) and W8A8 (MXFP8 expert weights) through
+the C ABI, against their oracle: the weight requantisations and the activation quantisation bit for bit,
+the layers under the parity rule (selection exact outside the margin, max-abs and relative-L2 bounds)."""
 import numpy as np
 import pytest
 import torch
@@ -11,32 +11,52 @@ import synth
 from sparse_moe_expert_sigmoid_amd import abi
 from sparse_moe_expert_sigmoid_amd.layer import DeviceWeights, Workspace, layer_call, to_device
 from gpu_util import check_parity, say
-from test_gpu_pack import ref_pack_codes, ref_pack_scales
+from test_gpu_pack import ref_pack_scales
+
+
+def ref_pack_blocks(codes: np.ndarray, bb: int) -> np.ndarray:
+    """Row-major codes [..., rows, K/32 * bb] -> [..., rows/16, K/32, 16, bb]: block b of row r moves to
+    byte ((r/16)*(K/32) + b)*16*bb + (r%16)*bb of its matrix (the header's layout)."""
+    *lead, rows, width = codes.shape
+    nkb = width // bb
+    return np.ascontiguousarray(codes.reshape(*lead, rows // 16, 16, nkb, bb).swapaxes(-3, -2))
 
 pytestmark = pytest.mark.gpu
 
 GROUPED = abi.MOE_FLAG_FORCE_GROUPED
 
 
-def mx_upload(w: DeviceWeights) -> dict:
-    """MXFP4 copies of the packed Q4 stacks, made on the device by moe_q4_to_mxfp4."""
+VARIANTS = {
+    # name: (requantisation entry, forward entry, scratch query, oracle forward, oracle requantisation,
+    #        code bytes per Q4 code byte)
+    "w4a8": (abi.moe_q4_to_mxfp4, abi.moe_w4a8_forward, abi.moe_w4a8_scratch_bytes, w4.forward_w4a8,
+             w4.mx_requant, 1),
+    "w8a8": (abi.moe_q4_to_mxfp8, abi.moe_w8a8_forward, abi.moe_w8a8_scratch_bytes, w4.forward_w8a8,
+             w4.mx8_requant, 2),
+}
+
+
+def mx_upload(w: DeviceWeights, variant: str = "w4a8") -> dict:
+    """MXFP4 / MXFP8 copies of the packed Q4 stacks, made on the device by moe_q4_to_mxfp4 / _mxfp8."""
+    requant, *_, ratio = VARIANTS[variant]
     dims = w.dims
     shapes = {"w13": (dims.E, 2 * dims.I, dims.d), "w2": (dims.E, dims.d, dims.I),
               "s13": (1, 2 * dims.I_shared, dims.d), "s2": (1, dims.d, dims.I_shared)}
     mx = {}
     for name, (n, rows, K) in shapes.items():
-        codes = torch.empty_like(w[name + "_qs"])
+        codes = torch.empty(w[name + "_qs"].numel() * ratio, dtype=torch.uint8, device="cuda")
         exps = torch.empty(n * rows * (K // 32), dtype=torch.uint8, device=codes.device)
-        abi.moe_q4_to_mxfp4(n, rows, K, w[name + "_qs"], w[name + "_sc"], codes, exps)
+        requant(n, rows, K, w[name + "_qs"], w[name + "_sc"], codes, exps)
         mx[name + "_codes"], mx[name + "_exps"] = codes, exps
     return mx
 
 
-def w4a8_call(dims, x, ws: Workspace, mx: dict, flags: int) -> torch.Tensor:
-    """route + build (the W4A16 calls) then the W4A8 forward into a fresh output."""
+def w4a8_call(dims, x, ws: Workspace, mx: dict, flags: int, variant: str = "w4a8") -> torch.Tensor:
+    """route + build (the W4A16 calls) then the fp8-activation forward into a fresh output."""
+    _, forward, scratch_bytes, *_ = VARIANTS[variant]
     y = torch.full((dims.T, dims.d), float("nan"), dtype=torch.float32, device="cuda")
-    scratch = torch.empty(abi.moe_w4a8_scratch_bytes(dims, flags), dtype=torch.uint8, device="cuda")
-    abi.moe_w4a8_forward(dims, x, ws.topk_ids, ws.topk_w, ws.routing, mx, y, scratch, flags=flags)
+    scratch = torch.empty(scratch_bytes(dims, flags), dtype=torch.uint8, device="cuda")
+    forward(dims, x, ws.topk_ids, ws.topk_w, ws.routing, mx, y, scratch, flags=flags)
     return y
 
 
@@ -61,31 +81,34 @@ def special_q4(rng, rows, K):
     return qs, sc
 
 
+@pytest.mark.parametrize("variant", list(VARIANTS))
 @pytest.mark.parametrize("n_mats,rows,K", [(1, 16, 32), (2, 48, 256), (3, 64, 4096), (1, 2048, 1024)])
-def test_q4_to_mxfp4_bit_exact(n_mats, rows, K):
-    say(f"[case] q4_to_mxfp4 n_mats={n_mats} rows={rows} K={K}")
+def test_q4_to_mx_bit_exact(n_mats, rows, K, variant):
+    say(f"[case] q4_to_mx {variant} n_mats={n_mats} rows={rows} K={K}")
+    requant_gpu, _, _, _, requant_ref, ratio = VARIANTS[variant]
+    bb = 16 * ratio  # code bytes per block
     rng = np.random.default_rng(rows + K + n_mats)
     qs = np.empty((n_mats, rows, K // 2), np.uint8)
     sc = np.empty((n_mats, rows, K // 32), np.uint16)
     for m in range(n_mats):
         qs[m], sc[m] = special_q4(rng, rows, K)
-    ref = [w4.mx_requant(qs[m], sc[m]) for m in range(n_mats)]
+    ref = [requant_ref(qs[m], sc[m]) for m in range(n_mats)]
     ref_c = np.stack([r[0] for r in ref])
     ref_e = np.stack([r[1] for r in ref])
     # row-major in, row-major out (block b to block b)
     qi, si = to_device(qs, "cuda"), to_device(sc, "cuda")
-    co = torch.full_like(qi, 0x5A)
+    co = torch.full((qi.numel() * ratio,), 0x5A, dtype=torch.uint8, device="cuda")
     eo = torch.full((n_mats * rows * (K // 32),), 0x5A, dtype=torch.uint8, device="cuda")
-    abi.moe_q4_to_mxfp4(n_mats, rows, K, qi, si, co, eo)
+    requant_gpu(n_mats, rows, K, qi, si, co, eo)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(co.cpu().numpy().reshape(-1), ref_c.reshape(-1))
     np.testing.assert_array_equal(eo.cpu().numpy().reshape(-1), ref_e.reshape(-1))
     # the packed 16-row groups in, the same layout out
     qp, sp = torch.empty_like(qi), torch.empty_like(si)
     abi.moe_q4_pack(n_mats, rows, K, qi, si, qp, sp)
-    abi.moe_q4_to_mxfp4(n_mats, rows, K, qp, sp, co, eo)
+    requant_gpu(n_mats, rows, K, qp, sp, co, eo)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(co.cpu().numpy().reshape(-1), ref_pack_codes(ref_c).reshape(-1))
+    np.testing.assert_array_equal(co.cpu().numpy().reshape(-1), ref_pack_blocks(ref_c, bb).reshape(-1))
     np.testing.assert_array_equal(eo.cpu().numpy().reshape(-1), ref_pack_scales(ref_e).reshape(-1))
 
 
@@ -135,40 +158,43 @@ SMALL = {
 }
 
 
+@pytest.mark.parametrize("variant", list(VARIANTS))
 @pytest.mark.parametrize("name", list(SMALL))
-def test_w4a8_small_shapes(name):
+def test_fp8act_small_shapes(name, variant):
     dims, bias = SMALL[name]
-    say(f"[case] w4a8 small {name} dims={dims}")
+    say(f"[case] {variant} small {name} dims={dims}")
     inp = synth.make_inputs(dims, seed=300 + len(name), bias=bias)
     w = DeviceWeights.upload(inp)
     x = to_device(inp["x"], "cuda")
     ws = Workspace(dims, GROUPED)
     layer_call(x, w, ws)
-    mx = mx_upload(w)
-    y = w4a8_call(dims, x, ws, mx, GROUPED)
+    mx = mx_upload(w, variant)
+    y = w4a8_call(dims, x, ws, mx, GROUPED, variant)
     torch.cuda.synchronize()
-    check_parity(inp, ws, label=f"w4a8/{name}", forward=w4.forward_w4a8, y=y)
+    check_parity(inp, ws, label=f"{variant}/{name}", forward=VARIANTS[variant][3], y=y)
 
 
-def test_w4a8_schedule_orders_give_the_same_bits():
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_fp8act_schedule_orders_give_the_same_bits(variant):
     dims, bias = SMALL["skewed"]
     inp = synth.make_inputs(dims, seed=9, bias=bias)
     w = DeviceWeights.upload(inp)
     x = to_device(inp["x"], "cuda")
-    mx = mx_upload(w)
+    mx = mx_upload(w, variant)
     outs = []
     for flags in (GROUPED, GROUPED | abi.MOE_FLAG_NO_BANDING, GROUPED | abi.MOE_FLAG_BAND_MAJOR,
                   GROUPED | abi.MOE_FLAG_ID_ORDER):
         ws = Workspace(dims, flags)
         layer_call(x, w, ws)
-        outs.append(w4a8_call(dims, x, ws, mx, flags))
-        outs.append(w4a8_call(dims, x, ws, mx, flags))   # and run to run
+        outs.append(w4a8_call(dims, x, ws, mx, flags, variant))
+        outs.append(w4a8_call(dims, x, ws, mx, flags, variant))   # and run to run
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
 
 
-def test_w4a8_doubling_down_scales_doubles_output():
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_fp8act_doubling_down_scales_doubles_output(variant):
     """Doubling every Q4 down scale raises each block exponent by one: y doubles exactly."""
     dims, bias = SMALL["ragged"]
     inp = synth.make_inputs(dims, seed=21, bias=bias)
@@ -181,7 +207,7 @@ def test_w4a8_doubling_down_scales_doubles_output():
         w = DeviceWeights.upload(i)
         ws = Workspace(dims, GROUPED)
         layer_call(x, w, ws)
-        ys.append(w4a8_call(dims, x, ws, mx_upload(w), GROUPED))
+        ys.append(w4a8_call(dims, x, ws, mx_upload(w, variant), GROUPED, variant))
     torch.cuda.synchronize()
     # exact, except where a per-pair down output (stored in fp16) falls in the fp16 subnormal range, whose
     # absolute spacing 2^-24 does not scale: at most k + 1 such roundings per output element
@@ -193,20 +219,20 @@ def test_w4a8_doubling_down_scales_doubles_output():
 _MX_CACHE: dict = {}
 
 
-def oracle_mx(inp: dict, key: str, experts) -> dict:
+def oracle_mx(inp: dict, key: str, experts, variant: str = "w4a8") -> dict:
     """The oracle's requantised matrices for the given experts (and the shared expert), memoised per input
     set so that a full-size check requantises each matrix once."""
     out = {}
     for name in ("w13", "w2"):
         for e in experts:
-            k = (key, name, int(e))
+            k = (key, variant, name, int(e))
             if k not in _MX_CACHE:
-                _MX_CACHE[k] = w4.mx_requant(inp[name + "_qs"][e], inp[name + "_sc"][e])
+                _MX_CACHE[k] = VARIANTS[variant][4](inp[name + "_qs"][e], inp[name + "_sc"][e])
             out[(name, int(e))] = _MX_CACHE[k]
     for name in ("s13", "s2"):
-        k = (key, name, None)
+        k = (key, variant, name, None)
         if k not in _MX_CACHE:
-            _MX_CACHE[k] = w4.mx_requant(inp[name + "_qs"], inp[name + "_sc"])
+            _MX_CACHE[k] = VARIANTS[variant][4](inp[name + "_qs"], inp[name + "_sc"])
         out[(name, None)] = _MX_CACHE[k]
     return out
 
@@ -222,21 +248,24 @@ def few_expert_tokens(ids: np.ndarray, n: int) -> list:
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("variant", list(VARIANTS))
 @pytest.mark.parametrize("name,ntok", [("decode", 1), ("prefill", 3), ("long_prefill", 3)])
-def test_w4a8_full_size_sampled_tokens(name, ntok):
+def test_fp8act_full_size_sampled_tokens(name, ntok, variant):
     """The full-size workloads (T = 1 on the grouped path), the grouped GEMMs in their default launch
     configuration; the oracle evaluates a few tokens chosen to share experts, with its own requantised
     weights."""
     cfg = synth.CONFIGS[name]
     dims = cfg.dims
-    say(f"[case] w4a8 full {name} dims={dims}")
+    say(f"[case] {variant} full {name} dims={dims}")
     inp = synth.make_inputs(cfg)
     w = DeviceWeights.upload(inp)
     x = to_device(inp["x"], "cuda")
     ws = Workspace(dims, GROUPED)
     layer_call(x, w, ws)
-    y = w4a8_call(dims, x, ws, mx_upload(w), GROUPED)
-    y2 = w4a8_call(dims, x, ws, mx_upload(w), GROUPED)
+    mx = mx_upload(w, variant)
+    y = w4a8_call(dims, x, ws, mx, GROUPED, variant)
+    y2 = w4a8_call(dims, x, ws, mx_upload(w, variant), GROUPED, variant)
+    del mx
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
     assert torch.isfinite(y).all()
@@ -244,6 +273,7 @@ def test_w4a8_full_size_sampled_tokens(name, ntok):
     tokens = few_expert_tokens(ids, ntok)
     experts = np.unique(ids[tokens])
     say(f"[sample] {name}: tokens {tokens}, {len(experts)} experts")
-    mx = oracle_mx(inp, name, experts)
-    fwd = lambda i, tokens, ids_override: w4.forward_w4a8(i, tokens=tokens, ids_override=ids_override, mx=mx)
-    check_parity(inp, ws, tokens=np.array(tokens), label=f"w4a8/{name}", forward=fwd, y=y)
+    mx = oracle_mx(inp, name, experts, variant)
+    ref_forward = VARIANTS[variant][3]
+    fwd = lambda i, tokens, ids_override: ref_forward(i, tokens=tokens, ids_override=ids_override, mx=mx)
+    check_parity(inp, ws, tokens=np.array(tokens), label=f"{variant}/{name}", forward=fwd, y=y)
