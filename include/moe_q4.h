@@ -44,6 +44,10 @@
  *     (the error reported by hipGetLastError right after the launch).
  *   - Expert ids passed back in (topk_ids) must lie in [0, E); this is not
  *     checked on the device.
+ *   - With MOE_ROCTX=1 in the environment, every call that enqueues work is
+ *     wrapped in a roctx range named after it (for rocprofv3
+ *     --marker-trace); the roctx library is looked up at run time and the
+ *     ranges stay off without it.
  *
  * Storage formats
  *   x         bf16 bit patterns, row-major [T][d]

@@ -8,14 +8,49 @@
 // device-to-host copy), which keeps them capturable into a HIP graph.
 #include <hip/hip_runtime.h>
 
+#include <dlfcn.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "moe_q4.h"
 #include "moe_kernels.hpp"
 
 namespace {
+
+// roctx ranges around the entry points that enqueue work, for rocprofv3 --marker-trace.  Off unless the
+// environment sets MOE_ROCTX=1 when the library first needs them; the roctx library is then looked up
+// at run time, so nothing links against it and a missing one leaves the ranges off.
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+  Roctx() {
+    const char* on = getenv("MOE_ROCTX");
+    if (!on || strcmp(on, "1") != 0) return;
+    void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+    if (!h) h = dlopen("libroctx64.so.4", RTLD_NOW | RTLD_LOCAL);
+    if (!h) return;
+    push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+    pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+    if (!push || !pop) push = nullptr, pop = nullptr;
+  }
+};
+const Roctx& roctx() {
+  static const Roctx r;
+  return r;
+}
+struct Range {
+  const bool on;
+  explicit Range(const char* name) : on(roctx().push != nullptr) {
+    if (on) roctx().push(name);
+  }
+  ~Range() {
+    if (on) roctx().pop();
+  }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
@@ -228,11 +263,13 @@ int route_impl(const moe_dims* dims, const uint16_t* x_bf16, const float* w_rout
 
 int moe_route(const moe_dims* dims, const uint16_t* x_bf16, const float* w_router, const float* bias,
               int32_t* topk_ids, float* topk_w, void* routing, size_t routing_bytes, uint32_t flags, void* stream) {
+  const Range range("moe_route");
   return route_impl(dims, x_bf16, w_router, bias, topk_ids, topk_w, routing, routing_bytes, flags, stream, nullptr);
 }
 
 int moe_build_descriptors(const moe_dims* dims, const int32_t* topk_ids, void* routing, size_t routing_bytes,
                           uint32_t flags, void* stream) {
+  const Range range("moe_build_descriptors");
   int rc = check_dims(dims, flags);
   if (rc) return rc;
   if (!topk_ids || !routing) return MOE_EINVAL;
@@ -296,6 +333,7 @@ int forward_impl(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* to
 int moe_q4_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
                    const void* routing, size_t routing_bytes, const moe_q4_weights* w, float* y, void* scratch,
                    size_t scratch_bytes, uint32_t flags, void* stream) {
+  const Range range("moe_q4_forward");
   return forward_impl(dims, x_bf16, topk_ids, topk_w, routing, routing_bytes, w, nullptr, y, scratch, scratch_bytes,
                       flags, stream);
 }
@@ -304,6 +342,7 @@ int moe_q4_forward_residual(const moe_dims* dims, const uint16_t* x_bf16, const 
                             const float* topk_w, const void* routing, size_t routing_bytes,
                             const moe_q4_weights* w, const float* residual, float* y, void* scratch,
                             size_t scratch_bytes, uint32_t flags, void* stream) {
+  const Range range("moe_q4_forward_residual");
   const int rc = check_dims(dims, flags);
   if (rc) return rc;
   if (!residual) return MOE_EINVAL;
@@ -376,6 +415,7 @@ int layer_forward(const moe_dims* dims, const uint16_t* x_bf16, const float* w_r
                   const moe_q4_weights* w, const float* residual, float* y, int32_t* topk_ids, float* topk_w,
                   void* routing, size_t routing_bytes, void* scratch, size_t scratch_bytes, uint32_t flags,
                   void* stream) {
+  const Range range("moe_layer_forward_noalloc");
   return layer_impl(dims, x_bf16, w_router, bias, w, residual, y, topk_ids, topk_w, routing, routing_bytes, scratch,
                     scratch_bytes, flags, stream);
 }
@@ -399,6 +439,7 @@ int moe_layer_forward(const moe_dims* dims, const uint16_t* x_bf16, const float*
                       const moe_q4_weights* w, const float* residual, float* y, int32_t* topk_ids, float* topk_w,
                       void* routing, size_t routing_bytes, void* scratch, size_t scratch_bytes, uint32_t flags,
                       void* stream) {
+  const Range range("moe_layer_forward");
   return layer_impl(dims, x_bf16, w_router, bias, w, residual, y, topk_ids, topk_w, routing, routing_bytes, scratch,
                     scratch_bytes, flags, stream);
 }
@@ -468,6 +509,7 @@ extern "C" {
 
 int moe_rmsnorm_bf16(int T, int d, const float* h, const float* gamma, float eps, uint16_t* x_bf16,
                      void* stream) {
+  const Range range("moe_rmsnorm_bf16");
   if (T < 1 || d < 1 || !h || !gamma || !x_bf16 || !(isfinite(eps) && eps >= 0.f)) return MOE_EINVAL;
   if (d % 8 || d > (1 << 20)) return MOE_EUNSUPPORTED;
   if (!aligned(h, 16) || !aligned(gamma, 16) || !aligned(x_bf16, 16)) return MOE_EALIGN;
@@ -482,6 +524,7 @@ size_t moe_decode_ctx_workspace_bytes(const moe_dims* dims, uint32_t flags) {
 
 int moe_decode_ctx_create(const moe_dims* dims, int n_layers, const moe_layer* layers, float* h, void* workspace,
                           size_t workspace_bytes, uint32_t flags, moe_decode_ctx** out) {
+  const Range range("moe_decode_ctx_create");
   const int rc0 = check_dims(dims, flags);
   if (rc0) return rc0;
   if (!layers || !h || !workspace || !out || n_layers < 1 || n_layers > 4096) return MOE_EINVAL;
@@ -521,6 +564,7 @@ int moe_decode_ctx_create(const moe_dims* dims, int n_layers, const moe_layer* l
 }
 
 int moe_decode_ctx_run(moe_decode_ctx* ctx, void* stream) {
+  const Range range("moe_decode_ctx_run");
   if (!ctx) return MOE_EINVAL;
   return hip_rc(hipGraphLaunch(ctx->exec, static_cast<hipStream_t>(stream)));
 }
@@ -535,6 +579,7 @@ int moe_decode_ctx_destroy(moe_decode_ctx* ctx) {
 
 int moe_q4_pack(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs_in, const uint16_t* scales_in,
                 uint8_t* qs_out, uint16_t* scales_out, void* stream) {
+  const Range range("moe_q4_pack");
   if (n_mats < 1 || rows < 1 || K < 1 || !qs_in || !scales_in || !qs_out || !scales_out) return MOE_EINVAL;
   if (rows % 16 || K % 32 || rows > (1 << 24) || K > (1 << 24)) return MOE_EUNSUPPORTED;
   if (!aligned(qs_in, 16) || !aligned(qs_out, 16) || !aligned(scales_out, 16) || !aligned(scales_in, 2))
@@ -572,16 +617,19 @@ int q4_to_mx(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs, const u
 
 int moe_q4_to_mxfp4(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs, const uint16_t* scales,
                     uint8_t* codes_out, uint8_t* exps_out, void* stream) {
+  const Range range("moe_q4_to_mxfp4");
   return q4_to_mx(n_mats, rows, K, qs, scales, codes_out, exps_out, false, stream);
 }
 
 int moe_q4_to_mxfp8(int32_t n_mats, int32_t rows, int32_t K, const uint8_t* qs, const uint16_t* scales,
                     uint8_t* codes_out, uint8_t* exps_out, void* stream) {
+  const Range range("moe_q4_to_mxfp8");
   return q4_to_mx(n_mats, rows, K, qs, scales, codes_out, exps_out, true, stream);
 }
 
 int moe_rows_to_fp8(int32_t rows, int32_t K, const uint16_t* in, int in_is_fp16, uint8_t* codes_out,
                     float* scales_out, void* stream) {
+  const Range range("moe_rows_to_fp8");
   if (rows < 1 || K < 1 || !in || !codes_out || !scales_out) return MOE_EINVAL;
   if (K % 4 || (long long)rows * K >= (1LL << 31)) return MOE_EUNSUPPORTED;
   if (!aligned(in, 16) || !aligned(codes_out, 16) || !aligned(scales_out, 4)) return MOE_EALIGN;
@@ -642,6 +690,7 @@ int fp8act_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* 
 int moe_w4a8_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
                      const void* routing, size_t routing_bytes, const moe_mx_weights* w, float* y,
                      void* scratch, size_t scratch_bytes, uint32_t flags, void* stream) {
+  const Range range("moe_w4a8_forward");
   return fp8act_forward(dims, x_bf16, topk_ids, topk_w, routing, routing_bytes, w, y, scratch, scratch_bytes, flags,
                         false, stream);
 }
@@ -649,6 +698,7 @@ int moe_w4a8_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t
 int moe_w8a8_forward(const moe_dims* dims, const uint16_t* x_bf16, const int32_t* topk_ids, const float* topk_w,
                      const void* routing, size_t routing_bytes, const moe_mx_weights* w, float* y,
                      void* scratch, size_t scratch_bytes, uint32_t flags, void* stream) {
+  const Range range("moe_w8a8_forward");
   return fp8act_forward(dims, x_bf16, topk_ids, topk_w, routing, routing_bytes, w, y, scratch, scratch_bytes, flags,
                         true, stream);
 }

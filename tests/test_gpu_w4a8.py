@@ -277,3 +277,45 @@ def test_fp8act_full_size_sampled_tokens(name, ntok, variant):
     ref_forward = VARIANTS[variant][3]
     fwd = lambda i, tokens, ids_override: ref_forward(i, tokens=tokens, ids_override=ids_override, mx=mx)
     check_parity(inp, ws, tokens=np.array(tokens), label=f"{variant}/{name}", forward=fwd, y=y)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_fp8act_graph_capture_replays_match_eager(variant):
+    """route + build + the fp8-activation forward recorded into a HIP graph: every replay, with eager work
+    between replays, gives the eager bits."""
+    dims = synth.Dims(T=150, d=256, E=16, k=4, I=128, I_shared=128)
+    inp = synth.make_inputs(dims, seed=13)
+    w = DeviceWeights.upload(inp)
+    x = to_device(inp["x"], "cuda")
+    mx = mx_upload(w, variant)
+    ws = Workspace(dims, GROUPED)
+    layer_call(x, w, ws)
+    ref = w4a8_call(dims, x, ws, mx, GROUPED, variant)
+    torch.cuda.synchronize()
+    _, forward, scratch_bytes, *_ = VARIANTS[variant]
+    ws2 = Workspace(dims, GROUPED)
+    y = torch.empty((dims.T, dims.d), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(scratch_bytes(dims, GROUPED), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+
+    def step():
+        abi.moe_route(dims, x, w["w_router"], w["bias"], ws2.topk_ids, ws2.topk_w, ws2.routing, flags=GROUPED,
+                      stream=s)
+        abi.moe_build_descriptors(dims, ws2.topk_ids, ws2.routing, flags=GROUPED, stream=s)
+        forward(dims, x, ws2.topk_ids, ws2.topk_w, ws2.routing, mx, y, scratch, flags=GROUPED, stream=s)
+
+    with torch.cuda.stream(s):
+        step()  # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for i in range(3):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"replay {i}"
+        _ = (y * 2).sum().item()  # eager work between replays
