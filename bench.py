@@ -142,6 +142,7 @@ def short_name(mangled: str) -> str:
                       ("k_x_to_f16", "x_to_f16"), ("k_groupedILb1", "grouped_gateup"),
                       ("k_groupedILb0", "grouped_down"), ("k_combine", "combine"),
                       ("k_grouped_mxILb1", "grouped_mx_gateup"), ("k_grouped_mxILb0", "grouped_mx_down"),
+                      ("k_rows_fp8_waveILb0", "rows_fp8_x"), ("k_rows_fp8_waveILb1", "rows_fp8_h"),
                       ("k_rows_fp8ILb0", "rows_fp8_x"), ("k_rows_fp8ILb1", "rows_fp8_h")):
         if key in mangled:
             return nice

@@ -493,20 +493,34 @@ __global__ __launch_bounds__(256) void k_q4_to_mx(const uint8_t* __restrict__ qs
   }
 }
 
-// One workgroup per row: s = amax / 448 (1 for an all-zero row), codes = e4m3(x / s), both divisions
-// correctly rounded in fp32.  IN_F16: the input row is fp16 (h), else bf16 (x).
-template <bool IN_F16>
+// One workgroup per row (any K % 4 == 0): s = amax / 448 (1 for an all-zero row), codes = e4m3(x / s), both
+// divisions correctly rounded in fp32.  IN_F16: the input row is fp16 (h), else bf16 (x).  NIT > 0: the
+// row fits in NIT groups of 4 values per thread (K <= 1024 NIT) and is read once, kept in registers;
+// NIT = 0: any K, the row read twice.
+template <bool IN_F16, int NIT>
 __global__ __launch_bounds__(256) void k_rows_fp8(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
                                                   float* __restrict__ scale, int K) {
   __shared__ float red[4];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint16_t* src = in + (size_t)r * K;
   auto val = [&](uint16_t b) { return IN_F16 ? (float)__builtin_bit_cast(_Float16, b) : bf16_bits_to_float(b); };
+  auto amax4 = [&](uint2 u) {
+    return fmaxf(fmaxf(fabsf(val((uint16_t)(u.x & 0xFFFF))), fabsf(val((uint16_t)(u.x >> 16)))),
+                 fmaxf(fabsf(val((uint16_t)(u.y & 0xFFFF))), fabsf(val((uint16_t)(u.y >> 16)))));
+  };
+  constexpr int NR = NIT > 0 ? NIT : 1;
+  uint2 keep[NR];
   float m = 0.f;
-  for (int i = 4 * tid; i < K; i += 4 * 256) {
-    const uint2 u = *reinterpret_cast<const uint2*>(src + i);
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(val((uint16_t)(u.x & 0xFFFF))), fabsf(val((uint16_t)(u.x >> 16)))),
-                       fmaxf(fabsf(val((uint16_t)(u.y & 0xFFFF))), fabsf(val((uint16_t)(u.y >> 16))))));
+  if constexpr (NIT > 0) {
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      const int i = 4 * tid + 1024 * j;
+      keep[j] = i < K ? *reinterpret_cast<const uint2*>(src + i) : uint2{0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) m = fmaxf(m, amax4(keep[j]));
+  } else {
+    for (int i = 4 * tid; i < K; i += 4 * 256) m = fmaxf(m, amax4(*reinterpret_cast<const uint2*>(src + i)));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
@@ -515,13 +529,65 @@ __global__ __launch_bounds__(256) void k_rows_fp8(const uint16_t* __restrict__ i
   const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
   if (tid == 0) scale[r] = s;
-  for (int i = 4 * tid; i < K; i += 4 * 256) {
-    const uint2 u = *reinterpret_cast<const uint2*>(src + i);
+  auto store = [&](int i, uint2 u) {
     const uint32_t c0 = e4m3_code(__fdiv_rn(val((uint16_t)(u.x & 0xFFFF)), s));
     const uint32_t c1 = e4m3_code(__fdiv_rn(val((uint16_t)(u.x >> 16)), s));
     const uint32_t c2 = e4m3_code(__fdiv_rn(val((uint16_t)(u.y & 0xFFFF)), s));
     const uint32_t c3 = e4m3_code(__fdiv_rn(val((uint16_t)(u.y >> 16)), s));
     *reinterpret_cast<uint32_t*>(out + (size_t)r * K + i) = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+  };
+  if constexpr (NIT > 0) {
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      const int i = 4 * tid + 1024 * j;
+      if (i < K) store(i, keep[j]);
+    }
+  } else {
+    for (int i = 4 * tid; i < K; i += 4 * 256) store(i, *reinterpret_cast<const uint2*>(src + i));
+  }
+}
+
+// One wavefront per row, the row held in registers (a single pass over it): lane l takes the 16-byte
+// chunks l, l + 64, ... (8 values each, coalesced), the row's amax is a wavefront reduction, and the
+// codes leave as 8 bytes per chunk.  The same arithmetic as k_rows_fp8, for K % 8 == 0 and
+// K <= 512 * NCH (short rows, where a workgroup per row would leave most lanes idle).
+template <bool IN_F16, int NCH>
+__global__ __launch_bounds__(256) void k_rows_fp8_wave(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
+                                                       float* __restrict__ scale, int rows, int K) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;  // whole wavefronts
+  const uint16_t* src = in + (size_t)r * K;
+  const int nch = K / 8;
+  auto val = [&](uint32_t b) { return IN_F16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)b) : bf16_bits_to_float(b); };
+  u32x4 v[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = c < nch ? ld16(src + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) m = fmaxf(m, fmaxf(fabsf(val(v[i][w] & 0xFFFF)), fabsf(val(v[i][w] >> 16))));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  const float s = m > 0.f ? __fdiv_rn(m, 448.f) : 1.f;
+  if (lane == 0) scale[r] = s;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      uint32_t o[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t a = v[i][2 * h], b = v[i][2 * h + 1];
+        o[h] = e4m3_code(__fdiv_rn(val(a & 0xFFFF), s)) | (e4m3_code(__fdiv_rn(val(a >> 16), s)) << 8) |
+               (e4m3_code(__fdiv_rn(val(b & 0xFFFF), s)) << 16) | (e4m3_code(__fdiv_rn(val(b >> 16), s)) << 24);
+      }
+      *reinterpret_cast<uint2*>(out + (size_t)r * K + 8 * c) = uint2{o[0], o[1]};
+    }
   }
 }
 
@@ -540,8 +606,23 @@ hipError_t launch_q4_to_mx(size_t nblocks, const uint8_t* qs, const uint16_t* sc
 hipError_t launch_rows_fp8(const uint16_t* in, bool in_f16, int rows, int K, uint8_t* out, float* scale,
                            hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (in_f16) hipLaunchKernelGGL(k_rows_fp8<true>, dim3(rows), dim3(256), 0, st, in, out, scale, K);
-  else hipLaunchKernelGGL(k_rows_fp8<false>, dim3(rows), dim3(256), 0, st, in, out, scale, K);
+  // short rows (K <= 1024, K % 8 == 0): one wavefront per row, the row in registers; longer ones: one
+  // workgroup per row, the row in registers up to K = 8192 (one read), else read twice
+  if (K % 8 == 0 && K <= 1024) {
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (in_f16) hipLaunchKernelGGL((k_rows_fp8_wave<true, 2>), grid, dim3(256), 0, st, in, out, scale, rows, K);
+    else hipLaunchKernelGGL((k_rows_fp8_wave<false, 2>), grid, dim3(256), 0, st, in, out, scale, rows, K);
+    return hipGetLastError();
+  }
+  const int nit = (K + 1023) / 1024;
+#define MOE_ROWS_BLOCK(N)                                                                               \
+  if (in_f16) hipLaunchKernelGGL((k_rows_fp8<true, N>), dim3(rows), dim3(256), 0, st, in, out, scale, K); \
+  else hipLaunchKernelGGL((k_rows_fp8<false, N>), dim3(rows), dim3(256), 0, st, in, out, scale, K);
+  if (nit <= 2) { MOE_ROWS_BLOCK(2) }
+  else if (nit <= 4) { MOE_ROWS_BLOCK(4) }
+  else if (nit <= 8) { MOE_ROWS_BLOCK(8) }
+  else { MOE_ROWS_BLOCK(0) }
+#undef MOE_ROWS_BLOCK
   return hipGetLastError();
 }
 

@@ -131,7 +131,7 @@ def special_rows(rng, rows, K, fp16: bool):
 
 
 @pytest.mark.parametrize("fp16", [False, True], ids=["bf16", "fp16"])
-@pytest.mark.parametrize("rows,K", [(8, 4), (8, 256), (37, 4096), (300, 1024)])
+@pytest.mark.parametrize("rows,K", [(8, 4), (8, 256), (37, 4096), (300, 1024), (7, 520), (9, 8192), (8, 8196)])
 def test_rows_to_fp8_bit_exact(rows, K, fp16):
     say(f"[case] rows_to_fp8 rows={rows} K={K} fp16={fp16}")
     rng = np.random.default_rng(rows * 7 + K)
