@@ -21,8 +21,8 @@
 // output columns.
 //
 // Work items, schedule order, XCD remapping and the launch shape are those of the W4A16 grouped
-// GEMM (grouped.hip); the K loop is 128 values per iteration with the next step's operands in
-// flight (activation tile in LDS, weight blocks in registers).  d, I and I_shared must be multiples of 128.
+// GEMM (grouped.hip); the K loop is 128 values per iteration with the next one or two steps'
+// operands in flight (activation tiles in LDS, weight blocks in registers).  d, I and I_shared must be multiples of 128.
 #include <type_traits>
 
 #include "moe_device.hpp"
@@ -88,8 +88,8 @@ constexpr int kFmtFp8 = 0;
 template <int WF> constexpr int kBlockBytes = WF == kFmtFp4 ? 16 : 32;
 template <int WF> constexpr int kWLoads = WF == kFmtFp4 ? 1 : 2;
 
-template <bool GATEUP, int WF, int BME, int NMT>
-__device__ __forceinline__ void mx_tile(const MxArgs& a, char* As0, char* As1, char* Aout,
+template <bool GATEUP, int WF, int BME, int NS, int NMT>
+__device__ __forceinline__ void mx_tile(const MxArgs& a, char* As0, char* As1, char* As2, char* Aout,
                                         const __amdgpu_buffer_rsrc_t& rq,
                                         const __amdgpu_buffer_rsrc_t& rs, const __amdgpu_buffer_rsrc_t& ra,
                                         const uint32_t (&aoff)[kMxLoadsPerWave<BME>], const int (&qns)[4],
@@ -99,7 +99,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As0, char* As1, c
   // The ring's stages are separate LDS objects (stage numbers are compile-time constants below), so the
   // compiler can tell that reading one stage does not depend on the loads still filling the other and
   // puts no wait for them in front of the reads.
-  auto ring = [&](int buf) __attribute__((always_inline)) { return buf == 0 ? As0 : As1; };
+  auto ring = [&](int buf) __attribute__((always_inline)) { return buf == 0 ? As0 : buf == 1 ? As1 : As2; };
   auto issue_a = [&](int it, int buf) {
 #pragma unroll
     for (int i = 0; i < kMxLoadsPerWave<BME>; ++i) {
@@ -163,28 +163,48 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As0, char* As1, c
     }
   };
 
-  // Two-stage pipeline: while step `it` is computed, step it+1's activation tile (LDS) and weight
-  // blocks (registers) are in flight.
-  u32x4 q[2][4][NW];
-  uint32_t sc[2][4];
+  // NS-stage pipeline (2 or 3): while step `it` is computed, the activation tiles (LDS) and weight
+  // blocks (registers) of the next NS - 1 steps are in flight.  A step's loads are nA tile loads (this
+  // wavefront's share) and NWL weight loads, so with three stages the wait before step `it` leaves the
+  // next step's nA + NWL in flight.
+  static_assert(NS == 2 || NS == 3, "two or three stages");
+  u32x4 q[NS][4][NW];
+  uint32_t sc[NS][4];
+  constexpr int NI = kMxLoadInst<BME>;
+  const int nA = (NI % kMxWaves == 0 || wave < NI % kMxWaves) ? (NI + kMxWaves - 1) / kMxWaves : NI / kMxWaves;
+  constexpr int NWL = 4 * NW + 4;
   issue_a(0, 0);
   load_w(0, q[0], sc[0]);
+  if (NS == 3 && 1 < nit) {
+    issue_a(1, 1);
+    load_w(1, q[1 % NS], sc[1 % NS]);
+  }
   auto step = [&](int it, auto st_c) __attribute__((always_inline)) {
     constexpr int st = decltype(st_c)::value;
-    vm_lgkm_wait<0>();
-    tile_barrier();  // every wavefront's part of tile `it` is in LDS; tile it-1 is no longer read
-    if (it + 1 < nit) {
-      issue_a(it + 1, st ^ 1);
-      load_w(it + 1, q[st ^ 1], sc[st ^ 1]);
+    constexpr int nx = (st + NS - 1) % NS;  // stage of step it + NS - 1
+    if (NS == 3 && it + 1 < nit) {
+      if (nA == 3) vm_lgkm_wait<3 + NWL>();
+      else if (nA == 2) vm_lgkm_wait<2 + NWL>();
+      else vm_lgkm_wait<1 + NWL>();
+    } else {
+      vm_lgkm_wait<0>();
+    }
+    tile_barrier();  // every wavefront's part of tile `it` is in LDS; the stage refilled below was last
+                     // read by step it - 1
+    if (it + NS - 1 < nit) {
+      issue_a(it + NS - 1, nx);
+      load_w(it + NS - 1, q[nx], sc[nx]);
     }
     compute(st, q[st], sc[st]);
   };
   int it0 = 0;
-  for (; it0 + 2 <= nit; it0 += 2) {
+  for (; it0 + NS <= nit; it0 += NS) {
     step(it0 + 0, std::integral_constant<int, 0>{});
     step(it0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (NS == 3) step(it0 + 2, std::integral_constant<int, 2 % NS>{});
   }
   if (it0 < nit) step(it0, std::integral_constant<int, 0>{});
+  if (NS == 3 && it0 + 1 < nit) step(it0 + 1, std::integral_constant<int, 1>{});
 
   // ---- epilogue: lane (n, G) holds, for activation row 16 mt + n, output columns 4G .. 4G+3 of each
   // 16-column slice; the row's activation scale multiplies them.
@@ -256,9 +276,14 @@ __global__ __launch_bounds__(kMxThreads, 8 / kMxWaves) void k_grouped_mx(MxArgs 
   // XCD, adjacent in time, so the second reads the weight band from L2)
   constexpr bool HALF = WF == kFmtFp8;
   constexpr int BME = HALF ? kMxBM / 2 : kMxBM;
+  // three pipeline stages where they fit two workgroups per CU beside the down output staging (measured:
+  // MXFP8 gate+up -8%, down -3%, MXFP4 gate+up -1%; the MXFP4 down keeps two, its 96-row staging would
+  // leave room for one workgroup)
+  constexpr int NS = (GATEUP || HALF) ? 3 : 2;
   constexpr int BANDW = GATEUP ? kMxGateUpBandCols : kMxDownBandCols;
   __shared__ __attribute__((aligned(1024))) char As0[BME * kMxRowBytes];
   __shared__ __attribute__((aligned(1024))) char As1[BME * kMxRowBytes];
+  __shared__ __attribute__((aligned(1024))) char As2[NS == 3 ? BME * kMxRowBytes : 16];
   __shared__ __attribute__((aligned(1024))) char Aout[GATEUP ? 16 : BME * kMxDownBandCols * 2];
   __shared__ int s_prefix[kMaxExperts + 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = ufl(tid >> 6);
@@ -376,7 +401,7 @@ __global__ __launch_bounds__(kMxThreads, 8 / kMxWaves) void k_grouped_mx(MxArgs 
     sns[ns] = ufl((int)((uint32_t)(rowbase[ns] / 16) * nkb * 16u));
   }
 #define MX_TILE(NMT)                                                                                      \
-  mx_tile<GATEUP, WF, BME, NMT>(a, As0, As1, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, \
+  mx_tile<GATEUP, WF, BME, NS, NMT>(a, As0, As1, As2, Aout, rq, rs, ra, aoff, qns, sns, nok, nit, c0, wave, lane, mlen, \
                                 rbase, m0, Iw, shared)
   const int nmt16 = (mlen + 15) >> 4;
   if constexpr (BME == 48) {
