@@ -191,11 +191,17 @@ def device_copy(cfg, seed, torch, device):
     return x.bfloat16().view(torch.int16), w
 
 
-def expert_bytes(dims):
-    gu = 2 * dims.I * dims.d // 2 + 2 * dims.I * dims.d // 32 * 2
-    dn = dims.d * dims.I // 2 + dims.d * dims.I // 32 * 2
-    sgu = 2 * dims.I_shared * dims.d // 2 + 2 * dims.I_shared * dims.d // 32 * 2
-    sdn = dims.d * dims.I_shared // 2 + dims.d * dims.I_shared // 32 * 2
+# bytes per block of 32 weights: Q4 (16 code bytes + an fp16 scale), MXFP4 (16 + an exponent byte),
+# MXFP8 (32 + an exponent byte)
+BLOCK_BYTES = {"w4a16": 18, "w4a8": 17, "w8a8": 33}
+
+
+def expert_bytes(dims, variant="w4a16"):
+    bb = BLOCK_BYTES[variant]
+    gu = 2 * dims.I * dims.d // 32 * bb
+    dn = dims.d * dims.I // 32 * bb
+    sgu = 2 * dims.I_shared * dims.d // 32 * bb
+    sdn = dims.d * dims.I_shared // 32 * bb
     return gu, dn, sgu, sdn
 
 
@@ -351,7 +357,7 @@ def run_workload(name, steps, warmup, torch, hip, abi, layer, synth, oracle_samp
     sizes = np.bincount(ids.ravel(), minlength=dims.E)
     group_stats = {"max": int(sizes.max()), "median": float(np.median(sizes)), "min": int(sizes.min()),
                    "empty": int((sizes == 0).sum())}
-    gu, dn, sgu, sdn = expert_bytes(dims)
+    gu, dn, sgu, sdn = expert_bytes(dims, variant)
     T, d, E, P = dims.T, dims.d, dims.E, dims.T * dims.k
     layer_bytes = (E * d * 4 + E * 4 + T * d * 2 + distinct * (gu + dn) + (sgu + sdn) + T * d * 4
                    + P * 8)
