@@ -25,6 +25,9 @@ CASES = [  # (T, d, E, k, I, Is, flags): every key-register count of the selecti
     # the decode workload bench.py times (d = 4096, E = 256, top-10, I = I_shared = 1024) at T = 1 and 8
     (1, 4096, 256, 10, 1024, 1024, 0),
     (8, 4096, 256, 10, 1024, 1024, 0),
+    # large T: the router's 128-token tiles write the gate+up's fp16 copy of x (ragged last tiles)
+    (2000, 1024, 256, 10, 64, 64, 0),
+    (4100, 1024, 256, 10, 64, 64, 0),
 ]
 
 

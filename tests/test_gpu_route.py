@@ -99,13 +99,15 @@ def test_slot_order_matches_oracle(E, k, path):
     assert ordered > 0 or k == 1
 
 
+@pytest.mark.parametrize("d", [512, 1024, 4096])
 @pytest.mark.parametrize("T", [2000, 2048, 4096, 4100])
-def test_large_t_router_tile(T):
+def test_large_t_router_tile(T, d):
     """The 128-token router tiles: over 128 experts with two K halves (T = 2048; 2000: a ragged last tile)
-    and over all 256 experts (T = 4096; 4100: a ragged last tile of 4 tokens)."""
-    dims = synth.Dims(T=T, d=512, E=256, k=10, I=32, I_shared=32)
-    inp = synth.make_inputs(dims, seed=T, weights=False)
-    say(f"[case] large-T router T={T}")
+    and over all 256 experts (T = 4096; 4100: a ragged last tile of 4 tokens), with K parts of 2, 4 and 16
+    K steps."""
+    dims = synth.Dims(T=T, d=d, E=256, k=10, I=32, I_shared=32)
+    inp = synth.make_inputs(dims, seed=T + d, weights=False)
+    say(f"[case] large-T router T={T} d={d}")
     ids, w = route(inp, abi.MOE_FLAG_FORCE_GROUPED)
     s = oracle.sigmoid(oracle.router_logits(inp["x"], inp["w_router"]))
     ref_ids, margin = oracle.select_experts(s, inp["bias"], dims.k)
