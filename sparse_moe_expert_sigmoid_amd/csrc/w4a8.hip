@@ -1,14 +1,14 @@
-// W4A8 variant of the grouped path: MXFP4 expert weights times FP8 activations on the block-scaled
-// MFMA of gfx950.
+// W4A8 and W8A8 variants of the grouped path: MXFP4 or MXFP8 expert weights times FP8 activations on
+// the block-scaled MFMA of gfx950.
 //
 // Page thewafflehaus/FFAI pull request 72 ("Nemotron-Nano-30B GB10 prefill quality + speed wins"):
-// W4A8 grouped MoE (fp8 activations times fp4 weights) beside the Q4 W4A16 path; the fp4 MoE weights
-// are the Q4 weights requantised to a block-scaled fp4 grid, and the fp8 activations carry a
-// per-token scale applied to the product.  Here the fp4 grid is e2m1 in blocks of 32 with a shared
-// power-of-two exponent (one byte, bias 127), the block format that
+// W4A8 and W8A8 grouped MoE (fp8 activations times fp4 or fp8 weights) beside the Q4 W4A16 path; the
+// fp4 MoE weights are the Q4 weights requantised to a block-scaled fp4 grid, and the fp8 activations
+// carry a per-token scale applied to the product.  Here the fp4 grid is e2m1 (the fp8 one e4m3) in
+// blocks of 32 with a shared power-of-two exponent (one byte, bias 127), the block formats that
 // v_mfma_scale_f32_16x16x128_f8f6f4 multiplies directly: one such MFMA takes, per lane, one 32-value
-// block of one weight row as its fp4 operand with that block's exponent as its scale, so the main
-// loop has no dequantisation at all.  Activations (x, then h) are e4m3 with one fp32 scale per row
+// block of one weight row (MXFP8: two half blocks) as its weight operand with that block's exponent as
+// its scale, so the main loop has no dequantisation at all.  Activations (x, then h) are e4m3 with one fp32 scale per row
 // (amax / 448), applied to the fp32 accumulators in the epilogues.
 //
 // Operand layout of the MFMA (16 x 16 x 128, checked on the GPU against a host product): the fp4
@@ -61,7 +61,7 @@ struct MxArgs {
   const float* as_r;        // fp32 row scales of a_r rows: gate+up -> xs [T]; down -> hs_r [P]
   const float* as_s;        // ... of a_s rows: gate+up -> xs [T]; down -> hs_s [T]
   uint32_t a_r_bytes, a_s_bytes;
-  const uint8_t* wr_codes;  // routed stack (w13 or w2): e2m1 codes in 16-row groups
+  const uint8_t* wr_codes;  // routed stack (w13 or w2): e2m1 or e4m3 codes in 16-row groups
   const uint8_t* wr_exp;    //   and the blocks' biased exponents
   const uint8_t* ws_codes;  // shared expert
   const uint8_t* ws_exp;
@@ -575,13 +575,24 @@ __global__ __launch_bounds__(256) void k_rows_fp8(const uint16_t* __restrict__ i
 // One wavefront per row, the row held in registers (a single pass over it): lane l takes the 16-byte
 // chunks l, l + 64, ... (8 values each, coalesced), the row's amax is a wavefront reduction, and the
 // codes leave as 8 bytes per chunk.  The same arithmetic as k_rows_fp8, for K % 8 == 0 and
-// K <= 512 * NCH (short rows, where a workgroup per row would leave most lanes idle).
+// K <= 512 * NCH (short rows, where a workgroup per row would leave most lanes idle).  One launch can
+// take two matrices: rows * K, then rows2 * K2 (the routed and the shared h).
 template <bool IN_F16, int NCH>
 __global__ __launch_bounds__(256) void k_rows_fp8_wave(const uint16_t* __restrict__ in, uint8_t* __restrict__ out,
-                                                       float* __restrict__ scale, int rows, int K) {
+                                                       float* __restrict__ scale, int rows, int K,
+                                                       const uint16_t* __restrict__ in2, uint8_t* __restrict__ out2,
+                                                       float* __restrict__ scale2, int rows2, int K2) {
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;  // whole wavefronts
+  int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // rows past the first matrix's belong to the second (rows2 = 0: none); the choice is per wavefront
+  if (r >= rows) {
+    r -= rows;
+    if (r >= rows2) return;  // whole wavefronts
+    in = in2;
+    out = out2;
+    scale = scale2;
+    K = K2;
+  }
   const uint16_t* src = in + (size_t)r * K;
   const int nch = K / 8;
   auto val = [&](uint32_t b) { return IN_F16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)b) : bf16_bits_to_float(b); };
@@ -635,8 +646,12 @@ hipError_t launch_rows_fp8(const uint16_t* in, bool in_f16, int rows, int K, uin
   // workgroup per row, the row in registers up to K = 8192 (one read), else read twice
   if (K % 8 == 0 && K <= 1024) {
     const dim3 grid((unsigned)((rows + 3) / 4));
-    if (in_f16) hipLaunchKernelGGL((k_rows_fp8_wave<true, 2>), grid, dim3(256), 0, st, in, out, scale, rows, K);
-    else hipLaunchKernelGGL((k_rows_fp8_wave<false, 2>), grid, dim3(256), 0, st, in, out, scale, rows, K);
+    if (in_f16)
+      hipLaunchKernelGGL((k_rows_fp8_wave<true, 2>), grid, dim3(256), 0, st, in, out, scale, rows, K, nullptr,
+                         nullptr, nullptr, 0, 0);
+    else
+      hipLaunchKernelGGL((k_rows_fp8_wave<false, 2>), grid, dim3(256), 0, st, in, out, scale, rows, K, nullptr,
+                         nullptr, nullptr, 0, 0);
     return hipGetLastError();
   }
   const int nit = (K + 1023) / 1024;
@@ -677,12 +692,18 @@ hipError_t launch_w4a8_forward(const Shape& s, const uint16_t* x, const Routing&
   if (fp8) hipLaunchKernelGGL((k_grouped_mx<true, kFmtFp8>), dim3((unsigned)(2 * grid)), dim3(kMxThreads), 0, st, a);
   else hipLaunchKernelGGL((k_grouped_mx<true, kFmtFp4>), dim3((unsigned)grid), dim3(kMxThreads), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // h rows to fp8 (routed rows by sorted position, then the shared expert's token rows)
-  if ((e = launch_rows_fp8(reinterpret_cast<const uint16_t*>(o.h_r), true, P, s.I, o.h8_r, o.hs_r, st)) != hipSuccess)
-    return e;
-  if ((e = launch_rows_fp8(reinterpret_cast<const uint16_t*>(o.h_s), true, s.T, s.Is, o.h8_s, o.hs_s, st)) !=
-      hipSuccess)
-    return e;
+  // h rows to fp8 (routed rows by sorted position, then the shared expert's token rows): one launch of
+  // the wavefront-per-row kernel for both when their rows are short enough, else one launch each
+  const uint16_t* hr = reinterpret_cast<const uint16_t*>(o.h_r);
+  const uint16_t* hs = reinterpret_cast<const uint16_t*>(o.h_s);
+  if (s.I <= 1024 && s.Is <= 1024) {  // multiples of 128 (checked on the host)
+    hipLaunchKernelGGL((k_rows_fp8_wave<true, 2>), dim3((unsigned)((P + s.T + 3) / 4)), dim3(256), 0, st, hr, o.h8_r,
+                       o.hs_r, P, s.I, hs, o.h8_s, o.hs_s, s.T, s.Is);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    if ((e = launch_rows_fp8(hr, true, P, s.I, o.h8_r, o.hs_r, st)) != hipSuccess) return e;
+    if ((e = launch_rows_fp8(hs, true, s.T, s.Is, o.h8_s, o.hs_s, st)) != hipSuccess) return e;
+  }
   // down
   a.a_r = o.h8_r; a.a_s = o.h8_s; a.as_r = o.hs_r; a.as_s = o.hs_s;
   a.a_r_bytes = (uint32_t)((size_t)P * s.I);
