@@ -155,6 +155,10 @@ SMALL = {
     "single_expert": (synth.Dims(T=5, d=128, E=1, k=1, I=128, I_shared=128), "uniform"),
     "one_token": (synth.Dims(T=1, d=256, E=16, k=4, I=128, I_shared=128), "uniform"),
     "skewed": (synth.Dims(T=200, d=256, E=32, k=4, I=128, I_shared=256), "zipf"),
+    # h rows longer than 1024 (quantised one workgroup per row, routed and shared rows apart)
+    "wide_h": (synth.Dims(T=40, d=256, E=8, k=2, I=1280, I_shared=2048), "uniform"),
+    # 1024 experts, top-32: most groups empty or of one row
+    "many_experts": (synth.Dims(T=64, d=256, E=1024, k=32, I=128, I_shared=128), "uniform"),
 }
 
 
