@@ -284,6 +284,25 @@ def test_fp8act_full_size_sampled_tokens(name, ntok, variant):
 
 
 @pytest.mark.parametrize("variant", list(VARIANTS))
+def test_fp8act_prefill_routing_every_token(variant):
+    """The prefill workload's token count, expert count, top-k and Zipf-skewed groups (the largest about
+    650 rows: several M-tiles, and for MXFP8 weights every tile as two half tiles) with smaller matrices
+    (d = 512, I = I_shared = 256), so that the oracle can evaluate every token."""
+    dims = synth.Dims(T=2048, d=512, E=256, k=10, I=256, I_shared=256)
+    say(f"[case] {variant} prefill routing dims={dims}")
+    inp = synth.make_inputs(dims, seed=77, bias="zipf")
+    w = DeviceWeights.upload(inp)
+    x = to_device(inp["x"], "cuda")
+    ws = Workspace(dims, GROUPED)
+    layer_call(x, w, ws)
+    y = w4a8_call(dims, x, ws, mx_upload(w, variant), GROUPED, variant)
+    torch.cuda.synchronize()
+    counts = np.bincount(ws.topk_ids.cpu().numpy().ravel(), minlength=dims.E)
+    assert counts.max() > 4 * 96  # several M-tiles in the largest group
+    check_parity(inp, ws, label=f"{variant}/prefill-routing", forward=VARIANTS[variant][3], y=y)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
 def test_fp8act_graph_capture_replays_match_eager(variant):
     """route + build + the fp8-activation forward recorded into a HIP graph: every replay, with eager work
     between replays, gives the eager bits."""
