@@ -241,7 +241,10 @@ __device__ __forceinline__ void mx_tile(const MxArgs& a, char* As0, char* As1, c
     }
   }
   if (!GATEUP) {
-    // the down tile leaves through LDS (a region of its own) so that every store writes whole rows
+    // the down tile leaves through LDS so that every store writes whole rows; the staging region is
+    // stage 0 of the ring, enlarged (every wavefront is done reading its last tile first; no load into it
+    // is in flight after the last step's wait)
+    tile_barrier();
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       const int row = mt * 16 + n;
@@ -276,15 +279,15 @@ __global__ __launch_bounds__(kMxThreads, 8 / kMxWaves) void k_grouped_mx(MxArgs 
   // XCD, adjacent in time, so the second reads the weight band from L2)
   constexpr bool HALF = WF == kFmtFp8;
   constexpr int BME = HALF ? kMxBM / 2 : kMxBM;
-  // three pipeline stages where they fit two workgroups per CU beside the down output staging (measured:
-  // MXFP8 gate+up -8%, down -3%, MXFP4 gate+up -1%; the MXFP4 down keeps two, its 96-row staging would
-  // leave room for one workgroup)
-  constexpr int NS = (GATEUP || HALF) ? 3 : 2;
+  // three pipeline stages (measured against two: MXFP8 gate+up -8%, down -3%, MXFP4 gate+up -1%); the
+  // down projection's output staging reuses stage 0, so that two workgroups per CU still fit
+  constexpr int NS = 3;
   constexpr int BANDW = GATEUP ? kMxGateUpBandCols : kMxDownBandCols;
-  __shared__ __attribute__((aligned(1024))) char As0[BME * kMxRowBytes];
-  __shared__ __attribute__((aligned(1024))) char As1[BME * kMxRowBytes];
-  __shared__ __attribute__((aligned(1024))) char As2[NS == 3 ? BME * kMxRowBytes : 16];
-  __shared__ __attribute__((aligned(1024))) char Aout[GATEUP ? 16 : BME * kMxDownBandCols * 2];
+  constexpr int kStage = BME * kMxRowBytes, kOut = GATEUP ? 0 : BME * kMxDownBandCols * 2;
+  __shared__ __attribute__((aligned(1024))) char As0[kStage > kOut ? kStage : kOut];
+  __shared__ __attribute__((aligned(1024))) char As1[kStage];
+  __shared__ __attribute__((aligned(1024))) char As2[kStage];
+  char* const Aout = As0;
   __shared__ int s_prefix[kMaxExperts + 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = ufl(tid >> 6);
   const int ngroups = a.E + 1;
