@@ -18,8 +18,9 @@ I=1024, shared I=1024) gives `value`; the 2048-token prefill chunk is
 measured the same way and reported under `secondary`, and again as the W4A8
 and W8A8 variants (moe_route + moe_build_descriptors + moe_w4a8_forward /
 moe_w8a8_forward on MXFP4 / MXFP8 copies of the weights, fp8 activations)
-under `secondary_w4a8` / `secondary_w8a8`, whose rooflines are priced against
-the fp8 MFMA peak.  Per-kernel average
+under `secondary_w4a8` / `secondary_w8a8`, whose gate+up rooflines are priced
+against HBM (those GEMMs stream weights: 315 / 166 FLOP per byte, under the
+fp8 ridge), with the fraction of the fp8 MFMA peak beside.  Per-kernel average
 durations come from graphs that replay only that kernel's nodes, extracted
 from the captured layer graph, timed with HIP events on the same stream
 (every launch of the layer is idempotent, so replaying one alone is valid).
