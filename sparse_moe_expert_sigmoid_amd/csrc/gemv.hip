@@ -87,20 +87,47 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
   u32x4 xr[4];
 #pragma unroll
   for (int dw = 0; dw < 4; ++dw) xr[dw] = ld16(xb + 8 * dw);
-  int e = 0;
+  // the expert of this job and the slot whose h row it writes: with the selection inside (NPER > 0) job
+  // (t, j) takes the j-th chosen expert in id order, which needs only the chosen set, and writes the row
+  // of that expert's slot; the slot order and the weights for the down pass are written by the workgroup
+  // of row group 0 and j = 0, while its weight loads are in flight
+  int e = 0, hslot = routed ? job % k : 0;
+  uint64_t chosen[NPER > 0 ? NPER : 1];
+  uint32_t key[NPER > 0 ? NPER : 1];
+  float ssc[NPER > 0 ? NPER : 1];
+  bool rank_pending = false;
+  __shared__ TopkLds tsm;
   if constexpr (NPER > 0) {
-    __shared__ TopkLds tsm;
-    if (routed && wave == 0)
-      topk_wave<NPER, 1>(logits + (size_t)t * E, 0, bias, ids + (size_t)t * k, topk_w + (size_t)t * k, E, k, lane,
-                         tsm, blockIdx.x == 0 && job % k == 0);
+    __shared__ int sel[2];
+    if (routed && wave == 0) {
+      topk_chosen<NPER, 1>(logits + (size_t)t * E, 0, bias, E, k, lane, chosen, key, ssc);
+      const int ej = topk_nth_chosen<NPER>(chosen, job % k);
+      const int sj = topk_slot_of<NPER>(chosen, key, ej, lane);
+      if (lane == 0) {
+        sel[0] = ej;
+        sel[1] = sj;
+      }
+      rank_pending = blockIdx.x == 0 && job % k == 0;
+    }
     __syncthreads();
-    if (routed) e = __builtin_amdgcn_readfirstlane(tsm.slot_id[job % k]);
+    if (routed) {
+      e = __builtin_amdgcn_readfirstlane(sel[0]);
+      hslot = __builtin_amdgcn_readfirstlane(sel[1]);
+    }
   } else {
     if (routed) e = ids[job];
   }
+  auto rank_write = [&]() __attribute__((always_inline)) {
+    if constexpr (NPER > 0) {
+      if (rank_pending) {  // uniform over the wavefront
+        topk_rank_write<NPER>(chosen, key, ssc, ids + (size_t)t * k, topk_w + (size_t)t * k, k, lane, tsm, true);
+        rank_pending = false;
+      }
+    }
+  };
   const uint8_t* qs = routed ? w13.qs + (size_t)e * (2 * (size_t)I) * (d / 2) : s13.qs;
   const uint16_t* sc = routed ? w13.sc + (size_t)e * (2 * (size_t)I) * (d / 32) : s13.sc;
-  _Float16* out = routed ? h_r + (size_t)job * I : h_s + (size_t)t * Is;
+  _Float16* out = routed ? h_r + ((size_t)t * k + hslot) * I : h_s + (size_t)t * Is;
   const size_t grp_bytes = (size_t)nkb * 256;  // one 16-row group of codes
   const uint8_t* qg = qs + (size_t)(i0 >> 4) * grp_bytes;          // gate rows i0 .. i0+15
   const uint8_t* qu = qs + (size_t)((Iw + i0) >> 4) * grp_bytes;   // up rows Iw+i0 ..
@@ -148,6 +175,7 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
   float accg = 0.f, accu = 0.f;
   for (int tb = tw0; tb < tw1; tb += kGemvTiles) {
     MOE_GU_LOAD(tb);
+    rank_write();  // the slot order and weights while this batch of weights is in flight
 #pragma unroll
     for (int j = 0; j < kGemvTiles; ++j) {
       const int b = 4 * (tb + j) + G;  // the block this lane owns in tile tb + j
@@ -174,6 +202,7 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
     }
   }
 #undef MOE_GU_LOAD
+  rank_write();  // a wavefront without K tiles of its own
   // sum over G (lanes n, n+16, n+32, n+48), then over the 4 quarters in order
   accg += __shfl_xor(accg, 16, kWave);
   accu += __shfl_xor(accu, 16, kWave);

@@ -41,14 +41,12 @@ struct TopkLds {  // one wavefront's staging: the chosen entries in id order, th
 
 __device__ __forceinline__ int popc(uint64_t m) { return __builtin_popcountll(m); }
 
-// Selection for one token by one wavefront: writes ids[0..k) and w[0..k) (unless write is false) and
-// leaves the ids and scores in slot order in sm.slot_id / sm.slot_s.  The lanes exchange entries
-// through LDS, with wave_lds_sync between each write and the reads of other lanes.
+// The chosen set of one token, by one wavefront: bit l of chosen[i] set when expert l + 64 i is among the k
+// chosen (exactly k bits over all registers); key[i] / sc[i] are lane l's keys and sigmoid scores.
 template <int NPER, int NPARTS>
-__device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t part_stride,
-                                          const float* __restrict__ bias, int32_t* __restrict__ ids,
-                                          float* __restrict__ w, int E, int k, int lane, TopkLds& sm,
-                                          bool write = true) {
+__device__ __forceinline__ void topk_chosen(const float* __restrict__ lrow, size_t part_stride,
+                                            const float* __restrict__ bias, int E, int k, int lane,
+                                            uint64_t (&chosen)[NPER], uint32_t (&key)[NPER], float (&sc)[NPER]) {
   // every load first, from clamped indices: one memory round trip
   float lg[NPARTS][NPER], bs[NPER];
 #pragma unroll
@@ -58,8 +56,6 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t
 #pragma unroll
     for (int p = 0; p < NPARTS; ++p) lg[p][i] = lrow[p * part_stride + e];
   }
-  uint32_t key[NPER];
-  float sc[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     float l = lg[0][i];
@@ -87,7 +83,6 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t
     tau = cnt > k ? cand : tau;
   }
   // chosen: every key above tau (fewer than k), then the lowest ids among the keys equal to tau
-  uint64_t chosen[NPER];
   int need = k;
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
@@ -104,6 +99,49 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t
       --need;
     }
   }
+}
+
+// Expert id of the j-th chosen expert (0 <= j < k) in id order.
+template <int NPER>
+__device__ __forceinline__ int topk_nth_chosen(const uint64_t (&chosen)[NPER], int j) {
+  int e = 0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int c = popc(chosen[i]);
+    if (j >= 0 && j < c) {
+      uint64_t m = chosen[i];
+      for (int q = 0; q < j; ++q) m &= m - 1u;  // drop the j lowest set bits
+      e = 64 * i + (int)__builtin_ctzll(m);
+    }
+    j -= c;
+  }
+  return e;
+}
+
+// Slot (0 .. k-1: rank by descending key, equal keys by ascending id) of the chosen expert e.
+template <int NPER>
+__device__ __forceinline__ int topk_slot_of(const uint64_t (&chosen)[NPER], const uint32_t (&key)[NPER], int e,
+                                            int lane) {
+  uint32_t ke = 0u;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i)  // uniform branches: e is the same in every lane
+    if (e / 64 == i) ke = (uint32_t)__builtin_amdgcn_readlane((int)key[i], e % 64);
+  int slot = 0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int id = lane + 64 * i;
+    slot += popc(chosen[i] & __builtin_amdgcn_ballot_w64(key[i] > ke || (key[i] == ke && id < e)));
+  }
+  return slot;
+}
+
+// The slot order of a chosen set (topk_chosen) and the weights: writes ids[0..k) and w[0..k) (unless
+// write is false) and leaves the ids and scores in slot order in sm.slot_id / sm.slot_s.  The lanes
+// exchange entries through LDS, with wave_lds_sync between each write and the reads of other lanes.
+template <int NPER>
+__device__ __forceinline__ void topk_rank_write(const uint64_t (&chosen)[NPER], const uint32_t (&key)[NPER],
+                                                const float (&sc)[NPER], int32_t* __restrict__ ids,
+                                                float* __restrict__ w, int k, int lane, TopkLds& sm, bool write) {
   // compact the k chosen entries into LDS in id order
   int base = 0;
 #pragma unroll
@@ -146,6 +184,20 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t
     w[lane] = my_s / tot;
   }
   wave_lds_sync();  // callers read sm.slot_id / sm.slot_s in any lane
+}
+
+// Selection for one token by one wavefront: writes ids[0..k) and w[0..k) (unless write is false) and
+// leaves the ids and scores in slot order in sm.slot_id / sm.slot_s.
+template <int NPER, int NPARTS>
+__device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, size_t part_stride,
+                                          const float* __restrict__ bias, int32_t* __restrict__ ids,
+                                          float* __restrict__ w, int E, int k, int lane, TopkLds& sm,
+                                          bool write = true) {
+  uint64_t chosen[NPER];
+  uint32_t key[NPER];
+  float sc[NPER];
+  topk_chosen<NPER, NPARTS>(lrow, part_stride, bias, E, k, lane, chosen, key, sc);
+  topk_rank_write<NPER>(chosen, key, sc, ids, w, k, lane, sm, write);
 }
 
 }  // namespace moe
