@@ -98,21 +98,12 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
   bool rank_pending = false;
   __shared__ TopkLds tsm;
   if constexpr (NPER > 0) {
-    __shared__ int sel[2];
-    if (routed && wave == 0) {
-      topk_chosen<NPER, 1>(logits + (size_t)t * E, 0, bias, E, k, lane, chosen, key, ssc);
-      const int ej = topk_nth_chosen<NPER>(chosen, job % k);
-      const int sj = topk_slot_of<NPER>(chosen, key, ej, lane);
-      if (lane == 0) {
-        sel[0] = ej;
-        sel[1] = sj;
-      }
-      rank_pending = blockIdx.x == 0 && job % k == 0;
-    }
-    __syncthreads();
+    // every wavefront finds the chosen set itself (the same bits in each), so no barrier hands it over
     if (routed) {
-      e = __builtin_amdgcn_readfirstlane(sel[0]);
-      hslot = __builtin_amdgcn_readfirstlane(sel[1]);
+      topk_chosen<NPER, 1>(logits + (size_t)t * E, 0, bias, E, k, lane, chosen, key, ssc);
+      e = __builtin_amdgcn_readfirstlane(topk_nth_chosen<NPER>(chosen, job % k));
+      hslot = __builtin_amdgcn_readfirstlane(topk_slot_of<NPER>(chosen, key, e, lane));
+      rank_pending = wave == 0 && blockIdx.x == 0 && job % k == 0;
     }
   } else {
     if (routed) e = ids[job];
