@@ -250,23 +250,26 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
   const int t = blockIdx.y;
   const int n0 = blockIdx.x * 16;  // one 16-row group (d % 32 == 0: all rows valid)
   for (int slot = wave; slot <= k; slot += nw) {
+    // the slot's h first: its address does not depend on the expert id, so these loads are in flight
+    // while the id is read (lane l takes block l, clamped; blocks past nkb are never read; nkb <= 64 as
+    // I <= 2048)
+    const int Kw = slot < k ? I : Is;
+    const _Float16* h = slot < k ? h_r + ((size_t)t * k + slot) * I : h_s + (size_t)t * Is;
+    const int nkb = Kw / 32;
+    const int bl = min(lane, nkb - 1);
+    u32x4 hv[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) hv[g] = ld16(h + 32 * bl + 8 * g);
     const uint8_t* qs;
     const uint16_t* sc;
-    const _Float16* h;
-    int Kw;
     if (slot < k) {
       const int e = ids[(size_t)t * k + slot];
-      Kw = I;
       qs = w2.qs + (size_t)e * d * (I / 2);
       sc = w2.sc + (size_t)e * d * (I / 32);
-      h = h_r + ((size_t)t * k + slot) * I;
     } else {
-      Kw = Is;
       qs = s2.qs;
       sc = s2.sc;
-      h = h_s + (size_t)t * Is;
     }
-    const int nkb = Kw / 32;
     const int ntile = (nkb + 3) / 4;
     const uint8_t* qg = qs + (size_t)(n0 >> 4) * nkb * 256;
     const uint16_t* sg = sc + (size_t)(n0 >> 4) * nkb * 16;
@@ -283,13 +286,12 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
       dq[j] = sg[(size_t)b * 16 + n];                                          \
     }
     MOE_DN_LOAD(0);
-    // stage h: lane l takes block l (clamped; blocks past nkb are never read; nkb <= 64 as I <= 2048)
+    // stage h
     {
-      const int bl = min(lane, nkb - 1);
       float sa = 0.f, sb = 0.f;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        u32x4 v = ld16(h + 32 * bl + 8 * g);
+        u32x4 v = hv[g];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const half2v hv = as_half2(v[m]);
