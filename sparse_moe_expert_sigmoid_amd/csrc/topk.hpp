@@ -19,8 +19,13 @@ namespace moe {
 // candidate bit stays set when at least k keys are >= the candidate (one
 // ballot and popcount per key register), so the search costs at most 32
 // short steps whatever k is (it stops once a candidate splits off exactly k
-// keys).  The chosen experts are the keys above tau and, of the keys equal
-// to tau, the lowest ids (ties go to the lower id).  They are compacted
+// keys).  It starts below the bits that every contender shares: when at least
+// k keys lie at or above the binade below the largest key's, tau is among
+// them, so their common leading bits (AND and OR over the wavefront) are
+// tau's; for scores in (0, 1) that skips the sign and exponent steps.  The
+// scores come from the hardware exp2 and reciprocal (s = 1/2 exactly at a
+// zero logit).  The chosen experts are the keys above tau and, of the keys
+// equal to tau, the lowest ids (ties go to the lower id).  They are compacted
 // into LDS; each finds its slot by counting the chosen keys that rank before
 // it (a larger key, or an equal key and a lower id), and the weights are
 // normalised by the sum of the chosen scores taken in slot order.
@@ -40,6 +45,31 @@ struct TopkLds {  // one wavefront's staging: the chosen entries in id order, th
 };
 
 __device__ __forceinline__ int popc(uint64_t m) { return __builtin_popcountll(m); }
+
+// sigma(l) from v_exp_f32 and v_rcp_f32: exact at l = 0; the rounding of l * log2(e) sets the relative
+// error, about |l| * 6e-8 (1e-6 at |l| = 16)
+__device__ __forceinline__ float sigmoid_score(float l) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * l));
+}
+
+// max (OP 0), and (1) or or (2) of v over the wavefront, the same in every lane: four rotations within
+// each row of 16 lanes (every lane then holds its row's value), then the four rows combined
+template <int OP>
+__device__ __forceinline__ uint32_t u32_op(uint32_t a, uint32_t b) {
+  return OP == 0 ? (a > b ? a : b) : OP == 1 ? (a & b) : (a | b);
+}
+template <int OP>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+  v = u32_op<OP>(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));  // row_ror:1
+  v = u32_op<OP>(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));  // row_ror:2
+  v = u32_op<OP>(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+  v = u32_op<OP>(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return u32_op<OP>(u32_op<OP>(r0, r1), u32_op<OP>(r2, r3));
+}
 
 // The chosen set of one token, by one wavefront: bit l of chosen[i] set when expert l + 64 i is among the k
 // chosen (exactly k bits over all registers); key[i] / sc[i] are lane l's keys and sigmoid scores.
@@ -61,7 +91,7 @@ __device__ __forceinline__ void topk_chosen(const float* __restrict__ lrow, size
     float l = lg[0][i];
 #pragma unroll
     for (int p = 1; p < NPARTS; ++p) l += lg[p][i];  // partial logits, in order
-    sc[i] = sigmoidf_(l);
+    sc[i] = sigmoid_score(l);
     const uint32_t valid = lane + 64 * i < E ? 0xFFFFFFFFu : 0u;
     key[i] = ordered_bits(sc[i] + bs[i]) & valid;
   }
@@ -70,8 +100,39 @@ __device__ __forceinline__ void topk_chosen(const float* __restrict__ lrow, size
   // (the k-th largest key is >= it, the next one below it): the search stops there with tau just under
   // the candidate, so that the keys above tau are those k and no tie is left to break.
   uint32_t tau = 0u;
-#pragma unroll 4
-  for (int bit = 31; bit >= 0; --bit) {
+  int top = 31;  // the first bit the search decides
+  {
+    uint32_t m = key[0];
+#pragma unroll
+    for (int i = 1; i < NPER; ++i) m = max(m, key[i]);
+    const uint32_t M = wave_reduce_u32<0>(m);
+    // v0: the start of the binade below the largest key's (0 when that would leave the key range)
+    const uint32_t v0 = M >= 0x01000000u ? (M & 0xFF800000u) - 0x00800000u : 0u;
+    int n0 = 0;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) n0 += popc(__builtin_amdgcn_ballot_w64(key[i] >= v0));
+    if (n0 == k && v0 != 0u) {  // exactly k keys at or above v0: they are the k largest
+      tau = v0 - 1u;
+      top = -1;
+    } else if (n0 >= k) {  // tau >= v0: tau shares the leading bits of every key >= v0
+      uint32_t a = 0xFFFFFFFFu, o = 0u;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        const bool c = key[i] >= v0;
+        a &= c ? key[i] : 0xFFFFFFFFu;
+        o |= c ? key[i] : 0u;
+      }
+      const uint32_t A = wave_reduce_u32<1>(a), O = wave_reduce_u32<2>(o);
+      if (A == O) {  // every key >= v0 is the same value: that value is tau
+        tau = A;
+        top = -1;
+      } else {
+        top = 31 - __builtin_clz(A ^ O);
+        tau = top == 31 ? 0u : (A & ~((2u << top) - 1u));
+      }
+    }
+  }
+  for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = tau | (1u << bit);
     int cnt = 0;
 #pragma unroll

@@ -13,7 +13,7 @@ import torch
 import oracle
 import synth
 from sparse_moe_expert_sigmoid_amd import abi
-from sparse_moe_expert_sigmoid_amd.layer import Workspace, to_device
+from sparse_moe_expert_sigmoid_amd.layer import DeviceWeights, Workspace, layer_call_fused, to_device
 from gpu_util import MARGIN, W_ABS, say
 
 pytestmark = pytest.mark.gpu
@@ -72,6 +72,52 @@ def test_one_ulp_apart_at_the_kth_place(E, k, path, tie):
     ref_ids, _ = oracle.select_experts(s, inp["bias"], k)
     np.testing.assert_array_equal(ids, ref_ids)
     np.testing.assert_allclose(w, oracle.routing_weights(s, ref_ids), rtol=0, atol=W_ABS)
+
+
+def _search_bias(case: str, E: int, k: int, rng) -> np.ndarray:
+    """Biases that, with every score exactly 1/2, put the keys where each start of the search applies."""
+    if case == "all_equal":  # every key the same: the k lowest ids
+        return np.full(E, 0.125, dtype=np.float32)
+    if case == "k_high":  # exactly k keys in [1, 2) and the rest below 1/2: taken without a search step
+        b = -0.375 + rng.permutation(E) * 2.0 ** -12
+        b[rng.choice(E, size=k, replace=False)] = 0.75 + np.arange(k) * 2.0 ** -8
+        return b.astype(np.float32)
+    # one key in [4, 8) and every other below 1: fewer than k keys at or above 2, a search from the top bit
+    b = rng.permutation(E) * 2.0 ** -12 - 0.4375
+    b[rng.integers(E)] = 3.5
+    return b.astype(np.float32)
+
+
+SEARCH_SHAPES = [(20, 4), (64, 10), (256, 10), (1000, 16)]
+
+
+@pytest.mark.parametrize("case", ["all_equal", "k_high", "few_high"])
+@pytest.mark.parametrize("E,k", SEARCH_SHAPES, ids=[f"E{e}k{k}" for e, k in SEARCH_SHAPES])
+def test_search_starts(E, k, case):
+    # W_r = 0 (every score exactly 1/2, every key exact in fp32 and fp64).  The search for the k-th key
+    # starts from the leading bits shared by the keys at or above the binade below the largest one:
+    # all_equal leaves nothing to search, k_high has exactly k such keys, few_high too few (the search
+    # then starts at the top bit).  The top-k launch on both router paths and the selection inside the
+    # whole-layer call (small-T path) must give the oracle's ids, in slot order, and its weights.
+    dims = synth.Dims(T=6, d=128, E=E, k=k, I=64, I_shared=64)
+    inp = synth.make_inputs(dims, seed=31 + E + k)
+    rng = np.random.default_rng(E * 3 + k + len(case))
+    inp["w_router"] = np.zeros((E, dims.d), dtype=np.float32)
+    inp["bias"] = _search_bias(case, E, k, rng)
+    s = np.full((dims.T, E), 0.5)
+    ref_ids, _ = oracle.select_experts(s, inp["bias"], k)
+    ref_w = oracle.routing_weights(s, ref_ids)
+    for path, flags in PATHS.items():
+        say(f"[case] search start {case} E={E} k={k} {path}")
+        ids, w = route(inp, flags)
+        np.testing.assert_array_equal(ids, ref_ids)
+        np.testing.assert_allclose(w, ref_w, rtol=0, atol=W_ABS)
+    say(f"[case] search start {case} E={E} k={k} whole-layer call")
+    ws = Workspace(dims, 0)
+    layer_call_fused(to_device(inp["x"], "cuda"), DeviceWeights.upload(inp), ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ws.topk_ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(ws.topk_w.cpu().numpy(), ref_w, rtol=0, atol=W_ABS)
 
 
 @pytest.mark.parametrize("path", list(PATHS))
