@@ -55,6 +55,21 @@ static_assert(kMaxGemvBlocksPerWave == kWave, "activation staging gives every la
 // logits with one wavefront (the same selection as the top-k launch, so the same experts, order and
 // weights), and the workgroup of row group 0 and slot 0 writes the selection to ids and topk_w for
 // the down pass; this takes the top-k launch off the decode step.
+
+// v plus its value in lane l ^ 16 (XOR16) or l ^ 32: gfx950 lane swaps between rows / halves of the
+// wavefront, no LDS round trip.  The swap returns {first operand, second operand} after the exchange.
+template <int XOR>
+__device__ __forceinline__ float add_lane_xor(float v, int lane) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  if constexpr (XOR == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    return v + __builtin_bit_cast(float, ((lane >> 4) & 1) ? p[0] : p[1]);
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return v + __builtin_bit_cast(float, lane >= 32 ? p[0] : p[1]);
+  }
+}
+
 template <int NPER>
 __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict__ x, int32_t* __restrict__ ids,
                                                      Q4 w13, Q4 s13, _Float16* __restrict__ h_r, _Float16* __restrict__ h_s,
@@ -195,10 +210,10 @@ __global__ __launch_bounds__(256) void k_gemv_gateup(const uint16_t* __restrict_
 #undef MOE_GU_LOAD
   rank_write();  // a wavefront without K tiles of its own
   // sum over G (lanes n, n+16, n+32, n+48), then over the 4 quarters in order
-  accg += __shfl_xor(accg, 16, kWave);
-  accu += __shfl_xor(accu, 16, kWave);
-  accg += __shfl_xor(accg, 32, kWave);
-  accu += __shfl_xor(accu, 32, kWave);
+  accg = add_lane_xor<16>(accg, lane);
+  accu = add_lane_xor<16>(accu, lane);
+  accg = add_lane_xor<32>(accg, lane);
+  accu = add_lane_xor<32>(accu, lane);
   if (lane < 16) {
     red[wave][0][lane] = accg;
     red[wave][1][lane] = accu;
@@ -330,8 +345,8 @@ __global__ __launch_bounds__(1024) void k_gemv_down_combine(const int32_t* __res
       }
     }
 #undef MOE_DN_LOAD
-    acc += __shfl_xor(acc, 16, kWave);
-    acc += __shfl_xor(acc, 32, kWave);
+    acc = add_lane_xor<16>(acc, lane);
+    acc = add_lane_xor<32>(acc, lane);
     if (lane < 16) part[slot][lane] = clamp_f16_range(acc);  // each expert's output saturates as on the grouped path
   }
   __syncthreads();
